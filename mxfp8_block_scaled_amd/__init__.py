@@ -1,0 +1,22 @@
+"""MXFP8 dense linear layer for AMD Instinct MI355X (gfx950).
+
+The arithmetic lives in hand-written HIP kernels behind a C-ABI shared library
+(``libmxfp8.so``); this package is the thin Python binding over it.  Importing
+the package does not load the library; the first call does, and fails with an
+error if it has not been built.
+"""
+
+_API = (
+    "PreparedWeight", "linear", "prepare_weight", "quantize_act", "moe_grouped",
+    "mxfp8_quantize_act", "mxfp8_prepared_weight_bytes", "mxfp8_prepare_weight",
+    "mxfp8_unpack_weight", "mxfp8_linear_workspace_bytes", "mxfp8_linear",
+    "mxfp8_gemm_prequant", "mxfp8_moe_grouped", "mxfp8_moe_workspace_bytes",
+    "mxfp8_status_string", "MXFP8Error",
+)
+
+
+def __getattr__(name):
+    if name in _API:
+        from . import api
+        return getattr(api, name)
+    raise AttributeError(name)
