@@ -1,0 +1,147 @@
+/*
+ * mxfp8.h -- C ABI of libmxfp8.so, the MXFP8 dense linear layer (and its
+ * top-k routed MoE variant) for AMD Instinct MI355X (gfx950).
+ *
+ * The layer, as the pages define it ("[Kernel] Add FlashInfer TRTLLM MXFP8
+ * linear backend", vLLM PR #52204, §Purpose and the review of apply_weights):
+ *   1. BF16 activations are quantized on the fly to E4M3 elements with one
+ *      UE8M0 (power-of-two) scale per 32 elements along K;
+ *   2. the MXFP8 weight and its scales are prepared once after loading, with
+ *      N physically padded to a multiple of 128 and K a multiple of 256;
+ *   3. a block-scaled FP8 GEMM accumulates in fp32; the padded output is cut
+ *      back to the logical N, bias is added and the result is BF16.
+ * The quantization rule is the OCP Microscaling (MX) v1.0 conversion:
+ *   scale = 2^(floor(log2(max |v|)) - 8), elements round-to-nearest-even on
+ *   the E4M3 grid, saturated to +-448; an all-zero block gets scale byte 0.
+ *
+ * Conventions for every call:
+ *   - Tensor pointers are DEVICE pointers unless stated; sizes are elements.
+ *     E4M3 and UE8M0 data travel as raw bytes (uint8); BF16 as 16-bit words.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls only enqueue work on it: none allocates, none synchronizes, so
+ *     every call can be captured into a HIP graph.  The caller owns every
+ *     buffer, including workspaces and prepared weights.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     negative mxfp8_status is returned with nothing launched.  A launch
+ *     failure reported by the runtime is MXFP8_E_LAUNCH.  Faults inside a
+ *     kernel surface at the caller's next synchronization (HIP semantics).
+ *   - M == 0 is a valid no-op (returns MXFP8_OK, launches nothing).
+ */
+#ifndef MXFP8_H_
+#define MXFP8_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MXFP8_OK = 0,
+  MXFP8_E_NULLPTR = -1,   /* a required pointer is NULL */
+  MXFP8_E_SHAPE = -2,     /* a size is negative / zero where it must not be, or breaks K % 32, K % 256 */
+  MXFP8_E_ALIGN = -3,     /* a pointer is not aligned as documented */
+  MXFP8_E_LD = -4,        /* a leading dimension is too small or not a documented multiple */
+  MXFP8_E_WORKSPACE = -5, /* workspace NULL or smaller than the *_workspace_bytes query */
+  MXFP8_E_DEVICE = -6,    /* the current device is not gfx950, or no device */
+  MXFP8_E_LAUNCH = -7     /* the HIP runtime reported an error at launch */
+} mxfp8_status;
+
+/* Static, human readable text for a status code (never NULL). */
+const char* mxfp8_status_string(int status);
+
+/*
+ * Activation quantization (step 1 of the layer; the on-the-fly quantize of
+ * vLLM PR #52204 §Purpose).  For each row m and block b:
+ *   q[m, 32b .. 32b+31] = E4M3 elements, s[m, b] = UE8M0 scale byte.
+ * x_bf16 [M, K] row-major with row stride ldx (elements);
+ * q_e4m3 [M, K] bytes with row stride ldq; s_e8m0 [M, K/32] bytes, stride lds.
+ * Requires K % 32 == 0; ldx >= K, ldx % 8 == 0; ldq >= K, ldq % 8 == 0;
+ * lds >= K/32; x_bf16 and q_e4m3 16-byte aligned.
+ */
+int mxfp8_quantize_act(const void* x_bf16, int64_t M, int64_t K, int64_t ldx,
+                       void* q_e4m3, int64_t ldq, void* s_e8m0, int64_t lds,
+                       void* stream);
+
+/*
+ * Sizes in bytes of the prepared (packed) weight for a logical [N, K] MXFP8
+ * weight: *w_bytes = N_pad * K, *s_bytes = N_pad * K / 32, where
+ * N_pad = ceil(N / 128) * 128.  Host-only; requires N >= 1, K % 256 == 0.
+ */
+int mxfp8_prepared_weight_bytes(int64_t N, int64_t K, size_t* w_bytes, size_t* s_bytes);
+
+/*
+ * One-time weight preparation (step 2; process_weights_after_loading in the
+ * vLLM PR #52204 digest, "implementation breakdown": require K % 256 == 0,
+ * take the logical [:N, :K/32] scale region, pad N to a multiple of 128,
+ * reorder into the GEMM's layout).  Reads the MXFP8 weight as a checkpoint
+ * holds it:
+ *   w_e4m3   [N, K] bytes, row stride ldw (ldw >= K, ldw % 16 == 0, 16-byte aligned)
+ *   w_s_e8m0 [>= N, >= K/32] bytes, row stride ldws (ldws >= K/32), any alignment
+ * and writes w_packed (w_bytes) and s_packed (s_bytes), 256-byte aligned, in
+ * an opaque order owned by this library.  Pad rows N..N_pad-1 are zero
+ * elements with scale byte 127; they never reach the output.
+ */
+int mxfp8_prepare_weight(const void* w_e4m3, const void* w_s_e8m0, int64_t N, int64_t K,
+                         int64_t ldw, int64_t ldws, void* w_packed, void* s_packed,
+                         void* stream);
+
+/*
+ * Inverse of mxfp8_prepare_weight, for tests and tooling: writes the full
+ * padded weight w_e4m3 [N_pad, K] (contiguous) and w_s_e8m0 [N_pad, K/32]
+ * (contiguous).  Same size rules as mxfp8_prepare_weight.
+ */
+int mxfp8_unpack_weight(const void* w_packed, const void* s_packed, int64_t N, int64_t K,
+                        void* w_e4m3, void* w_s_e8m0, void* stream);
+
+/*
+ * Workspace bytes mxfp8_linear needs for this shape (host-only).  The
+ * workspace holds the quantized activations and split-K partial sums.  It
+ * must be zero-filled once when first allocated; every call leaves its
+ * counters back at zero.  Calls that share one workspace must be ordered on
+ * one stream (concurrent calls on one workspace race).
+ */
+int mxfp8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes);
+
+/*
+ * The MXFP8 dense linear layer (steps 1 + 3; apply_weights in vLLM PR
+ * #52204):  y[m, n] = bf16( sum_k deq(q(x))[m, k] * deq(W)[n, k] + bias[n] )
+ * for m < M, n < N, accumulated in fp32.
+ *   x_bf16    [M, K] row stride ldx (ldx >= K, ldx % 8 == 0, 16-byte aligned)
+ *   w_packed, s_packed  from mxfp8_prepare_weight for this (N, K)
+ *   bias_bf16 [N] or NULL
+ *   y_bf16    [M, N] row stride ldy (ldy >= N); columns >= N are not written
+ *   workspace >= mxfp8_linear_workspace_bytes(M, N, K), 256-byte aligned
+ * Requires K % 256 == 0, N >= 1.  Bias is added to the fp32 accumulator and
+ * the sum is rounded to bf16 once.
+ */
+int mxfp8_linear(const void* x_bf16, int64_t M, int64_t K, int64_t ldx,
+                 const void* w_packed, const void* s_packed, int64_t N,
+                 const void* bias_bf16, void* y_bf16, int64_t ldy,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The GEMM + epilogue on already quantized activations (step 3 alone; the
+ * mm_mxfp8 call of vLLM PR #52204's apply_weights):
+ *   q_e4m3 [M, K] row stride ldq (ldq % 16 == 0, 16-byte aligned),
+ *   s_e8m0 [M, K/32] row stride lds (lds % 4 == 0, 4-byte aligned),
+ * other arguments as mxfp8_linear.  Needs no workspace.
+ */
+int mxfp8_gemm_prequant(const void* q_e4m3, int64_t ldq, const void* s_e8m0, int64_t lds,
+                        int64_t M, int64_t K, const void* w_packed, const void* s_packed,
+                        int64_t N, const void* bias_bf16, void* y_bf16, int64_t ldy,
+                        void* stream);
+
+/*
+ * Test hook: force the GEMM path of mxfp8_linear (0 = automatic by shape,
+ * 1 = large-tile path, 2 = skinny path).  Process-wide; returns the previous
+ * value, or MXFP8_E_SHAPE for an unknown path.
+ */
+int mxfp8_debug_force_path(int path);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP8_H_ */

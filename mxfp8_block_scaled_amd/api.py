@@ -1,0 +1,263 @@
+"""Thin Python binding over libmxfp8.so (ctypes).
+
+Argument marshalling only: torch tensors supply device memory and the current
+HIP stream; every step of the layer runs in the library's HIP kernels.  If the
+library has not been built, the first call raises ``MXFP8Error``; there is no
+fallback.
+
+Names mirror the C ABI (include/mxfp8.h): ``mxfp8_quantize_act``,
+``mxfp8_prepare_weight``, ``mxfp8_linear``, ... take raw pointers and sizes;
+``quantize_act``, ``prepare_weight`` and ``linear`` are the tensor-level
+wrappers (the apply path of vLLM PR #52204: assert bf16, view the input as
+``[-1, K]``, run the layer, restore the leading dims).
+"""
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmxfp8.so")
+_lib = None
+_lock = threading.Lock()
+
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+_sz = ctypes.c_size_t
+
+_SIGNATURES = {
+    "mxfp8_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "mxfp8_quantize_act": ([_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp], ctypes.c_int),
+    "mxfp8_prepared_weight_bytes": ([_i64, _i64, ctypes.POINTER(_sz), ctypes.POINTER(_sz)], ctypes.c_int),
+    "mxfp8_prepare_weight": ([_vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
+    "mxfp8_unpack_weight": ([_vp, _vp, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
+    "mxfp8_linear_workspace_bytes": ([_i64, _i64, _i64, ctypes.POINTER(_sz)], ctypes.c_int),
+    "mxfp8_linear": ([_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _sz, _vp], ctypes.c_int),
+    "mxfp8_gemm_prequant": ([_vp, _i64, _vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp],
+                            ctypes.c_int),
+    "mxfp8_debug_force_path": ([ctypes.c_int], ctypes.c_int),
+}
+
+
+class MXFP8Error(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = lib().mxfp8_status_string(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{where}: {msg} (status {status})")
+
+
+def lib_path():
+    return _LIB_PATH
+
+
+def lib():
+    """Load libmxfp8.so once; raise if it is missing."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(_LIB_PATH):
+                    raise RuntimeError(
+                        f"libmxfp8.so not built at {_LIB_PATH}; run "
+                        "`python -m mxfp8_block_scaled_amd.build` (hipcc, gfx950)")
+                handle = ctypes.CDLL(_LIB_PATH)
+                for name, (args, res) in _SIGNATURES.items():
+                    fn = getattr(handle, name)
+                    fn.argtypes = args
+                    fn.restype = res
+                _lib = handle
+    return _lib
+
+
+def _check(status, where):
+    if status != 0:
+        raise MXFP8Error(status, where)
+
+
+def _stream(device=None):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+# ---------------------------------------------------------------------------
+# Raw C-ABI mirrors (pointers are ints or None; stream is an int handle)
+# ---------------------------------------------------------------------------
+
+def mxfp8_status_string(status):
+    return lib().mxfp8_status_string(status).decode()
+
+
+def mxfp8_quantize_act(x, M, K, ldx, q, ldq, s, lds, stream):
+    return lib().mxfp8_quantize_act(x, M, K, ldx, q, ldq, s, lds, stream)
+
+
+def mxfp8_prepared_weight_bytes(N, K):
+    w, s = _sz(), _sz()
+    _check(lib().mxfp8_prepared_weight_bytes(N, K, ctypes.byref(w), ctypes.byref(s)),
+           "mxfp8_prepared_weight_bytes")
+    return w.value, s.value
+
+
+def mxfp8_prepare_weight(w, ws, N, K, ldw, ldws, wp, sp, stream):
+    return lib().mxfp8_prepare_weight(w, ws, N, K, ldw, ldws, wp, sp, stream)
+
+
+def mxfp8_unpack_weight(wp, sp, N, K, w, ws, stream):
+    return lib().mxfp8_unpack_weight(wp, sp, N, K, w, ws, stream)
+
+
+def mxfp8_linear_workspace_bytes(M, N, K):
+    b = _sz()
+    _check(lib().mxfp8_linear_workspace_bytes(M, N, K, ctypes.byref(b)), "mxfp8_linear_workspace_bytes")
+    return b.value
+
+
+def mxfp8_linear(x, M, K, ldx, wp, sp, N, bias, y, ldy, ws, ws_bytes, stream):
+    return lib().mxfp8_linear(x, M, K, ldx, wp, sp, N, bias, y, ldy, ws, ws_bytes, stream)
+
+
+def mxfp8_gemm_prequant(q, ldq, s, lds, M, K, wp, sp, N, bias, y, ldy, stream):
+    return lib().mxfp8_gemm_prequant(q, ldq, s, lds, M, K, wp, sp, N, bias, y, ldy, stream)
+
+
+def mxfp8_debug_force_path(path):
+    return lib().mxfp8_debug_force_path(path)
+
+
+# ---------------------------------------------------------------------------
+# Tensor-level API
+# ---------------------------------------------------------------------------
+
+def _require_cuda(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
+def quantize_act(x):
+    """bf16 ``x[M, K]`` (GPU) -> (E4M3 bytes uint8 ``[M, K]``, UE8M0 bytes uint8 ``[M, K/32]``)."""
+    assert x.dtype == torch.bfloat16, f"MXFP8 quantization takes bfloat16, got {x.dtype}"
+    _require_cuda(x, "x")
+    x2 = x.reshape(-1, x.shape[-1])
+    if x2.stride(-1) != 1:
+        x2 = x2.contiguous()
+    M, K = x2.shape
+    q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    s = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+    _check(mxfp8_quantize_act(_ptr(x2), M, K, x2.stride(0), _ptr(q), K, _ptr(s), K // 32,
+                              _stream(x.device)), "mxfp8_quantize_act")
+    return q, s
+
+
+class PreparedWeight:
+    """An MXFP8 weight after the one-time preparation: packed payload and
+    scales (opaque layout, N padded to 128) plus the logical output size."""
+
+    def __init__(self, w_packed, s_packed, N, K):
+        self.w_packed = w_packed
+        self.s_packed = s_packed
+        self.N = N
+        self.K = K
+
+    @property
+    def device(self):
+        return self.w_packed.device
+
+    def unpack(self):
+        """(E4M3 ``[N_pad, K]``, UE8M0 ``[N_pad, K/32]``) as uint8 tensors."""
+        n_pad = (self.N + 127) // 128 * 128
+        w = torch.empty((n_pad, self.K), dtype=torch.uint8, device=self.device)
+        s = torch.empty((n_pad, self.K // 32), dtype=torch.uint8, device=self.device)
+        _check(mxfp8_unpack_weight(_ptr(self.w_packed), _ptr(self.s_packed), self.N, self.K, _ptr(w), _ptr(s),
+                                   _stream(self.device)), "mxfp8_unpack_weight")
+        return w, s
+
+
+def _as_bytes(t):
+    return t.view(torch.uint8) if t.dtype != torch.uint8 else t
+
+
+def prepare_weight(w_q, w_s):
+    """MXFP8 weight ``w_q`` E4M3 ``[N, K]`` (uint8 or float8_e4m3fn) with UE8M0
+    scales ``w_s`` ``[>= N, >= K/32]`` (uint8) -> PreparedWeight."""
+    w_q = _as_bytes(w_q)
+    w_s = _as_bytes(w_s)
+    _require_cuda(w_q, "w_q")
+    N, K = w_q.shape
+    if w_q.stride(-1) != 1:
+        w_q = w_q.contiguous()
+    if w_s.stride(-1) != 1:
+        w_s = w_s.contiguous()
+    wb, sb = mxfp8_prepared_weight_bytes(N, K)
+    wp = torch.empty(wb, dtype=torch.uint8, device=w_q.device)
+    sp = torch.empty(sb, dtype=torch.uint8, device=w_q.device)
+    _check(mxfp8_prepare_weight(_ptr(w_q), _ptr(w_s), N, K, w_q.stride(0), w_s.stride(0), _ptr(wp), _ptr(sp),
+                                _stream(w_q.device)), "mxfp8_prepare_weight")
+    return PreparedWeight(wp, sp, N, K)
+
+
+_workspaces = {}
+
+
+def workspace(M, N, K, device):
+    """A zero-initialised workspace big enough for (M, N, K), cached per
+    device and grown on demand (allocation happens here, never in the library)."""
+    need = mxfp8_linear_workspace_bytes(M, N, K)
+    key = torch.device(device).index if torch.device(device).index is not None else torch.cuda.current_device()
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def linear(x, pw, bias=None, out=None):
+    """The MXFP8 dense linear layer: ``y = bf16(deq(q(x)) @ deq(W).T + bias)``.
+
+    ``x`` bf16 ``[..., K]`` (GPU), ``pw`` a PreparedWeight, ``bias`` bf16 ``[N]``
+    or None.  Returns bf16 ``[..., N]`` (contiguous)."""
+    assert x.dtype == torch.bfloat16, f"MXFP8 linear requires bfloat16 activations, got {x.dtype}"
+    _require_cuda(x, "x")
+    K = pw.K
+    lead = x.shape[:-1]
+    x2 = x.reshape(-1, K)
+    if x2.stride(-1) != 1 or x2.stride(0) % 8 != 0 or x2.data_ptr() % 16 != 0:
+        x2 = x2.contiguous()
+    M = x2.shape[0]
+    N = pw.N
+    if bias is not None:
+        assert bias.dtype == torch.bfloat16 and bias.numel() == N
+        bias = bias.contiguous()
+    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    ws = workspace(M, N, K, x.device)
+    _check(mxfp8_linear(_ptr(x2), M, K, x2.stride(0), _ptr(pw.w_packed), _ptr(pw.s_packed), N, _ptr(bias),
+                        _ptr(y), y.stride(0), _ptr(ws), ws.numel(), _stream(x.device)), "mxfp8_linear")
+    return y.view(*lead, N)
+
+
+def gemm_prequant(q, s, pw, bias=None):
+    """The GEMM + epilogue on already quantized activations ``q`` [M, K] /
+    ``s`` [M, K/32] (uint8, GPU)."""
+    M, K = q.shape
+    N = pw.N
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=q.device)
+    _check(mxfp8_gemm_prequant(_ptr(q), q.stride(0), _ptr(s), s.stride(0), M, K, _ptr(pw.w_packed),
+                               _ptr(pw.s_packed), N, _ptr(bias), _ptr(y), y.stride(0), _stream(q.device)),
+           "mxfp8_gemm_prequant")
+    return y
+
+
+def moe_grouped(*args, **kwargs):
+    raise NotImplementedError("the routed MoE entry point is not built yet")
+
+
+def mxfp8_moe_grouped(*args, **kwargs):
+    raise NotImplementedError("the routed MoE entry point is not built yet")
+
+
+def mxfp8_moe_workspace_bytes(*args, **kwargs):
+    raise NotImplementedError("the routed MoE entry point is not built yet")

@@ -1,0 +1,109 @@
+// Shared device/host helpers of libmxfp8: MX block quantization, the packed
+// weight layout, and the gfx950 scaled-MFMA operand conventions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxfp8 {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------------------
+// Packed weight layout (written once by the prepare kernel, read by both GEMM
+// paths).  N is padded to a multiple of 128 ("pad N to 128" in the
+// process_weights_after_loading step of vLLM PR #52204); K is a multiple of
+// 256.  The weight is cut into 128-row groups and 128-byte K steps:
+//
+//   W_p[g][ks] = 16 KiB tile: 128 rows x 8 chunks of 16 B; chunk c of row r
+//                sits at chunk slot r*8 + (c ^ (r & 7)) (an XOR swizzle so
+//                that eight consecutive rows reading the same logical chunk
+//                hit eight different 16-byte bank groups of LDS);
+//   S_p[g][ks] = 512 B: 128 rows x 4 UE8M0 bytes (the 4 MX blocks of the
+//                K step, in K order).
+//
+// A tile is one contiguous run of bytes, so a GEMM workgroup copies it to LDS
+// unchanged with direct global->LDS loads.
+// ---------------------------------------------------------------------------
+constexpr int kGroupRows = 128;
+constexpr int kStepK = 128;
+constexpr int kTileBytes = kGroupRows * kStepK;   // 16384
+constexpr int kTileScaleBytes = kGroupRows * 4;   // 512
+
+__host__ __device__ inline int swz_slot(int r, int c) { return r * 8 + (c ^ (r & 7)); }
+
+// ---------------------------------------------------------------------------
+// Scaled MFMA operand conventions on gfx950 (pinned by probes on the device):
+//
+// v_mfma_scale_f32_16x16x128_f8f6f4: lane l = i + 16 g (i = row/col index,
+//   g = 0..3).  Its 32 operand bytes are K [16g, 16g+16) followed by
+//   K [64+16g, 64+16g+16).  The UE8M0 scale of MX block b (K [32b, 32b+32))
+//   is taken from the scale register of lane i + 16 b (byte chosen by
+//   op_sel).  Result: lane l holds D[4g + j][i], j = 0..3.
+//
+// v_mfma_scale_f32_32x32x64_f8f6f4: lane l = i + 32 g (g = 0..1).  Operand
+//   bytes K [16g, 16g+16) then K [32+16g, 32+16g+16); the scale of block b
+//   comes from lane i + 32 b.  Result: lane l holds
+//   D[8 (r/4) + 4 g + (r%4)][i], r = 0..15.
+//
+// Format code 0 selects E4M3 for both operands.
+// ---------------------------------------------------------------------------
+
+// bf16 helpers (raw 16-bit words).
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16, round to nearest even (finite inputs; NaN kept as NaN).
+__device__ inline uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Magnitude bits (fp32 layout) of the two bf16 elements of a word.  Integer
+// order of these bit patterns equals the order of the magnitudes for every
+// finite value, so the block maximum can be taken on integers.
+__device__ inline uint32_t absmax_bits(uint32_t acc, uint32_t w) {
+  uint32_t lo = (w << 16) & 0x7FFF0000u;
+  uint32_t hi = w & 0x7FFF0000u;
+  return max(acc, max(lo, hi));
+}
+
+// UE8M0 scale byte of a block from the fp32 bits of its largest magnitude:
+// shared exponent floor(log2 amax) - 8, clamped at -127 (byte 0).  For a
+// normal fp32 amax the exponent field F gives floor(log2 amax) = F - 127, so
+// the byte is F - 127 - 8 + 127 = F - 8.  A zero or subnormal amax (F = 0)
+// lands on byte 0.  bf16 magnitudes have F <= 254, so the byte is <= 246.
+__device__ inline uint32_t mx_scale_byte(uint32_t amax_bits) {
+  int f = (int)(amax_bits >> 23);
+  return (uint32_t)max(f - 8, 0);
+}
+
+// 2^(-e_s) as fp32 for a scale byte s (e_s = s - 127): exponent field 254 - s,
+// always a normal number for s in [0, 246].
+__device__ inline float mx_inv_scale(uint32_t sbyte) { return __uint_as_float((254u - sbyte) << 23); }
+
+// Two bf16 elements (one word) -> two E4M3 bytes, scaled by 2^(-e_s) and
+// saturated to +-448; the hardware convert rounds to nearest even.  The
+// product is exact (power-of-two scaling; f32 denormals are kept).
+template <bool kHiWord>
+__device__ inline uint32_t cvt2(uint32_t w, float inv, uint32_t old) {
+  float a = __builtin_amdgcn_fmed3f(bf16_lo(w) * inv, -448.0f, 448.0f);
+  float b = __builtin_amdgcn_fmed3f(bf16_hi(w) * inv, -448.0f, 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, kHiWord);
+}
+
+// Four bf16 words (8 elements) -> two dwords of E4M3 bytes, in element order.
+__device__ inline void cvt8(const uint32_t* w, float inv, uint32_t* q) {
+  uint32_t d0 = cvt2<false>(w[0], inv, 0u);
+  d0 = cvt2<true>(w[1], inv, d0);
+  uint32_t d1 = cvt2<false>(w[2], inv, 0u);
+  d1 = cvt2<true>(w[3], inv, d1);
+  q[0] = d0;
+  q[1] = d1;
+}
+
+}  // namespace mxfp8

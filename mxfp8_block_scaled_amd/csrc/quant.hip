@@ -1,0 +1,63 @@
+// Activation quantization: bf16 [M, K] -> E4M3 [M, K] + UE8M0 [M, K/32].
+//
+// The on-the-fly activation quantize of "[Kernel] Add FlashInfer TRTLLM MXFP8
+// linear backend" (vLLM PR #52204, §Purpose), with the OCP MX conversion rule
+// (shared exponent floor(log2 amax) - 8, RNE, saturate to +-448) and the
+// linear row-major scale layout.
+//
+// HBM-bound: 2 bytes read + 1 + 1/32 bytes written per element.  Four
+// consecutive lanes own one 32-element block, each loading 16 contiguous
+// bytes (8 elements), so a wave's loads cover 1 KiB of one or more rows
+// without gaps; the block maximum is combined across the four lanes with two
+// lane exchanges, and each lane writes its 8 E4M3 bytes as one 8-byte store.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace mxfp8 {
+
+template <typename Idx>
+__global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restrict__ x, int64_t ldx,
+                                                        Idx chunks_per_row, Idx total,
+                                                        uint8_t* __restrict__ q, int64_t ldq,
+                                                        uint8_t* __restrict__ s, int64_t lds) {
+  Idx t = (Idx)blockIdx.x * 256 + threadIdx.x;
+  const bool valid = t < total;
+  // Threads past the end come in whole groups of four (total and the block
+  // size are multiples of 4), so they only exchange among themselves.
+  if (!valid) t = total - 1;
+  const Idx row = t / chunks_per_row;
+  const Idx c8 = t - row * chunks_per_row;
+  const uint4 v = *reinterpret_cast<const uint4*>(x + (int64_t)row * ldx + (int64_t)c8 * 8);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m = absmax_bits(m, w[i]);
+  m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+  const uint32_t sb = mx_scale_byte(m);
+  uint32_t qd[2];
+  cvt8(w, mx_inv_scale(sb), qd);
+  if (valid) {
+    *reinterpret_cast<uint2*>(q + (int64_t)row * ldq + (int64_t)c8 * 8) = make_uint2(qd[0], qd[1]);
+    if ((c8 & 3) == 0) s[(int64_t)row * lds + (int64_t)(c8 >> 2)] = (uint8_t)sb;
+  }
+}
+
+int launch_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx, void* q, int64_t ldq, void* s,
+                        int64_t lds, hipStream_t stream) {
+  const int64_t per_row = K / 8;
+  const int64_t total = M * per_row;
+  const int64_t blocks = (total + 255) / 256;
+  if (total < ((int64_t)1 << 32)) {
+    hipLaunchKernelGGL(quant_act_kernel<uint32_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const uint16_t*)x, ldx, (uint32_t)per_row, (uint32_t)total, (uint8_t*)q, ldq,
+                       (uint8_t*)s, lds);
+  } else {
+    hipLaunchKernelGGL(quant_act_kernel<uint64_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const uint16_t*)x, ldx, (uint64_t)per_row, (uint64_t)total, (uint8_t*)q, ldq,
+                       (uint8_t*)s, lds);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+}  // namespace mxfp8

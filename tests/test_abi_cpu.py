@@ -1,0 +1,107 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects invalid arguments before touching a device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from mxfp8_block_scaled_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxfp8.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(api.lib_path()), reason="libmxfp8.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mxfp8_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert "mxfp8_linear" in names and "mxfp8_quantize_act" in names
+    handle = ctypes.CDLL(api.lib_path())
+    for n in names:
+        assert hasattr(handle, n), n
+
+
+def test_status_strings():
+    for s in range(0, -8, -1):
+        assert api.mxfp8_status_string(s)
+    assert api.mxfp8_status_string(-99) == "unknown status"
+
+
+def test_prepared_weight_bytes():
+    assert api.mxfp8_prepared_weight_bytes(130, 256) == (256 * 256, 256 * 8)
+    assert api.mxfp8_prepared_weight_bytes(4096, 4096) == (4096 * 4096, 4096 * 128)
+    with pytest.raises(api.MXFP8Error):
+        api.mxfp8_prepared_weight_bytes(130, 224)
+    with pytest.raises(api.MXFP8Error):
+        api.mxfp8_prepared_weight_bytes(0, 256)
+
+
+P = 0x10000  # a fake, 256-byte aligned "device" address; never dereferenced
+
+
+def test_quantize_validation():
+    f = api.mxfp8_quantize_act
+    assert f(P, 4, 48, 48, P, 48, P, 2, None) == -2         # K % 32
+    assert f(P, -1, 64, 64, P, 64, P, 2, None) == -2        # M < 0
+    assert f(P, 0, 64, 64, P, 64, P, 2, None) == 0          # empty: no-op
+    assert f(None, 4, 64, 64, P, 64, P, 2, None) == -1
+    assert f(P, 4, 64, 32, P, 64, P, 2, None) == -4         # ldx < K
+    assert f(P, 4, 64, 68, P, 64, P, 2, None) == -4         # ldx % 8
+    assert f(P, 4, 64, 64, P, 64, P, 1, None) == -4         # lds < K/32
+    assert f(P + 8, 4, 64, 64, P, 64, P, 2, None) == -3     # x alignment
+    assert f(P, 4, 64, 64, P, 64, P, 2, None) == -6         # valid, but no gfx950 device here
+
+
+def test_prepare_validation():
+    f = api.mxfp8_prepare_weight
+    assert f(P, P, 130, 224, 224, 7, P, P, None) == -2      # K % 256
+    assert f(P, P, 0, 256, 256, 8, P, P, None) == -2
+    assert f(None, P, 130, 256, 256, 8, P, P, None) == -1
+    assert f(P, P, 130, 256, 256, 8, None, P, None) == -1
+    assert f(P, P, 130, 256, 255, 8, P, P, None) == -4
+    assert f(P, P, 130, 256, 256, 7, P, P, None) == -4
+    assert f(P, P, 130, 256, 256, 8, P + 16, P, None) == -3
+    assert f(P, P, 130, 256, 256, 8, P, P, None) == -6
+
+
+def test_linear_validation():
+    f = api.mxfp8_linear
+    ws = api.mxfp8_linear_workspace_bytes(512, 130, 256)
+    assert ws >= 512 * 256 + 512 * 8
+    ok = (P, 512, 256, 256, P, P, 130, None, P, 130, P, ws, None)
+    assert f(*ok) == -6
+    bad = list(ok); bad[2] = 320; assert f(*bad) == -2          # K % 256
+    bad = list(ok); bad[6] = 0; assert f(*bad) == -2            # N < 1
+    bad = list(ok); bad[1] = -3; assert f(*bad) == -2
+    bad = list(ok); bad[1] = 0; assert f(*bad) == 0             # M == 0 no-op
+    bad = list(ok); bad[0] = None; assert f(*bad) == -1
+    bad = list(ok); bad[8] = None; assert f(*bad) == -1
+    bad = list(ok); bad[9] = 129; assert f(*bad) == -4          # ldy < N
+    bad = list(ok); bad[3] = 200; assert f(*bad) == -4          # ldx < K
+    bad = list(ok); bad[10] = None; assert f(*bad) == -5
+    bad = list(ok); bad[11] = ws - 1; assert f(*bad) == -5
+    bad = list(ok); bad[4] = P + 64; assert f(*bad) == -3       # packed weight alignment
+    bad = list(ok); bad[0] = P + 2; assert f(*bad) == -3
+
+
+def test_gemm_prequant_validation():
+    f = api.mxfp8_gemm_prequant
+    ok = (P, 256, P, 8, 64, 256, P, P, 130, None, P, 130, None)
+    assert f(*ok) == -6
+    bad = list(ok); bad[1] = 264; assert f(*bad) == -4          # ldq % 16
+    bad = list(ok); bad[3] = 6; assert f(*bad) == -4            # lds % 4
+    bad = list(ok); bad[2] = P + 2; assert f(*bad) == -3
+
+
+def test_force_path_hook():
+    prev = api.mxfp8_debug_force_path(1)
+    assert api.mxfp8_debug_force_path(prev) == 1
+    assert api.mxfp8_debug_force_path(7) == -2

@@ -1,0 +1,212 @@
+"""The MXFP8 linear layer on the GPU vs the oracle (tolerance derived in
+tests/gpu_util.py), plus exact pins, layout round trip, path agreement and
+HIP-graph replay."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mxfp8_block_scaled_amd import api, synth
+from tests import gpu_util
+
+pytestmark = pytest.mark.gpu
+
+
+def test_prepare_unpack_roundtrip():
+    g = torch.Generator().manual_seed(2)
+    for N, K in [(130, 256), (256, 512), (1, 768), (300, 1024)]:
+        print("CASE roundtrip", N, K, flush=True)
+        wq = torch.randint(0, 256, (N, K), generator=g, dtype=torch.uint8)
+        ws = torch.randint(0, 256, (N + 3, K // 32 + 5), generator=g, dtype=torch.uint8)  # larger, strided
+        pw = api.prepare_weight(wq.to(gpu_util.dev()), ws.to(gpu_util.dev()))
+        w2, s2 = pw.unpack()
+        torch.cuda.synchronize()
+        n_pad = (N + 127) // 128 * 128
+        assert w2.shape == (n_pad, K) and s2.shape == (n_pad, K // 32)
+        assert torch.equal(w2[:N].cpu(), wq)
+        assert torch.equal(s2[:N].cpu(), ws[:N, : K // 32])
+        assert bool((w2[N:] == 0).all()) and bool((s2[N:] == 127).all())
+
+
+@pytest.mark.parametrize("path", [1, 2])
+def test_one_hot_weight_exact(path):
+    """W[n, perm[n]] = 1: y[m, n] = bf16(deq(A)[m, perm[n]]) exactly (a single
+    nonzero term per output).  Pins the MFMA operand/scale lane mapping, the K
+    and N indexing, padding and zero-scale blocks, on both GEMM paths."""
+    M = 9 if path == 2 else 300
+    g = torch.Generator().manual_seed(4)
+    K, N = 512, 200
+    x = synth.scale_stress(synth.randn_bf16((M, K), 1.0, g), seed=8)
+    perm = torch.randint(0, K, (N,), generator=g)
+    w = torch.zeros(N, K, dtype=torch.bfloat16)
+    w[torch.arange(N), perm] = 1.0
+    pw = gpu_util.gpu_prepare(w)
+    prev = api.mxfp8_debug_force_path(path)
+    try:
+        y = api.linear(x.to(gpu_util.dev()), pw).float().cpu().numpy()
+    finally:
+        api.mxfp8_debug_force_path(prev)
+    qa, sa = oracle.quantize_mx(x.double().numpy())
+    deqa = oracle.dequantize_mx(qa, sa)
+    exp = oracle.bf16_round(deqa[:, perm.numpy()])
+    assert np.array_equal(y, exp)
+
+
+@pytest.mark.parametrize("path", [1, 2])
+def test_one_hot_activation_exact(path):
+    """x[m, perm[m]] = 1 (scale-stressed weight): y[m, n] = bf16(deq(W)[n, perm[m]] + bias[n])."""
+    M = 11 if path == 2 else 260
+    g = torch.Generator().manual_seed(6)
+    K, N = 768, 384
+    perm = torch.randint(0, K, (M,), generator=g)
+    x = torch.zeros(M, K, dtype=torch.bfloat16)
+    x[torch.arange(M), perm] = 1.0
+    w = synth.scale_stress(synth.randn_bf16((N, K), 0.02, g), seed=9)
+    bias = synth.randn_bf16((N,), 0.1, g)
+    pw = gpu_util.gpu_prepare(w)
+    prev = api.mxfp8_debug_force_path(path)
+    try:
+        y = api.linear(x.to(gpu_util.dev()), pw, bias.to(gpu_util.dev())).float().cpu().numpy()
+    finally:
+        api.mxfp8_debug_force_path(prev)
+    wq, ws = gpu_util.oracle_weight(w)
+    deqw = oracle.dequantize_mx(wq, ws)
+    # one fp32 add of the bias: exact here? compare after the same fp32 add + bf16 rounding
+    v = (deqw[:, perm.numpy()].T.astype(np.float32) + bias.float().numpy()[None, :]).astype(np.float64)
+    assert np.array_equal(y, oracle.bf16_round(v))
+
+
+def test_config1_single():
+    x, w, b = synth.config_inputs(1)
+    gpu_util.run_linear_and_check(x, w, b, "config1", force_path=0)
+    gpu_util.run_linear_and_check(x, w, b, "config1-tile", force_path=1)
+
+
+@pytest.mark.parametrize("M", [1, 7, 16, 128])
+def test_config2_decode(M):
+    x, w, b = synth.config_inputs(2, M)
+    gpu_util.run_linear_and_check(x, w, b, f"config2 M={M}")
+
+
+@pytest.mark.parametrize("M,N,K", [(m, n, k) for m in (1, 2, 3, 5, 15, 16, 17, 33, 127, 128, 129, 257)
+                                   for n, k in ((1, 256), (130, 512), (255, 768), (384, 256))])
+def test_edge_grid(M, N, K):
+    g = torch.Generator().manual_seed(M * 1000 + N + K)
+    x = synth.scale_stress(synth.randn_bf16((M, K), 1.0, g), seed=M + 1)
+    w = synth.scale_stress(synth.randn_bf16((N, K), 0.02, g), seed=N + 2)
+    b = synth.randn_bf16((N,), 0.1, g) if (M + N) % 2 else None
+    gpu_util.run_linear_and_check(x, w, b, f"edge {M}x{N}x{K}")
+
+
+def test_skinny_and_tile_paths_agree():
+    """Same inputs through both GEMM paths: each within the bound of the
+    oracle; their difference stays within the sum of the two bounds."""
+    for M in (1, 5, 16):
+        x, w, b = synth.config_inputs(2, M)
+        s1 = gpu_util.run_linear_and_check(x, w, b, f"skinny M={M}", force_path=2)
+        s2 = gpu_util.run_linear_and_check(x, w, b, f"tile M={M}", force_path=1)
+        assert s1["over_bound"] == 0 and s2["over_bound"] == 0
+
+
+def test_prequant_entry_matches_linear():
+    g = torch.Generator().manual_seed(3)
+    x = synth.randn_bf16((300, 512), 1.0, g).to(gpu_util.dev())
+    w = synth.randn_bf16((260, 512), 0.02, g)
+    b = synth.randn_bf16((260,), 0.1, g).to(gpu_util.dev())
+    pw = gpu_util.gpu_prepare(w)
+    q, s = api.quantize_act(x)
+    y1 = api.gemm_prequant(q, s, pw, b)
+    y2 = api.linear(x, pw, b)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
+def test_deterministic_repeat():
+    x, w, b = synth.config_inputs(2, 16)
+    pw = gpu_util.gpu_prepare(w)
+    xs, bs = x.to(gpu_util.dev()), b.to(gpu_util.dev())
+    ys = [api.linear(xs, pw, bs) for _ in range(3)]
+    torch.cuda.synchronize()
+    assert all(torch.equal(ys[0], y) for y in ys[1:])
+
+
+def test_leading_dims_and_output_contiguity():
+    g = torch.Generator().manual_seed(9)
+    x = synth.randn_bf16((2, 3, 256), 1.0, g).to(gpu_util.dev())
+    w = synth.randn_bf16((130, 256), 0.02, g)
+    pw = gpu_util.gpu_prepare(w)
+    y = api.linear(x, pw)
+    assert y.shape == (2, 3, 130) and y.is_contiguous()
+    y2 = api.linear(x.reshape(6, 256), pw)
+    torch.cuda.synchronize()
+    assert torch.equal(y.reshape(6, 130), y2)
+
+
+def test_hip_graph_replay_matches_eager():
+    """The layer captured into a HIP graph and replayed several times, with
+    eager work in between, matches the eager result every time (vLLM PR
+    #52204 tested CUDA-graph capture and replay the same way)."""
+    for M in (7, 300):
+        x, w, b = synth.config_inputs(1) if M == 7 else synth.linear_inputs(M, 640, 512, seed=4)
+        pw = gpu_util.gpu_prepare(w)
+        xs = x.to(gpu_util.dev())
+        bs = None if b is None else b.to(gpu_util.dev())
+        eager = api.linear(xs, pw, bs).clone()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            api.linear(xs, pw, bs)        # warm the workspace outside the capture
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            out = api.linear(xs, pw, bs)
+        for it in range(4):
+            out.zero_()
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, eager), (M, it)
+            _ = api.linear(xs, pw, bs)    # eager work between replays
+            torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("shape", [(1, 130, 256), (7, 256, 512), (128, 130, 768)])
+def test_pages_cosine_check(shape):
+    """vLLM PR #52204's own acceptance rule on its own shapes: seed 0, x and W
+    ~ N(0,1) bf16; cosine similarity with the unquantized product > 0.98;
+    output shape (m, n) and contiguous."""
+    torch.manual_seed(0)
+    m, n, k = shape
+    x = torch.randn((m, k), dtype=torch.bfloat16)
+    w = torch.randn((n, k), dtype=torch.bfloat16)
+    pw = gpu_util.gpu_prepare(w)
+    y = api.linear(x.to(gpu_util.dev()), pw)
+    ref = x.float() @ w.float().t()
+    cos = torch.nn.functional.cosine_similarity(y.float().cpu().flatten(), ref.flatten(), dim=0)
+    assert y.shape == (m, n) and y.is_contiguous()
+    assert cos.item() > 0.98
+
+
+@pytest.mark.parametrize("cfg", [3, 4])
+def test_full_size_sampled(cfg):
+    """Full-size configs in the launch configuration the bench times; the
+    oracle checks sampled rows x columns (quantization is row-local, so the
+    samples are exact sub-problems), including the last row and column."""
+    x, w, b = synth.config_inputs(cfg)
+    M, K = x.shape
+    N = w.shape[0]
+    print("CASE full", cfg, M, N, K, flush=True)
+    pw = gpu_util.gpu_prepare(w)
+    y = api.linear(x.to(gpu_util.dev()), pw, None if b is None else b.to(gpu_util.dev()))
+    torch.cuda.synchronize()
+    gen = torch.Generator().manual_seed(100 + cfg)
+    rows = torch.cat([torch.randperm(M, generator=gen)[:96], torch.tensor([0, M - 1])])
+    cols = torch.cat([torch.randperm(N, generator=gen)[:96], torch.tensor([0, N - 1])])
+    ys = y[rows.to(y.device)][:, cols.to(y.device)].float().cpu().numpy()
+    wq, ws = gpu_util.oracle_weight(w[cols])
+    xn = x[rows].to(torch.float64).numpy()
+    bn = None if b is None else b[cols].to(torch.float64).numpy()
+    r = oracle.linear_ref(xn, wq, ws, bn)
+    gpu_util.compare(ys, r, gpu_util.tolerance(xn, wq, ws, len(cols), K), f"config{cfg} sampled")
