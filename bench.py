@@ -1,0 +1,301 @@
+"""Benchmark of the MXFP8 dense linear layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep] [--no-cpu]
+
+Prints ONE JSON line.  The headline workload is the large compute-bound layer
+M=8192, N=28672, K=8192 (x ~ N(0,1), W ~ N(0,0.01) MXFP8, bf16 bias): a step is
+one pass of the whole hot path over that batch -- activation quantization
+(mxfp8_quantize_act) then the block-scaled GEMM with its bias/bf16 epilogue
+(mxfp8_gemm_prequant), the same two kernels mxfp8_linear launches for M > 16.
+The one-time weight preparation runs before the timed region.  ``value`` is
+2*M*N*K / step time in TFLOP/s, inputs resident in HBM.
+
+Also reported: ``roofline`` for the dominant kernel (the GEMM) from HIP events
+on the launch stream inside the timed region; ``sweep`` with the other
+workload shapes (M=7 single layer, the decode sweep M in {1,7,16,128} at
+N=K=4096 with the weights rotated through 48 copies so they do not sit in the
+256 MB last-level cache, the M=16384 prefill shape, and the standalone
+quantizer); ``cpu_baseline``, the CPU oracle timed on a bounded sample of the
+headline workload.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MFMA_FP8_TFLOPS = 5000.0   # MI355X dense FP8 / MXFP8 MFMA
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_tile_large.json")
+GEMM_SOURCES = ["mxfp8_block_scaled_amd/csrc/gemm_tile.hip", "mxfp8_block_scaled_amd/csrc/common.hpp"]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-sweep", action="store_true")
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--calib-copy", action="store_true",
+                   help="also run a plain 1 GiB device copy (for HBM counter calibration)")
+    return p.parse_args()
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(bytes_per_launch_expected):
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter runs, or
+    None if they were taken on a different version of the kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != source_hash(GEMM_SOURCES):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus N > 1 is not supported "
+                                   "(the layer shards by N or K across GPUs as described in DESIGN.md, "
+                                   "but no multi-GPU path is built)"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from mxfp8_block_scaled_amd import api, synth
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+
+    # ---------------- headline workload: M=8192, N=28672, K=8192 ----------------
+    x, w_g, bias = synth.config_inputs(4, device=dev)
+    M, K = x.shape
+    N = w_g.shape[0]
+    wq, ws = api.quantize_act(w_g)
+    pw = api.prepare_weight(wq, ws)
+    del wq, ws, w_g
+    q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    s = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        st = api.mxfp8_quantize_act(x.data_ptr(), M, K, K, q.data_ptr(), K, s.data_ptr(), K // 32, sptr)
+        if ev is not None:
+            ev[1].record(stream)
+        st |= api.mxfp8_gemm_prequant(q.data_ptr(), K, s.data_ptr(), K // 32, M, K, pw.w_packed.data_ptr(),
+                                      pw.s_packed.data_ptr(), N, bias.data_ptr(), y.data_ptr(), N, sptr)
+        if ev is not None:
+            ev[2].record(stream)
+        if st != 0:
+            raise RuntimeError(f"launch failed: {st}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    quant_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    gemm_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    flops = 2.0 * M * N * K
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
+    quant_bytes = M * K * (2 + 1 + 1 / 32)
+
+    # Same shape through the single product entry point, for reference.
+    ws_t = api.workspace(M, N, K, dev)
+    for _ in range(2):
+        api.linear(x, pw, bias, out=y)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        api.linear(x, pw, bias, out=y)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    linear_ms = e0.elapsed_time(e1) / args.steps
+    del ws_t
+
+    out = {
+        "metric": "mxfp8_linear TFLOP/s & % MFMA peak (M=1..16384); act-quant GB/s % HBM",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3 x fp8-e4m3 (MXFP8, fp32 accumulate, bf16 out)",
+        "data": "synthetic (seeded; x ~ N(0,1) bf16, W ~ N(0,0.01) quantized to MXFP8, bias ~ N(0,0.1))",
+        "config": {"workload": "large compute-bound MXFP8 linear M=8192 N=28672 K=8192 with bias",
+                   "M": M, "N": N, "K": K, "parallelism": "single GPU"},
+        "pct_mfma_peak": round(100 * value / PEAK_MFMA_FP8_TFLOPS, 2),
+        "kernels_ms": {"act_quant": round(quant_ms, 4), "gemm": round(gemm_ms, 4),
+                       "mxfp8_linear_entry": round(linear_ms, 4)},
+        "act_quant": {"GB/s": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
+                      "pct_hbm": round(100 * quant_bytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_MFMA_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_MFMA_FP8_TFLOPS, 4),
+                     "traffic": measured_traffic(None), "kernel": "gemm_tile_kernel"},
+    }
+    del q, s, y, x
+
+    if not args.no_sweep:
+        out["sweep"] = sweep(api, synth, torch, np, dev, stream)
+
+    if args.calib_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        bcp = torch.empty_like(a)
+        for _ in range(3):
+            bcp.copy_(a)
+        torch.cuda.synchronize()
+        out["calib_copy_bytes"] = 1 << 30
+
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(synth, np, torch)
+
+    print(json.dumps(out))
+
+
+def time_calls(fn, reps, stream, torch):
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for r in range(reps):
+        fn(r)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def sweep(api, synth, torch, np, dev, stream):
+    rows = []
+    sptr = stream.cuda_stream
+
+    def linear_entry(x_list, pw_list, b, M, N, K, y, reps, label, extra=None):
+        ws_t = api.workspace(M, N, K, dev)
+
+        def fn(r):
+            xx = x_list[r % len(x_list)]
+            pp = pw_list[r % len(pw_list)]
+            st = api.mxfp8_linear(xx.data_ptr(), M, K, K, pp.w_packed.data_ptr(), pp.s_packed.data_ptr(), N,
+                                  None if b is None else b.data_ptr(), y.data_ptr(), N, ws_t.data_ptr(),
+                                  ws_t.numel(), sptr)
+            if st != 0:
+                raise RuntimeError(st)
+        for r in range(5):
+            fn(r)
+        torch.cuda.synchronize()
+        ms = time_calls(fn, reps, stream, torch)
+        flops = 2.0 * M * N * K
+        alg_bytes = M * K * 2 + N * K + N * K / 32 + (0 if b is None else 2 * N) + M * N * 2
+        row = {"workload": label, "M": M, "N": N, "K": K, "us": round(ms * 1e3, 3),
+               "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 3),
+               "GB/s": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
+               "pct_mfma_peak": round(100 * flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_FP8_TFLOPS, 2),
+               "pct_hbm": round(100 * alg_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}
+        if extra:
+            row.update(extra)
+        rows.append(row)
+
+    # single layer, M=7 N=130 K=256 (launch-latency bound)
+    x, w, b = synth.config_inputs(1, device=dev)
+    wq, ws = api.quantize_act(w)
+    pw = api.prepare_weight(wq, ws)
+    y = torch.empty((7, 130), dtype=torch.bfloat16, device=dev)
+    linear_entry([x], [pw], b, 7, 130, 256, y, 200, "single M=7 N=130 K=256")
+
+    # decode sweep, weights rotated over 48 copies (> 3x the 256 MB MALL)
+    w, bd = synth.decode_weight(device=dev)
+    wq, ws = api.quantize_act(w)
+    pw0 = api.prepare_weight(wq, ws)
+    copies = [pw0] + [api.PreparedWeight(pw0.w_packed.clone(), pw0.s_packed.clone(), pw0.N, pw0.K)
+                      for _ in range(47)]
+    for M in (1, 7, 16, 128):
+        xm, _, _ = synth.config_inputs(2, M, device=dev)
+        xs = [xm.clone() for _ in range(8)]
+        y = torch.empty((M, 4096), dtype=torch.bfloat16, device=dev)
+        linear_entry(xs, copies, bd, M, 4096, 4096, y, 480, f"decode M={M} N=4096 K=4096",
+                     {"weight_copies_rotated": 48})
+    del copies, pw0
+
+    # prefill QKV shape, M=16384 N=5120 K=2048, no bias
+    xd, w, _ = synth.config_inputs(3, device=dev)
+    wq, ws = api.quantize_act(w)
+    pw = api.prepare_weight(wq, ws)
+    y = torch.empty((16384, 5120), dtype=torch.bfloat16, device=dev)
+    linear_entry([xd], [pw], None, 16384, 5120, 2048, y, 50, "prefill_qkv M=16384 N=5120 K=2048")
+
+    # standalone quantizer on the prefill activations
+    q = torch.empty((16384, 2048), dtype=torch.uint8, device=dev)
+    s = torch.empty((16384, 64), dtype=torch.uint8, device=dev)
+
+    def qf(r):
+        api.mxfp8_quantize_act(xd.data_ptr(), 16384, 2048, 2048, q.data_ptr(), 2048, s.data_ptr(), 64,
+                               stream.cuda_stream)
+    qf(0)
+    ms = time_calls(qf, 100, stream, torch)
+    nb = 16384 * 2048 * (2 + 1 + 1 / 32)
+    rows.append({"workload": "act-quant M=16384 K=2048", "us": round(ms * 1e3, 3),
+                 "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
+                 "pct_hbm": round(100 * nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)})
+    return rows
+
+
+def cpu_baseline(synth, np, torch):
+    """The oracle as it stands, on a bounded sample of the headline workload:
+    256 activation rows x 2048 weight rows x the full K = 8192, drawn with the
+    workload's distributions (quantize both, exact dequantized fp64 product,
+    bias).  Reported in the metric's unit."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    c = synth.LINEAR_CONFIGS[4]
+    Ms, Ns, K = 256, 2048, c["K"]
+    x, w, b = synth.linear_inputs(Ms, Ns, K, c["seed"], c["x_std"], c["w_std"], c["bias_std"])
+    xs = x.to(torch.float64).numpy()
+    wsub = w.to(torch.float64).numpy()
+    bs = b.to(torch.float64).numpy()
+    t0 = time.perf_counter()
+    wq, wsc = oracle.quantize_mx(wsub)
+    oracle.linear_ref(xs, wq, wsc, bs)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * Ms * Ns * K
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas_threads),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"M={Ms} x N={Ns} x K={K} slice of the M=8192 N=28672 K=8192 "
+                      "workload: MX-quantize x and W (numpy, 1 thread), fp64 dequantized product "
+                      "(BLAS threads) + bias"}
+
+
+if __name__ == "__main__":
+    main()

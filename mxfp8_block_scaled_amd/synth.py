@@ -24,6 +24,12 @@ Workloads (sizes and distributions of the layer's benchmark shapes):
 
 Draw order inside one generator: x, (outlier mask), W, bias; MoE: x, logits,
 w13, w2.
+
+Every function takes ``device``: "cpu" (default) draws with torch's CPU
+generator, so tests and the oracle see the same bytes on every machine; a GPU
+device draws the same distributions with that device's generator (a
+different random stream), which the benchmark uses to create its
+multi-gigabyte inputs in place.
 """
 
 import torch
@@ -42,54 +48,52 @@ MOE_CONFIG = dict(name="moe", T=4096, H=2048, E=128, topk=8, I=768, x_std=1.0,
                   logit_std=1.0, w_std=0.02, seed=4)
 
 
-def _gen(seed):
-    return torch.Generator(device="cpu").manual_seed(int(seed))
+def _gen(seed, device="cpu"):
+    return torch.Generator(device=device).manual_seed(int(seed))
 
 
 def randn_bf16(shape, std, gen):
     """N(0, std^2) drawn in fp32, cast to bf16 (RNE)."""
-    return (torch.randn(*shape, generator=gen, dtype=torch.float32) * std).to(torch.bfloat16)
+    return (torch.randn(*shape, generator=gen, dtype=torch.float32, device=gen.device) * std).to(torch.bfloat16)
 
 
 def activations(M, K, std, gen, outlier_frac=0.0, outlier_scale=1.0):
-    x = torch.randn(M, K, generator=gen, dtype=torch.float32) * std
+    x = torch.randn(M, K, generator=gen, dtype=torch.float32, device=gen.device) * std
     if outlier_frac > 0:
-        mask = torch.rand(M, K, generator=gen) < outlier_frac
+        mask = torch.rand(M, K, generator=gen, device=gen.device) < outlier_frac
         x = torch.where(mask, x * outlier_scale, x)
     return x.to(torch.bfloat16)
 
 
 def linear_inputs(M, N, K, seed, x_std=1.0, w_std=0.02, bias_std=0.1,
-                  outlier_frac=0.0, outlier_scale=1.0):
-    """(x bf16 [M,K], W bf16 [N,K], bias bf16 [N] or None), all on the CPU."""
-    g = _gen(seed)
+                  outlier_frac=0.0, outlier_scale=1.0, device="cpu"):
+    """(x bf16 [M,K], W bf16 [N,K], bias bf16 [N] or None) on ``device``."""
+    g = _gen(seed, device)
     x = activations(M, K, x_std, g, outlier_frac, outlier_scale)
     w = randn_bf16((N, K), w_std, g)
     bias = randn_bf16((N,), bias_std, g) if bias_std else None
     return x, w, bias
 
 
-def config_inputs(cfg, M=None):
+def config_inputs(cfg, M=None, device="cpu"):
     """Inputs of one linear workload; for "decode" pass the M of the sweep."""
     c = LINEAR_CONFIGS[cfg]
     if cfg == 2:
         if M is None:
             raise ValueError("the decode workload needs M")
-        g = _gen(c["seed"])
-        w = randn_bf16((c["N"], c["K"]), c["w_std"], g)
-        bias = randn_bf16((c["N"],), c["bias_std"], g)
-        x = activations(M, c["K"], c["x_std"], _gen(c["seed"] * 100003 + M),
+        w, bias = decode_weight(cfg, device)
+        x = activations(M, c["K"], c["x_std"], _gen(c["seed"] * 100003 + M, device),
                         c["outlier_frac"], c["outlier_scale"])
         return x, w, bias
     return linear_inputs(c["M"], c["N"], c["K"], c["seed"], c["x_std"], c["w_std"],
-                         c["bias_std"])
+                         c["bias_std"], device=device)
 
 
-def decode_weight(cfg=2):
+def decode_weight(cfg=2, device="cpu"):
     """Just the shared (W, bias) of the decode workload, drawn as config_inputs
     draws them."""
     c = LINEAR_CONFIGS[cfg]
-    g = _gen(c["seed"])
+    g = _gen(c["seed"], device)
     w = randn_bf16((c["N"], c["K"]), c["w_std"], g)
     bias = randn_bf16((c["N"],), c["bias_std"], g)
     return w, bias
