@@ -5,8 +5,9 @@
 Prints ONE JSON line.  The headline workload is the large compute-bound layer
 M=8192, N=28672, K=8192 (x ~ N(0,1), W ~ N(0,0.01) MXFP8, bf16 bias): a step is
 one pass of the whole hot path over that batch -- activation quantization
-(mxfp8_quantize_act) then the block-scaled GEMM with its bias/bf16 epilogue
-(mxfp8_gemm_prequant), the same two kernels mxfp8_linear launches for M > 16.
+into the GEMM's packed layout (mxfp8_quantize_act_packed) then the
+block-scaled GEMM with its bias/bf16 epilogue (mxfp8_gemm_packed), the same
+two kernels mxfp8_linear launches for M > 16.
 The one-time weight preparation runs before the timed region.  ``value`` is
 2*M*N*K / step time in TFLOP/s, inputs resident in HBM.
 
@@ -93,18 +94,19 @@ def main():
     wq, ws = api.quantize_act(w_g)
     pw = api.prepare_weight(wq, ws)
     del wq, ws, w_g
-    q = torch.empty((M, K), dtype=torch.uint8, device=dev)
-    s = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+    qb, sb = api.mxfp8_packed_act_bytes(M, K)
+    q = torch.empty(qb, dtype=torch.uint8, device=dev)
+    s = torch.empty(sb, dtype=torch.uint8, device=dev)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        st = api.mxfp8_quantize_act(x.data_ptr(), M, K, K, q.data_ptr(), K, s.data_ptr(), K // 32, sptr)
+        st = api.mxfp8_quantize_act_packed(x.data_ptr(), M, K, K, q.data_ptr(), s.data_ptr(), sptr)
         if ev is not None:
             ev[1].record(stream)
-        st |= api.mxfp8_gemm_prequant(q.data_ptr(), K, s.data_ptr(), K // 32, M, K, pw.w_packed.data_ptr(),
-                                      pw.s_packed.data_ptr(), N, bias.data_ptr(), y.data_ptr(), N, sptr)
+        st |= api.mxfp8_gemm_packed(q.data_ptr(), s.data_ptr(), M, K, pw.w_packed.data_ptr(),
+                                    pw.s_packed.data_ptr(), N, bias.data_ptr(), y.data_ptr(), N, sptr)
         if ev is not None:
             ev[2].record(stream)
         if st != 0:
@@ -270,9 +272,10 @@ def sweep(api, synth, torch, np, dev, stream):
 
 def cpu_baseline(synth, np, torch):
     """The oracle as it stands, on a bounded sample of the headline workload:
-    256 activation rows x 2048 weight rows x the full K = 8192, drawn with the
-    workload's distributions (quantize both, exact dequantized fp64 product,
-    bias).  Reported in the metric's unit."""
+    4096 activation rows x 16384 weight rows x the full K = 8192, drawn with
+    the workload's distributions (quantize both, exact dequantized fp64
+    product, bias; about 10-20 s on a 16-core host).  Reported in the
+    metric's unit."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -280,7 +283,7 @@ def cpu_baseline(synth, np, torch):
     except Exception:  # pragma: no cover
         blas_threads = 1
     c = synth.LINEAR_CONFIGS[4]
-    Ms, Ns, K = 256, 2048, c["K"]
+    Ms, Ns, K = 4096, 16384, c["K"]
     x, w, b = synth.linear_inputs(Ms, Ns, K, c["seed"], c["x_std"], c["w_std"], c["bias_std"])
     xs = x.to(torch.float64).numpy()
     wsub = w.to(torch.float64).numpy()

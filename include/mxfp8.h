@@ -89,8 +89,9 @@ int mxfp8_prepare_weight(const void* w_e4m3, const void* w_s_e8m0, int64_t N, in
 
 /*
  * Inverse of mxfp8_prepare_weight, for tests and tooling: writes the full
- * padded weight w_e4m3 [N_pad, K] (contiguous) and w_s_e8m0 [N_pad, K/32]
- * (contiguous).  Same size rules as mxfp8_prepare_weight.
+ * padded operand w_e4m3 [N_pad, K] (contiguous) and w_s_e8m0 [N_pad, K/32]
+ * (contiguous).  Same size rules as mxfp8_prepare_weight.  Also unpacks the
+ * packed activations of mxfp8_quantize_act_packed (pass M as N).
  */
 int mxfp8_unpack_weight(const void* w_packed, const void* s_packed, int64_t N, int64_t K,
                         void* w_e4m3, void* w_s_e8m0, void* stream);
@@ -122,16 +123,30 @@ int mxfp8_linear(const void* x_bf16, int64_t M, int64_t K, int64_t ldx,
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * The GEMM + epilogue on already quantized activations (step 3 alone; the
- * mm_mxfp8 call of vLLM PR #52204's apply_weights):
- *   q_e4m3 [M, K] row stride ldq (ldq % 16 == 0, 16-byte aligned),
- *   s_e8m0 [M, K/32] row stride lds (lds % 4 == 0, 4-byte aligned),
- * other arguments as mxfp8_linear.  Needs no workspace.
+ * The two kernels of mxfp8_linear's large-M path, exposed separately (for
+ * timing each, and for callers that reuse one quantized activation across
+ * several weights).  The packed activation layout is the packed weight
+ * layout with M in place of N: rows padded to a multiple of 128, opaque
+ * order owned by this library; mxfp8_unpack_weight(qp, sp, M, K, ...)
+ * returns it to plain [M_pad, K] / [M_pad, K/32] bytes.
+ *
+ * mxfp8_packed_act_bytes: host-only sizes for M rows (M >= 1, K % 256 == 0):
+ *   *q_bytes = M_pad * K, *s_bytes = M_pad * K / 32, M_pad = ceil(M/128)*128.
+ * mxfp8_quantize_act_packed: step 1 into that layout (same bytes as
+ *   mxfp8_quantize_act, reordered; pad rows are zero with scale byte 0).
+ *   x_bf16 as in mxfp8_quantize_act; qp, sp 256-byte aligned.
+ * mxfp8_gemm_packed: step 3 (the mm_mxfp8 GEMM of vLLM PR #52204's
+ *   apply_weights) + epilogue on packed activations; other arguments as
+ *   mxfp8_linear.  Needs no workspace.
  */
-int mxfp8_gemm_prequant(const void* q_e4m3, int64_t ldq, const void* s_e8m0, int64_t lds,
-                        int64_t M, int64_t K, const void* w_packed, const void* s_packed,
-                        int64_t N, const void* bias_bf16, void* y_bf16, int64_t ldy,
-                        void* stream);
+int mxfp8_packed_act_bytes(int64_t M, int64_t K, size_t* q_bytes, size_t* s_bytes);
+
+int mxfp8_quantize_act_packed(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, void* q_packed,
+                              void* s_packed, void* stream);
+
+int mxfp8_gemm_packed(const void* q_packed, const void* s_packed, int64_t M, int64_t K,
+                      const void* w_packed, const void* ws_packed, int64_t N, const void* bias_bf16,
+                      void* y_bf16, int64_t ldy, void* stream);
 
 /*
  * Test hook: force the GEMM path of mxfp8_linear (0 = automatic by shape,

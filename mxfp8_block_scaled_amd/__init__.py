@@ -10,7 +10,9 @@ _API = (
     "PreparedWeight", "linear", "prepare_weight", "quantize_act", "moe_grouped",
     "mxfp8_quantize_act", "mxfp8_prepared_weight_bytes", "mxfp8_prepare_weight",
     "mxfp8_unpack_weight", "mxfp8_linear_workspace_bytes", "mxfp8_linear",
-    "mxfp8_gemm_prequant", "mxfp8_moe_grouped", "mxfp8_moe_workspace_bytes",
+    "mxfp8_packed_act_bytes", "mxfp8_quantize_act_packed", "mxfp8_gemm_packed",
+    "quantize_act_packed", "gemm_packed", "PackedActivation",
+    "mxfp8_moe_grouped", "mxfp8_moe_workspace_bytes",
     "mxfp8_status_string", "MXFP8Error",
 )
 

@@ -35,8 +35,9 @@ _SIGNATURES = {
     "mxfp8_unpack_weight": ([_vp, _vp, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
     "mxfp8_linear_workspace_bytes": ([_i64, _i64, _i64, ctypes.POINTER(_sz)], ctypes.c_int),
     "mxfp8_linear": ([_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _sz, _vp], ctypes.c_int),
-    "mxfp8_gemm_prequant": ([_vp, _i64, _vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp],
-                            ctypes.c_int),
+    "mxfp8_packed_act_bytes": ([_i64, _i64, ctypes.POINTER(_sz), ctypes.POINTER(_sz)], ctypes.c_int),
+    "mxfp8_quantize_act_packed": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
+    "mxfp8_gemm_packed": ([_vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp], ctypes.c_int),
     "mxfp8_debug_force_path": ([ctypes.c_int], ctypes.c_int),
 }
 
@@ -121,8 +122,18 @@ def mxfp8_linear(x, M, K, ldx, wp, sp, N, bias, y, ldy, ws, ws_bytes, stream):
     return lib().mxfp8_linear(x, M, K, ldx, wp, sp, N, bias, y, ldy, ws, ws_bytes, stream)
 
 
-def mxfp8_gemm_prequant(q, ldq, s, lds, M, K, wp, sp, N, bias, y, ldy, stream):
-    return lib().mxfp8_gemm_prequant(q, ldq, s, lds, M, K, wp, sp, N, bias, y, ldy, stream)
+def mxfp8_packed_act_bytes(M, K):
+    q, s = _sz(), _sz()
+    _check(lib().mxfp8_packed_act_bytes(M, K, ctypes.byref(q), ctypes.byref(s)), "mxfp8_packed_act_bytes")
+    return q.value, s.value
+
+
+def mxfp8_quantize_act_packed(x, M, K, ldx, qp, sp, stream):
+    return lib().mxfp8_quantize_act_packed(x, M, K, ldx, qp, sp, stream)
+
+
+def mxfp8_gemm_packed(qp, sp, M, K, wp, wsp, N, bias, y, ldy, stream):
+    return lib().mxfp8_gemm_packed(qp, sp, M, K, wp, wsp, N, bias, y, ldy, stream)
 
 
 def mxfp8_debug_force_path(path):
@@ -239,15 +250,45 @@ def linear(x, pw, bias=None, out=None):
     return y.view(*lead, N)
 
 
-def gemm_prequant(q, s, pw, bias=None):
-    """The GEMM + epilogue on already quantized activations ``q`` [M, K] /
-    ``s`` [M, K/32] (uint8, GPU)."""
-    M, K = q.shape
-    N = pw.N
-    y = torch.empty((M, N), dtype=torch.bfloat16, device=q.device)
-    _check(mxfp8_gemm_prequant(_ptr(q), q.stride(0), _ptr(s), s.stride(0), M, K, _ptr(pw.w_packed),
-                               _ptr(pw.s_packed), N, _ptr(bias), _ptr(y), y.stride(0), _stream(q.device)),
-           "mxfp8_gemm_prequant")
+class PackedActivation:
+    """Activations quantized into the GEMM's packed operand layout (rows padded
+    to 128): the first kernel of the large-M path."""
+
+    def __init__(self, q_packed, s_packed, M, K):
+        self.q_packed = q_packed
+        self.s_packed = s_packed
+        self.M = M
+        self.K = K
+
+    def unpack(self):
+        """(E4M3 ``[M_pad, K]``, UE8M0 ``[M_pad, K/32]``) as uint8 tensors."""
+        return PreparedWeight(self.q_packed, self.s_packed, self.M, self.K).unpack()
+
+
+def quantize_act_packed(x):
+    """bf16 ``x[M, K]`` (GPU, K % 256 == 0) -> PackedActivation."""
+    assert x.dtype == torch.bfloat16
+    _require_cuda(x, "x")
+    x2 = x.reshape(-1, x.shape[-1])
+    if x2.stride(-1) != 1 or x2.stride(0) % 8 != 0 or x2.data_ptr() % 16 != 0:
+        x2 = x2.contiguous()
+    M, K = x2.shape
+    qb, sb = mxfp8_packed_act_bytes(M, K)
+    qp = torch.empty(qb, dtype=torch.uint8, device=x.device)
+    sp = torch.empty(sb, dtype=torch.uint8, device=x.device)
+    _check(mxfp8_quantize_act_packed(_ptr(x2), M, K, x2.stride(0), _ptr(qp), _ptr(sp), _stream(x.device)),
+           "mxfp8_quantize_act_packed")
+    return PackedActivation(qp, sp, M, K)
+
+
+def gemm_packed(pa, pw, bias=None):
+    """The GEMM + epilogue on packed activations (the second kernel of the
+    large-M path)."""
+    assert pa.K == pw.K
+    y = torch.empty((pa.M, pw.N), dtype=torch.bfloat16, device=pa.q_packed.device)
+    _check(mxfp8_gemm_packed(_ptr(pa.q_packed), _ptr(pa.s_packed), pa.M, pa.K, _ptr(pw.w_packed),
+                             _ptr(pw.s_packed), pw.N, _ptr(bias), _ptr(y), y.stride(0),
+                             _stream(pa.q_packed.device)), "mxfp8_gemm_packed")
     return y
 
 

@@ -52,10 +52,11 @@ int check_output(const void* y, int64_t N, int64_t ldy, const void* bias) {
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Workspace of the tile path: quantized activations [M, K] then scales
-// [M, K/32], each 256-byte aligned.
+// Workspace of the tile path: packed activations (M padded to 128 rows) then
+// their packed scales, each 256-byte aligned.
 size_t tile_ws_bytes(int64_t M, int64_t K) {
-  return round_up((size_t)M * (size_t)K, 256) + round_up((size_t)M * (size_t)(K / 32), 256);
+  const size_t mp = (size_t)((M + 127) / 128 * 128);
+  return round_up(mp * (size_t)K, 256) + round_up(mp * (size_t)(K / 32), 256);
 }
 
 bool use_skinny(int64_t M) {
@@ -149,24 +150,44 @@ int mxfp8_linear(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, const vo
   if (skinny)
     return mxfp8::launch_gemm_skinny(x_bf16, ldx, M, K, w_packed, s_packed, N, bias_bf16, y_bf16, ldy, s);
   uint8_t* q = (uint8_t*)workspace;
-  uint8_t* sc = q + round_up((size_t)M * (size_t)K, 256);
-  if (int st = mxfp8::launch_quantize_act(x_bf16, M, K, ldx, q, K, sc, K / 32, s)) return st;
-  return mxfp8::launch_gemm_tile(q, K, sc, K / 32, M, K, w_packed, s_packed, N, bias_bf16, y_bf16, ldy, s);
+  uint8_t* sc = q + round_up((size_t)n_pad(M) * (size_t)K, 256);
+  if (int st = mxfp8::launch_quantize_act_packed(x_bf16, M, K, ldx, q, sc, s)) return st;
+  return mxfp8::launch_gemm_tile(q, sc, M, K, w_packed, s_packed, N, bias_bf16, y_bf16, ldy, s);
 }
 
-int mxfp8_gemm_prequant(const void* q_e4m3, int64_t ldq, const void* s_e8m0, int64_t lds, int64_t M, int64_t K,
-                        const void* w_packed, const void* s_packed, int64_t N, const void* bias_bf16, void* y_bf16,
-                        int64_t ldy, void* stream) {
+int mxfp8_packed_act_bytes(int64_t M, int64_t K, size_t* q_bytes, size_t* s_bytes) {
+  if (!q_bytes || !s_bytes) return MXFP8_E_NULLPTR;
+  if (M < 1 || K < 256 || K % 256 != 0) return MXFP8_E_SHAPE;
+  *q_bytes = (size_t)n_pad(M) * (size_t)K;
+  *s_bytes = (size_t)n_pad(M) * (size_t)(K / 32);
+  return MXFP8_OK;
+}
+
+int mxfp8_quantize_act_packed(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, void* q_packed,
+                              void* s_packed, void* stream) {
+  if (M < 0 || K < 256 || K % 256 != 0) return MXFP8_E_SHAPE;
+  if (M == 0) return MXFP8_OK;
+  if (M > (int64_t)1 << 30 || K > (int64_t)1 << 30) return MXFP8_E_SHAPE;
+  if (!x_bf16 || !q_packed || !s_packed) return MXFP8_E_NULLPTR;
+  if (ldx < K || ldx % 8 != 0) return MXFP8_E_LD;
+  if (!aligned(x_bf16, 16) || !aligned(q_packed, 256) || !aligned(s_packed, 256)) return MXFP8_E_ALIGN;
+  if ((n_pad(M) * (K / 8) + 255) / 256 > INT32_MAX) return MXFP8_E_SHAPE;
+  if (int st = check_device()) return st;
+  return mxfp8::launch_quantize_act_packed(x_bf16, M, K, ldx, q_packed, s_packed, (hipStream_t)stream);
+}
+
+int mxfp8_gemm_packed(const void* q_packed, const void* s_packed, int64_t M, int64_t K, const void* w_packed,
+                      const void* ws_packed, int64_t N, const void* bias_bf16, void* y_bf16, int64_t ldy,
+                      void* stream) {
   if (M < 0) return MXFP8_E_SHAPE;
-  if (int st = check_packed(w_packed, s_packed, N, K)) return st;
+  if (int st = check_packed(w_packed, ws_packed, N, K)) return st;
   if (M == 0) return MXFP8_OK;
   if (M > (int64_t)1 << 30) return MXFP8_E_SHAPE;
-  if (!q_e4m3 || !s_e8m0) return MXFP8_E_NULLPTR;
+  if (!q_packed || !s_packed) return MXFP8_E_NULLPTR;
   if (int st = check_output(y_bf16, N, ldy, bias_bf16)) return st;
-  if (ldq < K || ldq % 16 != 0 || lds < K / 32 || lds % 4 != 0) return MXFP8_E_LD;
-  if (!aligned(q_e4m3, 16) || !aligned(s_e8m0, 4)) return MXFP8_E_ALIGN;
+  if (!aligned(q_packed, 256) || !aligned(s_packed, 256)) return MXFP8_E_ALIGN;
   if (int st = check_device()) return st;
-  return mxfp8::launch_gemm_tile(q_e4m3, ldq, s_e8m0, lds, M, K, w_packed, s_packed, N, bias_bf16, y_bf16, ldy,
+  return mxfp8::launch_gemm_tile(q_packed, s_packed, M, K, w_packed, ws_packed, N, bias_bf16, y_bf16, ldy,
                                  (hipStream_t)stream);
 }
 

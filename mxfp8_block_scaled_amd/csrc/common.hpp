@@ -12,27 +12,31 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------------------
-// Packed weight layout (written once by the prepare kernel, read by both GEMM
-// paths).  N is padded to a multiple of 128 ("pad N to 128" in the
-// process_weights_after_loading step of vLLM PR #52204); K is a multiple of
-// 256.  The weight is cut into 128-row groups and 128-byte K steps:
+// Packed operand layout.  The one-time weight preparation writes it, and so
+// does the activation quantizer of the large-M path (the same layout with M
+// in place of N), so both GEMM operands are read the same way.  Rows are
+// padded to a multiple of 128 ("pad N to 128" in the weight preparation step
+// of vLLM PR #52204); K is a multiple of 256.  Rows are cut into 128-row
+// groups and K into 64-byte steps:
 //
-//   W_p[g][ks] = 16 KiB tile: 128 rows x 8 chunks of 16 B; chunk c of row r
-//                sits at chunk slot r*8 + (c ^ (r & 7)) (an XOR swizzle so
-//                that eight consecutive rows reading the same logical chunk
-//                hit eight different 16-byte bank groups of LDS);
-//   S_p[g][ks] = 512 B: 128 rows x 4 UE8M0 bytes (the 4 MX blocks of the
-//                K step, in K order).
+//   data[g][ks]  = 8 KiB tile: 128 rows x 4 chunks of 16 bytes; logical chunk
+//                  c (K bytes [16c, 16c+16) of the step) of row r sits at
+//                  chunk position c ^ swz(r), swz(r) = ((r >> 1) ^ (r >> 3)) & 3,
+//                  so the 16-byte fragment reads of 8 (or 16) consecutive
+//                  rows at one logical chunk hit distinct LDS bank groups;
+//   scale[g][ks] = 256 B: 128 rows x 2 UE8M0 bytes (MX blocks 2ks, 2ks+1).
 //
 // A tile is one contiguous run of bytes, so a GEMM workgroup copies it to LDS
 // unchanged with direct global->LDS loads.
 // ---------------------------------------------------------------------------
 constexpr int kGroupRows = 128;
-constexpr int kStepK = 128;
-constexpr int kTileBytes = kGroupRows * kStepK;   // 16384
-constexpr int kTileScaleBytes = kGroupRows * 4;   // 512
+constexpr int kStepK = 64;
+constexpr int kTileBytes = kGroupRows * kStepK;   // 8192
+constexpr int kTileScaleBytes = kGroupRows * 2;   // 256
 
-__host__ __device__ inline int swz_slot(int r, int c) { return r * 8 + (c ^ (r & 7)); }
+__host__ __device__ inline int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// Byte offset of logical chunk c of row r inside a tile.
+__host__ __device__ inline int tile_off(int r, int c) { return r * kStepK + ((c ^ swz(r)) << 4); }
 
 // ---------------------------------------------------------------------------
 // Scaled MFMA operand conventions on gfx950 (pinned by probes on the device):

@@ -26,18 +26,21 @@ constexpr int kWaves = 8;
 constexpr int kUnroll = 4;
 
 struct StepLoads {
-  uint4 w0, w1;       // weight operand, two 16-byte halves
-  uint32_t wsd;       // the weight row's 4 block scales for this K step
+  uint4 w0, w1;          // weight operand, two 16-byte halves
+  uint32_t wsd;          // the weight row's scale word holding this lane's block
   uint4 x0, x1, x2, x3;  // 32 bf16 activations: 16 at 16g, 16 at 64 + 16g
 };
 
-__device__ inline void step_load(StepLoads& L, const uint8_t* wrow, int wc0, int wc1, const uint8_t* srow,
+// One 128-deep K step = packed tiles 2ks and 2ks+1.  Lane (i, g) takes chunk g
+// of row r from each; its scale (MX block g of the step) is byte g&1 of the
+// row's word in tile 2ks + g/2.
+__device__ inline void step_load(StepLoads& L, const uint8_t* wrow, int woff, const uint8_t* srow, int g,
                                  const uint16_t* xrow, int ks) {
-  const uint8_t* wt = wrow + (size_t)ks * kTileBytes;
-  L.w0 = *reinterpret_cast<const uint4*>(wt + wc0);
-  L.w1 = *reinterpret_cast<const uint4*>(wt + wc1);
-  L.wsd = *reinterpret_cast<const uint32_t*>(srow + (size_t)ks * kTileScaleBytes);
-  const uint16_t* xk = xrow + (size_t)ks * kStepK;
+  const uint8_t* wt = wrow + (size_t)(2 * ks) * kTileBytes + woff;
+  L.w0 = *reinterpret_cast<const uint4*>(wt);
+  L.w1 = *reinterpret_cast<const uint4*>(wt + kTileBytes);
+  L.wsd = (uint32_t)*reinterpret_cast<const uint16_t*>(srow + (size_t)(2 * ks + (g >> 1)) * kTileScaleBytes);
+  const uint16_t* xk = xrow + (size_t)ks * 128;
   L.x0 = *reinterpret_cast<const uint4*>(xk);
   L.x1 = *reinterpret_cast<const uint4*>(xk + 8);
   L.x2 = *reinterpret_cast<const uint4*>(xk + 64);
@@ -73,7 +76,7 @@ __device__ inline v4f step_compute(const StepLoads& L, int g, v4f acc) {
   for (int i = 0; i < 8; ++i) xb[i] = (int)q[i];
   wa[0] = (int)L.w0.x; wa[1] = (int)L.w0.y; wa[2] = (int)L.w0.z; wa[3] = (int)L.w0.w;
   wa[4] = (int)L.w1.x; wa[5] = (int)L.w1.y; wa[6] = (int)L.w1.z; wa[7] = (int)L.w1.w;
-  const int wscale = (int)(L.wsd >> (8 * g));
+  const int wscale = (int)(L.wsd >> (8 * (g & 1)));
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wa, xb, acc, 0, 0, 0, wscale, 0, (int)xscale);
 }
 
@@ -90,12 +93,12 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_skinny_kernel(
   const int n0 = blockIdx.x * 16;
   const int grp = n0 / kGroupRows;
   const int r = (n0 % kGroupRows) + i;
-  const int KS = K / kStepK;
+  const int KT = K / kStepK;   // packed tiles along K
+  const int KS = K / 128;      // MFMA steps along K
 
-  const uint8_t* wrow = wp + (size_t)grp * KS * kTileBytes + r * kStepK;
-  const int wc0 = swz_slot(0, g ^ (r & 7)) * 16;        // chunk g of row r, relative to the row
-  const int wc1 = swz_slot(0, (4 + g) ^ (r & 7)) * 16;  // chunk 4+g
-  const uint8_t* srow = sp + (size_t)grp * KS * kTileScaleBytes + r * 4;
+  const uint8_t* wrow = wp + (size_t)grp * KT * kTileBytes;
+  const int woff = tile_off(r, g);
+  const uint8_t* srow = sp + (size_t)grp * KT * kTileScaleBytes + r * 2;
   const int m = min(i, M - 1);
   const uint16_t* xrow = x + (size_t)m * ldx + 16 * g;
 
@@ -105,13 +108,13 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_skinny_kernel(
   for (; ks + kUnroll <= ke; ks += kUnroll) {
     StepLoads L[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) step_load(L[u], wrow, wc0, wc1, srow, xrow, ks + u);
+    for (int u = 0; u < kUnroll; ++u) step_load(L[u], wrow, woff, srow, g, xrow, ks + u);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) acc = step_compute(L[u], g, acc);
   }
   for (; ks < ke; ++ks) {
     StepLoads L;
-    step_load(L, wrow, wc0, wc1, srow, xrow, ks);
+    step_load(L, wrow, woff, srow, g, xrow, ks);
     acc = step_compute(L, g, acc);
   }
 

@@ -9,19 +9,26 @@
 // Design (gfx950):
 //  * Workgroup tile 256 (n, weight rows) x 256 (m, activation rows), 4 waves
 //    as 2 x 2, each wave 128 x 128 = 4 x 4 v_mfma_scale_f32_32x32x64_f8f6f4
-//    tiles.  The weight is the MFMA A operand, so each lane's results are 4
-//    consecutive n of one output row m: one 8-byte bf16 store per 4 values.
-//  * K advances 128 bytes (4 MX blocks) per stage.  A stage is 32 KiB of
-//    weight + 32 KiB of activations + 2 x 1 KiB of scales, copied straight
-//    from global memory into LDS with global_load_lds_dwordx4 / _dword (no
-//    VGPR staging).  Two stages double-buffer the K loop: the copy of step
-//    k+1 is in flight while step k computes.
-//  * The packed weight tile is already in LDS order; activation rows are
-//    placed with the same XOR swizzle (common.hpp) by choosing which global
-//    chunk each lane fetches, so LDS fragment reads are bank-conflict free.
+//    tiles (accumulators in AGPRs).  The weight is the MFMA A operand, so a
+//    lane's results are 4 consecutive n of one output row m.
+//  * Both operands arrive in the packed tile layout of common.hpp (8 KiB per
+//    128 rows x 64 K-bytes, contiguous), so a stage is four contiguous runs
+//    copied straight into LDS by global_load_lds_dwordx4 / _dword.
+//  * K advances 64 per stage; four LDS stages (4 x 33 KiB) keep three stages
+//    of loads in flight while one computes.  Each stage lives in its own
+//    __shared__ array and the loop is unrolled by four, so every LDS access
+//    names a distinct array: the compiler then needs no blanket vmcnt(0)
+//    before the fragment reads, and the kernel waits only for the stage it
+//    is about to use (partial vmcnt).
+//  * Epilogue through LDS: each wave parks its fp32 accumulators (64 rows at a
+//    time) in an LDS stage buffer, reads them back row-contiguous, adds the
+//    bias (loaded once per lane) and writes bf16 with 8-byte stores that
+//    cover whole 256-byte row segments.
 //  * Workgroups are dispatched round-robin over the 8 XCDs; the tile index is
 //    remapped so that each XCD works on a contiguous, M-grouped range of tiles
 //    and its private L2 sees the reuse of weight and activation K-slices.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -29,30 +36,34 @@ namespace mxfp8 {
 
 namespace {
 
-constexpr int kBM = 256;
-constexpr int kBN = 256;
 constexpr int kThreads = 256;
-constexpr int kWBytes = kBN * kStepK;  // 32768
-constexpr int kXBytes = kBM * kStepK;  // 32768
-constexpr int kWSBytes = kBN * 4;      // 1024
-constexpr int kXSBytes = kBM * 4;      // 1024
-constexpr int kStage = kWBytes + kXBytes + kWSBytes + kXSBytes;
-constexpr int kStages = 2;
-constexpr int kGroupM = 8;  // tiles along M per group of the tile order
+constexpr int kOpBytes = 256 * kStepK;                // one operand's 256 rows x 64 K-bytes
+constexpr int kScaleRegion = 1024;                    // 256 x 2 B weight + 256 x 2 B activation scales
+constexpr int kStage = 2 * kOpBytes + kScaleRegion;   // 33792
+constexpr int kLoadsPerStage = 9;                     // per thread: 4 + 4 data, 1 scale
+constexpr int kGroupM = 8;                            // tiles along M per group of the tile order
 constexpr int kXCD = 8;
+constexpr int kEpiPitch = 132;                        // floats per staged row (128 + 4 pad)
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ inline void g2l_16(const void* g, uint8_t* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_wave_base, 16, 0, 0);
+// Direct global -> LDS copies (each lane moves 16 or 4 bytes to
+// lds_wave_base + lane * size).  Issued from inline assembly so that the
+// compiler does not track them: the kernel orders them itself with explicit
+// vmcnt waits, and the compiler's own (untracked-aware) waits for its own
+// global loads can only be more conservative, never less.
+__device__ inline uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
+__device__ inline void g2l_16(const void* g, const uint8_t* lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr(lds_wave_base))
+               : "memory", "m0");
 }
-__device__ inline void g2l_4(const void* g, uint8_t* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_wave_base, 4, 0, 0);
+__device__ inline void g2l_4(const void* g, const uint8_t* lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_addr(lds_wave_base))
+               : "memory", "m0");
 }
 
-__device__ inline v8i lds_frag(const uint8_t* base, int row, int c0, int c1) {
-  const uint4 a = *reinterpret_cast<const uint4*>(base + swz_slot(row, c0) * 16);
-  const uint4 b = *reinterpret_cast<const uint4*>(base + swz_slot(row, c1) * 16);
+// 32x32x64 operand of row R: K bytes [16g, 16g+16) and [32+16g, 32+16g+16).
+__device__ inline v8i lds_frag(const uint8_t* base, int R, int g) {
+  const uint4 a = *reinterpret_cast<const uint4*>(base + tile_off(R, g));
+  const uint4 b = *reinterpret_cast<const uint4*>(base + tile_off(R, 2 + g));
   v8i v;
   v[0] = (int)a.x; v[1] = (int)a.y; v[2] = (int)a.z; v[3] = (int)a.w;
   v[4] = (int)b.x; v[5] = (int)b.y; v[6] = (int)b.z; v[7] = (int)b.w;
@@ -67,14 +78,24 @@ __device__ inline int xcd_remap(int bid, int total) {
   return (xcd < rem) ? xcd * (per + 1) + k : rem * (per + 1) + (xcd - rem) * per + k;
 }
 
+template <int N>
+__device__ inline void wait_vmcnt() {
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if constexpr (N == kLoadsPerStage) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+}
+
 }  // namespace
 
 __global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(
-    const uint8_t* __restrict__ xq, int64_t ldq, const uint8_t* __restrict__ xs, int64_t lds, int M, int K,
-    const uint8_t* __restrict__ wp, const uint8_t* __restrict__ sp, int N, int G,
+    const uint8_t* __restrict__ qp, const uint8_t* __restrict__ qsp, int M, int K,
+    const uint8_t* __restrict__ wp, const uint8_t* __restrict__ wsp, int N, int GN, int GM,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int64_t ldy, int tiles_m, int tiles_n,
     int vec_store) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t st0[kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t st3[kStage];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -91,34 +112,33 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(
   const int tm = first_m + in_group % gm;
   const int tn = in_group / gm;
 
-  const int m0 = tm * kBM;
   const int KS = K / kStepK;
-  const int ga = min(2 * tn, G - 1), gb = min(2 * tn + 1, G - 1);
-  const uint8_t* wt0 = wp + (size_t)ga * KS * kTileBytes + tid * 16;
-  const uint8_t* wt1 = wp + (size_t)gb * KS * kTileBytes + tid * 16;
-  const uint8_t* st = sp + (size_t)(tid < 128 ? ga : gb) * KS * kTileScaleBytes + (tid & 127) * 4;
+  const size_t op_stride = (size_t)KS * kTileBytes;     // bytes per 128-row group
+  const size_t sc_stride = (size_t)KS * kTileScaleBytes;
+  const int wa = min(2 * tn, GN - 1), wb = min(2 * tn + 1, GN - 1);
+  const int xa = min(2 * tm, GM - 1), xb = min(2 * tm + 1, GM - 1);
+  const uint8_t* w0 = wp + wa * op_stride + tid * 16;
+  const uint8_t* w1 = wp + wb * op_stride + tid * 16;
+  const uint8_t* x0 = qp + xa * op_stride + tid * 16;
+  const uint8_t* x1 = qp + xb * op_stride + tid * 16;
+  // Scale words: threads 0-63 weight rows 0-127, 64-127 weight rows 128-255,
+  // 128-191 activation rows 0-127, 192-255 activation rows 128-255.
+  const int sg = tid >> 6;
+  const uint8_t* ssrc = (sg == 0 ? wsp + wa * sc_stride : sg == 1 ? wsp + wb * sc_stride
+                         : sg == 2 ? qsp + xa * sc_stride : qsp + xb * sc_stride) + (tid & 63) * 4;
 
-  // Activation chunk fetched by this lane in copy round q: LDS slot
-  // q*256 + tid holds row r = q*32 + tid/8, chunk (tid%8) ^ (r%8).
-  const int xc = (tid & 7) ^ ((tid >> 3) & 7);
-  const uint8_t* xrow[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int r = min(m0 + q * 32 + (tid >> 3), M - 1);
-    xrow[q] = xq + (size_t)r * ldq + xc * 16;
-  }
-  const uint8_t* xsrow = xs + (size_t)min(m0 + tid, M - 1) * lds;
-
-  auto issue = [&](int ks, int stage) {
-    uint8_t* base = smem + stage * kStage + wave * 1024;
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-      g2l_16(((q < 4) ? wt0 : wt1) + (size_t)ks * kTileBytes + (q & 3) * 4096, base + q * 4096);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) g2l_16(xrow[q] + (size_t)ks * kStepK, base + kWBytes + q * 4096);
-    uint8_t* sbase = smem + stage * kStage + kWBytes + kXBytes + wave * 256;
-    g2l_4(st + (size_t)ks * kTileScaleBytes, sbase);
-    g2l_4(xsrow + ks * 4, sbase + kWSBytes);
+  auto issue = [&](int ks, uint8_t* st) {
+    uint8_t* base = st + wave * 1024;
+    const size_t off = (size_t)ks * kTileBytes;
+    g2l_16(w0 + off, base);
+    g2l_16(w0 + off + 4096, base + 4096);
+    g2l_16(w1 + off, base + 8192);
+    g2l_16(w1 + off + 4096, base + 12288);
+    g2l_16(x0 + off, base + kOpBytes);
+    g2l_16(x0 + off + 4096, base + kOpBytes + 4096);
+    g2l_16(x1 + off, base + kOpBytes + 8192);
+    g2l_16(x1 + off + 4096, base + kOpBytes + 12288);
+    g2l_4(ssrc + (size_t)ks * kTileScaleBytes, st + 2 * kOpBytes + wave * 256);
   };
 
   const int wn = wave >> 1, wm = wave & 1;
@@ -132,92 +152,138 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
-  issue(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  for (int ks = 0; ks < KS; ++ks) {
-    const int stage = ks & 1;
-    if (ks + 1 < KS) issue(ks + 1, stage ^ 1);
-    const uint8_t* wb = smem + stage * kStage;
-    const uint8_t* xb = wb + kWBytes;
-    const uint32_t* wsc = reinterpret_cast<const uint32_t*>(wb + kWBytes + kXBytes);
-    const uint32_t* xsc = reinterpret_cast<const uint32_t*>(wb + kWBytes + kXBytes + kWSBytes);
-    // Lane group lg supplies the scale of MX block (2j + lg) of this K step.
+  // One 64-deep K step from an LDS stage: lane group lg supplies the scale of
+  // MX block lg of the step (byte lg of the row's scale word).
+  auto compute = [&](const uint8_t* st) {
+    const uint8_t* xs = st + kOpBytes;
+    const uint16_t* wsc = reinterpret_cast<const uint16_t*>(st + 2 * kOpBytes);
+    const uint16_t* xsc = wsc + 256;
     int sw[4], sx[4];
+    v8i fa[4], fb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sw[i] = (int)(wsc[wn * 128 + 32 * i + li] >> (8 * lg));
-      sx[i] = (int)(xsc[wm * 128 + 32 * i + li] >> (8 * lg));
+      sw[i] = (int)((uint32_t)wsc[wn * 128 + 32 * i + li] >> (8 * lg));
+      sx[i] = (int)((uint32_t)xsc[wm * 128 + 32 * i + li] >> (8 * lg));
+      fa[i] = lds_frag(st, wn * 128 + 32 * i + li, lg);
+      fb[i] = lds_frag(xs, wm * 128 + 32 * i + li, lg);
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      v8i fa[4], fb[4];
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        fa[i] = lds_frag(wb, wn * 128 + 32 * i + li, 4 * j + lg, 4 * j + 2 + lg);
-        fb[i] = lds_frag(xb, wm * 128 + 32 * i + li, 4 * j + lg, 4 * j + 2 + lg);
-      }
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          if (j == 0)
-            acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[a], fb[b], acc[a][b], 0, 0, 0, sw[a],
-                                                                        0, sx[b]);
-          else
-            acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[a], fb[b], acc[a][b], 0, 0, 2, sw[a],
-                                                                        2, sx[b]);
-        }
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  }
+      for (int b = 0; b < 4; ++b)
+        acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[a], fb[b], acc[a][b], 0, 0, 0, sw[a], 0,
+                                                                    sx[b]);
+  };
 
-  // Epilogue: lane holds n = nb + 8*(r/4) + 4*lg + r%4 for m = mb + li.
+  // After computing step s, wait until step s+1 has landed: the loads of the
+  // (at most two) later steps already issued may stay in flight.
+  // One K step: optionally issue the copy of step s+3 into the buffer freed by
+  // step s-1, compute from this step's buffer, then wait until step s+1 has
+  // landed (LATER = number of copies issued after it, still allowed in
+  // flight).  The body has no branches, so the MFMAs stay between their own
+  // barriers; the scheduling fences keep the next step's fragment reads from
+  // being hoisted above the barrier.
+  //
+  // The barrier is a bare s_barrier: the copies of step s+1 are complete in
+  // LDS once this wave's vmcnt says so, and every wave waits for its own
+  // before arriving.  (__syncthreads() would add a workgroup fence, i.e. a
+  // vmcnt(0) that drains the copies still meant to be in flight.)
+  auto step = [&](auto do_issue, auto later, int s, uint8_t* st_issue, const uint8_t* st_use) {
+    if constexpr (decltype(do_issue)::value) issue(s + 3, st_issue);
+    compute(st_use);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<decltype(later)::value * kLoadsPerStage>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  using L0 = std::integral_constant<int, 0>;
+  using L1 = std::integral_constant<int, 1>;
+  using L2 = std::integral_constant<int, 2>;
+
+  // KS is a multiple of 4 (K % 256 == 0) and at least 4.
+  issue(0, st0);
+  issue(1, st1);
+  issue(2, st2);
+  wait_vmcnt<2 * kLoadsPerStage>();
+  __builtin_amdgcn_s_barrier();
+  int ks = 0;
+  for (; ks + 4 < KS; ks += 4) {
+    step(T{}, L2{}, ks, st3, st0);
+    step(T{}, L2{}, ks + 1, st0, st1);
+    step(T{}, L2{}, ks + 2, st1, st2);
+    step(T{}, L2{}, ks + 3, st2, st3);
+  }
+  // Last four steps: only the first still has a copy to issue (step KS-1).
+  step(T{}, L2{}, ks, st3, st0);
+  step(F{}, L1{}, ks + 1, st0, st1);
+  step(F{}, L0{}, ks + 2, st1, st2);
+  step(F{}, L0{}, ks + 3, st2, st3);
+
+  // ---------------- epilogue ----------------
+  // Lane (li, lg) holds n = 32a + 8(r/4) + 4lg + r%4, m = 32b + li of the
+  // wave's 128 x 128 block.  Stage 64 rows (b = 2h, 2h+1) at a time.
+  float* stage = reinterpret_cast<float*>(wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3);
+  const int n4 = lane & 31;          // readback: 4 consecutive n per lane
+  const int rsub = lane >> 5;        // readback: row parity
+  const int nw = tn * 256 + wn * 128;
+  const int nl = nw + 4 * n4;
+  float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (bias != nullptr) {
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int nb = tn * kBN + wn * 128 + 32 * a + 4 * lg;
+    for (int e = 0; e < 4; ++e)
+      if (nl + e < N) bv[e] = __uint_as_float((uint32_t)bias[nl + e] << 16);
+  }
+  const bool full_n = nl + 3 < N;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int m = m0 + wm * 128 + 32 * b + li;
-      if (m >= M) continue;
-      uint16_t* yrow = y + (size_t)m * ldy;
+  for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int n = nb + 8 * rr;
-        if (n >= N) continue;
-        float v[4];
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[e] = acc[a][b][4 * rr + e];
-          if (bias != nullptr && n + e < N) v[e] += __uint_as_float((uint32_t)bias[n + e] << 16);
+      for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const v16f& v = acc[a][2 * h + b2];
+          float4 f = make_float4(v[4 * rr], v[4 * rr + 1], v[4 * rr + 2], v[4 * rr + 3]);
+          *reinterpret_cast<float4*>(stage + (32 * b2 + li) * kEpiPitch + 32 * a + 8 * rr + 4 * lg) = f;
         }
-        if (vec_store && n + 3 < N) {
-          const uint32_t lo = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-          const uint32_t hi = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
-          *reinterpret_cast<uint2*>(yrow + n) = make_uint2(lo, hi);
-        } else {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int mbase = tm * 256 + wm * 128 + 64 * h;
+#pragma unroll 4
+    for (int it = 0; it < 32; ++it) {
+      const int row = 2 * it + rsub;
+      const int m = mbase + row;
+      const float4 f = *reinterpret_cast<const float4*>(stage + row * kEpiPitch + 4 * n4);
+      if (m >= M || nl >= N) continue;
+      const float v0 = f.x + bv[0], v1 = f.y + bv[1], v2 = f.z + bv[2], v3 = f.w + bv[3];
+      uint16_t* dst = y + (size_t)m * ldy + nl;
+      if (vec_store && full_n) {
+        *reinterpret_cast<uint2*>(dst) = make_uint2(f32_to_bf16_rne(v0) | (f32_to_bf16_rne(v1) << 16),
+                                                    f32_to_bf16_rne(v2) | (f32_to_bf16_rne(v3) << 16));
+      } else {
+        const float vv[4] = {v0, v1, v2, v3};
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (n + e < N) yrow[n + e] = (uint16_t)f32_to_bf16_rne(v[e]);
-        }
+        for (int e = 0; e < 4; ++e)
+          if (nl + e < N) dst[e] = (uint16_t)f32_to_bf16_rne(vv[e]);
       }
     }
+    // The next half overwrites the same rows: finish the reads first.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
 }
 
-int launch_gemm_tile(const void* q, int64_t ldq, const void* s, int64_t lds, int64_t M, int64_t K,
-                     const void* wp, const void* sp, int64_t N, const void* bias, void* y, int64_t ldy,
-                     hipStream_t stream) {
-  const int64_t G = (N + kGroupRows - 1) / kGroupRows;
-  const int tiles_n = (int)((G + 1) / 2);
-  const int tiles_m = (int)((M + kBM - 1) / kBM);
+int launch_gemm_tile(const void* qp, const void* sp, int64_t M, int64_t K, const void* wp, const void* wsp,
+                     int64_t N, const void* bias, void* y, int64_t ldy, hipStream_t stream) {
+  const int64_t GN = (N + kGroupRows - 1) / kGroupRows;
+  const int64_t GM = (M + kGroupRows - 1) / kGroupRows;
+  const int tiles_n = (int)((GN + 1) / 2);
+  const int tiles_m = (int)((GM + 1) / 2);
   const int vec = (ldy % 4 == 0) && (((uintptr_t)y & 7) == 0);
   hipLaunchKernelGGL(gemm_tile_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(kThreads), 0, stream,
-                     (const uint8_t*)q, ldq, (const uint8_t*)s, lds, (int)M, (int)K, (const uint8_t*)wp,
-                     (const uint8_t*)sp, (int)N, (int)G, (const uint16_t*)bias, (uint16_t*)y, ldy, tiles_m,
-                     tiles_n, vec);
+                     (const uint8_t*)qp, (const uint8_t*)sp, (int)M, (int)K, (const uint8_t*)wp,
+                     (const uint8_t*)wsp, (int)N, (int)GN, (int)GM, (const uint16_t*)bias, (uint16_t*)y, ldy,
+                     tiles_m, tiles_n, vec);
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 

@@ -43,6 +43,63 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
   }
 }
 
+// Same quantization, written in the packed operand layout of common.hpp for
+// the large-M GEMM (rows padded to a multiple of 128; pad rows are written as
+// zero elements with scale byte 0, so every byte the GEMM reads is defined).
+template <typename Idx>
+__global__ __launch_bounds__(256) void quant_act_packed_kernel(const uint16_t* __restrict__ x, int64_t ldx, int M,
+                                                               Idx chunks_per_row, Idx total, int64_t KS,
+                                                               uint8_t* __restrict__ qp, uint8_t* __restrict__ sp) {
+  Idx t = (Idx)blockIdx.x * 256 + threadIdx.x;
+  const bool valid = t < total;
+  if (!valid) t = total - 1;
+  const Idx row = t / chunks_per_row;
+  const Idx c8 = t - row * chunks_per_row;
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  if ((int64_t)row < M) {
+    const uint4 v = *reinterpret_cast<const uint4*>(x + (int64_t)row * ldx + (int64_t)c8 * 8);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m = absmax_bits(m, w[i]);
+  m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+  const uint32_t sb = mx_scale_byte(m);
+  uint32_t qd[2];
+  cvt8(w, mx_inv_scale(sb), qd);
+  if (valid) {
+    const int64_t g = (int64_t)row / kGroupRows;
+    const int r = (int)((int64_t)row % kGroupRows);
+    const int64_t k = (int64_t)c8 * 8;
+    const int64_t ks = k / kStepK;
+    const int c = (int)((k % kStepK) >> 4);
+    const int half = (int)((k >> 3) & 1);
+    uint8_t* tile = qp + (g * KS + ks) * kTileBytes;
+    *reinterpret_cast<uint2*>(tile + tile_off(r, c) + half * 8) = make_uint2(qd[0], qd[1]);
+    if ((c8 & 3) == 0) sp[(g * KS + ks) * kTileScaleBytes + r * 2 + (int)((k >> 5) & 1)] = (uint8_t)sb;
+  }
+}
+
+int launch_quantize_act_packed(const void* x, int64_t M, int64_t K, int64_t ldx, void* qp, void* sp,
+                               hipStream_t stream) {
+  const int64_t m_pad = (M + kGroupRows - 1) / kGroupRows * kGroupRows;
+  const int64_t per_row = K / 8;
+  const int64_t total = m_pad * per_row;
+  const int64_t blocks = (total + 255) / 256;
+  const int64_t KS = K / kStepK;
+  if (total < ((int64_t)1 << 32)) {
+    hipLaunchKernelGGL(quant_act_packed_kernel<uint32_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const uint16_t*)x, ldx, (int)M, (uint32_t)per_row, (uint32_t)total, KS, (uint8_t*)qp,
+                       (uint8_t*)sp);
+  } else {
+    hipLaunchKernelGGL(quant_act_packed_kernel<uint64_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const uint16_t*)x, ldx, (int)M, (uint64_t)per_row, (uint64_t)total, KS, (uint8_t*)qp,
+                       (uint8_t*)sp);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
 int launch_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx, void* q, int64_t ldq, void* s,
                         int64_t lds, hipStream_t stream) {
   const int64_t per_row = K / 8;

@@ -92,13 +92,21 @@ def test_linear_validation():
     bad = list(ok); bad[0] = P + 2; assert f(*bad) == -3
 
 
-def test_gemm_prequant_validation():
-    f = api.mxfp8_gemm_prequant
-    ok = (P, 256, P, 8, 64, 256, P, P, 130, None, P, 130, None)
-    assert f(*ok) == -6
-    bad = list(ok); bad[1] = 264; assert f(*bad) == -4          # ldq % 16
-    bad = list(ok); bad[3] = 6; assert f(*bad) == -4            # lds % 4
-    bad = list(ok); bad[2] = P + 2; assert f(*bad) == -3
+def test_packed_entries_validation():
+    assert api.mxfp8_packed_act_bytes(300, 512) == (384 * 512, 384 * 16)
+    f = api.mxfp8_quantize_act_packed
+    assert f(P, 4, 512, 512, P, P, None) == -6
+    assert f(P, 4, 288, 288, P, P, None) == -2               # K % 256
+    assert f(P, 4, 512, 500, P, P, None) == -4
+    assert f(P, 4, 512, 512, P + 16, P, None) == -3          # packed output alignment
+    assert f(P, 0, 512, 512, P, P, None) == 0
+    g = api.mxfp8_gemm_packed
+    ok = (P, P, 64, 256, P, P, 130, None, P, 130, None)
+    assert g(*ok) == -6
+    bad = list(ok); bad[0] = None; assert g(*bad) == -1
+    bad = list(ok); bad[1] = P + 4; assert g(*bad) == -3
+    bad = list(ok); bad[9] = 100; assert g(*bad) == -4
+    bad = list(ok); bad[3] = 320; assert g(*bad) == -2
 
 
 def test_force_path_hook():

@@ -109,17 +109,34 @@ def test_skinny_and_tile_paths_agree():
         assert s1["over_bound"] == 0 and s2["over_bound"] == 0
 
 
-def test_prequant_entry_matches_linear():
+def test_packed_entries_match_linear():
+    """mxfp8_quantize_act_packed + mxfp8_gemm_packed are the two kernels of
+    mxfp8_linear's large-M path: same bytes out."""
     g = torch.Generator().manual_seed(3)
     x = synth.randn_bf16((300, 512), 1.0, g).to(gpu_util.dev())
     w = synth.randn_bf16((260, 512), 0.02, g)
     b = synth.randn_bf16((260,), 0.1, g).to(gpu_util.dev())
     pw = gpu_util.gpu_prepare(w)
-    q, s = api.quantize_act(x)
-    y1 = api.gemm_prequant(q, s, pw, b)
+    pa = api.quantize_act_packed(x)
+    y1 = api.gemm_packed(pa, pw, b)
     y2 = api.linear(x, pw, b)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
+
+
+@pytest.mark.parametrize("M,K", [(1, 256), (130, 512), (300, 768), (256, 1024)])
+def test_packed_activation_quantizer_bit_exact(M, K):
+    """The packed-layout quantizer writes exactly the oracle's bytes (checked
+    after unpacking), with zero pad rows and zero scales."""
+    g = torch.Generator().manual_seed(M + K)
+    x = synth.scale_stress(synth.activations(M, K, 1.0, g, 0.01, 50.0), seed=M)
+    pa = api.quantize_act_packed(x.to(gpu_util.dev()))
+    q, s = pa.unpack()
+    torch.cuda.synchronize()
+    q2, s2 = oracle.quantize_mx(x.to(torch.float64).numpy())
+    assert np.array_equal(q[:M].cpu().numpy(), q2)
+    assert np.array_equal(s[:M].cpu().numpy(), s2)
+    assert bool((q[M:] == 0).all()) and bool((s[M:] == 0).all())
 
 
 def test_deterministic_repeat():
