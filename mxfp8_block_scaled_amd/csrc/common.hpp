@@ -21,9 +21,11 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 //
 //   data[g][ks]  = 8 KiB tile: 128 rows x 4 chunks of 16 bytes; logical chunk
 //                  c (K bytes [16c, 16c+16) of the step) of row r sits at
-//                  chunk position c ^ swz(r), swz(r) = ((r >> 1) ^ (r >> 3)) & 3,
-//                  so the 16-byte fragment reads of 8 (or 16) consecutive
-//                  rows at one logical chunk hit distinct LDS bank groups;
+//                  chunk position c ^ swz(r), swz(r) = (r >> 2) & 3, so the
+//                  16-byte fragment reads of 16 consecutive rows at one
+//                  logical chunk cover all 64 LDS banks once (measured on
+//                  gfx950: no bank-conflict cycles; without the swizzle 2.2
+//                  conflict cycles per access);
 //   scale[g][ks] = 256 B: 128 rows x 2 UE8M0 bytes (MX blocks 2ks, 2ks+1).
 //
 // A tile is one contiguous run of bytes, so a GEMM workgroup copies it to LDS
@@ -34,7 +36,7 @@ constexpr int kStepK = 64;
 constexpr int kTileBytes = kGroupRows * kStepK;   // 8192
 constexpr int kTileScaleBytes = kGroupRows * 2;   // 256
 
-__host__ __device__ inline int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__host__ __device__ inline int swz(int r) { return (r >> 2) & 3; }
 // Byte offset of logical chunk c of row r inside a tile.
 __host__ __device__ inline int tile_off(int r, int c) { return r * kStepK + ((c ^ swz(r)) << 4); }
 
@@ -59,12 +61,13 @@ __host__ __device__ inline int tile_off(int r, int c) { return r * kStepK + ((c 
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// fp32 -> bf16, round to nearest even (finite inputs; NaN kept as NaN).
-__device__ inline uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two fp32 -> two bf16 (round to nearest even) packed in one word, low
+// half = a: one v_cvt_pk_bf16_f32.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // Magnitude bits (fp32 layout) of the two bf16 elements of a word.  Integer

@@ -134,14 +134,15 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_skinny_kernel(
     if (bias != nullptr && n + e < N) v[e] += __uint_as_float((uint32_t)bias[n + e] << 16);
   }
   uint16_t* yrow = y + (size_t)i * ldy;
+  const uint32_t lo = pack_bf16x2(v[0], v[1]);
+  const uint32_t hi = pack_bf16x2(v[2], v[3]);
   if (vec_store && n + 3 < N) {
-    const uint32_t lo = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-    const uint32_t hi = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
     *reinterpret_cast<uint2*>(yrow + n) = make_uint2(lo, hi);
   } else {
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (n + e < N) yrow[n + e] = (uint16_t)f32_to_bf16_rne(v[e]);
+    yrow[n] = (uint16_t)lo;
+    if (n + 1 < N) yrow[n + 1] = (uint16_t)(lo >> 16);
+    if (n + 2 < N) yrow[n + 2] = (uint16_t)hi;
+    if (n + 3 < N) yrow[n + 3] = (uint16_t)(hi >> 16);
   }
 }
 

@@ -223,17 +223,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(
 
   // ---------------- epilogue ----------------
   // Lane (li, lg) holds n = 32a + 8(r/4) + 4lg + r%4, m = 32b + li of the
-  // wave's 128 x 128 block.  Stage 64 rows (b = 2h, 2h+1) at a time.
+  // wave's 128 x 128 block.  Stage 64 rows (b = 2h, 2h+1) at a time in this
+  // wave's own LDS buffer, then read them back as 4 consecutive n per lane
+  // (a wave instruction covers two whole 256-byte output row segments).
   float* stage = reinterpret_cast<float*>(wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3);
-  const int n4 = lane & 31;          // readback: 4 consecutive n per lane
-  const int rsub = lane >> 5;        // readback: row parity
-  const int nw = tn * 256 + wn * 128;
-  const int nl = nw + 4 * n4;
+  const int n4 = lane & 31;
+  const int rsub = lane >> 5;
+  const int nl = tn * 256 + wn * 128 + 4 * n4;
   float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   if (bias != nullptr) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (nl + e < N) bv[e] = __uint_as_float((uint32_t)bias[nl + e] << 16);
+    for (int e = 0; e < 4; ++e) {
+      const float b = __uint_as_float((uint32_t)bias[min(nl + e, N - 1)] << 16);
+      bv[e] = (nl + e < N) ? b : 0.0f;
+    }
   }
   const bool full_n = nl + 3 < N;
 #pragma unroll
@@ -249,23 +252,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(
           *reinterpret_cast<float4*>(stage + (32 * b2 + li) * kEpiPitch + 32 * a + 8 * rr + 4 * lg) = f;
         }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    const int mbase = tm * 256 + wm * 128 + 64 * h;
-#pragma unroll 4
-    for (int it = 0; it < 32; ++it) {
-      const int row = 2 * it + rsub;
-      const int m = mbase + row;
-      const float4 f = *reinterpret_cast<const float4*>(stage + row * kEpiPitch + 4 * n4);
-      if (m >= M || nl >= N) continue;
-      const float v0 = f.x + bv[0], v1 = f.y + bv[1], v2 = f.z + bv[2], v3 = f.w + bv[3];
-      uint16_t* dst = y + (size_t)m * ldy + nl;
-      if (vec_store && full_n) {
-        *reinterpret_cast<uint2*>(dst) = make_uint2(f32_to_bf16_rne(v0) | (f32_to_bf16_rne(v1) << 16),
-                                                    f32_to_bf16_rne(v2) | (f32_to_bf16_rne(v3) << 16));
-      } else {
-        const float vv[4] = {v0, v1, v2, v3};
+    const int m_first = tm * 256 + wm * 128 + 64 * h + rsub;
+    const int rows_left = M - m_first;          // this lane's rows are m_first + 2 it
+    const float* src = stage + rsub * kEpiPitch + 4 * n4;
+    uint16_t* dst = y + (size_t)max(m_first, 0) * ldy + nl;
+    if (vec_store && full_n && rows_left >= 63) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (nl + e < N) dst[e] = (uint16_t)f32_to_bf16_rne(vv[e]);
+      for (int it = 0; it < 32; ++it) {
+        const float4 f = *reinterpret_cast<const float4*>(src + 2 * it * kEpiPitch);
+        *reinterpret_cast<uint2*>(dst + (size_t)(2 * it) * ldy) =
+            make_uint2(pack_bf16x2(f.x + bv[0], f.y + bv[1]), pack_bf16x2(f.z + bv[2], f.w + bv[3]));
+      }
+    } else if (nl < N) {
+      for (int it = 0; 2 * it < rows_left && it < 32; ++it) {
+        const float4 f = *reinterpret_cast<const float4*>(src + 2 * it * kEpiPitch);
+        const uint32_t lo = pack_bf16x2(f.x + bv[0], f.y + bv[1]);
+        const uint32_t hi = pack_bf16x2(f.z + bv[2], f.w + bv[3]);
+        uint16_t* d = dst + (size_t)(2 * it) * ldy;
+        d[0] = (uint16_t)lo;
+        if (nl + 1 < N) d[1] = (uint16_t)(lo >> 16);
+        if (nl + 2 < N) d[2] = (uint16_t)hi;
+        if (nl + 3 < N) d[3] = (uint16_t)(hi >> 16);
       }
     }
     // The next half overwrites the same rows: finish the reads first.
