@@ -59,11 +59,9 @@ size_t tile_ws_bytes(int64_t M, int64_t K) {
   return round_up(mp * (size_t)K, 256) + round_up(mp * (size_t)(K / 32), 256);
 }
 
-bool use_skinny(int64_t M) {
-  const int f = g_force_path.load(std::memory_order_relaxed);
-  if (f == 1) return false;
-  if (f == 2) return M <= mxfp8::kSkinnyMaxM;
-  return M <= mxfp8::kSkinnyMaxM;
+bool use_skinny(int64_t M, int64_t K) {
+  if (g_force_path.load(std::memory_order_relaxed) == 1) return false;
+  return M <= mxfp8::kSkinnyMaxM && K <= mxfp8::kSkinnyMaxK;
 }
 
 }  // namespace
@@ -126,7 +124,7 @@ int mxfp8_unpack_weight(const void* w_packed, const void* s_packed, int64_t N, i
 int mxfp8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes) {
   if (!bytes) return MXFP8_E_NULLPTR;
   if (M < 0 || N < 1 || K < 256 || K % 256 != 0) return MXFP8_E_SHAPE;
-  *bytes = (M == 0 || use_skinny(M)) ? 256 : tile_ws_bytes(M, K);
+  *bytes = (M == 0 || use_skinny(M, K)) ? 256 : tile_ws_bytes(M, K);
   return MXFP8_OK;
 }
 
@@ -141,7 +139,7 @@ int mxfp8_linear(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, const vo
   if (int st = check_output(y_bf16, N, ldy, bias_bf16)) return st;
   if (ldx < K || ldx % 8 != 0) return MXFP8_E_LD;
   if (!aligned(x_bf16, 16)) return MXFP8_E_ALIGN;
-  const bool skinny = use_skinny(M);
+  const bool skinny = use_skinny(M, K);
   const size_t need = skinny ? 256 : tile_ws_bytes(M, K);
   if (!workspace || workspace_bytes < need) return MXFP8_E_WORKSPACE;
   if (!aligned(workspace, 256)) return MXFP8_E_ALIGN;

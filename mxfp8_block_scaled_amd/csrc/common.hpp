@@ -113,4 +113,58 @@ __device__ inline void cvt8(const uint32_t* w, float inv, uint32_t* q) {
   q[1] = d1;
 }
 
+// ---------------------------------------------------------------------------
+// The same element conversion with gfx950's scaled converter
+// v_cvt_scalef32_pk_fp8_bf16: two bf16 -> two E4M3 bytes of RNE(x / scale),
+// one instruction per pair, bf16 subnormals and signed zero handled (probed
+// on the device against the rule for every bf16 value under scales 2^-127,
+// 2^-20..2^20, 2^119, 2^127: identical wherever |x / scale| < 512).  It does
+// not saturate: a value that rounds past 448 becomes the NaN code 0x7F/0xFF,
+// which fix_sat turns into 0x7E/0xFE, i.e. the saturation to +-448.
+// ---------------------------------------------------------------------------
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// 2^(s - 127) as fp32 for a scale byte s in [0, 246] (s = 0 is the fp32
+// subnormal 2^-127).
+__device__ inline float mx_scale_value(uint32_t sbyte) {
+  return __uint_as_float(sbyte ? (sbyte << 23) : 0x00400000u);
+}
+
+template <bool kHiWord>
+__device__ inline uint32_t cvt2s(uint32_t w, float scale, uint32_t old) {
+  const s16x2 o = __builtin_bit_cast(s16x2, old);
+  const bf16x2 v = __builtin_bit_cast(bf16x2, w);
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(o, v, scale, kHiWord));
+}
+
+// Bytes whose low 7 bits are all ones (E4M3 NaN) step down to 0x7E / 0xFE.
+__device__ inline uint32_t fix_sat(uint32_t q) {
+  const uint32_t m = ((q & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u;
+  return q - (m >> 7);
+}
+
+// Four bf16 words (8 elements) -> two dwords of E4M3 bytes with the scale
+// 2^(e_s) passed as a value.
+__device__ inline void cvt8s(const uint32_t* w, float scale, uint32_t* q) {
+  uint32_t d0 = cvt2s<false>(w[0], scale, 0u);
+  d0 = cvt2s<true>(w[1], scale, d0);
+  uint32_t d1 = cvt2s<false>(w[2], scale, 0u);
+  d1 = cvt2s<true>(w[3], scale, d1);
+  q[0] = fix_sat(d0);
+  q[1] = fix_sat(d1);
+}
+
+// Running maximum of bf16 magnitudes, two lanes of 16 bits (v_pk_max_u16 on
+// the sign-cleared words; integer order = magnitude order for finite bf16).
+__device__ inline u16x2 absmax_pk(u16x2 acc, uint32_t w) {
+  return __builtin_elementwise_max(acc, __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu));
+}
+// Scale byte from a packed maximum: bf16 exponent field F = bits >> 7 equals
+// the fp32 one, so the byte is max(F - 8, 0) as in mx_scale_byte.
+__device__ inline uint32_t mx_scale_byte_bf16(u16x2 m) {
+  const uint32_t b = max((uint32_t)m[0], (uint32_t)m[1]);
+  return (uint32_t)max((int)(b >> 7) - 8, 0);
+}
+
 }  // namespace mxfp8

@@ -1,20 +1,22 @@
-// Skinny (decode-shaped, M <= 16) MXFP8 linear layer in one kernel: the
-// activation quantization is fused into the GEMM's operand load.
+// Skinny (decode-shaped, M <= 16) MXFP8 linear layer in one kernel, with the
+// activation quantization fused in.
 //
-// At M <= 16 the layer streams the whole packed weight once (N*K bytes + 1/32
-// of that in scales) and is bound by HBM bandwidth; the activations are a few
-// KiB and stay in L2.  Each workgroup owns 16 weight rows over the whole K;
-// its waves split K and each streams its share with independent 16-byte
-// loads, quantizing the matching activation blocks in registers, and one
-// v_mfma_scale_f32_16x16x128_f8f6f4 per 128-element K step (weight as the A
-// operand: 16 n x 16 m).  The per-wave partial sums are reduced through LDS;
-// wave 0 adds bias and writes bf16.
-//
-// Operand bytes of lane (i, g) (common.hpp): K [16g, 16g+16) and
-// [64+16g, 64+16g+16) of the step, i.e. halves of MX blocks g/2 and 2+g/2.
-// Lanes g and g^1 (lane ^ 16) hold the two halves of the same two blocks and
-// combine their block maxima with one exchange.  The MFMA takes the scale of
-// block b from lane group b, so groups 1 and 2 swap one scale (lane ^ 48).
+// At M <= 16 the layer streams the whole packed weight once (N*K bytes plus
+// 1/32 of that in scales): it is bound by HBM bandwidth and by how many
+// requests are in flight.  One workgroup owns 16 weight rows over the whole K:
+//  1. each of its 16 waves first issues the loads of its share of those rows
+//     (one 128-deep K step = 2 x 16 bytes per lane), so the HBM latency runs
+//     while the rest of the prologue works;
+//  2. the workgroup quantizes the M real activation rows (M x K bf16, read
+//     from L2) once, cooperatively, into LDS -- E4M3 bytes and UE8M0 scales
+//     by the MX rule, with gfx950's scaled converter;
+//  3. each wave runs one v_mfma_scale_f32_16x16x128_f8f6f4 per K step
+//     (weight rows as the A operand, activation rows as B, from LDS);
+//  4. the 16 per-wave partial sums are reduced through LDS; wave 0 adds the
+//     bias and writes bf16.
+// Operand bytes of lane (i, g) of the MFMA (common.hpp): K [16g, 16g+16) and
+// [64+16g, 64+16g+16) of the step; the scale of MX block b comes from lane
+// group b.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -22,108 +24,119 @@ namespace mxfp8 {
 
 namespace {
 
-constexpr int kWaves = 8;
-constexpr int kUnroll = 4;
-
-struct StepLoads {
-  uint4 w0, w1;          // weight operand, two 16-byte halves
-  uint32_t wsd;          // the weight row's scale word holding this lane's block
-  uint4 x0, x1, x2, x3;  // 32 bf16 activations: 16 at 16g, 16 at 64 + 16g
-};
-
-// One 128-deep K step = packed tiles 2ks and 2ks+1.  Lane (i, g) takes chunk g
-// of row r from each; its scale (MX block g of the step) is byte g&1 of the
-// row's word in tile 2ks + g/2.
-__device__ inline void step_load(StepLoads& L, const uint8_t* wrow, int woff, const uint8_t* srow, int g,
-                                 const uint16_t* xrow, int ks) {
-  const uint8_t* wt = wrow + (size_t)(2 * ks) * kTileBytes + woff;
-  L.w0 = *reinterpret_cast<const uint4*>(wt);
-  L.w1 = *reinterpret_cast<const uint4*>(wt + kTileBytes);
-  L.wsd = (uint32_t)*reinterpret_cast<const uint16_t*>(srow + (size_t)(2 * ks + (g >> 1)) * kTileScaleBytes);
-  const uint16_t* xk = xrow + (size_t)ks * 128;
-  L.x0 = *reinterpret_cast<const uint4*>(xk);
-  L.x1 = *reinterpret_cast<const uint4*>(xk + 8);
-  L.x2 = *reinterpret_cast<const uint4*>(xk + 64);
-  L.x3 = *reinterpret_cast<const uint4*>(xk + 72);
-}
-
-__device__ inline v4f step_compute(const StepLoads& L, int g, v4f acc) {
-  const uint32_t h0[8] = {L.x0.x, L.x0.y, L.x0.z, L.x0.w, L.x1.x, L.x1.y, L.x1.z, L.x1.w};
-  const uint32_t h1[8] = {L.x2.x, L.x2.y, L.x2.z, L.x2.w, L.x3.x, L.x3.y, L.x3.z, L.x3.w};
-  uint32_t m0 = 0, m1 = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    m0 = absmax_bits(m0, h0[i]);
-    m1 = absmax_bits(m1, h1[i]);
-  }
-  m0 = max(m0, (uint32_t)__shfl_xor((int)m0, 16));
-  m1 = max(m1, (uint32_t)__shfl_xor((int)m1, 16));
-  const uint32_t s0 = mx_scale_byte(m0);  // block g/2
-  const uint32_t s1 = mx_scale_byte(m1);  // block 2 + g/2
-  // Lane group b must present the scale of block b: group 0 has block 0 (s0),
-  // group 3 has block 3 (s1); groups 1 and 2 trade (block 1 lives in groups
-  // 2/3 as s0, block 2 in groups 0/1 as s1).
-  const uint32_t give = (g >= 2) ? s0 : s1;
-  const uint32_t got = (uint32_t)__shfl_xor((int)give, 48);
-  const uint32_t xscale = (g == 0) ? s0 : (g == 3) ? s1 : got;
-  uint32_t q[8];
-  cvt8(h0, mx_inv_scale(s0), q);
-  cvt8(h0 + 4, mx_inv_scale(s0), q + 2);
-  cvt8(h1, mx_inv_scale(s1), q + 4);
-  cvt8(h1 + 4, mx_inv_scale(s1), q + 6);
-  v8i xb, wa;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) xb[i] = (int)q[i];
-  wa[0] = (int)L.w0.x; wa[1] = (int)L.w0.y; wa[2] = (int)L.w0.z; wa[3] = (int)L.w0.w;
-  wa[4] = (int)L.w1.x; wa[5] = (int)L.w1.y; wa[6] = (int)L.w1.z; wa[7] = (int)L.w1.w;
-  const int wscale = (int)(L.wsd >> (8 * (g & 1)));
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wa, xb, acc, 0, 0, 0, wscale, 0, (int)xscale);
-}
+constexpr int kWaves = 16;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kMaxSteps = 4;   // K steps per wave: K <= 16 * 4 * 128 = 8192
+constexpr int kBatch = 8;      // activation chunks in flight per thread
 
 }  // namespace
 
-__global__ __launch_bounds__(64 * kWaves) void gemm_skinny_kernel(
+// LDS: activations [16][K + 16] E4M3 bytes (row pitch K + 16 puts the 16
+// rows' fragment reads on distinct banks), scales [16][K/32], partial sums
+// [16 waves][64 lanes] x 16 bytes.
+__global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int M, int K, const uint8_t* __restrict__ wp,
     const uint8_t* __restrict__ sp, int N, const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
     int64_t ldy, int vec_store) {
-  __shared__ v4f red[kWaves][64];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int pitch = K + 16;
+  uint8_t* xq = smem;
+  uint8_t* xs = smem + 16 * pitch;
+  v4f* red = reinterpret_cast<v4f*>(xs + 16 * (K / 32));
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int i = lane & 15, g = lane >> 4;
   const int n0 = blockIdx.x * 16;
   const int grp = n0 / kGroupRows;
   const int r = (n0 % kGroupRows) + i;
   const int KT = K / kStepK;   // packed tiles along K
   const int KS = K / 128;      // MFMA steps along K
-
-  const uint8_t* wrow = wp + (size_t)grp * KT * kTileBytes;
-  const int woff = tile_off(r, g);
-  const uint8_t* srow = sp + (size_t)grp * KT * kTileScaleBytes + r * 2;
-  const int m = min(i, M - 1);
-  const uint16_t* xrow = x + (size_t)m * ldx + 16 * g;
-
   const int kb = (KS * wave) / kWaves, ke = (KS * (wave + 1)) / kWaves;
-  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  int ks = kb;
-  for (; ks + kUnroll <= ke; ks += kUnroll) {
-    StepLoads L[kUnroll];
+
+  // 1. Weight loads for this wave's steps (tiles 2ks and 2ks+1, chunk g of
+  // row r; the scale word of tile 2ks + g/2 holds this lane's block).
+  const uint8_t* wrow = wp + (size_t)grp * KT * kTileBytes + tile_off(r, g);
+  const uint8_t* srow = sp + (size_t)grp * KT * kTileScaleBytes + r * 2;
+  uint4 w0[kMaxSteps], w1[kMaxSteps];
+  uint32_t wsd[kMaxSteps];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) step_load(L[u], wrow, woff, srow, g, xrow, ks + u);
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) acc = step_compute(L[u], g, acc);
-  }
-  for (; ks < ke; ++ks) {
-    StepLoads L;
-    step_load(L, wrow, woff, srow, g, xrow, ks);
-    acc = step_compute(L, g, acc);
+  for (int u = 0; u < kMaxSteps; ++u) {
+    if (kb + u < ke) {
+      const uint8_t* wt = wrow + (size_t)(2 * (kb + u)) * kTileBytes;
+      w0[u] = *reinterpret_cast<const uint4*>(wt);
+      w1[u] = *reinterpret_cast<const uint4*>(wt + kTileBytes);
+      wsd[u] = *reinterpret_cast<const uint16_t*>(srow + (size_t)(2 * (kb + u) + (g >> 1)) * kTileScaleBytes);
+    }
   }
 
-  red[wave][lane] = acc;
+  // 2. Quantize x[0:M, 0:K] into LDS: four threads per 32-element block,
+  // eight elements (16 bytes) each; a thread issues the loads of up to
+  // kBatch chunks before converting any, so their L2 latencies overlap.
+  const int per_row = K / 8;
+  const int chunks = M * per_row;
+  for (int c0 = tid; c0 < chunks; c0 += kBatch * kThreads) {
+    uint4 v[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int c = c0 + b * kThreads;
+      if (c < chunks) {
+        const int row = c / per_row, c8 = c - row * per_row;
+        v[b] = *reinterpret_cast<const uint4*>(x + (size_t)row * ldx + c8 * 8);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int c = c0 + b * kThreads;
+      if (c < chunks) {
+        const int row = c / per_row, c8 = c - row * per_row;
+        const uint32_t wv[4] = {v[b].x, v[b].y, v[b].z, v[b].w};
+        u16x2 m = {0, 0};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m = absmax_pk(m, wv[e]);
+        uint32_t mm = max((uint32_t)m[0], (uint32_t)m[1]);
+        mm = max(mm, (uint32_t)__shfl_xor((int)mm, 1));
+        mm = max(mm, (uint32_t)__shfl_xor((int)mm, 2));
+        const uint32_t sb = (uint32_t)max((int)(mm >> 7) - 8, 0);
+        uint32_t q[2];
+        cvt8s(wv, mx_scale_value(sb), q);
+        *reinterpret_cast<uint2*>(xq + row * pitch + c8 * 8) = make_uint2(q[0], q[1]);
+        if ((c8 & 3) == 0) xs[row * (K / 32) + (c8 >> 2)] = (uint8_t)sb;
+      }
+    }
+  }
+  __syncthreads();
+
+  // 3. MFMA steps.  Lanes i >= M use row M-1 (their outputs are dropped).
+  const int m = min(i, M - 1);
+  const uint8_t* xr = xq + m * pitch + 16 * g;
+  const uint8_t* sr = xs + m * (K / 32) + g;
+  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int u = 0; u < kMaxSteps; ++u) {
+    if (kb + u < ke) {
+      const int ks = kb + u;
+      const uint4 b0 = *reinterpret_cast<const uint4*>(xr + ks * 128);
+      const uint4 b1 = *reinterpret_cast<const uint4*>(xr + ks * 128 + 64);
+      const int xscale = sr[ks * 4];
+      v8i wa, xb;
+      wa[0] = (int)w0[u].x; wa[1] = (int)w0[u].y; wa[2] = (int)w0[u].z; wa[3] = (int)w0[u].w;
+      wa[4] = (int)w1[u].x; wa[5] = (int)w1[u].y; wa[6] = (int)w1[u].z; wa[7] = (int)w1[u].w;
+      xb[0] = (int)b0.x; xb[1] = (int)b0.y; xb[2] = (int)b0.z; xb[3] = (int)b0.w;
+      xb[4] = (int)b1.x; xb[5] = (int)b1.y; xb[6] = (int)b1.z; xb[7] = (int)b1.w;
+      const int wscale = (int)(wsd[u] >> (8 * (g & 1)));
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wa, xb, acc, 0, 0, 0, wscale, 0, xscale);
+    }
+  }
+
+  // 4. Reduce the waves' partial sums; lane (i, g) of wave 0 holds
+  // D[n = 4g + j][m = i], j = 0..3.
+  red[wave * 64 + lane] = acc;
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
-  for (int w = 1; w < kWaves; ++w) acc += red[w][lane];
-  // Lane (i, g) holds D[n = 4g + j][m = i], j = 0..3.
+  for (int w = 1; w < kWaves; ++w) acc += red[w * 64 + lane];
   if (i >= M) return;
   const int n = n0 + 4 * g;
   if (n >= N) return;
@@ -150,7 +163,13 @@ int launch_gemm_skinny(const void* x, int64_t ldx, int64_t M, int64_t K, const v
                        int64_t N, const void* bias, void* y, int64_t ldy, hipStream_t stream) {
   const int blocks = (int)((N + 15) / 16);
   const int vec = (ldy % 4 == 0) && (((uintptr_t)y & 7) == 0);
-  hipLaunchKernelGGL(gemm_skinny_kernel, dim3(blocks), dim3(64 * kWaves), 0, stream, (const uint16_t*)x, ldx,
+  const size_t lds = (size_t)16 * (K + 16) + (size_t)16 * (K / 32) + (size_t)kWaves * 64 * 16;
+  static const bool lds_ok = hipFuncSetAttribute((const void*)gemm_skinny_kernel,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 16 * (kSkinnyMaxK + 16) + 16 * (kSkinnyMaxK / 32) +
+                                                     kWaves * 64 * 16) == hipSuccess;
+  if (!lds_ok) return -7;
+  hipLaunchKernelGGL(gemm_skinny_kernel, dim3(blocks), dim3(kThreads), lds, stream, (const uint16_t*)x, ldx,
                      (int)M, (int)K, (const uint8_t*)wp, (const uint8_t*)sp, (int)N, (const uint16_t*)bias,
                      (uint16_t*)y, ldy, vec);
   return hipGetLastError() == hipSuccess ? 0 : -7;

@@ -25,8 +25,10 @@ int launch_unpack_weight(const void* wp, const void* sp, int64_t N, int64_t K, v
 int launch_gemm_tile(const void* qp, const void* sp, int64_t M, int64_t K, const void* wp, const void* wsp,
                      int64_t N, const void* bias, void* y, int64_t ldy, hipStream_t stream);
 
-// Skinny GEMM with the activation quantization fused in (M <= kSkinnyMaxM).
+// Skinny GEMM with the activation quantization fused in (M <= kSkinnyMaxM,
+// K <= kSkinnyMaxK).
 constexpr int64_t kSkinnyMaxM = 16;
+constexpr int64_t kSkinnyMaxK = 8192;
 int launch_gemm_skinny(const void* x, int64_t ldx, int64_t M, int64_t K, const void* wp, const void* sp,
                        int64_t N, const void* bias, void* y, int64_t ldy, hipStream_t stream);
 

@@ -8,8 +8,10 @@
 // HBM-bound: 2 bytes read + 1 + 1/32 bytes written per element.  Four
 // consecutive lanes own one 32-element block, each loading 16 contiguous
 // bytes (8 elements), so a wave's loads cover 1 KiB of one or more rows
-// without gaps; the block maximum is combined across the four lanes with two
-// lane exchanges, and each lane writes its 8 E4M3 bytes as one 8-byte store.
+// without gaps; the block maximum (packed 16-bit integer max of the
+// magnitudes) is combined across the four lanes with two lane exchanges, the
+// elements go through the hardware scaled converter (common.hpp), and each
+// lane writes its 8 E4M3 bytes as one 8-byte store.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -29,14 +31,15 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
   const Idx c8 = t - row * chunks_per_row;
   const uint4 v = *reinterpret_cast<const uint4*>(x + (int64_t)row * ldx + (int64_t)c8 * 8);
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  uint32_t m = 0;
+  u16x2 mp = {0, 0};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) m = absmax_bits(m, w[i]);
+  for (int i = 0; i < 4; ++i) mp = absmax_pk(mp, w[i]);
+  uint32_t m = max((uint32_t)mp[0], (uint32_t)mp[1]);
   m = max(m, (uint32_t)__shfl_xor((int)m, 1));
   m = max(m, (uint32_t)__shfl_xor((int)m, 2));
-  const uint32_t sb = mx_scale_byte(m);
+  const uint32_t sb = (uint32_t)max((int)(m >> 7) - 8, 0);
   uint32_t qd[2];
-  cvt8(w, mx_inv_scale(sb), qd);
+  cvt8s(w, mx_scale_value(sb), qd);
   if (valid) {
     *reinterpret_cast<uint2*>(q + (int64_t)row * ldq + (int64_t)c8 * 8) = make_uint2(qd[0], qd[1]);
     if ((c8 & 3) == 0) s[(int64_t)row * lds + (int64_t)(c8 >> 2)] = (uint8_t)sb;
@@ -60,14 +63,15 @@ __global__ __launch_bounds__(256) void quant_act_packed_kernel(const uint16_t* _
     const uint4 v = *reinterpret_cast<const uint4*>(x + (int64_t)row * ldx + (int64_t)c8 * 8);
     w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
   }
-  uint32_t m = 0;
+  u16x2 mp = {0, 0};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) m = absmax_bits(m, w[i]);
+  for (int i = 0; i < 4; ++i) mp = absmax_pk(mp, w[i]);
+  uint32_t m = max((uint32_t)mp[0], (uint32_t)mp[1]);
   m = max(m, (uint32_t)__shfl_xor((int)m, 1));
   m = max(m, (uint32_t)__shfl_xor((int)m, 2));
-  const uint32_t sb = mx_scale_byte(m);
+  const uint32_t sb = (uint32_t)max((int)(m >> 7) - 8, 0);
   uint32_t qd[2];
-  cvt8(w, mx_inv_scale(sb), qd);
+  cvt8s(w, mx_scale_value(sb), qd);
   if (valid) {
     const int64_t g = (int64_t)row / kGroupRows;
     const int r = (int)((int64_t)row % kGroupRows);
