@@ -14,12 +14,17 @@
 //  * Both operands arrive in the packed tile layout of common.hpp (8 KiB per
 //    128 rows x 64 K-bytes, contiguous), so a stage is four contiguous runs
 //    copied straight into LDS by global_load_lds_dwordx4 / _dword.
-//  * K advances 64 per stage; four LDS stages (4 x 33 KiB) keep three stages
-//    of loads in flight while one computes.  Each stage lives in its own
-//    __shared__ array and the loop is unrolled by four, so every LDS access
-//    names a distinct array: the compiler then needs no blanket vmcnt(0)
-//    before the fragment reads, and the kernel waits only for the stage it
-//    is about to use (partial vmcnt).
+//  * K advances 64 per stage; four LDS stages (4 x 33 KiB).  Each stage
+//    lives in its own __shared__ array and the loop is unrolled by four, so
+//    every LDS access names a distinct array: the compiler then needs no
+//    blanket vmcnt(0) before the fragment reads, and the kernel waits only
+//    for the stage it is about to use (partial vmcnt).
+//  * Software pipeline per 64-K step s: the MFMA operands of s are already in
+//    registers; each of the step's 16 MFMAs is followed by one of the 9 copies
+//    of step s+4 (into the buffer that held s) and by a slice of the LDS
+//    fragment reads of step s+1.  The copies then trickle into the memory
+//    pipeline at the MFMA rate instead of stalling the wave in a burst, and
+//    the fragment reads are hidden under the MFMAs.  One barrier per step.
 //  * Epilogue through LDS: each wave parks its fp32 accumulators (64 rows at a
 //    time) in an LDS stage buffer, reads them back row-contiguous, adds the
 //    bias (loaded once per lane) and writes bf16 with 8-byte stores that
@@ -52,22 +57,12 @@ constexpr int kEpiPitch = 132;                        // floats per staged row (
 // global loads can only be more conservative, never less.
 __device__ inline uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
 __device__ inline void g2l_16(const void* g, const uint8_t* lds_wave_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr(lds_wave_base))
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr(lds_wave_base))
                : "memory", "m0");
 }
 __device__ inline void g2l_4(const void* g, const uint8_t* lds_wave_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_addr(lds_wave_base))
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_addr(lds_wave_base))
                : "memory", "m0");
-}
-
-// 32x32x64 operand of row R: K bytes [16g, 16g+16) and [32+16g, 32+16g+16).
-__device__ inline v8i lds_frag(const uint8_t* base, int R, int g) {
-  const uint4 a = *reinterpret_cast<const uint4*>(base + tile_off(R, g));
-  const uint4 b = *reinterpret_cast<const uint4*>(base + tile_off(R, 2 + g));
-  v8i v;
-  v[0] = (int)a.x; v[1] = (int)a.y; v[2] = (int)a.z; v[3] = (int)a.w;
-  v[4] = (int)b.x; v[5] = (int)b.y; v[6] = (int)b.z; v[7] = (int)b.w;
-  return v;
 }
 
 // Bijection from dispatch order to a tile order in which XCD x (which gets
@@ -82,7 +77,8 @@ template <int N>
 __device__ inline void wait_vmcnt() {
   if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   else if constexpr (N == kLoadsPerStage) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+  else if constexpr (N == 2 * kLoadsPerStage) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(27)" ::: "memory");
 }
 
 }  // namespace
@@ -127,20 +123,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(
   const uint8_t* ssrc = (sg == 0 ? wsp + wa * sc_stride : sg == 1 ? wsp + wb * sc_stride
                          : sg == 2 ? qsp + xa * sc_stride : qsp + xb * sc_stride) + (tid & 63) * 4;
 
-  auto issue = [&](int ks, uint8_t* st) {
-    uint8_t* base = st + wave * 1024;
-    const size_t off = (size_t)ks * kTileBytes;
-    g2l_16(w0 + off, base);
-    g2l_16(w0 + off + 4096, base + 4096);
-    g2l_16(w1 + off, base + 8192);
-    g2l_16(w1 + off + 4096, base + 12288);
-    g2l_16(x0 + off, base + kOpBytes);
-    g2l_16(x0 + off + 4096, base + kOpBytes + 4096);
-    g2l_16(x1 + off, base + kOpBytes + 8192);
-    g2l_16(x1 + off + 4096, base + kOpBytes + 12288);
-    g2l_4(ssrc + (size_t)ks * kTileScaleBytes, st + 2 * kOpBytes + wave * 256);
-  };
-
   const int wn = wave >> 1, wm = wave & 1;
   const int li = lane & 31, lg = lane >> 5;
 
@@ -152,49 +134,77 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
-  // One 64-deep K step from an LDS stage: lane group lg supplies the scale of
-  // MX block lg of the step (byte lg of the row's scale word).
-  auto compute = [&](const uint8_t* st) {
-    const uint8_t* xs = st + kOpBytes;
-    const uint16_t* wsc = reinterpret_cast<const uint16_t*>(st + 2 * kOpBytes);
-    const uint16_t* xsc = wsc + 256;
-    int sw[4], sx[4];
-    v8i fa[4], fb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sw[i] = (int)((uint32_t)wsc[wn * 128 + 32 * i + li] >> (8 * lg));
-      sx[i] = (int)((uint32_t)xsc[wm * 128 + 32 * i + li] >> (8 * lg));
-      fa[i] = lds_frag(st, wn * 128 + 32 * i + li, lg);
-      fb[i] = lds_frag(xs, wm * 128 + 32 * i + li, lg);
+  // Fragments of one 64-deep K step (both operands, with the scale bytes of
+  // the lane's rows: lane group lg supplies MX block lg of the step).
+  struct Frags {
+    v8i a[4], b[4];
+    int sa[4], sb[4];
+  };
+  // Lane offsets inside a stage: rows R0 + 32 i share the swizzle of R0
+  // (swz depends on bits 2-3 of the row only), so fragment i is 2048 i bytes
+  // further; scale bytes sit at row * 2 + block.
+  const int offWa = tile_off(wn * 128 + li, lg), offWb = tile_off(wn * 128 + li, 2 + lg);
+  const int offXa = kOpBytes + tile_off(wm * 128 + li, lg), offXb = kOpBytes + tile_off(wm * 128 + li, 2 + lg);
+  const int offSw = 2 * kOpBytes + (wn * 128 + li) * 2 + lg;
+  const int offSx = 2 * kOpBytes + 512 + (wm * 128 + li) * 2 + lg;
+  auto rd16 = [](const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); };
+  // Copy j (0..8) of this thread's share of step ks into stage st.
+  auto dma_one = [&](int j, int ks, uint8_t* st) {
+    uint8_t* base = st + wave * 1024;
+    const size_t off = (size_t)ks * kTileBytes;
+    switch (j) {
+      case 0: g2l_16(w0 + off, base); break;
+      case 1: g2l_16(w0 + off + 4096, base + 4096); break;
+      case 2: g2l_16(w1 + off, base + 8192); break;
+      case 3: g2l_16(w1 + off + 4096, base + 12288); break;
+      case 4: g2l_16(x0 + off, base + kOpBytes); break;
+      case 5: g2l_16(x0 + off + 4096, base + kOpBytes + 4096); break;
+      case 6: g2l_16(x1 + off, base + kOpBytes + 8192); break;
+      case 7: g2l_16(x1 + off + 4096, base + kOpBytes + 12288); break;
+      default: g2l_4(ssrc + (size_t)ks * kTileScaleBytes, st + 2 * kOpBytes + wave * 256); break;
     }
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[a], fb[b], acc[a][b], 0, 0, 0, sw[a], 0,
-                                                                    sx[b]);
+  };
+  // Part j (0..15) of the fragment reads of a stage.
+  auto read_part = [&](int j, const uint8_t* st, Frags& f) {
+    if (j < 8) {
+      const int i = j >> 1;
+      if ((j & 1) == 0) {
+        const uint4 a0 = rd16(st + offWa + 2048 * i), a1 = rd16(st + offWb + 2048 * i);
+        f.a[i] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+      } else {
+        const uint4 b0 = rd16(st + offXa + 2048 * i), b1 = rd16(st + offXb + 2048 * i);
+        f.b[i] = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+      }
+    } else if (j < 12) {
+      f.sa[j - 8] = st[offSw + 64 * (j - 8)];
+    } else {
+      f.sb[j - 12] = st[offSx + 64 * (j - 12)];
+    }
   };
 
-  // After computing step s, wait until step s+1 has landed: the loads of the
-  // (at most two) later steps already issued may stay in flight.
-  // One K step: optionally issue the copy of step s+3 into the buffer freed by
-  // step s-1, compute from this step's buffer, then wait until step s+1 has
-  // landed (LATER = number of copies issued after it, still allowed in
-  // flight).  The body has no branches, so the MFMAs stay between their own
-  // barriers; the scheduling fences keep the next step's fragment reads from
-  // being hoisted above the barrier.
-  //
-  // The barrier is a bare s_barrier: the copies of step s+1 are complete in
-  // LDS once this wave's vmcnt says so, and every wave waits for its own
-  // before arriving.  (__syncthreads() would add a workgroup fence, i.e. a
-  // vmcnt(0) that drains the copies still meant to be in flight.)
-  auto step = [&](auto do_issue, auto later, int s, uint8_t* st_issue, const uint8_t* st_use) {
-    if constexpr (decltype(do_issue)::value) issue(s + 3, st_issue);
-    compute(st_use);
-    __builtin_amdgcn_sched_barrier(0);
+  // One K step s.  On entry the fragments of s are in registers (cur) and
+  // the copies of s+1 .. s+3 are in flight.  Wait until s+1 has landed in
+  // every wave (own vmcnt, then the barrier); then each of the 16 MFMAs of s
+  // is followed by one copy of s+4 (into the buffer that held s) and one
+  // part of the fragment reads of s+1, so the copy and read traffic is spread
+  // over the MFMA stream.  Before the next barrier every wave drains its LDS
+  // reads, so the buffer of s+1 may be refilled after it.
+  auto step = [&](auto do_issue, auto later, auto do_next, int s, uint8_t* st_free, const uint8_t* st_next,
+                  const Frags& cur, Frags& nxt) {
     wait_vmcnt<decltype(later)::value * kLoadsPerStage>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      acc[j >> 2][j & 3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          cur.a[j >> 2], cur.b[j & 3], acc[j >> 2][j & 3], 0, 0, 0, cur.sa[j >> 2], 0, cur.sb[j & 3]);
+      if constexpr (decltype(do_issue)::value) {
+        if (j < kLoadsPerStage) dma_one(j, s + 4, st_free);
+      }
+      if constexpr (decltype(do_next)::value) read_part(j, st_next, nxt);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   };
   using T = std::true_type;
   using F = std::false_type;
@@ -203,23 +213,34 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(
   using L2 = std::integral_constant<int, 2>;
 
   // KS is a multiple of 4 (K % 256 == 0) and at least 4.
-  issue(0, st0);
-  issue(1, st1);
-  issue(2, st2);
-  wait_vmcnt<2 * kLoadsPerStage>();
+  Frags f0, f1;
+  // Stage-major issue order: vmcnt retires loads in order, so "at most 27
+  // outstanding" means all of stage 0 has landed.
+#pragma unroll
+  for (int j = 0; j < kLoadsPerStage; ++j) dma_one(j, 0, st0);
+#pragma unroll
+  for (int j = 0; j < kLoadsPerStage; ++j) dma_one(j, 1, st1);
+#pragma unroll
+  for (int j = 0; j < kLoadsPerStage; ++j) dma_one(j, 2, st2);
+#pragma unroll
+  for (int j = 0; j < kLoadsPerStage; ++j) dma_one(j, 3, st3);
+  wait_vmcnt<3 * kLoadsPerStage>();
   __builtin_amdgcn_s_barrier();
+#pragma unroll
+  for (int j = 0; j < 16; ++j) read_part(j, st0, f0);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   int ks = 0;
-  for (; ks + 4 < KS; ks += 4) {
-    step(T{}, L2{}, ks, st3, st0);
-    step(T{}, L2{}, ks + 1, st0, st1);
-    step(T{}, L2{}, ks + 2, st1, st2);
-    step(T{}, L2{}, ks + 3, st2, st3);
+  for (; ks + 8 <= KS; ks += 4) {
+    step(T{}, L2{}, T{}, ks, st0, st1, f0, f1);
+    step(T{}, L2{}, T{}, ks + 1, st1, st2, f1, f0);
+    step(T{}, L2{}, T{}, ks + 2, st2, st3, f0, f1);
+    step(T{}, L2{}, T{}, ks + 3, st3, st0, f1, f0);
   }
-  // Last four steps: only the first still has a copy to issue (step KS-1).
-  step(T{}, L2{}, ks, st3, st0);
-  step(F{}, L1{}, ks + 1, st0, st1);
-  step(F{}, L0{}, ks + 2, st1, st2);
-  step(F{}, L0{}, ks + 3, st2, st3);
+  // Last four steps: nothing left to copy.
+  step(F{}, L2{}, T{}, ks, st0, st1, f0, f1);
+  step(F{}, L1{}, T{}, ks + 1, st1, st2, f1, f0);
+  step(F{}, L0{}, T{}, ks + 2, st2, st3, f0, f1);
+  step(F{}, L0{}, F{}, ks + 3, st3, st0, f1, f0);
 
   // ---------------- epilogue ----------------
   // Lane (li, lg) holds n = 32a + 8(r/4) + 4lg + r%4, m = 32b + li of the
