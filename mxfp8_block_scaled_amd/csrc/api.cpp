@@ -140,6 +140,7 @@ int mxfp8_linear(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, const vo
   if (ldx < K || ldx % 8 != 0) return MXFP8_E_LD;
   if (!aligned(x_bf16, 16)) return MXFP8_E_ALIGN;
   const bool skinny = use_skinny(M, K);
+  if (!skinny && (n_pad(M) * (K / 8) + 255) / 256 > INT32_MAX) return MXFP8_E_SHAPE;
   const size_t need = skinny ? 256 : tile_ws_bytes(M, K);
   if (!workspace || workspace_bytes < need) return MXFP8_E_WORKSPACE;
   if (!aligned(workspace, 256)) return MXFP8_E_ALIGN;

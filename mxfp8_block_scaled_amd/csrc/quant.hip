@@ -49,18 +49,24 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
 // Same quantization, written in the packed operand layout of common.hpp for
 // the large-M GEMM (rows padded to a multiple of 128; pad rows are written as
 // zero elements with scale byte 0, so every byte the GEMM reads is defined).
+// Threads are numbered tile by tile (1024 per 128-row x 64-K tile, row-major
+// inside it): a wave then reads 8 rows x 128 bytes and writes 512 contiguous
+// bytes of one packed tile.
 template <typename Idx>
 __global__ __launch_bounds__(256) void quant_act_packed_kernel(const uint16_t* __restrict__ x, int64_t ldx, int M,
-                                                               Idx chunks_per_row, Idx total, int64_t KS,
+                                                               Idx total, int64_t KS,
                                                                uint8_t* __restrict__ qp, uint8_t* __restrict__ sp) {
   Idx t = (Idx)blockIdx.x * 256 + threadIdx.x;
-  const bool valid = t < total;
-  if (!valid) t = total - 1;
-  const Idx row = t / chunks_per_row;
-  const Idx c8 = t - row * chunks_per_row;
+  if (t >= total) return;  // total is a multiple of 1024: whole waves leave
+  const Idx tile = t >> 10;                 // g * KS + ks
+  const int r = (int)((t >> 3) & 127);      // row inside the 128-row group
+  const int c8 = (int)(t & 7);              // 8-element chunk inside the 64-K step
+  const int64_t g = (int64_t)(tile / (Idx)KS);
+  const int64_t ks = (int64_t)tile - g * KS;
+  const int64_t row = g * kGroupRows + r;
   uint32_t w[4] = {0u, 0u, 0u, 0u};
-  if ((int64_t)row < M) {
-    const uint4 v = *reinterpret_cast<const uint4*>(x + (int64_t)row * ldx + (int64_t)c8 * 8);
+  if (row < M) {
+    const uint4 v = *reinterpret_cast<const uint4*>(x + row * ldx + ks * kStepK + c8 * 8);
     w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
   }
   u16x2 mp = {0, 0};
@@ -72,34 +78,23 @@ __global__ __launch_bounds__(256) void quant_act_packed_kernel(const uint16_t* _
   const uint32_t sb = (uint32_t)max((int)(m >> 7) - 8, 0);
   uint32_t qd[2];
   cvt8s(w, mx_scale_value(sb), qd);
-  if (valid) {
-    const int64_t g = (int64_t)row / kGroupRows;
-    const int r = (int)((int64_t)row % kGroupRows);
-    const int64_t k = (int64_t)c8 * 8;
-    const int64_t ks = k / kStepK;
-    const int c = (int)((k % kStepK) >> 4);
-    const int half = (int)((k >> 3) & 1);
-    uint8_t* tile = qp + (g * KS + ks) * kTileBytes;
-    *reinterpret_cast<uint2*>(tile + tile_off(r, c) + half * 8) = make_uint2(qd[0], qd[1]);
-    if ((c8 & 3) == 0) sp[(g * KS + ks) * kTileScaleBytes + r * 2 + (int)((k >> 5) & 1)] = (uint8_t)sb;
-  }
+  uint8_t* dst = qp + (int64_t)tile * kTileBytes;
+  *reinterpret_cast<uint2*>(dst + tile_off(r, c8 >> 1) + (c8 & 1) * 8) = make_uint2(qd[0], qd[1]);
+  if ((c8 & 3) == 0) sp[(int64_t)tile * kTileScaleBytes + r * 2 + (c8 >> 2)] = (uint8_t)sb;
 }
 
 int launch_quantize_act_packed(const void* x, int64_t M, int64_t K, int64_t ldx, void* qp, void* sp,
                                hipStream_t stream) {
   const int64_t m_pad = (M + kGroupRows - 1) / kGroupRows * kGroupRows;
-  const int64_t per_row = K / 8;
-  const int64_t total = m_pad * per_row;
-  const int64_t blocks = (total + 255) / 256;
   const int64_t KS = K / kStepK;
+  const int64_t total = m_pad * (K / 8);    // (m_pad / 128) * KS tiles x 1024 threads
+  const int64_t blocks = total / 256;
   if (total < ((int64_t)1 << 32)) {
     hipLaunchKernelGGL(quant_act_packed_kernel<uint32_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       (const uint16_t*)x, ldx, (int)M, (uint32_t)per_row, (uint32_t)total, KS, (uint8_t*)qp,
-                       (uint8_t*)sp);
+                       (const uint16_t*)x, ldx, (int)M, (uint32_t)total, KS, (uint8_t*)qp, (uint8_t*)sp);
   } else {
     hipLaunchKernelGGL(quant_act_packed_kernel<uint64_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       (const uint16_t*)x, ldx, (int)M, (uint64_t)per_row, (uint64_t)total, KS, (uint8_t*)qp,
-                       (uint8_t*)sp);
+                       (const uint16_t*)x, ldx, (int)M, (uint64_t)total, KS, (uint8_t*)qp, (uint8_t*)sp);
   }
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
