@@ -97,11 +97,12 @@ int mxfp8_unpack_weight(const void* w_packed, const void* s_packed, int64_t N, i
                         void* w_e4m3, void* w_s_e8m0, void* stream);
 
 /*
- * Workspace bytes mxfp8_linear needs for this shape (host-only).  The
- * workspace holds the quantized activations and split-K partial sums.  It
- * must be zero-filled once when first allocated; every call leaves its
- * counters back at zero.  Calls that share one workspace must be ordered on
- * one stream (concurrent calls on one workspace race).
+ * Workspace bytes mxfp8_linear needs for this shape (host-only).  For M > 16
+ * the workspace holds the activations quantized into the packed layout
+ * (M padded to 128 rows, plus their scales); for M <= 16 nothing is stored
+ * there (a 256-byte minimum is still required).  Its contents need no
+ * initialization.  Calls that share one workspace must be ordered on one
+ * stream (concurrent calls on one workspace race).
  */
 int mxfp8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes);
 
