@@ -45,6 +45,24 @@ SCALE_EXP_MIN = -127   # smallest encodable scale exponent (byte 0x00)
 SCALE_EXP_MAX = 127    # largest finite scale exponent (byte 0xFE)
 
 
+def floor_log2(a):
+    """floor(log2(a)) for float64 a > 0, exactly: the unbiased exponent field
+    of a normal float64 (the rare subnormals go through np.frexp).  Entries
+    with a <= 0 are returned as 0 (callers mask them)."""
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    e = ((a.view(np.int64) >> 52) & 0x7FF) - 1023
+    sub = (e == -1023) & (a > 0)
+    if np.any(sub):
+        _, p = np.frexp(a[sub])
+        e[sub] = p - 1
+    return np.where(a > 0, e, 0)
+
+
+def _ldexp(x, e):
+    """x * 2^e, exact (numpy's fast loop wants an int32 exponent)."""
+    return np.ldexp(x, np.asarray(e).astype(np.int32))
+
+
 def bf16_round(x):
     """Round real values to the nearest bfloat16 (ties to even), returned as
     float64.  bfloat16 keeps 8 significant bits, exponents down to -126 for
@@ -52,11 +70,10 @@ def bf16_round(x):
     to 2^128 or beyond overflow to infinity."""
     x = np.asarray(x, dtype=np.float64)
     a = np.abs(x)
-    _, p = np.frexp(a)
-    k = np.where(a > 0, p - 1, -126)
+    k = np.where(a > 0, floor_log2(a), -126)
     k = np.maximum(k, -126)
     qexp = k - 7
-    r = np.ldexp(np.rint(np.ldexp(a, -qexp)), qexp)
+    r = _ldexp(np.rint(_ldexp(a, -qexp)), qexp)
     r = np.where(r >= 2.0 ** 128, np.inf, r)
     r = np.where(np.isnan(x), np.nan, r)
     return np.copysign(r, x)
@@ -69,7 +86,7 @@ def e4m3_decode(q):
     efield = (b >> E4M3_MANT_BITS) & 0xF
     mant = b & 0x7
     sub = mant * 2.0 ** (1 - E4M3_EXP_BIAS - E4M3_MANT_BITS)           # m * 2^-9
-    nrm = (1.0 + mant / 8.0) * np.ldexp(1.0, efield - E4M3_EXP_BIAS)  # 1.m * 2^(E-7)
+    nrm = (1.0 + mant / 8.0) * _ldexp(1.0, efield - E4M3_EXP_BIAS)    # 1.m * 2^(E-7)
     val = sign * np.where(efield == 0, sub, nrm)
     return np.where((b & 0x7F) == 0x7F, np.nan, val)
 
@@ -77,7 +94,7 @@ def e4m3_decode(q):
 def e8m0_decode(s):
     """UE8M0 byte(s) -> float64 power of two 2^(s - 127); 0xFF is NaN."""
     s = np.asarray(s, dtype=np.uint8).astype(np.int64)
-    return np.where(s == 0xFF, np.nan, np.ldexp(1.0, s - E8M0_BIAS))
+    return np.where(s == 0xFF, np.nan, _ldexp(1.0, s - E8M0_BIAS))
 
 
 def e4m3_encode(t):
@@ -92,19 +109,17 @@ def e4m3_encode(t):
     t = np.asarray(t, dtype=np.float64)
     neg = np.signbit(t)
     a = np.minimum(np.abs(t), E4M3_MAX)                  # saturate
-    _, p = np.frexp(a)                                   # a = f * 2^p, f in [0.5, 1)
-    k = np.where(a > 0, p - 1, E4M3_EMIN)                # floor(log2 a)
+    k = np.where(a > 0, floor_log2(a), E4M3_EMIN)        # floor(log2 a)
     k = np.maximum(k, E4M3_EMIN)
     qexp = k - E4M3_MANT_BITS
-    n = np.rint(np.ldexp(a, -qexp))                      # numpy rint: ties to even
-    r = np.ldexp(n, qexp)                                # rounded magnitude, exact
+    n = np.rint(_ldexp(a, -qexp))                        # numpy rint: ties to even
+    r = _ldexp(n, qexp)                                  # rounded magnitude, exact
     # Encode the (exactly representable) magnitude r.
-    _, pr = np.frexp(r)
-    kr = pr - 1
+    kr = floor_log2(r)
     normal = (r > 0) & (kr >= E4M3_EMIN)
     efield = np.where(normal, kr + E4M3_EXP_BIAS, 0)
     mant = np.where(normal,
-                    np.ldexp(r, -kr) * 8.0 - 8.0,        # (r / 2^k - 1) * 8
+                    _ldexp(r, -kr) * 8.0 - 8.0,          # (r / 2^k - 1) * 8
                     np.ldexp(r, 9))                      # r / 2^-9
     mant = mant.astype(np.int64)
     code = (efield.astype(np.int64) << E4M3_MANT_BITS) | mant
@@ -115,11 +130,10 @@ def e4m3_encode(t):
 def scale_exponent(block_amax):
     """Shared exponent of a block from its max magnitude:
     floor(log2(amax)) - 8, clamped to [-127, 127]; an all-zero block gives
-    -127.  floor(log2) is taken exactly from frexp, never from a floating
-    log2."""
+    -127.  floor(log2) is taken exactly from the exponent bits, never from a
+    floating log2."""
     amax = np.asarray(block_amax, dtype=np.float64)
-    _, p = np.frexp(amax)
-    e = np.where(amax > 0, (p - 1) - E4M3_EMAX, SCALE_EXP_MIN)
+    e = np.where(amax > 0, floor_log2(amax) - E4M3_EMAX, SCALE_EXP_MIN)
     return np.clip(e, SCALE_EXP_MIN, SCALE_EXP_MAX).astype(np.int64)
 
 
@@ -136,7 +150,7 @@ def quantize_mx(x):
     xb = x.reshape(R, C // MX_BLOCK, MX_BLOCK)
     amax = np.max(np.abs(xb), axis=2)
     e_s = scale_exponent(amax)
-    t = np.ldexp(xb, -e_s[:, :, None])                   # exact power-of-two scaling
+    t = _ldexp(xb, -e_s[:, :, None])                     # exact power-of-two scaling
     q = e4m3_encode(t).reshape(R, C)
     s = (e_s + E8M0_BIAS).astype(np.uint8)
     return q, s
