@@ -2,7 +2,7 @@
  * mxfp8.h -- C ABI of libmxfp8.so, the MXFP8 dense linear layer (and its
  * top-k routed MoE variant) for AMD Instinct MI355X (gfx950).
  *
- * The layer, as the pages define it ("[Kernel] Add FlashInfer TRTLLM MXFP8
+ * The dense layer, as the pages define it ("[Kernel] Add FlashInfer TRTLLM MXFP8
  * linear backend", vLLM PR #52204, §Purpose and the review of apply_weights):
  *   1. BF16 activations are quantized on the fly to E4M3 elements with one
  *      UE8M0 (power-of-two) scale per 32 elements along K;
@@ -148,6 +148,76 @@ int mxfp8_quantize_act_packed(const void* x_bf16, int64_t M, int64_t K, int64_t 
 int mxfp8_gemm_packed(const void* q_packed, const void* s_packed, int64_t M, int64_t K,
                       const void* w_packed, const void* ws_packed, int64_t N, const void* bias_bf16,
                       void* y_bf16, int64_t ldy, void* stream);
+
+/*
+ * ---------------------------------------------------------------------------
+ * Top-k routed MXFP8 mixture-of-experts layer (the grouped variant).
+ *
+ * What is computed ("feat(moe): add unified block-scale FP8 support",
+ * flashinfer PR #4026, walkthrough: BF16 activations in, MXFP8 inside;
+ * "Feature/sm100 low latency nvfp4 kernels", flashinfer PR #1214, Highlights:
+ * the Renormalize routing; "Add support for FlashInfer mxfp8", sglang PR
+ * #18945: fused w13 = [gate; up] and w2 expert weights with 32-K UE8M0
+ * scales).  For each token t:
+ *   ids = the topk largest logits[t, :] (ties: lower expert id first),
+ *   w   = softmax over those topk logits (fp32),
+ *   for each selected e: h = deq(q(x_t)) . deq(w13[e])^T   ([2I], fp32 acc),
+ *                        a = bf16( silu(h[0:I]) * h[I:2I] ),  silu(z) = z/(1+e^-z),
+ *                        o_e = deq(q(a)) . deq(w2[e])^T        ([H], fp32 acc),
+ *   y[t] = bf16( sum_j w_j * o_{e_j} ), the products and the sum in fp32 (slot
+ *          order), rounded once.
+ * q() is the MX quantization of mxfp8_quantize_act along the contraction
+ * dimension (H for x, I for a).
+ *
+ * Shapes: H % 256 == 0, I % 256 == 0, 1 <= E <= 256, 1 <= topk <= min(E, 16),
+ * T >= 0 (T == 0 is a no-op).  Checkpoint layouts (contiguous, row-major):
+ *   w13 E4M3 [E, 2I, H] with UE8M0 [E, 2I, H/32]  (rows 0..I-1 gate, I..2I-1 up)
+ *   w2  E4M3 [E, H, I]  with UE8M0 [E, H, I/32]
+ * The whole layer runs in this library's kernels on `stream`; results are
+ * deterministic (no atomics in any sum).
+ * ---------------------------------------------------------------------------
+ */
+
+/* Host-only sizes of the prepared (packed) expert weights. */
+int mxfp8_moe_prepared_bytes(int64_t E, int64_t H, int64_t I, size_t* w13_bytes, size_t* s13_bytes,
+                             size_t* w2_bytes, size_t* s2_bytes);
+
+/*
+ * One-time preparation of the expert weights (the MoE counterpart of
+ * mxfp8_prepare_weight): packs w13 with its gate and up rows interleaved for
+ * the fused SiLU-gating epilogue, and w2, into opaque layouts owned by this
+ * library.  w13_e4m3 / w2_e4m3 16-byte aligned; outputs 256-byte aligned,
+ * sizes from mxfp8_moe_prepared_bytes.
+ */
+int mxfp8_moe_prepare_weights(const void* w13_e4m3, const void* w13_s_e8m0, const void* w2_e4m3,
+                              const void* w2_s_e8m0, int64_t E, int64_t H, int64_t I, void* w13_packed,
+                              void* s13_packed, void* w2_packed, void* s2_packed, void* stream);
+
+/* Host-only workspace bytes of mxfp8_moe_grouped (contents need no init). */
+int mxfp8_moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, size_t* bytes);
+
+/*
+ * The MoE layer.  x_bf16 [T, H] contiguous, 16-byte aligned; logits_f32
+ * [T, E] contiguous; y_bf16 [T, H] contiguous, 16-byte aligned (written
+ * entirely); prepared weights from mxfp8_moe_prepare_weights; workspace of at
+ * least mxfp8_moe_workspace_bytes, 256-byte aligned.  Calls sharing a
+ * workspace must be ordered on one stream.
+ */
+int mxfp8_moe_grouped(const void* x_bf16, const float* logits_f32, int64_t T, int64_t H, int64_t E,
+                      int64_t topk, int64_t I, const void* w13_packed, const void* s13_packed,
+                      const void* w2_packed, const void* s2_packed, void* y_bf16, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/*
+ * Test hook: when set (all five non-NULL), every later mxfp8_moe_grouped call
+ * also writes, for row t*topk + j (token t, slot j): the bf16 gated
+ * activation act_bf16 [T*topk, I], its MX quantization act_e4m3 [T*topk, I]
+ * and act_e8m0 [T*topk, I/32], the routed expert ids_i32 [T*topk] and the
+ * routing weight wts_f32 [T*topk] (act_bf16 8-byte aligned, the others
+ * 4-byte aligned).  All NULL turns it off; MXFP8_E_NULLPTR if only some are
+ * NULL.  Process-wide: set it between calls, never concurrently with one.
+ */
+int mxfp8_moe_debug_capture(void* act_bf16, void* act_e4m3, void* act_e8m0, void* ids_i32, void* wts_f32);
 
 /*
  * Test hook: force the GEMM path of mxfp8_linear (0 = automatic by shape,

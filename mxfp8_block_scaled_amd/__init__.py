@@ -1,4 +1,5 @@
-"""MXFP8 dense linear layer for AMD Instinct MI355X (gfx950).
+"""MXFP8 dense linear layer (and its top-k routed MoE variant) for AMD
+Instinct MI355X (gfx950).
 
 The arithmetic lives in hand-written HIP kernels behind a C-ABI shared library
 (``libmxfp8.so``); this package is the thin Python binding over it.  Importing
@@ -12,7 +13,9 @@ _API = (
     "mxfp8_unpack_weight", "mxfp8_linear_workspace_bytes", "mxfp8_linear",
     "mxfp8_packed_act_bytes", "mxfp8_quantize_act_packed", "mxfp8_gemm_packed",
     "quantize_act_packed", "gemm_packed", "PackedActivation",
-    "mxfp8_moe_grouped", "mxfp8_moe_workspace_bytes",
+    "mxfp8_moe_grouped", "mxfp8_moe_workspace_bytes", "mxfp8_moe_prepared_bytes",
+    "mxfp8_moe_prepare_weights", "mxfp8_moe_debug_capture", "MoEWeights", "moe_prepare_weights",
+    "moe_debug_capture",
     "mxfp8_status_string", "MXFP8Error",
 )
 

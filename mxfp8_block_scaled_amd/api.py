@@ -39,6 +39,13 @@ _SIGNATURES = {
     "mxfp8_quantize_act_packed": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
     "mxfp8_gemm_packed": ([_vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp], ctypes.c_int),
     "mxfp8_debug_force_path": ([ctypes.c_int], ctypes.c_int),
+    "mxfp8_moe_prepared_bytes": ([_i64, _i64, _i64, ctypes.POINTER(_sz), ctypes.POINTER(_sz),
+                                  ctypes.POINTER(_sz), ctypes.POINTER(_sz)], ctypes.c_int),
+    "mxfp8_moe_prepare_weights": ([_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "mxfp8_moe_workspace_bytes": ([_i64, _i64, _i64, _i64, _i64, ctypes.POINTER(_sz)], ctypes.c_int),
+    "mxfp8_moe_grouped": ([_vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+                          ctypes.c_int),
+    "mxfp8_moe_debug_capture": ([_vp, _vp, _vp, _vp, _vp], ctypes.c_int),
 }
 
 
@@ -292,13 +299,98 @@ def gemm_packed(pa, pw, bias=None):
     return y
 
 
-def moe_grouped(*args, **kwargs):
-    raise NotImplementedError("the routed MoE entry point is not built yet")
+# ---------------------------------------------------------------------------
+# Routed MoE
+# ---------------------------------------------------------------------------
+
+def mxfp8_moe_prepared_bytes(E, H, I):
+    out = [_sz() for _ in range(4)]
+    _check(lib().mxfp8_moe_prepared_bytes(E, H, I, *[ctypes.byref(o) for o in out]), "mxfp8_moe_prepared_bytes")
+    return tuple(o.value for o in out)
 
 
-def mxfp8_moe_grouped(*args, **kwargs):
-    raise NotImplementedError("the routed MoE entry point is not built yet")
+def mxfp8_moe_prepare_weights(w13, s13, w2, s2, E, H, I, w13p, s13p, w2p, s2p, stream):
+    return lib().mxfp8_moe_prepare_weights(w13, s13, w2, s2, E, H, I, w13p, s13p, w2p, s2p, stream)
 
 
-def mxfp8_moe_workspace_bytes(*args, **kwargs):
-    raise NotImplementedError("the routed MoE entry point is not built yet")
+def mxfp8_moe_workspace_bytes(T, H, I, E, topk):
+    b = _sz()
+    _check(lib().mxfp8_moe_workspace_bytes(T, H, I, E, topk, ctypes.byref(b)), "mxfp8_moe_workspace_bytes")
+    return b.value
+
+
+def mxfp8_moe_grouped(x, logits, T, H, E, topk, I, w13p, s13p, w2p, s2p, y, ws, ws_bytes, stream):
+    return lib().mxfp8_moe_grouped(x, logits, T, H, E, topk, I, w13p, s13p, w2p, s2p, y, ws, ws_bytes, stream)
+
+
+def mxfp8_moe_debug_capture(act, q, s, ids, wts):
+    return lib().mxfp8_moe_debug_capture(act, q, s, ids, wts)
+
+
+class MoEWeights:
+    """Expert weights after the one-time preparation (opaque packed layouts)."""
+
+    def __init__(self, w13p, s13p, w2p, s2p, E, H, I):
+        self.w13p, self.s13p, self.w2p, self.s2p = w13p, s13p, w2p, s2p
+        self.E, self.H, self.I = E, H, I
+
+    @property
+    def device(self):
+        return self.w13p.device
+
+
+def moe_prepare_weights(w13_q, w13_s, w2_q, w2_s):
+    """MXFP8 expert weights -> MoEWeights.
+
+    ``w13_q`` E4M3 ``[E, 2I, H]`` (gate rows then up rows) with UE8M0 ``w13_s``
+    ``[E, 2I, H/32]``; ``w2_q`` ``[E, H, I]`` with ``w2_s`` ``[E, H, I/32]``
+    (uint8 or float8_e4m3fn, GPU)."""
+    w13_q, w13_s, w2_q, w2_s = (_as_bytes(t).contiguous() for t in (w13_q, w13_s, w2_q, w2_s))
+    _require_cuda(w13_q, "w13_q")
+    E, two_i, H = w13_q.shape
+    I = two_i // 2
+    assert w2_q.shape == (E, H, I) and w13_s.shape == (E, 2 * I, H // 32) and w2_s.shape == (E, H, I // 32)
+    b = mxfp8_moe_prepared_bytes(E, H, I)
+    outs = [torch.empty(n, dtype=torch.uint8, device=w13_q.device) for n in b]
+    _check(mxfp8_moe_prepare_weights(_ptr(w13_q), _ptr(w13_s), _ptr(w2_q), _ptr(w2_s), E, H, I,
+                                     *[_ptr(o) for o in outs], _stream(w13_q.device)), "mxfp8_moe_prepare_weights")
+    return MoEWeights(*outs, E, H, I)
+
+
+_moe_workspaces = {}
+
+
+def moe_workspace(T, H, I, E, topk, device):
+    need = mxfp8_moe_workspace_bytes(T, H, I, E, topk)
+    key = torch.device(device).index if torch.device(device).index is not None else torch.cuda.current_device()
+    ws = _moe_workspaces.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+        _moe_workspaces[key] = ws
+    return ws
+
+
+def moe_grouped(x, logits, mw, topk, out=None):
+    """The MXFP8 routed MoE layer: ``x`` bf16 ``[T, H]``, ``logits`` fp32
+    ``[T, E]``, ``mw`` MoEWeights -> bf16 ``[T, H]``."""
+    assert x.dtype == torch.bfloat16, f"MXFP8 MoE takes bfloat16 activations, got {x.dtype}"
+    assert logits.dtype == torch.float32
+    _require_cuda(x, "x")
+    x = x.contiguous()
+    logits = logits.contiguous()
+    T, H = x.shape
+    assert H == mw.H and logits.shape == (T, mw.E)
+    y = out if out is not None else torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    ws = moe_workspace(T, H, mw.I, mw.E, topk, x.device)
+    _check(mxfp8_moe_grouped(_ptr(x), _ptr(logits), T, H, mw.E, topk, mw.I, _ptr(mw.w13p), _ptr(mw.s13p),
+                             _ptr(mw.w2p), _ptr(mw.s2p), _ptr(y), _ptr(ws), ws.numel(), _stream(x.device)),
+           "mxfp8_moe_grouped")
+    return y
+
+
+def moe_debug_capture(act=None, q=None, s=None, ids=None, wts=None):
+    """Test hook: capture, per row t*k + j, the gated activation (bf16
+    ``[T*k, I]``), its MX quantization (``[T*k, I]`` / ``[T*k, I/32]`` uint8),
+    the routed expert (int32 ``[T*k]``) and routing weight (fp32 ``[T*k]``) of
+    later MoE calls; no arguments turns it off."""
+    _check(mxfp8_moe_debug_capture(_ptr(act), _ptr(q), _ptr(s), _ptr(ids), _ptr(wts)), "mxfp8_moe_debug_capture")

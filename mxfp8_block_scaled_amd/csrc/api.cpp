@@ -59,6 +59,52 @@ size_t tile_ws_bytes(int64_t M, int64_t K) {
   return round_up(mp * (size_t)K, 256) + round_up(mp * (size_t)(K / 32), 256);
 }
 
+// Test hook state of mxfp8_moe_debug_capture.
+std::atomic<void*> g_dbg_act{nullptr}, g_dbg_q{nullptr}, g_dbg_s{nullptr}, g_dbg_ids{nullptr}, g_dbg_wts{nullptr};
+
+int check_moe_shape(int64_t T, int64_t H, int64_t E, int64_t topk, int64_t I) {
+  if (T < 0 || H < 256 || H % 256 != 0 || I < 256 || I % 256 != 0) return MXFP8_E_SHAPE;
+  if (E < 1 || E > mxfp8::kMoeMaxExperts || topk < 1 || topk > E || topk > mxfp8::kMoeMaxTopk) return MXFP8_E_SHAPE;
+  if (H > (1 << 20) || I > (1 << 20) || T > (1 << 24) || T * topk > (1 << 26)) return MXFP8_E_SHAPE;
+  return MXFP8_OK;
+}
+
+// Carves the MoE scratch out of a workspace (base may be NULL to size it).
+size_t moe_layout(int64_t T, int64_t H, int64_t E, int64_t topk, int64_t I, uint8_t* base, mxfp8::MoeWorkspace* w) {
+  const int64_t R = T * topk;
+  const int64_t nblk = (T + 15) / 16;
+  const int64_t groups_max = (R + (mxfp8::kGroupRowsHost - 1) * E) / mxfp8::kGroupRowsHost;
+  const int64_t p_max = (groups_max + 1) * mxfp8::kGroupRowsHost;
+  const int64_t mt_max = (groups_max + E) / 2 + 1;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    uint8_t* p = base ? base + off : nullptr;
+    off += round_up(bytes > 0 ? bytes : 1, 256);
+    return p;
+  };
+  mxfp8::MoeWorkspace v;
+  v.ids = (int*)take(R * 4);
+  v.wts = (float*)take(R * 4);
+  v.blk_cnt = (int*)take(E * nblk * 4);
+  v.blk_off = (int*)take(E * nblk * 4);
+  v.seg_off = (int*)take(E * 4);
+  v.meta = (int*)take(64);
+  v.tile_e = (int*)take(mt_max * 4);
+  v.tile_g0 = (int*)take(mt_max * 4);
+  v.tile_ng = (int*)take(mt_max * 4);
+  v.sorted_row = (int*)take(p_max * 4);
+  v.inv = (int*)take(R * 4);
+  v.a1q = take(p_max * H);
+  v.a1s = take(p_max * (H / 32));
+  v.a2q = take(p_max * I);
+  v.a2s = take(p_max * (I / 32));
+  v.ys = (float*)take(p_max * H * 4);
+  v.p_max = p_max;
+  v.mt_max = mt_max;
+  if (w) *w = v;
+  return off;
+}
+
 bool use_skinny(int64_t M, int64_t K) {
   if (g_force_path.load(std::memory_order_relaxed) == 1) return false;
   return M <= mxfp8::kSkinnyMaxM && K <= mxfp8::kSkinnyMaxK;
@@ -188,6 +234,91 @@ int mxfp8_gemm_packed(const void* q_packed, const void* s_packed, int64_t M, int
   if (int st = check_device()) return st;
   return mxfp8::launch_gemm_tile(q_packed, s_packed, M, K, w_packed, ws_packed, N, bias_bf16, y_bf16, ldy,
                                  (hipStream_t)stream);
+}
+
+int mxfp8_moe_prepared_bytes(int64_t E, int64_t H, int64_t I, size_t* w13_bytes, size_t* s13_bytes,
+                             size_t* w2_bytes, size_t* s2_bytes) {
+  if (!w13_bytes || !s13_bytes || !w2_bytes || !s2_bytes) return MXFP8_E_NULLPTR;
+  if (int st = check_moe_shape(0, H, E, 1, I)) return st;
+  *w13_bytes = (size_t)E * 2 * I * H;
+  *s13_bytes = (size_t)E * 2 * I * (H / 32);
+  *w2_bytes = (size_t)E * H * I;
+  *s2_bytes = (size_t)E * H * (I / 32);
+  return MXFP8_OK;
+}
+
+int mxfp8_moe_prepare_weights(const void* w13_e4m3, const void* w13_s_e8m0, const void* w2_e4m3,
+                              const void* w2_s_e8m0, int64_t E, int64_t H, int64_t I, void* w13_packed,
+                              void* s13_packed, void* w2_packed, void* s2_packed, void* stream) {
+  if (int st = check_moe_shape(0, H, E, 1, I)) return st;
+  if (!w13_e4m3 || !w13_s_e8m0 || !w2_e4m3 || !w2_s_e8m0 || !w13_packed || !s13_packed || !w2_packed || !s2_packed)
+    return MXFP8_E_NULLPTR;
+  if (!aligned(w13_e4m3, 16) || !aligned(w2_e4m3, 16)) return MXFP8_E_ALIGN;
+  if (!aligned(w13_packed, 256) || !aligned(s13_packed, 256) || !aligned(w2_packed, 256) || !aligned(s2_packed, 256))
+    return MXFP8_E_ALIGN;
+  if (int st = check_device()) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (int st = mxfp8::launch_pack_weight_gate_up(w13_e4m3, w13_s_e8m0, E, I, H, w13_packed, s13_packed, s))
+    return st;
+  return mxfp8::launch_pack_weight(w2_e4m3, w2_s_e8m0, E * H, I, I, I / 32, w2_packed, s2_packed, s);
+}
+
+int mxfp8_moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, size_t* bytes) {
+  if (!bytes) return MXFP8_E_NULLPTR;
+  if (int st = check_moe_shape(T, H, E, topk, I)) return st;
+  *bytes = moe_layout(T, H, E, topk, I, nullptr, nullptr);
+  return MXFP8_OK;
+}
+
+int mxfp8_moe_grouped(const void* x_bf16, const float* logits_f32, int64_t T, int64_t H, int64_t E, int64_t topk,
+                      int64_t I, const void* w13_packed, const void* s13_packed, const void* w2_packed,
+                      const void* s2_packed, void* y_bf16, void* workspace, size_t workspace_bytes, void* stream) {
+  if (int st = check_moe_shape(T, H, E, topk, I)) return st;
+  if (T == 0) return MXFP8_OK;
+  if (!x_bf16 || !logits_f32 || !w13_packed || !s13_packed || !w2_packed || !s2_packed || !y_bf16)
+    return MXFP8_E_NULLPTR;
+  if (!aligned(x_bf16, 16) || !aligned(y_bf16, 16) || !aligned(logits_f32, 4)) return MXFP8_E_ALIGN;
+  if (!aligned(w13_packed, 256) || !aligned(s13_packed, 256) || !aligned(w2_packed, 256) || !aligned(s2_packed, 256))
+    return MXFP8_E_ALIGN;
+  const size_t need = moe_layout(T, H, E, topk, I, nullptr, nullptr);
+  if (!workspace || workspace_bytes < need) return MXFP8_E_WORKSPACE;
+  if (!aligned(workspace, 256)) return MXFP8_E_ALIGN;
+  if (int st = check_device()) return st;
+  mxfp8::MoeArgs a;
+  a.x = x_bf16;
+  a.logits = logits_f32;
+  a.T = T;
+  a.H = H;
+  a.E = E;
+  a.topk = topk;
+  a.I = I;
+  a.w13p = w13_packed;
+  a.s13p = s13_packed;
+  a.w2p = w2_packed;
+  a.s2p = s2_packed;
+  a.y = y_bf16;
+  a.dbg_act = g_dbg_act.load();
+  a.dbg_q = g_dbg_q.load();
+  a.dbg_s = g_dbg_s.load();
+  a.dbg_ids = g_dbg_ids.load();
+  a.dbg_wts = g_dbg_wts.load();
+  moe_layout(T, H, E, topk, I, (uint8_t*)workspace, &a.ws);
+  return mxfp8::launch_moe(a, (hipStream_t)stream);
+}
+
+int mxfp8_moe_debug_capture(void* act_bf16, void* act_e4m3, void* act_e8m0, void* ids_i32, void* wts_f32) {
+  const int n = (act_bf16 != nullptr) + (act_e4m3 != nullptr) + (act_e8m0 != nullptr) + (ids_i32 != nullptr) +
+                (wts_f32 != nullptr);
+  if (n != 0 && n != 5) return MXFP8_E_NULLPTR;
+  if (n == 5 && (!aligned(act_bf16, 8) || !aligned(act_e4m3, 4) || !aligned(ids_i32, 4) || !aligned(wts_f32, 4)))
+    return MXFP8_E_ALIGN;
+  // Published one at a time: set them between calls, not concurrently with one.
+  g_dbg_act.store(act_bf16);
+  g_dbg_q.store(act_e4m3);
+  g_dbg_s.store(act_e8m0);
+  g_dbg_ids.store(ids_i32);
+  g_dbg_wts.store(wts_f32);
+  return MXFP8_OK;
 }
 
 int mxfp8_debug_force_path(int path) {

@@ -17,6 +17,13 @@ int launch_quantize_act_packed(const void* x, int64_t M, int64_t K, int64_t ldx,
 int launch_pack_weight(const void* w, const void* ws, int64_t N, int64_t K, int64_t ldw, int64_t ldws,
                        void* wp, void* sp, hipStream_t stream);
 
+// Packs E stacked fused gate/up expert weights [E * 2I, K] with the row order
+// of the MoE gate/up GEMM (moe.hip): within each expert, packed row
+// p = 256 t + 128 h + q holds gate row 128 t + 64 h + q (q < 64) or up row
+// I + 128 t + 64 h + q - 64 (q >= 64).  Requires I % 128 == 0.
+int launch_pack_weight_gate_up(const void* w, const void* ws, int64_t E, int64_t I, int64_t K, void* wp, void* sp,
+                               hipStream_t stream);
+
 int launch_unpack_weight(const void* wp, const void* sp, int64_t N, int64_t K, void* w, void* ws,
                          hipStream_t stream);
 
@@ -31,5 +38,51 @@ constexpr int64_t kSkinnyMaxM = 16;
 constexpr int64_t kSkinnyMaxK = 8192;
 int launch_gemm_skinny(const void* x, int64_t ldx, int64_t M, int64_t K, const void* wp, const void* sp,
                        int64_t N, const void* bias, void* y, int64_t ldy, hipStream_t stream);
+
+// Mixture of experts (moe.hip).
+constexpr int64_t kGroupRowsHost = 128;   // = kGroupRows of common.hpp
+constexpr int64_t kMoeMaxExperts = 256;
+constexpr int64_t kMoeMaxTopk = 16;
+
+// Device scratch of one MoE call, carved out of the caller's workspace.
+struct MoeWorkspace {
+  int* ids;          // [T*k] expert of row t*k + j
+  float* wts;        // [T*k] routing weight
+  int* blk_cnt;      // [E][nblk] rows of each route block per expert
+  int* blk_off;      // [E][nblk] their offsets inside the expert's segment
+  int* seg_off;      // [E] first sorted position of each expert
+  int* meta;         // [0] M-tiles, [1] 128-row groups in use
+  int* tile_e;       // [mt_max] expert of each M-tile
+  int* tile_g0;      // [mt_max] its first 128-row group
+  int* tile_ng;      // [mt_max] its groups (1 or 2)
+  int* sorted_row;   // [p_max] row t*k + j at each sorted position, -1 = pad
+  int* inv;          // [T*k] sorted position of each row
+  uint8_t* a1q;      // packed MXFP8 token rows, expert-sorted [p_max, H]
+  uint8_t* a1s;
+  uint8_t* a2q;      // packed MXFP8 gated activations [p_max, I]
+  uint8_t* a2s;
+  float* ys;         // weighted expert outputs, fp32 [p_max, H]
+  int64_t p_max;     // sorted positions (multiple of 128, one spare group)
+  int64_t mt_max;    // upper bound of M-tiles
+};
+
+struct MoeArgs {
+  const void* x;       // bf16 [T, H]
+  const float* logits; // fp32 [T, E]
+  int64_t T, H, E, topk, I;
+  const void* w13p;
+  const void* s13p;
+  const void* w2p;
+  const void* s2p;
+  void* y;             // bf16 [T, H]
+  void* dbg_act;       // optional bf16 [T*k, I]
+  void* dbg_q;         // optional E4M3 [T*k, I]
+  void* dbg_s;         // optional UE8M0 [T*k, I/32]
+  void* dbg_ids;       // optional int32 [T*k] routed expert
+  void* dbg_wts;       // optional fp32 [T*k] routing weight
+  MoeWorkspace ws;
+};
+
+int launch_moe(const MoeArgs& a, hipStream_t stream);
 
 }  // namespace mxfp8

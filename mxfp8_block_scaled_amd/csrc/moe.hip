@@ -1,0 +1,440 @@
+// Top-k routed MXFP8 mixture-of-experts layer (the grouped variant of the
+// linear layer): BF16 activations and fp32 router logits in, BF16 out.
+//
+// What is computed ("feat(moe): add unified block-scale FP8 support",
+// flashinfer PR #4026, walkthrough and sequence diagram: BF16 activations are
+// quantized to MXFP8 inside the MoE; "Feature/sm100 low latency nvfp4
+// kernels", flashinfer PR #1214, Highlights: the "Renormalize" routing, top-k
+// then softmax over the k; "Add support for FlashInfer mxfp8", sglang PR
+// #18945: fused w13 (gate + up) and w2 expert weights, MXFP8 with 32-K UE8M0
+// scales):
+//   ids, w   = top-k of the token's logits (ties: lower expert id), softmax
+//              over those k;
+//   h        = deq(q(x_t)) . deq(W13[e])^T            for each selected e,
+//   act      = bf16( silu(h[:I]) * h[I:] ),  q(act) = MX quantization along I,
+//   y_t      = bf16( sum_j w_j . deq(q(act_j)) . deq(W2[e_j])^T ), rounded once.
+//
+// Pipeline (one stream, every step deterministic):
+//  1. route    one wave per token: k rounds of a wave arg-max, softmax over
+//              the k; per-block (16-token) expert histograms.
+//  2. plan     one workgroup: per-expert counts, expert segments of the
+//              sorted row space padded to 128-row groups, per-block offsets,
+//              the M-tile list (256 rows = two groups of one expert).
+//  3. scatter  row (t, j) -> its position in its expert's segment, in
+//              increasing t*k + j order (wave ballots + per-wave counts).
+//  4. gather   quantize x rows straight into the packed, expert-sorted GEMM
+//              operand (pad rows zero).
+//  5. gemm1    per (M-tile, 256-row slice of W13[e]) the shared tile loop;
+//              W13 is packed with gate and up rows interleaved so that each
+//              lane holds gate and up of the same intermediate index; the
+//              epilogue applies SiLU-gating, rounds to bf16, MX-quantizes
+//              along I and writes the packed operand of gemm2.
+//  6. gemm2    per (M-tile, 256-row slice of W2[e]): the tile loop, then the
+//              routing weight of each row; rows written in fp32 to the
+//              expert-sorted output.
+//  7. combine  y_t = bf16( sum_j ys[pos(t, j)] ), fp32 sum in slot order, one
+//              rounding.
+#include <cfloat>
+#include <climits>
+
+#include "common.hpp"
+#include "launch.hpp"
+#include "tile_core.hpp"
+
+namespace mxfp8 {
+
+namespace {
+
+constexpr int kRouteTokens = 16;   // tokens (one wave each) per route / scatter block
+
+__device__ inline bool route_better(float v, int e, float bv, int be) { return v > bv || (v == bv && e < be); }
+
+}  // namespace
+
+// ---------------------------------------------------------------- 1. route
+__global__ __launch_bounds__(1024) void moe_route_kernel(const float* __restrict__ logits, int T, int E, int topk,
+                                                         int* __restrict__ ids, float* __restrict__ wts,
+                                                         int* __restrict__ blk_cnt, int nblk) {
+  __shared__ int hist[kMoeMaxExperts];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < E; e += 1024) hist[e] = 0;
+  __syncthreads();
+  const int t = blockIdx.x * kRouteTokens + wave;
+  if (t < T) {
+    float v[4];
+    bool ok[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int e = lane + 64 * c;
+      ok[c] = e < E;
+      v[c] = ok[c] ? logits[(int64_t)t * E + e] : 0.0f;
+    }
+    float selv = 0.0f;
+    int seli = 0;
+    for (int j = 0; j < topk; ++j) {
+      float bv = -INFINITY;
+      int bi = INT_MAX;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (ok[c] && route_better(v[c], lane + 64 * c, bv, bi)) {
+          bv = v[c];
+          bi = lane + 64 * c;
+        }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(bv, off);
+        const int oi = __shfl_xor(bi, off);
+        if (route_better(ov, oi, bv, bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (lane + 64 * c == bi) ok[c] = false;
+      if (lane == j) {
+        selv = bv;
+        seli = bi;
+      }
+    }
+    // Selection 0 is the largest logit.
+    const float mx = __shfl(selv, 0);
+    const float z = lane < topk ? expf(selv - mx) : 0.0f;
+    float s = z;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+    if (lane < topk) {
+      ids[(int64_t)t * topk + lane] = seli;
+      wts[(int64_t)t * topk + lane] = z / s;
+      atomicAdd(&hist[seli], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 1024) blk_cnt[(int64_t)e * nblk + blockIdx.x] = hist[e];
+}
+
+// ---------------------------------------------------------------- 2. plan
+// meta[0] = number of M-tiles, meta[1] = number of 128-row groups in use.
+__global__ __launch_bounds__(1024) void moe_plan_kernel(const int* __restrict__ blk_cnt, int nblk, int E,
+                                                        int* __restrict__ blk_off, int* __restrict__ seg_off,
+                                                        int* __restrict__ tile_e, int* __restrict__ tile_g0,
+                                                        int* __restrict__ tile_ng, int* __restrict__ meta,
+                                                        int* __restrict__ sorted_row, int p_max) {
+  __shared__ int part[1024];
+  __shared__ int cnt[kMoeMaxExperts], gstart[kMoeMaxExperts], tstart[kMoeMaxExperts];
+  const int tid = threadIdx.x;
+  for (int p = tid; p < p_max; p += 1024) sorted_row[p] = -1;
+  // Thread (e, c) owns blocks [c*per, (c+1)*per) of expert e.
+  const int tpe = 1024 / E;                       // threads per expert (E <= 256: >= 4)
+  const int e = tid / tpe, c = tid % tpe;
+  const int per = (nblk + tpe - 1) / tpe;
+  const int b0 = min(c * per, nblk), b1 = min(b0 + per, nblk);
+  int sum = 0;
+  if (e < E)
+    for (int b = b0; b < b1; ++b) sum += blk_cnt[(int64_t)e * nblk + b];
+  part[tid] = sum;
+  __syncthreads();
+  if (e < E) {
+    int run = 0;
+    for (int k = 0; k < c; ++k) run += part[e * tpe + k];
+    for (int b = b0; b < b1; ++b) {
+      blk_off[(int64_t)e * nblk + b] = run;
+      run += blk_cnt[(int64_t)e * nblk + b];
+    }
+    if (c == tpe - 1) cnt[e] = run;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int g = 0, tt = 0;
+    for (int x = 0; x < E; ++x) {
+      const int groups = (cnt[x] + kGroupRows - 1) / kGroupRows;
+      gstart[x] = g;
+      tstart[x] = tt;
+      g += groups;
+      tt += (groups + 1) / 2;
+    }
+    meta[0] = tt;
+    meta[1] = g;
+  }
+  __syncthreads();
+  if (tid < E) {
+    const int groups = (cnt[tid] + kGroupRows - 1) / kGroupRows;
+    seg_off[tid] = gstart[tid] * kGroupRows;
+    for (int u = 0; 2 * u < groups; ++u) {
+      tile_e[tstart[tid] + u] = tid;
+      tile_g0[tstart[tid] + u] = gstart[tid] + 2 * u;
+      tile_ng[tstart[tid] + u] = min(2, groups - 2 * u);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- 3. scatter
+__global__ __launch_bounds__(256) void moe_scatter_kernel(const int* __restrict__ ids, int R, int topk, int nblk,
+                                                          const int* __restrict__ blk_off,
+                                                          const int* __restrict__ seg_off,
+                                                          int* __restrict__ sorted_row, int* __restrict__ inv) {
+  __shared__ int wcnt[4][kMoeMaxExperts];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < 4 * kMoeMaxExperts; i += 256) (&wcnt[0][0])[i] = 0;
+  __syncthreads();
+  const int rows = kRouteTokens * topk;
+  const int r = blockIdx.x * rows + tid;
+  const bool valid = tid < rows && r < R;
+  const int e = valid ? ids[r] : -1;
+  // Rank among the lower lanes of this wave routed to the same expert.
+  uint64_t todo = __ballot(valid);
+  int local = 0;
+  while (todo != 0) {
+    const int leader = __ffsll((unsigned long long)todo) - 1;
+    const int e0 = __builtin_amdgcn_readlane(e, leader);
+    const uint64_t m = __ballot(e == e0);
+    if (e == e0) local = __popcll(m & ((1ull << lane) - 1ull));
+    if (lane == leader) wcnt[wave][e0] = __popcll(m);
+    todo &= ~m;
+  }
+  __syncthreads();
+  if (valid) {
+    int pos = seg_off[e] + blk_off[(int64_t)e * nblk + blockIdx.x] + local;
+    for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
+    sorted_row[pos] = r;
+    inv[r] = pos;
+  }
+}
+
+// ---------------------------------------------------------------- 4. gather
+// The packed act-quant of quant.hip with a row indirection: position pos of
+// the expert-sorted operand holds token sorted_row[pos] / k (or zeros).
+template <typename Idx>
+__global__ __launch_bounds__(256) void moe_gather_quant_kernel(const uint16_t* __restrict__ x, int H, int topk,
+                                                               const int* __restrict__ sorted_row,
+                                                               const int* __restrict__ meta, Idx total, int KS,
+                                                               uint8_t* __restrict__ qp, uint8_t* __restrict__ sp) {
+  const Idx t = (Idx)blockIdx.x * 256 + threadIdx.x;
+  if (t >= total) return;
+  const Idx tile = t >> 10;
+  const int64_t g = (int64_t)(tile / (Idx)KS);
+  if (g >= meta[1]) return;                 // whole tiles leave together
+  const int64_t ks = (int64_t)tile - g * KS;
+  const int r = (int)((t >> 3) & 127);
+  const int c8 = (int)(t & 7);
+  const int src = sorted_row[g * kGroupRows + r];
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  if (src >= 0) {
+    const uint4 v = *reinterpret_cast<const uint4*>(x + (int64_t)(src / topk) * H + ks * kStepK + c8 * 8);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  }
+  u16x2 mp = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) mp = absmax_pk(mp, w[i]);
+  uint32_t m = max((uint32_t)mp[0], (uint32_t)mp[1]);
+  m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+  const uint32_t sb = (uint32_t)max((int)(m >> 7) - 8, 0);
+  uint32_t qd[2];
+  cvt8s(w, mx_scale_value(sb), qd);
+  uint8_t* dst = qp + (int64_t)tile * kTileBytes;
+  *reinterpret_cast<uint2*>(dst + tile_off(r, c8 >> 1) + (c8 & 1) * 8) = make_uint2(qd[0], qd[1]);
+  if ((c8 & 3) == 0) sp[(int64_t)tile * kTileScaleBytes + r * 2 + (c8 >> 2)] = (uint8_t)sb;
+}
+
+// ---------------------------------------------------------------- 5. gemm1
+// Packed W13 row p of an expert's 256-row slice nt holds, for wave half
+// wn = (p / 128) % 2 and q = p % 128: gate row nt*128 + wn*64 + q (q < 64) or
+// up row I + nt*128 + wn*64 + q - 64 (q >= 64).  So in the tile loop's lane
+// layout acc[a][b][r] (a < 2) is the gate and acc[a + 2][b][r] the up value of
+// intermediate index i = nt*128 + wn*64 + 32a + 8(r/4) + 4lg + r%4.
+__global__ __launch_bounds__(tile::kThreads, 1) void moe_gemm1_kernel(
+    const uint8_t* __restrict__ a1q, const uint8_t* __restrict__ a1s, const uint8_t* __restrict__ w13p,
+    const uint8_t* __restrict__ s13p, const int* __restrict__ meta, const int* __restrict__ tile_e,
+    const int* __restrict__ tile_g0, const int* __restrict__ tile_ng, const int* __restrict__ sorted_row, int H,
+    int I, uint8_t* __restrict__ a2q, uint8_t* __restrict__ a2s, uint16_t* __restrict__ dbg_act,
+    uint8_t* __restrict__ dbg_q, uint8_t* __restrict__ dbg_s) {
+  __shared__ __attribute__((aligned(16))) uint8_t st0[tile::kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[tile::kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[tile::kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t st3[tile::kStage];
+  const int NT = (2 * I) / 256;
+  const int total = meta[0] * NT;
+  if ((int)blockIdx.x >= total) return;
+  const int logical = tile::xcd_remap((int)blockIdx.x, total);
+  const int mt = logical / NT, nt = logical % NT;
+  const int e = tile_e[mt], g0 = tile_g0[mt], ng = tile_ng[mt];
+
+  const int KS = H / kStepK;
+  const size_t op_stride = (size_t)KS * kTileBytes, sc_stride = (size_t)KS * kTileScaleBytes;
+  const uint8_t* we = w13p + (size_t)e * (size_t)(2 * I) * (size_t)H;
+  const uint8_t* se = s13p + (size_t)e * (size_t)(2 * I) * (size_t)(H / 32);
+  v16f acc[4][4];
+  tile::mainloop(st0, st1, st2, st3, we + (2 * nt) * op_stride, we + (2 * nt + 1) * op_stride,
+                 a1q + (size_t)g0 * op_stride, a1q + (size_t)(g0 + 1) * op_stride, se + (2 * nt) * sc_stride,
+                 se + (2 * nt + 1) * sc_stride, a1s + (size_t)g0 * sc_stride, a1s + (size_t)(g0 + 1) * sc_stride,
+                 KS, acc);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = wave >> 1, wm = wave & 1;
+  const int li = lane & 31, lg = lane >> 5;
+  const int KS2 = I / kStepK;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int ml = wm * 128 + 32 * b + li;      // row inside the tile
+    const int pos = g0 * kGroupRows + ml;
+    const bool row_ok = ml < ng * kGroupRows;
+    const int g = pos / kGroupRows, rr = pos % kGroupRows;
+    const int src = (dbg_act != nullptr && row_ok) ? sorted_row[pos] : -1;
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      // Gated activation, rounded to bf16 (pairs r, r+1 in one word).
+      uint32_t w[8];
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        float o[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float gt = acc[a][b][2 * p + h], up = acc[a + 2][b][2 * p + h];
+          o[h] = gt / (1.0f + expf(-gt)) * up;
+        }
+        w[p] = pack_bf16x2(o[0], o[1]);
+      }
+      // MX block = this lane's 16 values and those of lane ^ 32.
+      u16x2 mp = {0, 0};
+#pragma unroll
+      for (int p = 0; p < 8; ++p) mp = absmax_pk(mp, w[p]);
+      uint32_t m = max((uint32_t)mp[0], (uint32_t)mp[1]);
+      m = max(m, (uint32_t)__shfl_xor((int)m, 32));
+      const uint32_t sb = (uint32_t)max((int)(m >> 7) - 8, 0);
+      const float scale = mx_scale_value(sb);
+      uint32_t q[4];
+      cvt8s(w, scale, q);
+      cvt8s(w + 4, scale, q + 2);
+      const int iblk = nt * 128 + wn * 64 + 32 * a;   // first intermediate index of the block
+      const int ks = iblk / kStepK;
+      uint8_t* tbase = a2q + ((size_t)g * KS2 + ks) * kTileBytes;
+      if (row_ok) {
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const int k = (iblk % kStepK) + 8 * s4 + 4 * lg;  // within the 64-K step
+          *reinterpret_cast<uint32_t*>(tbase + tile_off(rr, k >> 4) + (k & 15)) = q[s4];
+        }
+        if (lg == 0) a2s[((size_t)g * KS2 + ks) * kTileScaleBytes + rr * 2 + ((iblk >> 5) & 1)] = (uint8_t)sb;
+      }
+      if (src >= 0) {
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const int i0 = iblk + 8 * s4 + 4 * lg;
+          uint16_t* da = dbg_act + (int64_t)src * I + i0;
+          da[0] = (uint16_t)w[2 * s4];
+          da[1] = (uint16_t)(w[2 * s4] >> 16);
+          da[2] = (uint16_t)w[2 * s4 + 1];
+          da[3] = (uint16_t)(w[2 * s4 + 1] >> 16);
+          *reinterpret_cast<uint32_t*>(dbg_q + (int64_t)src * I + i0) = q[s4];
+        }
+        if (lg == 0) dbg_s[(int64_t)src * (I / 32) + iblk / 32] = (uint8_t)sb;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- 6. gemm2
+__global__ __launch_bounds__(tile::kThreads, 1) void moe_gemm2_kernel(
+    const uint8_t* __restrict__ a2q, const uint8_t* __restrict__ a2s, const uint8_t* __restrict__ w2p,
+    const uint8_t* __restrict__ s2p, const int* __restrict__ meta, const int* __restrict__ tile_e,
+    const int* __restrict__ tile_g0, const int* __restrict__ tile_ng, const int* __restrict__ sorted_row,
+    const float* __restrict__ wts, int H, int I, float* __restrict__ ys) {
+  __shared__ float row_w[256];
+  __shared__ __attribute__((aligned(16))) uint8_t st0[tile::kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[tile::kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[tile::kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t st3[tile::kStage];
+  const int NT = H / 256;
+  const int total = meta[0] * NT;
+  if ((int)blockIdx.x >= total) return;
+  const int logical = tile::xcd_remap((int)blockIdx.x, total);
+  const int mt = logical / NT, nt = logical % NT;
+  const int e = tile_e[mt], g0 = tile_g0[mt], ng = tile_ng[mt];
+
+  const int KS = I / kStepK;
+  const size_t op_stride = (size_t)KS * kTileBytes, sc_stride = (size_t)KS * kTileScaleBytes;
+  const uint8_t* we = w2p + (size_t)e * (size_t)H * (size_t)I;
+  const uint8_t* se = s2p + (size_t)e * (size_t)H * (size_t)(I / 32);
+  v16f acc[4][4];
+  tile::mainloop(st0, st1, st2, st3, we + (2 * nt) * op_stride, we + (2 * nt + 1) * op_stride,
+                 a2q + (size_t)g0 * op_stride, a2q + (size_t)(g0 + 1) * op_stride, se + (2 * nt) * sc_stride,
+                 se + (2 * nt + 1) * sc_stride, a2s + (size_t)g0 * sc_stride, a2s + (size_t)(g0 + 1) * sc_stride,
+                 KS, acc);
+
+  // Routing weight of each tile row (zero for pad rows), applied in the
+  // epilogue before the one rounding to bf16.
+  for (int m = threadIdx.x; m < 256; m += tile::kThreads) {
+    float wv = 0.0f;
+    if (m < ng * kGroupRows) {
+      const int src = sorted_row[g0 * kGroupRows + m];
+      if (src >= 0) wv = wts[src];
+    }
+    row_w[m] = wv;
+  }
+  __syncthreads();
+  tile::store_bf16<true, float>(st0, st1, st2, st3, acc, ys, H, g0 * kGroupRows, (g0 + ng) * kGroupRows, nt * 256,
+                                H, nullptr, 1, row_w);
+}
+
+// ---------------------------------------------------------------- 7. combine
+__global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ ys, const int* __restrict__ inv,
+                                                          int T, int H, int topk, uint16_t* __restrict__ y) {
+  const int64_t t8 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int per_row = H / 8;
+  if (t8 >= (int64_t)T * per_row) return;
+  const int64_t t = t8 / per_row;
+  const int c = (int)(t8 - t * per_row);
+  float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = s0;
+  for (int j = 0; j < topk; ++j) {
+    const float4* p = reinterpret_cast<const float4*>(ys + (int64_t)inv[t * topk + j] * H + c * 8);
+    const float4 a = p[0], b = p[1];
+    s0.x += a.x; s0.y += a.y; s0.z += a.z; s0.w += a.w;
+    s1.x += b.x; s1.y += b.y; s1.z += b.z; s1.w += b.w;
+  }
+  *reinterpret_cast<uint4*>(y + t * H + c * 8) = make_uint4(pack_bf16x2(s0.x, s0.y), pack_bf16x2(s0.z, s0.w),
+                                                            pack_bf16x2(s1.x, s1.y), pack_bf16x2(s1.z, s1.w));
+}
+
+// ---------------------------------------------------------------- launcher
+int launch_moe(const MoeArgs& a, hipStream_t stream) {
+  const int nblk = (int)((a.T + kRouteTokens - 1) / kRouteTokens);
+  const int R = (int)(a.T * a.topk);
+  hipLaunchKernelGGL(moe_route_kernel, dim3(nblk), dim3(1024), 0, stream, a.logits, (int)a.T, (int)a.E,
+                     (int)a.topk, a.ws.ids, a.ws.wts, a.ws.blk_cnt, nblk);
+  if (a.dbg_ids != nullptr) {
+    hipMemcpyAsync(a.dbg_ids, a.ws.ids, (size_t)R * 4, hipMemcpyDeviceToDevice, stream);
+    hipMemcpyAsync(a.dbg_wts, a.ws.wts, (size_t)R * 4, hipMemcpyDeviceToDevice, stream);
+  }
+  hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(1024), 0, stream, a.ws.blk_cnt, nblk, (int)a.E, a.ws.blk_off,
+                     a.ws.seg_off, a.ws.tile_e, a.ws.tile_g0, a.ws.tile_ng, a.ws.meta, a.ws.sorted_row,
+                     (int)a.ws.p_max);
+  hipLaunchKernelGGL(moe_scatter_kernel, dim3(nblk), dim3(256), 0, stream, a.ws.ids, R, (int)a.topk, nblk,
+                     a.ws.blk_off, a.ws.seg_off, a.ws.sorted_row, a.ws.inv);
+  const int KS1 = (int)(a.H / kStepK);
+  const int64_t gq_total = a.ws.p_max * (a.H / 8);
+  if (gq_total < ((int64_t)1 << 32)) {
+    hipLaunchKernelGGL(moe_gather_quant_kernel<uint32_t>, dim3((unsigned)(gq_total / 256)), dim3(256), 0, stream,
+                       (const uint16_t*)a.x, (int)a.H, (int)a.topk, a.ws.sorted_row, a.ws.meta, (uint32_t)gq_total,
+                       KS1, a.ws.a1q, a.ws.a1s);
+  } else {
+    hipLaunchKernelGGL(moe_gather_quant_kernel<uint64_t>, dim3((unsigned)(gq_total / 256)), dim3(256), 0, stream,
+                       (const uint16_t*)a.x, (int)a.H, (int)a.topk, a.ws.sorted_row, a.ws.meta, (uint64_t)gq_total,
+                       KS1, a.ws.a1q, a.ws.a1s);
+  }
+  const int nt1 = (int)(2 * a.I / 256), nt2 = (int)(a.H / 256);
+  hipLaunchKernelGGL(moe_gemm1_kernel, dim3((unsigned)(a.ws.mt_max * nt1)), dim3(tile::kThreads), 0, stream,
+                     a.ws.a1q, a.ws.a1s, (const uint8_t*)a.w13p, (const uint8_t*)a.s13p, a.ws.meta, a.ws.tile_e,
+                     a.ws.tile_g0, a.ws.tile_ng, a.ws.sorted_row, (int)a.H, (int)a.I, a.ws.a2q, a.ws.a2s,
+                     (uint16_t*)a.dbg_act, (uint8_t*)a.dbg_q, (uint8_t*)a.dbg_s);
+  hipLaunchKernelGGL(moe_gemm2_kernel, dim3((unsigned)(a.ws.mt_max * nt2)), dim3(tile::kThreads), 0, stream,
+                     a.ws.a2q, a.ws.a2s, (const uint8_t*)a.w2p, (const uint8_t*)a.s2p, a.ws.meta, a.ws.tile_e,
+                     a.ws.tile_g0, a.ws.tile_ng, a.ws.sorted_row, a.ws.wts, (int)a.H, (int)a.I, a.ws.ys);
+  const int64_t cb_total = a.T * (a.H / 8);
+  hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((cb_total + 255) / 256)), dim3(256), 0, stream, a.ws.ys,
+                     a.ws.inv, (int)a.T, (int)a.H, (int)a.topk, (uint16_t*)a.y);
+  return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+}  // namespace mxfp8

@@ -14,9 +14,21 @@ namespace mxfp8 {
 
 constexpr int kChunksPerTile = kTileBytes / 16;  // 512
 
+// Source row of packed row n: n itself, or (gate_up_I > 0) the gate/up
+// interleave of stacked [E * 2I] expert weights described in launch.hpp.
+__device__ inline int64_t src_row(int64_t n, int64_t gate_up_I) {
+  if (gate_up_I == 0) return n;
+  const int64_t per = 2 * gate_up_I;
+  const int64_t e = n / per, p = n - e * per;
+  const int64_t t = p / 256, h = (p / 128) & 1, q = p & 127;
+  const int64_t row = q < 64 ? t * 128 + h * 64 + q : gate_up_I + t * 128 + h * 64 + (q - 64);
+  return e * per + row;
+}
+
 // One thread per 16-byte chunk of the packed data.
 __global__ __launch_bounds__(256) void pack_w_kernel(const uint8_t* __restrict__ w, int64_t ldw, int64_t N,
-                                                     int64_t KS, int64_t total, uint8_t* __restrict__ wp) {
+                                                     int64_t KS, int64_t total, uint8_t* __restrict__ wp,
+                                                     int64_t gate_up_I) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= total) return;
   const int64_t tile = t / kChunksPerTile;
@@ -26,13 +38,14 @@ __global__ __launch_bounds__(256) void pack_w_kernel(const uint8_t* __restrict__
   const int c = (slot & 3) ^ swz(r);
   const int64_t n = g * kGroupRows + r;
   uint4 v = make_uint4(0u, 0u, 0u, 0u);
-  if (n < N) v = *reinterpret_cast<const uint4*>(w + n * ldw + ks * kStepK + c * 16);
+  if (n < N) v = *reinterpret_cast<const uint4*>(w + src_row(n, gate_up_I) * ldw + ks * kStepK + c * 16);
   reinterpret_cast<uint4*>(wp)[t] = v;
 }
 
 // One thread per 2-byte (one row, one 64-element K step) scale word.
 __global__ __launch_bounds__(256) void pack_s_kernel(const uint8_t* __restrict__ ws, int64_t ldws, int64_t N,
-                                                     int64_t KS, int64_t total, uint16_t* __restrict__ sp) {
+                                                     int64_t KS, int64_t total, uint16_t* __restrict__ sp,
+                                                     int64_t gate_up_I) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= total) return;
   const int64_t tile = t / kGroupRows;
@@ -41,7 +54,7 @@ __global__ __launch_bounds__(256) void pack_s_kernel(const uint8_t* __restrict__
   const int64_t n = g * kGroupRows + r;
   uint16_t d = 0x7F7F;
   if (n < N) {
-    const uint8_t* p = ws + n * ldws + ks * 2;
+    const uint8_t* p = ws + src_row(n, gate_up_I) * ldws + ks * 2;
     d = (uint16_t)(p[0] | (p[1] << 8));
   }
   sp[t] = d;
@@ -74,17 +87,27 @@ __global__ __launch_bounds__(256) void unpack_s_kernel(const uint16_t* __restric
   p[1] = (uint8_t)(d >> 8);
 }
 
-int launch_pack_weight(const void* w, const void* ws, int64_t N, int64_t K, int64_t ldw, int64_t ldws,
-                       void* wp, void* sp, hipStream_t stream) {
+static int pack(const void* w, const void* ws, int64_t N, int64_t K, int64_t ldw, int64_t ldws, void* wp,
+                void* sp, int64_t gate_up_I, hipStream_t stream) {
   const int64_t KS = K / kStepK;
   const int64_t G = (N + kGroupRows - 1) / kGroupRows;
   const int64_t tw = G * KS * kChunksPerTile;
   const int64_t ts = G * KS * kGroupRows;
   hipLaunchKernelGGL(pack_w_kernel, dim3((unsigned)((tw + 255) / 256)), dim3(256), 0, stream,
-                     (const uint8_t*)w, ldw, N, KS, tw, (uint8_t*)wp);
+                     (const uint8_t*)w, ldw, N, KS, tw, (uint8_t*)wp, gate_up_I);
   hipLaunchKernelGGL(pack_s_kernel, dim3((unsigned)((ts + 255) / 256)), dim3(256), 0, stream,
-                     (const uint8_t*)ws, ldws, N, KS, ts, (uint16_t*)sp);
+                     (const uint8_t*)ws, ldws, N, KS, ts, (uint16_t*)sp, gate_up_I);
   return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+int launch_pack_weight(const void* w, const void* ws, int64_t N, int64_t K, int64_t ldw, int64_t ldws,
+                       void* wp, void* sp, hipStream_t stream) {
+  return pack(w, ws, N, K, ldw, ldws, wp, sp, 0, stream);
+}
+
+int launch_pack_weight_gate_up(const void* w, const void* ws, int64_t E, int64_t I, int64_t K, void* wp, void* sp,
+                               hipStream_t stream) {
+  return pack(w, ws, E * 2 * I, K, K, K / 32, wp, sp, I, stream);
 }
 
 int launch_unpack_weight(const void* wp, const void* sp, int64_t N, int64_t K, void* w, void* ws,

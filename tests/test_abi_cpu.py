@@ -113,3 +113,56 @@ def test_force_path_hook():
     prev = api.mxfp8_debug_force_path(1)
     assert api.mxfp8_debug_force_path(prev) == 1
     assert api.mxfp8_debug_force_path(7) == -2
+
+
+def test_moe_sizes():
+    E, H, I = 128, 2048, 768
+    assert api.mxfp8_moe_prepared_bytes(E, H, I) == (E * 2 * I * H, E * 2 * I * H // 32, E * H * I, E * H * I // 32)
+    with pytest.raises(api.MXFP8Error):
+        api.mxfp8_moe_prepared_bytes(E, H, 640)        # I % 256
+    with pytest.raises(api.MXFP8Error):
+        api.mxfp8_moe_prepared_bytes(257, H, I)        # too many experts
+    T, k = 4096, 8
+    ws = api.mxfp8_moe_workspace_bytes(T, H, I, E, k)
+    # at least the expert-sorted operands of both GEMMs and the bf16 expert outputs
+    rows = T * k
+    assert ws >= rows * (H + H // 32 + I + I // 32 + 2 * H)
+    assert api.mxfp8_moe_workspace_bytes(0, H, I, E, k) > 0
+    with pytest.raises(api.MXFP8Error):
+        api.mxfp8_moe_workspace_bytes(T, H, I, E, 17)  # top-k above 16
+    with pytest.raises(api.MXFP8Error):
+        api.mxfp8_moe_workspace_bytes(T, H, I, 4, 8)   # top-k above E
+
+
+def test_moe_validation():
+    T, H, E, k, I = 64, 256, 8, 2, 256
+    ws = api.mxfp8_moe_workspace_bytes(T, H, I, E, k)
+    f = api.mxfp8_moe_grouped
+    ok = [P, P, T, H, E, k, I, P, P, P, P, P, P, ws, None]
+    assert f(*ok) == -6                                # valid, but no gfx950 device here
+    bad = list(ok); bad[2] = 0; assert f(*bad) == 0    # T == 0 no-op
+    bad = list(ok); bad[3] = 320; assert f(*bad) == -2
+    bad = list(ok); bad[6] = 128; assert f(*bad) == -2
+    bad = list(ok); bad[5] = 0; assert f(*bad) == -2
+    bad = list(ok); bad[0] = None; assert f(*bad) == -1
+    bad = list(ok); bad[1] = None; assert f(*bad) == -1
+    bad = list(ok); bad[11] = None; assert f(*bad) == -1
+    bad = list(ok); bad[0] = P + 8; assert f(*bad) == -3
+    bad = list(ok); bad[7] = P + 16; assert f(*bad) == -3
+    bad = list(ok); bad[12] = None; assert f(*bad) == -5
+    bad = list(ok); bad[13] = ws - 1; assert f(*bad) == -5
+    bad = list(ok); bad[12] = P + 128; assert f(*bad) == -3
+    g = api.mxfp8_moe_prepare_weights
+    okp = [P, P, P, P, E, H, I, P, P, P, P, None]
+    assert g(*okp) == -6
+    bad = list(okp); bad[6] = 300; assert g(*bad) == -2
+    bad = list(okp); bad[2] = None; assert g(*bad) == -1
+    bad = list(okp); bad[8] = P + 4; assert g(*bad) == -3
+
+
+def test_moe_debug_hook():
+    assert api.mxfp8_moe_debug_capture(P, None, None, None, None) == -1
+    assert api.mxfp8_moe_debug_capture(P, P, P, P, None) == -1
+    assert api.mxfp8_moe_debug_capture(P + 2, P, P, P, P) == -3
+    assert api.mxfp8_moe_debug_capture(P, P, P, P, P) == 0
+    assert api.mxfp8_moe_debug_capture(None, None, None, None, None) == 0
