@@ -16,8 +16,9 @@ on the launch stream inside the timed region; ``sweep`` with the other
 workload shapes (M=7 single layer, the decode sweep M in {1,7,16,128} at
 N=K=4096 with the weights rotated through 48 copies so they do not sit in the
 256 MB last-level cache, the M=16384 prefill shape, and the standalone
-quantizer); ``cpu_baseline``, the CPU oracle timed on a bounded sample of the
-headline workload.
+quantizer, and one forward of the routed MoE layer at its full size);
+``cpu_baseline``, the CPU oracle timed on a bounded sample of the headline
+workload.
 """
 
 import argparse
@@ -33,7 +34,8 @@ sys.path.insert(0, ROOT)
 PEAK_MFMA_FP8_TFLOPS = 5000.0   # MI355X dense FP8 / MXFP8 MFMA
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_tile_large.json")
-GEMM_SOURCES = ["mxfp8_block_scaled_amd/csrc/gemm_tile.hip", "mxfp8_block_scaled_amd/csrc/common.hpp"]
+GEMM_SOURCES = ["mxfp8_block_scaled_amd/csrc/gemm_tile.hip", "mxfp8_block_scaled_amd/csrc/tile_core.hpp",
+                "mxfp8_block_scaled_amd/csrc/common.hpp"]
 
 
 def parse():
@@ -254,6 +256,9 @@ def sweep(api, synth, torch, np, dev, stream):
     y = torch.empty((16384, 5120), dtype=torch.bfloat16, device=dev)
     linear_entry([xd], [pw], None, 16384, 5120, 2048, y, 50, "prefill_qkv M=16384 N=5120 K=2048")
 
+    # routed MoE layer: 4096 tokens, H=2048, 128 experts, top-8, I=768
+    rows.append(moe_row(api, synth, torch, dev, stream))
+
     # standalone quantizer on the prefill activations
     q = torch.empty((16384, 2048), dtype=torch.uint8, device=dev)
     s = torch.empty((16384, 64), dtype=torch.uint8, device=dev)
@@ -268,6 +273,33 @@ def sweep(api, synth, torch, np, dev, stream):
                  "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
                  "pct_hbm": round(100 * nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)})
     return rows
+
+
+def moe_row(api, synth, torch, dev, stream):
+    """One forward of the MoE layer (every kernel of mxfp8_moe_grouped).
+    FLOPs count the routed rows only (2 T k (2I H + H I)); bytes are the
+    minimum a forward must move: both expert weights with their scales, x,
+    logits and y."""
+    c = synth.MOE_CONFIG
+    T, H, E, k, inter = c["T"], c["H"], c["E"], c["topk"], c["I"]
+    x, logits, w13, w2 = synth.moe_inputs(device=dev)
+    q13, s13 = api.quantize_act(w13.reshape(E * 2 * inter, H))
+    q2, s2 = api.quantize_act(w2.reshape(E * H, inter))
+    del w13, w2
+    mw = api.moe_prepare_weights(q13.view(E, 2 * inter, H), s13.view(E, 2 * inter, H // 32),
+                                 q2.view(E, H, inter), s2.view(E, H, inter // 32))
+    del q13, s13, q2, s2
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        api.moe_grouped(x, logits, mw, k, out=y)
+    torch.cuda.synchronize()
+    ms = time_calls(lambda r: api.moe_grouped(x, logits, mw, k, out=y), 20, stream, torch)
+    flops = 2.0 * T * k * (2 * inter * H + H * inter)
+    nbytes = E * (2 * inter * H + H * inter) * (1 + 1 / 32) + T * H * 2 * 2 + T * E * 4
+    return {"workload": f"moe T={T} H={H} E={E} top{k} I={inter}", "us": round(ms * 1e3, 3),
+            "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 3), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "pct_mfma_peak": round(100 * flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_FP8_TFLOPS, 2),
+            "pct_hbm": round(100 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}
 
 
 def cpu_baseline(synth, np, torch):

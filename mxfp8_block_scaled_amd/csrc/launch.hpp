@@ -48,8 +48,8 @@ constexpr int64_t kMoeMaxTopk = 16;
 struct MoeWorkspace {
   int* ids;          // [T*k] expert of row t*k + j
   float* wts;        // [T*k] routing weight
-  int* blk_cnt;      // [E][nblk] rows of each route block per expert
-  int* blk_off;      // [E][nblk] their offsets inside the expert's segment
+  int* blk_cnt;      // [nblk][E] rows of each route block per expert
+  int* blk_off;      // [nblk][E] their offsets inside the expert's segment
   int* seg_off;      // [E] first sorted position of each expert
   int* meta;         // [0] M-tiles, [1] 128-row groups in use
   int* tile_e;       // [mt_max] expert of each M-tile

@@ -110,11 +110,16 @@ __global__ __launch_bounds__(1024) void moe_route_kernel(const float* __restrict
     }
   }
   __syncthreads();
-  for (int e = tid; e < E; e += 1024) blk_cnt[(int64_t)e * nblk + blockIdx.x] = hist[e];
+  for (int e = tid; e < E; e += 1024) blk_cnt[(int64_t)blockIdx.x * E + e] = hist[e];
 }
 
 // ---------------------------------------------------------------- 2. plan
 // meta[0] = number of M-tiles, meta[1] = number of 128-row groups in use.
+// One workgroup; every phase is parallel over experts and blocks.  Stores
+// count in the same vmcnt as loads, so each phase issues its loads, waits
+// once, and only then stores; the large -1 fill of sorted_row comes last.
+constexpr int kPlanChunk = 32;
+
 __global__ __launch_bounds__(1024) void moe_plan_kernel(const int* __restrict__ blk_cnt, int nblk, int E,
                                                         int* __restrict__ blk_off, int* __restrict__ seg_off,
                                                         int* __restrict__ tile_e, int* __restrict__ tile_g0,
@@ -122,41 +127,87 @@ __global__ __launch_bounds__(1024) void moe_plan_kernel(const int* __restrict__ 
                                                         int* __restrict__ sorted_row, int p_max) {
   __shared__ int part[1024];
   __shared__ int cnt[kMoeMaxExperts], gstart[kMoeMaxExperts], tstart[kMoeMaxExperts];
-  const int tid = threadIdx.x;
-  for (int p = tid; p < p_max; p += 1024) sorted_row[p] = -1;
-  // Thread (e, c) owns blocks [c*per, (c+1)*per) of expert e.
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // Thread (c, e) = (tid / E, tid % E) owns blocks [b0, b1) of expert e; the
+  // counts are stored block-major ([nblk][E]), so a wave's load reads
+  // consecutive experts of one block (contiguous bytes).
   const int tpe = 1024 / E;                       // threads per expert (E <= 256: >= 4)
-  const int e = tid / tpe, c = tid % tpe;
+  const int e = tid % E, c = tid / E;
+  const bool mine = c < tpe;
   const int per = (nblk + tpe - 1) / tpe;
   const int b0 = min(c * per, nblk), b1 = min(b0 + per, nblk);
+  // (Indices are clamped rather than the loads predicated, so a chunk's loads
+  // are straight-line code and overlap.)
+  auto load_chunk = [&](int b, int (&v)[kPlanChunk]) {
+#pragma unroll
+    for (int u = 0; u < kPlanChunk; ++u) v[u] = blk_cnt[(int64_t)min(b + u, b1 - 1) * E + e];
+  };
   int sum = 0;
-  if (e < E)
-    for (int b = b0; b < b1; ++b) sum += blk_cnt[(int64_t)e * nblk + b];
+  if (mine)
+    for (int b = b0; b < b1; b += kPlanChunk) {
+      int v[kPlanChunk];
+      load_chunk(b, v);
+#pragma unroll
+      for (int u = 0; u < kPlanChunk; ++u) sum += (b + u < b1) ? v[u] : 0;
+    }
   part[tid] = sum;
   __syncthreads();
-  if (e < E) {
+  if (tid < E) {
+    int t = 0;
+    for (int k = 0; k < tpe; ++k) t += part[k * E + tid];
+    cnt[tid] = t;
+  }
+  __syncthreads();
+  // Exclusive scan of groups and M-tiles over experts: wave 0, lane l holds
+  // experts 4l .. 4l+3.
+  if (wave == 0) {
+    int g4[4], t4[4], gs = 0, ts = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int x = 4 * lane + u;
+      const int groups = x < E ? (cnt[x] + kGroupRows - 1) / kGroupRows : 0;
+      g4[u] = gs;
+      t4[u] = ts;
+      gs += groups;
+      ts += (groups + 1) / 2;
+    }
+    int gi = gs, ti = ts;                          // inclusive scan across lanes
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int go = __shfl_up(gi, off), to = __shfl_up(ti, off);
+      if (lane >= off) {
+        gi += go;
+        ti += to;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int x = 4 * lane + u;
+      if (x < E) {
+        gstart[x] = gi - gs + g4[u];
+        tstart[x] = ti - ts + t4[u];
+      }
+    }
+    if (lane == 63) {
+      meta[0] = ti;
+      meta[1] = gi;
+    }
+  }
+  __syncthreads();
+  if (mine) {
     int run = 0;
-    for (int k = 0; k < c; ++k) run += part[e * tpe + k];
-    for (int b = b0; b < b1; ++b) {
-      blk_off[(int64_t)e * nblk + b] = run;
-      run += blk_cnt[(int64_t)e * nblk + b];
+    for (int k = 0; k < c; ++k) run += part[k * E + e];
+    for (int b = b0; b < b1; b += kPlanChunk) {
+      int v[kPlanChunk];
+      load_chunk(b, v);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int u = 0; u < kPlanChunk; ++u) {
+        if (b + u < b1) blk_off[(int64_t)(b + u) * E + e] = run;
+        run += (b + u < b1) ? v[u] : 0;
+      }
     }
-    if (c == tpe - 1) cnt[e] = run;
   }
-  __syncthreads();
-  if (tid == 0) {
-    int g = 0, tt = 0;
-    for (int x = 0; x < E; ++x) {
-      const int groups = (cnt[x] + kGroupRows - 1) / kGroupRows;
-      gstart[x] = g;
-      tstart[x] = tt;
-      g += groups;
-      tt += (groups + 1) / 2;
-    }
-    meta[0] = tt;
-    meta[1] = g;
-  }
-  __syncthreads();
   if (tid < E) {
     const int groups = (cnt[tid] + kGroupRows - 1) / kGroupRows;
     seg_off[tid] = gstart[tid] * kGroupRows;
@@ -166,10 +217,12 @@ __global__ __launch_bounds__(1024) void moe_plan_kernel(const int* __restrict__ 
       tile_ng[tstart[tid] + u] = min(2, groups - 2 * u);
     }
   }
+  // p_max is a multiple of 128: fill with 16-byte stores.
+  for (int p = tid; p < p_max / 4; p += 1024) reinterpret_cast<int4*>(sorted_row)[p] = make_int4(-1, -1, -1, -1);
 }
 
 // ---------------------------------------------------------------- 3. scatter
-__global__ __launch_bounds__(256) void moe_scatter_kernel(const int* __restrict__ ids, int R, int topk, int nblk,
+__global__ __launch_bounds__(256) void moe_scatter_kernel(const int* __restrict__ ids, int R, int topk, int E,
                                                           const int* __restrict__ blk_off,
                                                           const int* __restrict__ seg_off,
                                                           int* __restrict__ sorted_row, int* __restrict__ inv) {
@@ -194,7 +247,7 @@ __global__ __launch_bounds__(256) void moe_scatter_kernel(const int* __restrict_
   }
   __syncthreads();
   if (valid) {
-    int pos = seg_off[e] + blk_off[(int64_t)e * nblk + blockIdx.x] + local;
+    int pos = seg_off[e] + blk_off[(int64_t)blockIdx.x * E + e] + local;
     for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
     sorted_row[pos] = r;
     inv[r] = pos;
@@ -203,38 +256,50 @@ __global__ __launch_bounds__(256) void moe_scatter_kernel(const int* __restrict_
 
 // ---------------------------------------------------------------- 4. gather
 // The packed act-quant of quant.hip with a row indirection: position pos of
-// the expert-sorted operand holds token sorted_row[pos] / k (or zeros).
-template <typename Idx>
+// the expert-sorted operand holds token sorted_row[pos] / k (or zeros).  A
+// thread owns one (row, 8-element chunk) pair and walks every 64-K step of
+// the row, kBatch steps' loads in flight at a time; a wave covers 8 rows x 8
+// chunks, i.e. 512 contiguous bytes of each packed tile it writes.
+template <int kBatch>
 __global__ __launch_bounds__(256) void moe_gather_quant_kernel(const uint16_t* __restrict__ x, int H, int topk,
                                                                const int* __restrict__ sorted_row,
-                                                               const int* __restrict__ meta, Idx total, int KS,
+                                                               const int* __restrict__ meta, int KS,
                                                                uint8_t* __restrict__ qp, uint8_t* __restrict__ sp) {
-  const Idx t = (Idx)blockIdx.x * 256 + threadIdx.x;
-  if (t >= total) return;
-  const Idx tile = t >> 10;
-  const int64_t g = (int64_t)(tile / (Idx)KS);
-  if (g >= meta[1]) return;                 // whole tiles leave together
-  const int64_t ks = (int64_t)tile - g * KS;
-  const int r = (int)((t >> 3) & 127);
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;   // over p_max * 8
+  const int64_t pos = t >> 3;
+  const int64_t g = pos / kGroupRows;
+  if (g >= meta[1]) return;                 // whole groups (16 waves) leave together
+  const int r = (int)(pos % kGroupRows);
   const int c8 = (int)(t & 7);
-  const int src = sorted_row[g * kGroupRows + r];
-  uint32_t w[4] = {0u, 0u, 0u, 0u};
-  if (src >= 0) {
-    const uint4 v = *reinterpret_cast<const uint4*>(x + (int64_t)(src / topk) * H + ks * kStepK + c8 * 8);
-    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-  }
-  u16x2 mp = {0, 0};
+  const int src = sorted_row[pos];
+  const uint16_t* xrow = x + (int64_t)(src >= 0 ? src / topk : 0) * H + c8 * 8;
+  uint8_t* qg = qp + g * KS * kTileBytes + tile_off(r, c8 >> 1) + (c8 & 1) * 8;
+  uint8_t* sg = sp + g * KS * kTileScaleBytes + r * 2 + (c8 >> 2);
+  for (int ks0 = 0; ks0 < KS; ks0 += kBatch) {
+    uint4 v[kBatch];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) mp = absmax_pk(mp, w[i]);
-  uint32_t m = max((uint32_t)mp[0], (uint32_t)mp[1]);
-  m = max(m, (uint32_t)__shfl_xor((int)m, 1));
-  m = max(m, (uint32_t)__shfl_xor((int)m, 2));
-  const uint32_t sb = (uint32_t)max((int)(m >> 7) - 8, 0);
-  uint32_t qd[2];
-  cvt8s(w, mx_scale_value(sb), qd);
-  uint8_t* dst = qp + (int64_t)tile * kTileBytes;
-  *reinterpret_cast<uint2*>(dst + tile_off(r, c8 >> 1) + (c8 & 1) * 8) = make_uint2(qd[0], qd[1]);
-  if ((c8 & 3) == 0) sp[(int64_t)tile * kTileScaleBytes + r * 2 + (c8 >> 2)] = (uint8_t)sb;
+    for (int u = 0; u < kBatch; ++u)
+      v[u] = (src >= 0 && ks0 + u < KS) ? *reinterpret_cast<const uint4*>(xrow + (int64_t)(ks0 + u) * kStepK)
+                                        : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      u16x2 mp = {0, 0};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mp = absmax_pk(mp, w[i]);
+      uint32_t m = max((uint32_t)mp[0], (uint32_t)mp[1]);
+      m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+      m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+      const uint32_t sb = (uint32_t)max((int)(m >> 7) - 8, 0);
+      uint32_t qd[2];
+      cvt8s(w, mx_scale_value(sb), qd);
+      const int ks = ks0 + u;
+      if (ks < KS) {
+        *reinterpret_cast<uint2*>(qg + (int64_t)ks * kTileBytes) = make_uint2(qd[0], qd[1]);
+        if ((c8 & 3) == 0) sg[(int64_t)ks * kTileScaleBytes] = (uint8_t)sb;
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------- 5. gemm1
@@ -410,19 +475,12 @@ int launch_moe(const MoeArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(1024), 0, stream, a.ws.blk_cnt, nblk, (int)a.E, a.ws.blk_off,
                      a.ws.seg_off, a.ws.tile_e, a.ws.tile_g0, a.ws.tile_ng, a.ws.meta, a.ws.sorted_row,
                      (int)a.ws.p_max);
-  hipLaunchKernelGGL(moe_scatter_kernel, dim3(nblk), dim3(256), 0, stream, a.ws.ids, R, (int)a.topk, nblk,
+  hipLaunchKernelGGL(moe_scatter_kernel, dim3(nblk), dim3(256), 0, stream, a.ws.ids, R, (int)a.topk, (int)a.E,
                      a.ws.blk_off, a.ws.seg_off, a.ws.sorted_row, a.ws.inv);
   const int KS1 = (int)(a.H / kStepK);
-  const int64_t gq_total = a.ws.p_max * (a.H / 8);
-  if (gq_total < ((int64_t)1 << 32)) {
-    hipLaunchKernelGGL(moe_gather_quant_kernel<uint32_t>, dim3((unsigned)(gq_total / 256)), dim3(256), 0, stream,
-                       (const uint16_t*)a.x, (int)a.H, (int)a.topk, a.ws.sorted_row, a.ws.meta, (uint32_t)gq_total,
-                       KS1, a.ws.a1q, a.ws.a1s);
-  } else {
-    hipLaunchKernelGGL(moe_gather_quant_kernel<uint64_t>, dim3((unsigned)(gq_total / 256)), dim3(256), 0, stream,
-                       (const uint16_t*)a.x, (int)a.H, (int)a.topk, a.ws.sorted_row, a.ws.meta, (uint64_t)gq_total,
-                       KS1, a.ws.a1q, a.ws.a1s);
-  }
+  hipLaunchKernelGGL(moe_gather_quant_kernel<4>, dim3((unsigned)(a.ws.p_max * 8 / 256)), dim3(256), 0, stream,
+                     (const uint16_t*)a.x, (int)a.H, (int)a.topk, a.ws.sorted_row, a.ws.meta, KS1, a.ws.a1q,
+                     a.ws.a1s);
   const int nt1 = (int)(2 * a.I / 256), nt2 = (int)(a.H / 256);
   hipLaunchKernelGGL(moe_gemm1_kernel, dim3((unsigned)(a.ws.mt_max * nt1)), dim3(tile::kThreads), 0, stream,
                      a.ws.a1q, a.ws.a1s, (const uint8_t*)a.w13p, (const uint8_t*)a.s13p, a.ws.meta, a.ws.tile_e,

@@ -111,8 +111,8 @@ def scale_stress(t, seed, block=32, lo=-16, hi=16):
     return (t.to(torch.float32) * f).to(t.dtype)
 
 
-def moe_inputs(T=None, H=None, E=None, topk=None, inter=None, seed=None, w_std=None):
-    """(x bf16 [T,H], logits fp32 [T,E], w13 bf16 [E,2I,H], w2 bf16 [E,H,I])."""
+def moe_inputs(T=None, H=None, E=None, topk=None, inter=None, seed=None, w_std=None, device="cpu"):
+    """(x bf16 [T,H], logits fp32 [T,E], w13 bf16 [E,2I,H], w2 bf16 [E,H,I]) on ``device``."""
     c = dict(MOE_CONFIG)
     T = T or c["T"]
     H = H or c["H"]
@@ -120,9 +120,9 @@ def moe_inputs(T=None, H=None, E=None, topk=None, inter=None, seed=None, w_std=N
     inter = inter or c["I"]
     seed = c["seed"] if seed is None else seed
     w_std = w_std or c["w_std"]
-    g = _gen(seed)
+    g = _gen(seed, device)
     x = randn_bf16((T, H), c["x_std"], g)
-    logits = torch.randn(T, E, generator=g, dtype=torch.float32) * c["logit_std"]
+    logits = torch.randn(T, E, generator=g, dtype=torch.float32, device=g.device) * c["logit_std"]
     w13 = randn_bf16((E, 2 * inter, H), w_std, g)
     w2 = randn_bf16((E, H, inter), w_std, g)
     return x, logits, w13, w2
