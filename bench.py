@@ -247,6 +247,9 @@ def sweep(api, synth, torch, np, dev, stream):
         y = torch.empty((M, 4096), dtype=torch.bfloat16, device=dev)
         linear_entry(xs, copies, bd, M, 4096, 4096, y, 480, f"decode M={M} N=4096 K=4096",
                      {"weight_copies_rotated": 48})
+        # The same 48 calls captured once in a HIP graph and replayed: the
+        # per-call time without the host's per-launch cost.
+        rows[-1]["graph_replay_us"] = graph_replay_us(api, torch, dev, xs, copies, bd, M, y)
     del copies, pw0
 
     # prefill QKV shape, M=16384 N=5120 K=2048, no bias
@@ -273,6 +276,36 @@ def sweep(api, synth, torch, np, dev, stream):
                  "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
                  "pct_hbm": round(100 * nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)})
     return rows
+
+
+def graph_replay_us(api, torch, dev, xs, copies, bias, M, y, replays=10):
+    """Per-call time of mxfp8_linear over the 48 weight copies, captured in a
+    HIP graph on a side stream and replayed (checked against eager first)."""
+    N, K = copies[0].N, copies[0].K
+    ws_t = api.workspace(M, N, K, dev)
+    side = torch.cuda.Stream(device=dev)
+
+    def calls(sp):
+        for r, pp in enumerate(copies):
+            st = api.mxfp8_linear(xs[r % len(xs)].data_ptr(), M, K, K, pp.w_packed.data_ptr(),
+                                  pp.s_packed.data_ptr(), N, bias.data_ptr(), y.data_ptr(), N, ws_t.data_ptr(),
+                                  ws_t.numel(), sp)
+            if st != 0:
+                raise RuntimeError(st)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        calls(side.cuda_stream)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cur = torch.cuda.current_stream(dev)
+    e0.record(cur)
+    for _ in range(replays):
+        g.replay()
+    e1.record(cur)
+    torch.cuda.synchronize()
+    return round(e0.elapsed_time(e1) * 1e3 / (replays * len(copies)), 3)
 
 
 def moe_row(api, synth, torch, dev, stream):

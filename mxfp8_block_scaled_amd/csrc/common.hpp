@@ -26,7 +26,12 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 //                  logical chunk cover all 64 LDS banks once (measured on
 //                  gfx950: no bank-conflict cycles; without the swizzle 2.2
 //                  conflict cycles per access);
-//   scale[g][ks] = 256 B: 128 rows x 2 UE8M0 bytes (MX blocks 2ks, 2ks+1).
+//   scale[g][ks] = 256 B: 128 rows x 2 UE8M0 bytes (MX blocks 2ks, 2ks+1),
+//                  lane-major: the byte of row r, block b sits at
+//                  (r % 32) * 8 + b * 4 + r / 32, so one 4-byte read gives a
+//                  32x32 MFMA lane (row r % 32, block b) the scales of its
+//                  rows r % 32 + 32 i, i = 0..3 (the MFMA picks byte i with
+//                  the scale operand's op_sel).
 //
 // A tile is one contiguous run of bytes, so a GEMM workgroup copies it to LDS
 // unchanged with direct global->LDS loads.
@@ -39,6 +44,8 @@ constexpr int kTileScaleBytes = kGroupRows * 2;   // 256
 __host__ __device__ inline int swz(int r) { return (r >> 2) & 3; }
 // Byte offset of logical chunk c of row r inside a tile.
 __host__ __device__ inline int tile_off(int r, int c) { return r * kStepK + ((c ^ swz(r)) << 4); }
+// Byte offset of the scale of row r (0..127), block b (0..1) inside a scale tile.
+__host__ __device__ inline int scale_off(int r, int b) { return (r & 31) * 8 + b * 4 + (r >> 5); }
 
 // ---------------------------------------------------------------------------
 // Scaled MFMA operand conventions on gfx950 (pinned by probes on the device):

@@ -56,9 +56,9 @@ __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(
   const int kb = (KS * wave) / kWaves, ke = (KS * (wave + 1)) / kWaves;
 
   // 1. Weight loads for this wave's steps (tiles 2ks and 2ks+1, chunk g of
-  // row r; the scale word of tile 2ks + g/2 holds this lane's block).
+  // row r; this lane's block 4ks + g is block g & 1 of tile 2ks + g/2).
   const uint8_t* wrow = wp + (size_t)grp * KT * kTileBytes + tile_off(r, g);
-  const uint8_t* srow = sp + (size_t)grp * KT * kTileScaleBytes + r * 2;
+  const uint8_t* srow = sp + (size_t)grp * KT * kTileScaleBytes + scale_off(r, g & 1);
   uint4 w0[kMaxSteps], w1[kMaxSteps];
   uint32_t wsd[kMaxSteps];
 #pragma unroll
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(
       const uint8_t* wt = wrow + (size_t)(2 * (kb + u)) * kTileBytes;
       w0[u] = *reinterpret_cast<const uint4*>(wt);
       w1[u] = *reinterpret_cast<const uint4*>(wt + kTileBytes);
-      wsd[u] = *reinterpret_cast<const uint16_t*>(srow + (size_t)(2 * (kb + u) + (g >> 1)) * kTileScaleBytes);
+      wsd[u] = srow[(size_t)(2 * (kb + u) + (g >> 1)) * kTileScaleBytes];
     }
   }
 
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(
       wa[4] = (int)w1[u].x; wa[5] = (int)w1[u].y; wa[6] = (int)w1[u].z; wa[7] = (int)w1[u].w;
       xb[0] = (int)b0.x; xb[1] = (int)b0.y; xb[2] = (int)b0.z; xb[3] = (int)b0.w;
       xb[4] = (int)b1.x; xb[5] = (int)b1.y; xb[6] = (int)b1.z; xb[7] = (int)b1.w;
-      const int wscale = (int)(wsd[u] >> (8 * (g & 1)));
+      const int wscale = (int)wsd[u];
       acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wa, xb, acc, 0, 0, 0, wscale, 0, xscale);
     }
   }

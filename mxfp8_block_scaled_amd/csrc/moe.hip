@@ -274,7 +274,7 @@ __global__ __launch_bounds__(256) void moe_gather_quant_kernel(const uint16_t* _
   const int src = sorted_row[pos];
   const uint16_t* xrow = x + (int64_t)(src >= 0 ? src / topk : 0) * H + c8 * 8;
   uint8_t* qg = qp + g * KS * kTileBytes + tile_off(r, c8 >> 1) + (c8 & 1) * 8;
-  uint8_t* sg = sp + g * KS * kTileScaleBytes + r * 2 + (c8 >> 2);
+  uint8_t* sg = sp + g * KS * kTileScaleBytes + scale_off(r, c8 >> 2);
   for (int ks0 = 0; ks0 < KS; ks0 += kBatch) {
     uint4 v[kBatch];
 #pragma unroll
@@ -381,7 +381,7 @@ __global__ __launch_bounds__(tile::kThreads, 1) void moe_gemm1_kernel(
           const int k = (iblk % kStepK) + 8 * s4 + 4 * lg;  // within the 64-K step
           *reinterpret_cast<uint32_t*>(tbase + tile_off(rr, k >> 4) + (k & 15)) = q[s4];
         }
-        if (lg == 0) a2s[((size_t)g * KS2 + ks) * kTileScaleBytes + rr * 2 + ((iblk >> 5) & 1)] = (uint8_t)sb;
+        if (lg == 0) a2s[((size_t)g * KS2 + ks) * kTileScaleBytes + scale_off(rr, (iblk >> 5) & 1)] = (uint8_t)sb;
       }
       if (src >= 0) {
 #pragma unroll

@@ -42,9 +42,9 @@ __global__ __launch_bounds__(256) void pack_w_kernel(const uint8_t* __restrict__
   reinterpret_cast<uint4*>(wp)[t] = v;
 }
 
-// One thread per 2-byte (one row, one 64-element K step) scale word.
+// One thread per (row, 64-element K step): its two scale bytes.
 __global__ __launch_bounds__(256) void pack_s_kernel(const uint8_t* __restrict__ ws, int64_t ldws, int64_t N,
-                                                     int64_t KS, int64_t total, uint16_t* __restrict__ sp,
+                                                     int64_t KS, int64_t total, uint8_t* __restrict__ sp,
                                                      int64_t gate_up_I) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= total) return;
@@ -52,12 +52,15 @@ __global__ __launch_bounds__(256) void pack_s_kernel(const uint8_t* __restrict__
   const int r = (int)(t % kGroupRows);
   const int64_t g = tile / KS, ks = tile - g * KS;
   const int64_t n = g * kGroupRows + r;
-  uint16_t d = 0x7F7F;
+  uint8_t b0 = 0x7F, b1 = 0x7F;
   if (n < N) {
     const uint8_t* p = ws + src_row(n, gate_up_I) * ldws + ks * 2;
-    d = (uint16_t)(p[0] | (p[1] << 8));
+    b0 = p[0];
+    b1 = p[1];
   }
-  sp[t] = d;
+  uint8_t* d = sp + tile * kTileScaleBytes;
+  d[scale_off(r, 0)] = b0;
+  d[scale_off(r, 1)] = b1;
 }
 
 __global__ __launch_bounds__(256) void unpack_w_kernel(const uint8_t* __restrict__ wp, int64_t K, int64_t KS,
@@ -73,7 +76,7 @@ __global__ __launch_bounds__(256) void unpack_w_kernel(const uint8_t* __restrict
   *reinterpret_cast<uint4*>(w + n * K + ks * kStepK + c * 16) = reinterpret_cast<const uint4*>(wp)[t];
 }
 
-__global__ __launch_bounds__(256) void unpack_s_kernel(const uint16_t* __restrict__ sp, int64_t K, int64_t KS,
+__global__ __launch_bounds__(256) void unpack_s_kernel(const uint8_t* __restrict__ sp, int64_t K, int64_t KS,
                                                        int64_t total, uint8_t* __restrict__ ws) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= total) return;
@@ -81,10 +84,10 @@ __global__ __launch_bounds__(256) void unpack_s_kernel(const uint16_t* __restric
   const int r = (int)(t % kGroupRows);
   const int64_t g = tile / KS, ks = tile - g * KS;
   const int64_t n = g * kGroupRows + r;
-  const uint16_t d = sp[t];
+  const uint8_t* d = sp + tile * kTileScaleBytes;
   uint8_t* p = ws + n * (K / 32) + ks * 2;
-  p[0] = (uint8_t)d;
-  p[1] = (uint8_t)(d >> 8);
+  p[0] = d[scale_off(r, 0)];
+  p[1] = d[scale_off(r, 1)];
 }
 
 static int pack(const void* w, const void* ws, int64_t N, int64_t K, int64_t ldw, int64_t ldws, void* wp,
@@ -96,7 +99,7 @@ static int pack(const void* w, const void* ws, int64_t N, int64_t K, int64_t ldw
   hipLaunchKernelGGL(pack_w_kernel, dim3((unsigned)((tw + 255) / 256)), dim3(256), 0, stream,
                      (const uint8_t*)w, ldw, N, KS, tw, (uint8_t*)wp, gate_up_I);
   hipLaunchKernelGGL(pack_s_kernel, dim3((unsigned)((ts + 255) / 256)), dim3(256), 0, stream,
-                     (const uint8_t*)ws, ldws, N, KS, ts, (uint16_t*)sp, gate_up_I);
+                     (const uint8_t*)ws, ldws, N, KS, ts, (uint8_t*)sp, gate_up_I);
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 
@@ -119,7 +122,7 @@ int launch_unpack_weight(const void* wp, const void* sp, int64_t N, int64_t K, v
   hipLaunchKernelGGL(unpack_w_kernel, dim3((unsigned)((tw + 255) / 256)), dim3(256), 0, stream,
                      (const uint8_t*)wp, K, KS, tw, (uint8_t*)w);
   hipLaunchKernelGGL(unpack_s_kernel, dim3((unsigned)((ts + 255) / 256)), dim3(256), 0, stream,
-                     (const uint16_t*)sp, K, KS, ts, (uint8_t*)ws);
+                     (const uint8_t*)sp, K, KS, ts, (uint8_t*)ws);
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 

@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void quant_act_packed_kernel(const uint16_t* _
   cvt8s(w, mx_scale_value(sb), qd);
   uint8_t* dst = qp + (int64_t)tile * kTileBytes;
   *reinterpret_cast<uint2*>(dst + tile_off(r, c8 >> 1) + (c8 & 1) * 8) = make_uint2(qd[0], qd[1]);
-  if ((c8 & 3) == 0) sp[(int64_t)tile * kTileScaleBytes + r * 2 + (c8 >> 2)] = (uint8_t)sb;
+  if ((c8 & 3) == 0) sp[(int64_t)tile * kTileScaleBytes + scale_off(r, c8 >> 2)] = (uint8_t)sb;
 }
 
 int launch_quantize_act_packed(const void* x, int64_t M, int64_t K, int64_t ldx, void* qp, void* sp,

@@ -31,6 +31,16 @@
 namespace mxfp8 {
 namespace tile {
 
+// Calls f(std::integral_constant<int, I>{}) for I = 0 .. N-1 (indices usable
+// as compile-time constants, e.g. MFMA op_sel values).
+template <int I, int N, typename Fn>
+__device__ __forceinline__ void static_for(Fn&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
 constexpr int kThreads = 256;
 constexpr int kOpBytes = 256 * kStepK;                // one operand's 256 rows x 64 K-bytes
 constexpr int kScaleRegion = 1024;                    // 256 x 2 B weight + 256 x 2 B activation scales
@@ -104,15 +114,15 @@ __device__ __forceinline__ void mainloop(uint8_t* st0, uint8_t* st1, uint8_t* st
   // the lane's rows: lane group lg supplies MX block lg of the step).
   struct Frags {
     v8i a[4], b[4];
-    int sa[4], sb[4];
+    int sa, sb;     // scale bytes of the lane's 4 rows (byte i: row li + 32 i)
   };
   // Lane offsets inside a stage: rows R0 + 32 i share the swizzle of R0
   // (swz depends on bits 2-3 of the row only), so fragment i is 2048 i bytes
-  // further; scale bytes sit at row * 2 + block.
+  // further; the scales of the lane's four rows are one 4-byte word.
   const int offWa = tile_off(wn * 128 + li, lg), offWb = tile_off(wn * 128 + li, 2 + lg);
   const int offXa = kOpBytes + tile_off(wm * 128 + li, lg), offXb = kOpBytes + tile_off(wm * 128 + li, 2 + lg);
-  const int offSw = 2 * kOpBytes + (wn * 128 + li) * 2 + lg;
-  const int offSx = 2 * kOpBytes + 512 + (wm * 128 + li) * 2 + lg;
+  const int offSw = 2 * kOpBytes + wn * kTileScaleBytes + scale_off(li, lg);
+  const int offSx = 2 * kOpBytes + 2 * kTileScaleBytes + wm * kTileScaleBytes + scale_off(li, lg);
   auto rd16 = [](const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); };
   // Copy j (0..8) of this thread's share of step ks into stage st.
   auto dma_one = [&](int j, int ks, uint8_t* st) {
@@ -130,8 +140,12 @@ __device__ __forceinline__ void mainloop(uint8_t* st0, uint8_t* st1, uint8_t* st
       default: g2l_4(ssrc + (size_t)ks * kTileScaleBytes, st + 2 * kOpBytes + wave * 256); break;
     }
   };
-  // Part j (0..15) of the fragment reads of a stage.
+  // Part j (0..15) of the fragment reads of a stage (parts 8..15 are empty).
+  // The scale words go first: read after the fragments (parts 8, 9) they
+  // cost the loop about 12 % (measured).
   auto read_part = [&](int j, const uint8_t* st, Frags& f) {
+    if (j == 0) f.sa = *reinterpret_cast<const int*>(st + offSw);
+    if (j == 1) f.sb = *reinterpret_cast<const int*>(st + offSx);
     if (j < 8) {
       const int i = j >> 1;
       if ((j & 1) == 0) {
@@ -141,10 +155,6 @@ __device__ __forceinline__ void mainloop(uint8_t* st0, uint8_t* st1, uint8_t* st
         const uint4 b0 = rd16(st + offXa + 2048 * i), b1 = rd16(st + offXb + 2048 * i);
         f.b[i] = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
       }
-    } else if (j < 12) {
-      f.sa[j - 8] = st[offSw + 64 * (j - 8)];
-    } else {
-      f.sb[j - 12] = st[offSx + 64 * (j - 12)];
     }
   };
 
@@ -160,16 +170,18 @@ __device__ __forceinline__ void mainloop(uint8_t* st0, uint8_t* st1, uint8_t* st
     wait_vmcnt<decltype(later)::value * kLoadsPerStage>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    static_for<0, 16>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      // op_sel picks byte (row block) j >> 2 of the weight scales and j & 3
+      // of the activation scales.
       acc[j >> 2][j & 3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          cur.a[j >> 2], cur.b[j & 3], acc[j >> 2][j & 3], 0, 0, 0, cur.sa[j >> 2], 0, cur.sb[j & 3]);
+          cur.a[j >> 2], cur.b[j & 3], acc[j >> 2][j & 3], 0, 0, j >> 2, cur.sa, j & 3, cur.sb);
       if constexpr (decltype(do_issue)::value) {
         if (j < kLoadsPerStage) dma_one(j, s + 4, st_free);
       }
       if constexpr (decltype(do_next)::value) read_part(j, st_next, nxt);
       __builtin_amdgcn_sched_barrier(0);
-    }
+    });
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   };
   using T = std::true_type;
