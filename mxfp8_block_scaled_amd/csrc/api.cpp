@@ -52,11 +52,17 @@ int check_output(const void* y, int64_t N, int64_t ldy, const void* bias) {
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Workspace of the tile path: packed activations (M padded to 128 rows) then
-// their packed scales, each 256-byte aligned.
-size_t tile_ws_bytes(int64_t M, int64_t K) {
+// Workspace of the tile path: packed activations (M padded to 128 rows), their
+// packed scales, then (split-K shapes) the fp32 partial outputs, each
+// 256-byte aligned.
+size_t tile_ws_act_bytes(int64_t M, int64_t K) {
   const size_t mp = (size_t)((M + 127) / 128 * 128);
   return round_up(mp * (size_t)K, 256) + round_up(mp * (size_t)(K / 32), 256);
+}
+size_t tile_ws_bytes(int64_t M, int64_t N, int64_t K) {
+  const int splits = mxfp8::gemm_tile_splits(M, N, K);
+  const size_t part = splits > 1 ? (size_t)splits * (size_t)M * (size_t)((N + 3) / 4 * 4) * 4 : 0;
+  return tile_ws_act_bytes(M, K) + round_up(part, 256);
 }
 
 // Test hook state of mxfp8_moe_debug_capture.
@@ -170,7 +176,7 @@ int mxfp8_unpack_weight(const void* w_packed, const void* s_packed, int64_t N, i
 int mxfp8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes) {
   if (!bytes) return MXFP8_E_NULLPTR;
   if (M < 0 || N < 1 || K < 256 || K % 256 != 0) return MXFP8_E_SHAPE;
-  *bytes = (M == 0 || use_skinny(M, K)) ? 256 : tile_ws_bytes(M, K);
+  *bytes = (M == 0 || use_skinny(M, K)) ? 256 : tile_ws_bytes(M, N, K);
   return MXFP8_OK;
 }
 
@@ -187,7 +193,7 @@ int mxfp8_linear(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, const vo
   if (!aligned(x_bf16, 16)) return MXFP8_E_ALIGN;
   const bool skinny = use_skinny(M, K);
   if (!skinny && (n_pad(M) * (K / 8) + 255) / 256 > INT32_MAX) return MXFP8_E_SHAPE;
-  const size_t need = skinny ? 256 : tile_ws_bytes(M, K);
+  const size_t need = skinny ? 256 : tile_ws_bytes(M, N, K);
   if (!workspace || workspace_bytes < need) return MXFP8_E_WORKSPACE;
   if (!aligned(workspace, 256)) return MXFP8_E_ALIGN;
   if (int st = check_device()) return st;
@@ -196,8 +202,10 @@ int mxfp8_linear(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, const vo
     return mxfp8::launch_gemm_skinny(x_bf16, ldx, M, K, w_packed, s_packed, N, bias_bf16, y_bf16, ldy, s);
   uint8_t* q = (uint8_t*)workspace;
   uint8_t* sc = q + round_up((size_t)n_pad(M) * (size_t)K, 256);
+  uint8_t* part = q + tile_ws_act_bytes(M, K);
   if (int st = mxfp8::launch_quantize_act_packed(x_bf16, M, K, ldx, q, sc, s)) return st;
-  return mxfp8::launch_gemm_tile(q, sc, M, K, w_packed, s_packed, N, bias_bf16, y_bf16, ldy, s);
+  return mxfp8::launch_gemm_tile(q, sc, M, K, w_packed, s_packed, N, bias_bf16, y_bf16, ldy, s,
+                                 mxfp8::gemm_tile_splits(M, N, K), part);
 }
 
 int mxfp8_packed_act_bytes(int64_t M, int64_t K, size_t* q_bytes, size_t* s_bytes) {

@@ -30,15 +30,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(
     const uint8_t* __restrict__ qp, const uint8_t* __restrict__ qsp, int M, int K,
     const uint8_t* __restrict__ wp, const uint8_t* __restrict__ wsp, int N, int GN, int GM,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int64_t ldy, int tiles_m, int tiles_n,
-    int vec_store) {
+    int vec_store, int splits, float* __restrict__ part, int64_t ldp) {
   __shared__ __attribute__((aligned(16))) uint8_t st0[kStage];
   __shared__ __attribute__((aligned(16))) uint8_t st1[kStage];
   __shared__ __attribute__((aligned(16))) uint8_t st2[kStage];
   __shared__ __attribute__((aligned(16))) uint8_t st3[kStage];
 
+  // Split-K: workgroup b takes K slice b % splits of tile b / splits.
+  const int split = (int)blockIdx.x % splits;
   // Tile order: XCD-contiguous, then groups of kGroupM tiles along M.
   const int total = tiles_m * tiles_n;
-  const int logical = tile::xcd_remap((int)blockIdx.x, total);
+  const int logical = tile::xcd_remap((int)blockIdx.x / splits, total);
   const int per_group = kGroupM * tiles_n;
   const int group = logical / per_group;
   const int first_m = group * kGroupM;
@@ -53,25 +55,74 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(
   const int wa = min(2 * tn, GN - 1), wb = min(2 * tn + 1, GN - 1);
   const int xa = min(2 * tm, GM - 1), xb = min(2 * tm + 1, GM - 1);
 
-  v16f acc[4][4];
-  tile::mainloop(st0, st1, st2, st3, wp + wa * op_stride, wp + wb * op_stride, qp + xa * op_stride,
-                 qp + xb * op_stride, wsp + wa * sc_stride, wsp + wb * sc_stride, qsp + xa * sc_stride,
-                 qsp + xb * sc_stride, KS, acc);
+  const int ksl = KS / splits;                           // steps of this slice (multiple of 4)
+  const size_t k0 = (size_t)split * ksl * kTileBytes, s0 = (size_t)split * ksl * kTileScaleBytes;
 
-  tile::store_bf16(st0, st1, st2, st3, acc, y, ldy, tm * 256, M, tn * 256, N, bias, vec_store);
+  v16f acc[4][4];
+  tile::mainloop(st0, st1, st2, st3, wp + wa * op_stride + k0, wp + wb * op_stride + k0, qp + xa * op_stride + k0,
+                 qp + xb * op_stride + k0, wsp + wa * sc_stride + s0, wsp + wb * sc_stride + s0,
+                 qsp + xa * sc_stride + s0, qsp + xb * sc_stride + s0, ksl, acc);
+
+  if (splits == 1) {
+    tile::store_bf16(st0, st1, st2, st3, acc, y, ldy, tm * 256, M, tn * 256, N, bias, vec_store);
+  } else {
+    // fp32 partial of this slice: part[split][m][n], row stride ldp (% 4 == 0).
+    tile::store_bf16<false, float>(st0, st1, st2, st3, acc, part + (size_t)split * M * ldp, ldp, tm * 256, M,
+                                   tn * 256, N, nullptr, 1);
+  }
+}
+
+// y[m][n] = bf16( sum_s part[s][m][n] + bias[n] ), slices added in order.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int splits, int M, int N,
+                                                            int64_t ldp, const uint16_t* __restrict__ bias,
+                                                            uint16_t* __restrict__ y, int64_t ldy) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;   // one thread per 4 columns
+  const int64_t per_row = (N + 3) / 4;
+  if (t >= (int64_t)M * per_row) return;
+  const int64_t m = t / per_row;
+  const int n = (int)(t - m * per_row) * 4;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int sp = 0; sp < splits; ++sp) {
+    const float4 v = *reinterpret_cast<const float4*>(part + ((size_t)sp * M + m) * ldp + n);
+    a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+  }
+  float b[4] = {0.f, 0.f, 0.f, 0.f};
+  if (bias != nullptr)
+    for (int e = 0; e < 4; ++e) b[e] = (n + e < N) ? __uint_as_float((uint32_t)bias[n + e] << 16) : 0.f;
+  const uint32_t lo = pack_bf16x2(a.x + b[0], a.y + b[1]), hi = pack_bf16x2(a.z + b[2], a.w + b[3]);
+  uint16_t* d = y + m * ldy + n;
+  d[0] = (uint16_t)lo;
+  if (n + 1 < N) d[1] = (uint16_t)(lo >> 16);
+  if (n + 2 < N) d[2] = (uint16_t)hi;
+  if (n + 3 < N) d[3] = (uint16_t)(hi >> 16);
+}
+
+int gemm_tile_splits(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t KS = K / kStepK;
+  int s = 1;
+  while (s < kMaxSplitK && tiles * s * 2 <= 256 && KS % (8 * s) == 0) s *= 2;
+  return tiles < 128 ? s : 1;
 }
 
 int launch_gemm_tile(const void* qp, const void* sp, int64_t M, int64_t K, const void* wp, const void* wsp,
-                     int64_t N, const void* bias, void* y, int64_t ldy, hipStream_t stream) {
+                     int64_t N, const void* bias, void* y, int64_t ldy, hipStream_t stream, int splits,
+                     void* part) {
   const int64_t GN = (N + kGroupRows - 1) / kGroupRows;
   const int64_t GM = (M + kGroupRows - 1) / kGroupRows;
   const int tiles_n = (int)((GN + 1) / 2);
   const int tiles_m = (int)((GM + 1) / 2);
   const int vec = (ldy % 4 == 0) && (((uintptr_t)y & 7) == 0);
-  hipLaunchKernelGGL(gemm_tile_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(kThreads), 0, stream,
+  const int64_t ldp = (N + 3) / 4 * 4;
+  hipLaunchKernelGGL(gemm_tile_kernel, dim3((unsigned)(tiles_m * tiles_n * splits)), dim3(kThreads), 0, stream,
                      (const uint8_t*)qp, (const uint8_t*)sp, (int)M, (int)K, (const uint8_t*)wp,
                      (const uint8_t*)wsp, (int)N, (int)GN, (int)GM, (const uint16_t*)bias, (uint16_t*)y, ldy,
-                     tiles_m, tiles_n, vec);
+                     tiles_m, tiles_n, vec, splits, (float*)part, ldp);
+  if (splits > 1) {
+    const int64_t threads = M * ((N + 3) / 4);
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+                       (const float*)part, splits, (int)M, (int)N, ldp, (const uint16_t*)bias, (uint16_t*)y, ldy);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 

@@ -28,9 +28,14 @@ int launch_unpack_weight(const void* wp, const void* sp, int64_t N, int64_t K, v
                          hipStream_t stream);
 
 // Large-tile GEMM on packed activations (qp, sp: M rows) and the packed
-// weight (wp, wsp: N rows).
+// weight (wp, wsp: N rows).  splits > 1 splits K across that many
+// workgroups per tile: fp32 partials go to part (splits * M * round_up(N, 4)
+// floats), then one reduce kernel adds them with the bias into y.
+constexpr int kMaxSplitK = 8;
+int gemm_tile_splits(int64_t M, int64_t N, int64_t K);
 int launch_gemm_tile(const void* qp, const void* sp, int64_t M, int64_t K, const void* wp, const void* wsp,
-                     int64_t N, const void* bias, void* y, int64_t ldy, hipStream_t stream);
+                     int64_t N, const void* bias, void* y, int64_t ldy, hipStream_t stream, int splits = 1,
+                     void* part = nullptr);
 
 // Skinny GEMM with the activation quantization fused in (M <= kSkinnyMaxM,
 // K <= kSkinnyMaxK).
