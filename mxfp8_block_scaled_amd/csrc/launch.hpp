@@ -61,12 +61,11 @@ struct MoeWorkspace {
   int* tile_g0;      // [mt_max] its first 128-row group
   int* tile_ng;      // [mt_max] its groups (1 or 2)
   int* sorted_row;   // [p_max] row t*k + j at each sorted position, -1 = pad
-  int* inv;          // [T*k] sorted position of each row
   uint8_t* a1q;      // packed MXFP8 token rows, expert-sorted [p_max, H]
   uint8_t* a1s;
   uint8_t* a2q;      // packed MXFP8 gated activations [p_max, I]
   uint8_t* a2s;
-  float* ys;         // weighted expert outputs, fp32 [p_max, H]
+  float* ys;         // weighted expert outputs, fp32 [T*k, H], row t*k + j
   int64_t p_max;     // sorted positions (multiple of 128, one spare group)
   int64_t mt_max;    // upper bound of M-tiles
 };

@@ -30,10 +30,10 @@
 //              epilogue applies SiLU-gating, rounds to bf16, MX-quantizes
 //              along I and writes the packed operand of gemm2.
 //  6. gemm2    per (M-tile, 256-row slice of W2[e]): the tile loop, then the
-//              routing weight of each row; rows written in fp32 to the
-//              expert-sorted output.
-//  7. combine  y_t = bf16( sum_j ys[pos(t, j)] ), fp32 sum in slot order, one
-//              rounding.
+//              routing weight of each row; each real row written in fp32 to
+//              its slot row t*k + j (pad rows are not stored).
+//  7. combine  y_t = bf16( sum_j ys[t*k + j] ), fp32 sum in slot order, one
+//              rounding; a token's k slot rows are contiguous.
 #include <cfloat>
 #include <climits>
 
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(1024) void moe_plan_kernel(const int* __restrict__ 
 __global__ __launch_bounds__(256) void moe_scatter_kernel(const int* __restrict__ ids, int R, int topk, int E,
                                                           const int* __restrict__ blk_off,
                                                           const int* __restrict__ seg_off,
-                                                          int* __restrict__ sorted_row, int* __restrict__ inv) {
+                                                          int* __restrict__ sorted_row) {
   __shared__ int wcnt[4][kMoeMaxExperts];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int i = tid; i < 4 * kMoeMaxExperts; i += 256) (&wcnt[0][0])[i] = 0;
@@ -250,7 +250,6 @@ __global__ __launch_bounds__(256) void moe_scatter_kernel(const int* __restrict_
     int pos = seg_off[e] + blk_off[(int64_t)blockIdx.x * E + e] + local;
     for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
     sorted_row[pos] = r;
-    inv[r] = pos;
   }
 }
 
@@ -356,8 +355,13 @@ __global__ __launch_bounds__(tile::kThreads, 1) void moe_gemm1_kernel(
         float o[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
+          // silu(g) = g / (1 + e^-g), with e^-g = 2^(-g log2 e) from the
+          // hardware exp2 and the hardware reciprocal (each within about an
+          // ulp of fp32; far below the bf16 rounding that follows).  For
+          // g < -88 the exponential overflows to +inf and silu(g) -> 0.
           const float gt = acc[a][b][2 * p + h], up = acc[a + 2][b][2 * p + h];
-          o[h] = gt / (1.0f + expf(-gt)) * up;
+          const float ex = __builtin_amdgcn_exp2f(-gt * 1.44269504088896341f);
+          o[h] = gt * __builtin_amdgcn_rcpf(1.0f + ex) * up;
         }
         w[p] = pack_bf16x2(o[0], o[1]);
       }
@@ -407,6 +411,7 @@ __global__ __launch_bounds__(tile::kThreads, 1) void moe_gemm2_kernel(
     const int* __restrict__ tile_g0, const int* __restrict__ tile_ng, const int* __restrict__ sorted_row,
     const float* __restrict__ wts, int H, int I, float* __restrict__ ys) {
   __shared__ float row_w[256];
+  __shared__ int row_dst[256];
   __shared__ __attribute__((aligned(16))) uint8_t st0[tile::kStage];
   __shared__ __attribute__((aligned(16))) uint8_t st1[tile::kStage];
   __shared__ __attribute__((aligned(16))) uint8_t st2[tile::kStage];
@@ -428,24 +433,26 @@ __global__ __launch_bounds__(tile::kThreads, 1) void moe_gemm2_kernel(
                  se + (2 * nt + 1) * sc_stride, a2s + (size_t)g0 * sc_stride, a2s + (size_t)(g0 + 1) * sc_stride,
                  KS, acc);
 
-  // Routing weight of each tile row (zero for pad rows), applied in the
-  // epilogue before the one rounding to bf16.
+  // Routing weight and slot (t * k + j) of each tile row; pad rows and the
+  // rows past the tile's groups are not stored.
   for (int m = threadIdx.x; m < 256; m += tile::kThreads) {
     float wv = 0.0f;
+    int src = -1;
     if (m < ng * kGroupRows) {
-      const int src = sorted_row[g0 * kGroupRows + m];
+      src = sorted_row[g0 * kGroupRows + m];
       if (src >= 0) wv = wts[src];
     }
     row_w[m] = wv;
+    row_dst[m] = src;
   }
   __syncthreads();
-  tile::store_bf16<true, float>(st0, st1, st2, st3, acc, ys, H, g0 * kGroupRows, (g0 + ng) * kGroupRows, nt * 256,
-                                H, nullptr, 1, row_w);
+  tile::store_bf16<true, float, true>(st0, st1, st2, st3, acc, ys, H, 0, 0, nt * 256, H, nullptr, 1, row_w,
+                                      row_dst);
 }
 
 // ---------------------------------------------------------------- 7. combine
-__global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ ys, const int* __restrict__ inv,
-                                                          int T, int H, int topk, uint16_t* __restrict__ y) {
+__global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ ys, int T, int H, int topk,
+                                                          uint16_t* __restrict__ y) {
   const int64_t t8 = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int per_row = H / 8;
   if (t8 >= (int64_t)T * per_row) return;
@@ -453,7 +460,7 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
   const int c = (int)(t8 - t * per_row);
   float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = s0;
   for (int j = 0; j < topk; ++j) {
-    const float4* p = reinterpret_cast<const float4*>(ys + (int64_t)inv[t * topk + j] * H + c * 8);
+    const float4* p = reinterpret_cast<const float4*>(ys + (t * topk + j) * H + c * 8);
     const float4 a = p[0], b = p[1];
     s0.x += a.x; s0.y += a.y; s0.z += a.z; s0.w += a.w;
     s1.x += b.x; s1.y += b.y; s1.z += b.z; s1.w += b.w;
@@ -476,7 +483,7 @@ int launch_moe(const MoeArgs& a, hipStream_t stream) {
                      a.ws.seg_off, a.ws.tile_e, a.ws.tile_g0, a.ws.tile_ng, a.ws.meta, a.ws.sorted_row,
                      (int)a.ws.p_max);
   hipLaunchKernelGGL(moe_scatter_kernel, dim3(nblk), dim3(256), 0, stream, a.ws.ids, R, (int)a.topk, (int)a.E,
-                     a.ws.blk_off, a.ws.seg_off, a.ws.sorted_row, a.ws.inv);
+                     a.ws.blk_off, a.ws.seg_off, a.ws.sorted_row);
   const int KS1 = (int)(a.H / kStepK);
   hipLaunchKernelGGL(moe_gather_quant_kernel<4>, dim3((unsigned)(a.ws.p_max * 8 / 256)), dim3(256), 0, stream,
                      (const uint16_t*)a.x, (int)a.H, (int)a.topk, a.ws.sorted_row, a.ws.meta, KS1, a.ws.a1q,
@@ -491,7 +498,7 @@ int launch_moe(const MoeArgs& a, hipStream_t stream) {
                      a.ws.tile_g0, a.ws.tile_ng, a.ws.sorted_row, a.ws.wts, (int)a.H, (int)a.I, a.ws.ys);
   const int64_t cb_total = a.T * (a.H / 8);
   hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((cb_total + 255) / 256)), dim3(256), 0, stream, a.ws.ys,
-                     a.ws.inv, (int)a.T, (int)a.H, (int)a.topk, (uint16_t*)a.y);
+                     (int)a.T, (int)a.H, (int)a.topk, (uint16_t*)a.y);
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 

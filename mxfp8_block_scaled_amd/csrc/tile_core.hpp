@@ -236,13 +236,16 @@ constexpr int kEpiPitch = 132;                        // floats per staged row (
 // over in every wave).  kRowScale: tile row m is first multiplied by
 // row_scale[m] (an LDS array of 256 floats), i.e. bf16(acc * s[m] + bias[n]).
 // OutT = float writes the fp32 values instead (no rounding; 16-byte stores,
-// requires y 16-byte aligned and ldy % 4 == 0 when vec_store).
-template <bool kRowScale = false, typename OutT = uint16_t>
+// requires y 16-byte aligned and ldy % 4 == 0 when vec_store).  kRowMap:
+// tile row m goes to output row row_map[m] (an LDS array of 256 ints; a
+// negative entry is not stored) instead of row0 + m, row_end is not used,
+// and every column of the tile must be < N with vec_store set.
+template <bool kRowScale = false, typename OutT = uint16_t, bool kRowMap = false>
 __device__ __forceinline__ void store_bf16(uint8_t* st0, uint8_t* st1, uint8_t* st2, uint8_t* st3,
                                            const v16f (&acc)[4][4], OutT* __restrict__ y, int64_t ldy,
                                            int row0, int row_end, int col0, int N,
                                            const uint16_t* __restrict__ bias, int vec_store,
-                                           const float* row_scale = nullptr) {
+                                           const float* row_scale = nullptr, const int* row_map = nullptr) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wave >> 1, wm = wave & 1;
@@ -281,7 +284,27 @@ __device__ __forceinline__ void store_bf16(uint8_t* st0, uint8_t* st1, uint8_t* 
     const int rows_left = row_end - m_first;          // this lane's rows are m_first + 2 it
     const float* src = stage + rsub * kEpiPitch + 4 * n4;
     OutT* dst = y + (size_t)max(m_first, 0) * ldy + nl;
-    if (vec_store && full_n && rows_left >= 63) {
+    if constexpr (kRowMap) {
+#pragma unroll
+      for (int it = 0; it < 32; ++it) {
+        float4 f = *reinterpret_cast<const float4*>(src + 2 * it * kEpiPitch);
+        const int tm = m_first - row0 + 2 * it;
+        if constexpr (kRowScale) {
+          const float sc = row_scale[tm];
+          f.x *= sc; f.y *= sc; f.z *= sc; f.w *= sc;
+        }
+        const int dr = row_map[tm];
+        if (dr >= 0) {
+          OutT* d = y + (size_t)dr * ldy + nl;
+          if constexpr (sizeof(OutT) == 4) {
+            *reinterpret_cast<float4*>(d) = make_float4(f.x + bv[0], f.y + bv[1], f.z + bv[2], f.w + bv[3]);
+          } else {
+            *reinterpret_cast<uint2*>(d) =
+                make_uint2(pack_bf16x2(f.x + bv[0], f.y + bv[1]), pack_bf16x2(f.z + bv[2], f.w + bv[3]));
+          }
+        }
+      }
+    } else if (vec_store && full_n && rows_left >= 63) {
 #pragma unroll
       for (int it = 0; it < 32; ++it) {
         float4 f = *reinterpret_cast<const float4*>(src + 2 * it * kEpiPitch);
