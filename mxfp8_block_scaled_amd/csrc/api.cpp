@@ -99,7 +99,8 @@ size_t moe_layout(int64_t T, int64_t H, int64_t E, int64_t topk, int64_t I, uint
   v.tile_g0 = (int*)take(mt_max * 4);
   v.tile_ng = (int*)take(mt_max * 4);
   v.sorted_row = (int*)take(p_max * 4);
-  v.a1q = take(p_max * H);
+  v.xq = take((T + 1) * H);
+  v.xs = take((T + 1) * (H / 32));
   v.a1s = take(p_max * (H / 32));
   v.a2q = take(p_max * I);
   v.a2s = take(p_max * (I / 32));

@@ -61,8 +61,9 @@ struct MoeWorkspace {
   int* tile_g0;      // [mt_max] its first 128-row group
   int* tile_ng;      // [mt_max] its groups (1 or 2)
   int* sorted_row;   // [p_max] row t*k + j at each sorted position, -1 = pad
-  uint8_t* a1q;      // packed MXFP8 token rows, expert-sorted [p_max, H]
-  uint8_t* a1s;
+  uint8_t* xq;       // MXFP8 token rows, row-major [T + 1, H] (row T all zero)
+  uint8_t* xs;       // their scales [T + 1, H / 32]
+  uint8_t* a1s;      // packed scales of the expert-sorted token rows [p_max, H / 32]
   uint8_t* a2q;      // packed MXFP8 gated activations [p_max, I]
   uint8_t* a2s;
   float* ys;         // weighted expert outputs, fp32 [T*k, H], row t*k + j

@@ -22,9 +22,11 @@
 //              the M-tile list (256 rows = two groups of one expert).
 //  3. scatter  row (t, j) -> its position in its expert's segment, in
 //              increasing t*k + j order (wave ballots + per-wave counts).
-//  4. gather   quantize x rows straight into the packed, expert-sorted GEMM
-//              operand (pad rows zero).
-//  5. gemm1    per (M-tile, 256-row slice of W13[e]) the shared tile loop;
+//  4. quant    x rows MX-quantized once, row-major, plus an all-zero row;
+//              the expert-sorted scale tiles of the GEMM operand gathered
+//              from them (pad rows: scale 0).
+//  5. gemm1    per (M-tile, 256-row slice of W13[e]) the shared tile loop,
+//              its activation rows copied from the quantized x by row index;
 //              W13 is packed with gate and up rows interleaved so that each
 //              lane holds gate and up of the same intermediate index; the
 //              epilogue applies SiLU-gating, rounds to bf16, MX-quantizes
@@ -254,51 +256,37 @@ __global__ __launch_bounds__(256) void moe_scatter_kernel(const int* __restrict_
 }
 
 // ---------------------------------------------------------------- 4. gather
-// The packed act-quant of quant.hip with a row indirection: position pos of
-// the expert-sorted operand holds token sorted_row[pos] / k (or zeros).  A
-// thread owns one (row, 8-element chunk) pair and walks every 64-K step of
-// the row, kBatch steps' loads in flight at a time; a wave covers 8 rows x 8
-// chunks, i.e. 512 contiguous bytes of each packed tile it writes.
-template <int kBatch>
-__global__ __launch_bounds__(256) void moe_gather_quant_kernel(const uint16_t* __restrict__ x, int H, int topk,
-                                                               const int* __restrict__ sorted_row,
-                                                               const int* __restrict__ meta, int KS,
-                                                               uint8_t* __restrict__ qp, uint8_t* __restrict__ sp) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;   // over p_max * 8
-  const int64_t pos = t >> 3;
-  const int64_t g = pos / kGroupRows;
-  if (g >= meta[1]) return;                 // whole groups (16 waves) leave together
-  const int r = (int)(pos % kGroupRows);
-  const int c8 = (int)(t & 7);
-  const int src = sorted_row[pos];
-  const uint16_t* xrow = x + (int64_t)(src >= 0 ? src / topk : 0) * H + c8 * 8;
-  uint8_t* qg = qp + g * KS * kTileBytes + tile_off(r, c8 >> 1) + (c8 & 1) * 8;
-  uint8_t* sg = sp + g * KS * kTileScaleBytes + scale_off(r, c8 >> 2);
-  for (int ks0 = 0; ks0 < KS; ks0 += kBatch) {
-    uint4 v[kBatch];
+// The token rows are MX-quantized once, row-major (quant.hip's row-major
+// kernel, into xq / xs with one extra all-zero row T for pad positions); the
+// gate/up GEMM then copies its activation rows straight from xq by row index.
+// What remains is the scale tile of the expert-sorted operand, in the packed
+// lane-major layout: one thread per 4-byte word w of the 256-byte block of
+// (group g, step ks), which holds MX block w & 1 of the step for the rows
+// (w >> 1) + 32 i, i = 0..3 (byte i).  Pad rows get scale byte 0.  Block 0
+// also clears row T of xq.
+__global__ __launch_bounds__(256) void moe_gather_scales_kernel(const uint8_t* __restrict__ xs, int H, int topk,
+                                                                const int* __restrict__ sorted_row,
+                                                                const int* __restrict__ meta, int KS,
+                                                                uint8_t* __restrict__ a1s,
+                                                                uint8_t* __restrict__ zero_row) {
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x * 16; i < H; i += 256 * 16) *reinterpret_cast<uint4*>(zero_row + i) = make_uint4(0, 0, 0, 0);
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;   // over (p_max / 128) * KS * 64
+  const int64_t blk = t >> 6;                                    // g * KS + ks
+  const int64_t g = blk / KS;
+  if (g >= meta[1]) return;
+  const int ks = (int)(blk - g * KS);
+  const int w = (int)(t & 63);
+  const int b = w & 1, r0 = w >> 1;
+  const int nb = H / 32;
+  uint32_t word = 0;
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u)
-      v[u] = (src >= 0 && ks0 + u < KS) ? *reinterpret_cast<const uint4*>(xrow + (int64_t)(ks0 + u) * kStepK)
-                                        : make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-      u16x2 mp = {0, 0};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mp = absmax_pk(mp, w[i]);
-      uint32_t m = max((uint32_t)mp[0], (uint32_t)mp[1]);
-      m = max(m, (uint32_t)__shfl_xor((int)m, 1));
-      m = max(m, (uint32_t)__shfl_xor((int)m, 2));
-      const uint32_t sb = (uint32_t)max((int)(m >> 7) - 8, 0);
-      uint32_t qd[2];
-      cvt8s(w, mx_scale_value(sb), qd);
-      const int ks = ks0 + u;
-      if (ks < KS) {
-        *reinterpret_cast<uint2*>(qg + (int64_t)ks * kTileBytes) = make_uint2(qd[0], qd[1]);
-        if ((c8 & 3) == 0) sg[(int64_t)ks * kTileScaleBytes] = (uint8_t)sb;
-      }
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int src = sorted_row[g * kGroupRows + r0 + 32 * i];
+    const uint32_t sb = src >= 0 ? xs[(int64_t)(src / topk) * nb + 2 * ks + b] : 0u;
+    word |= sb << (8 * i);
   }
+  *reinterpret_cast<uint32_t*>(a1s + blk * kTileScaleBytes + 4 * w) = word;
 }
 
 // ---------------------------------------------------------------- 5. gemm1
@@ -308,10 +296,10 @@ __global__ __launch_bounds__(256) void moe_gather_quant_kernel(const uint16_t* _
 // layout acc[a][b][r] (a < 2) is the gate and acc[a + 2][b][r] the up value of
 // intermediate index i = nt*128 + wn*64 + 32a + 8(r/4) + 4lg + r%4.
 __global__ __launch_bounds__(tile::kThreads, 1) void moe_gemm1_kernel(
-    const uint8_t* __restrict__ a1q, const uint8_t* __restrict__ a1s, const uint8_t* __restrict__ w13p,
-    const uint8_t* __restrict__ s13p, const int* __restrict__ meta, const int* __restrict__ tile_e,
-    const int* __restrict__ tile_g0, const int* __restrict__ tile_ng, const int* __restrict__ sorted_row, int H,
-    int I, uint8_t* __restrict__ a2q, uint8_t* __restrict__ a2s, uint16_t* __restrict__ dbg_act,
+    const uint8_t* __restrict__ xq, int T, int topk, const uint8_t* __restrict__ a1s,
+    const uint8_t* __restrict__ w13p, const uint8_t* __restrict__ s13p, const int* __restrict__ meta,
+    const int* __restrict__ tile_e, const int* __restrict__ tile_g0, const int* __restrict__ tile_ng,
+    const int* __restrict__ sorted_row, int H, int I, uint8_t* __restrict__ a2q, uint8_t* __restrict__ a2s, uint16_t* __restrict__ dbg_act,
     uint8_t* __restrict__ dbg_q, uint8_t* __restrict__ dbg_s) {
   __shared__ __attribute__((aligned(16))) uint8_t st0[tile::kStage];
   __shared__ __attribute__((aligned(16))) uint8_t st1[tile::kStage];
@@ -328,11 +316,27 @@ __global__ __launch_bounds__(tile::kThreads, 1) void moe_gemm1_kernel(
   const size_t op_stride = (size_t)KS * kTileBytes, sc_stride = (size_t)KS * kTileScaleBytes;
   const uint8_t* we = w13p + (size_t)e * (size_t)(2 * I) * (size_t)H;
   const uint8_t* se = s13p + (size_t)e * (size_t)(2 * I) * (size_t)(H / 32);
+  // Activation rows m = tid / 4 + 64 i of the tile, copied from their token's
+  // row of xq (row T, all zero, for pad rows and rows past the tile's groups).
+  tile::GatherX gx;
+  {
+    const int tid = threadIdx.x;
+    const int chunk = (tid & 3) ^ ((tid >> 4) & 3);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = (tid >> 2) + 64 * i;
+      int tok = T;
+      if (m < ng * kGroupRows) {
+        const int src = sorted_row[g0 * kGroupRows + m];
+        if (src >= 0) tok = src / topk;
+      }
+      gx.p[i] = xq + (size_t)tok * H + chunk * 16;
+    }
+  }
   v16f acc[4][4];
-  tile::mainloop(st0, st1, st2, st3, we + (2 * nt) * op_stride, we + (2 * nt + 1) * op_stride,
-                 a1q + (size_t)g0 * op_stride, a1q + (size_t)(g0 + 1) * op_stride, se + (2 * nt) * sc_stride,
-                 se + (2 * nt + 1) * sc_stride, a1s + (size_t)g0 * sc_stride, a1s + (size_t)(g0 + 1) * sc_stride,
-                 KS, acc);
+  tile::mainloop<true>(st0, st1, st2, st3, we + (2 * nt) * op_stride, we + (2 * nt + 1) * op_stride, xq, xq,
+                       se + (2 * nt) * sc_stride, se + (2 * nt + 1) * sc_stride, a1s + (size_t)g0 * sc_stride,
+                       a1s + (size_t)(g0 + 1) * sc_stride, KS, acc, gx);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -485,12 +489,14 @@ int launch_moe(const MoeArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(moe_scatter_kernel, dim3(nblk), dim3(256), 0, stream, a.ws.ids, R, (int)a.topk, (int)a.E,
                      a.ws.blk_off, a.ws.seg_off, a.ws.sorted_row);
   const int KS1 = (int)(a.H / kStepK);
-  hipLaunchKernelGGL(moe_gather_quant_kernel<4>, dim3((unsigned)(a.ws.p_max * 8 / 256)), dim3(256), 0, stream,
-                     (const uint16_t*)a.x, (int)a.H, (int)a.topk, a.ws.sorted_row, a.ws.meta, KS1, a.ws.a1q,
-                     a.ws.a1s);
+  const int qs = launch_quantize_act(a.x, a.T, a.H, a.H, a.ws.xq, a.H, a.ws.xs, a.H / 32, stream);
+  if (qs != 0) return qs;
+  hipLaunchKernelGGL(moe_gather_scales_kernel, dim3((unsigned)(a.ws.p_max / kGroupRows * KS1 / 4)), dim3(256), 0,
+                     stream, a.ws.xs, (int)a.H, (int)a.topk, a.ws.sorted_row, a.ws.meta, KS1, a.ws.a1s,
+                     a.ws.xq + a.T * a.H);
   const int nt1 = (int)(2 * a.I / 256), nt2 = (int)(a.H / 256);
   hipLaunchKernelGGL(moe_gemm1_kernel, dim3((unsigned)(a.ws.mt_max * nt1)), dim3(tile::kThreads), 0, stream,
-                     a.ws.a1q, a.ws.a1s, (const uint8_t*)a.w13p, (const uint8_t*)a.s13p, a.ws.meta, a.ws.tile_e,
+                     a.ws.xq, (int)a.T, (int)a.topk, a.ws.a1s, (const uint8_t*)a.w13p, (const uint8_t*)a.s13p, a.ws.meta, a.ws.tile_e,
                      a.ws.tile_g0, a.ws.tile_ng, a.ws.sorted_row, (int)a.H, (int)a.I, a.ws.a2q, a.ws.a2s,
                      (uint16_t*)a.dbg_act, (uint8_t*)a.dbg_q, (uint8_t*)a.dbg_s);
   hipLaunchKernelGGL(moe_gemm2_kernel, dim3((unsigned)(a.ws.mt_max * nt2)), dim3(tile::kThreads), 0, stream,

@@ -80,15 +80,28 @@ __device__ inline void wait_vmcnt() {
   else asm volatile("s_waitcnt vmcnt(27)" ::: "memory");
 }
 
+// Row-gathered activation operand: instead of a packed group, the 16 bytes
+// thread tid copies for tile row m and step ks come from p[i] + ks * 64,
+// where i = 0..3 stands for m = tid / 4 + 64 i and p[i] points at that row's
+// source (a row-major E4M3 matrix with K bytes per row) plus the logical
+// 16-byte chunk that lands in LDS slot tid % 4 of the packed layout, i.e.
+// chunk (tid % 4) ^ ((tid / 16) % 4).
+struct GatherX {
+  const uint8_t* p[4];
+};
+
 // acc = the tile's product over all KS 64-K steps.  wga / wgb: the packed
 // weight groups of tile rows 0-127 / 128-255 at step 0; xga / xgb: the packed
-// activation groups; swa, swb, sxa, sxb: their scale tiles at step 0.
+// activation groups (kGatherX: unused, gx gives the rows instead); swa, swb,
+// sxa, sxb: the scale tiles of all four at step 0 (always packed).
 // KS must be a multiple of 4 and at least 4.  Every thread of the 256-thread
 // workgroup calls this; st0..st3 are the workgroup's four stage arrays.
+template <bool kGatherX = false>
 __device__ __forceinline__ void mainloop(uint8_t* st0, uint8_t* st1, uint8_t* st2, uint8_t* st3,
                                          const uint8_t* wga, const uint8_t* wgb, const uint8_t* xga,
                                          const uint8_t* xgb, const uint8_t* swa, const uint8_t* swb,
-                                         const uint8_t* sxa, const uint8_t* sxb, int KS, v16f (&acc)[4][4]) {
+                                         const uint8_t* sxa, const uint8_t* sxb, int KS, v16f (&acc)[4][4],
+                                         GatherX gx = {}) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -133,10 +146,22 @@ __device__ __forceinline__ void mainloop(uint8_t* st0, uint8_t* st1, uint8_t* st
       case 1: g2l_16(w0 + off + 4096, base + 4096); break;
       case 2: g2l_16(w1 + off, base + 8192); break;
       case 3: g2l_16(w1 + off + 4096, base + 12288); break;
-      case 4: g2l_16(x0 + off, base + kOpBytes); break;
-      case 5: g2l_16(x0 + off + 4096, base + kOpBytes + 4096); break;
-      case 6: g2l_16(x1 + off, base + kOpBytes + 8192); break;
-      case 7: g2l_16(x1 + off + 4096, base + kOpBytes + 12288); break;
+      case 4:
+        if constexpr (kGatherX) g2l_16(gx.p[0] + (size_t)ks * kStepK, base + kOpBytes);
+        else g2l_16(x0 + off, base + kOpBytes);
+        break;
+      case 5:
+        if constexpr (kGatherX) g2l_16(gx.p[1] + (size_t)ks * kStepK, base + kOpBytes + 4096);
+        else g2l_16(x0 + off + 4096, base + kOpBytes + 4096);
+        break;
+      case 6:
+        if constexpr (kGatherX) g2l_16(gx.p[2] + (size_t)ks * kStepK, base + kOpBytes + 8192);
+        else g2l_16(x1 + off, base + kOpBytes + 8192);
+        break;
+      case 7:
+        if constexpr (kGatherX) g2l_16(gx.p[3] + (size_t)ks * kStepK, base + kOpBytes + 12288);
+        else g2l_16(x1 + off + 4096, base + kOpBytes + 12288);
+        break;
       default: g2l_4(ssrc + (size_t)ks * kTileScaleBytes, st + 2 * kOpBytes + wave * 256); break;
     }
   };
