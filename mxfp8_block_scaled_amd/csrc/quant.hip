@@ -49,45 +49,52 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
 // Same quantization, written in the packed operand layout of common.hpp for
 // the large-M GEMM (rows padded to a multiple of 128; pad rows are written as
 // zero elements with scale byte 0, so every byte the GEMM reads is defined).
-// Threads are numbered tile by tile (1024 per 128-row x 64-K tile, row-major
-// inside it): a wave then reads 8 rows x 128 bytes and writes 512 contiguous
-// bytes of one packed tile.
+// A wave owns two adjacent rows of a 128-row group and four consecutive
+// 64-K steps: it reads 512 contiguous bytes of each row (consecutive waves
+// continue along the same rows) and writes, in each of its four packed tiles,
+// the two rows' 128 contiguous bytes (one whole cache line).
 template <typename Idx>
 __global__ __launch_bounds__(256) void quant_act_packed_kernel(const uint16_t* __restrict__ x, int64_t ldx, int M,
                                                                Idx total, int64_t KS,
                                                                uint8_t* __restrict__ qp, uint8_t* __restrict__ sp) {
-  Idx t = (Idx)blockIdx.x * 256 + threadIdx.x;
-  if (t >= total) return;  // total is a multiple of 1024: whole waves leave
-  const Idx tile = t >> 10;                 // g * KS + ks
-  const int r = (int)((t >> 3) & 127);      // row inside the 128-row group
-  const int c8 = (int)(t & 7);              // 8-element chunk inside the 64-K step
-  const int64_t g = (int64_t)(tile / (Idx)KS);
-  const int64_t ks = (int64_t)tile - g * KS;
+  const Idx t = (Idx)blockIdx.x * 256 + threadIdx.x;
+  if (t >= total) return;  // total is a multiple of 64: whole waves leave
+  const Idx w = t >> 6;                     // wave: (g * 64 + row pair) * (KS / 4) + step quad
+  const int lane = (int)(t & 63);
+  const Idx nq = (Idx)(KS >> 2);
+  const Idx gp = w / nq;
+  const int64_t quad = (int64_t)(w - gp * nq);
+  const int64_t g = (int64_t)(gp >> 6);
+  const int r = (int)((gp & 63) * 2) + (lane >> 5);   // row inside the 128-row group
+  const int c = lane & 31;                            // 8-element chunk inside the 4 steps
+  const int64_t ks = quad * 4 + (c >> 3);
+  const int c8 = c & 7;                               // chunk inside the 64-K step
   const int64_t row = g * kGroupRows + r;
-  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  uint32_t v4[4] = {0u, 0u, 0u, 0u};
   if (row < M) {
     const uint4 v = *reinterpret_cast<const uint4*>(x + row * ldx + ks * kStepK + c8 * 8);
-    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    v4[0] = v.x; v4[1] = v.y; v4[2] = v.z; v4[3] = v.w;
   }
   u16x2 mp = {0, 0};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) mp = absmax_pk(mp, w[i]);
+  for (int i = 0; i < 4; ++i) mp = absmax_pk(mp, v4[i]);
   uint32_t m = max((uint32_t)mp[0], (uint32_t)mp[1]);
   m = max(m, (uint32_t)__shfl_xor((int)m, 1));
   m = max(m, (uint32_t)__shfl_xor((int)m, 2));
   const uint32_t sb = (uint32_t)max((int)(m >> 7) - 8, 0);
   uint32_t qd[2];
-  cvt8s(w, mx_scale_value(sb), qd);
-  uint8_t* dst = qp + (int64_t)tile * kTileBytes;
+  cvt8s(v4, mx_scale_value(sb), qd);
+  const int64_t tile = g * KS + ks;
+  uint8_t* dst = qp + tile * kTileBytes;
   *reinterpret_cast<uint2*>(dst + tile_off(r, c8 >> 1) + (c8 & 1) * 8) = make_uint2(qd[0], qd[1]);
-  if ((c8 & 3) == 0) sp[(int64_t)tile * kTileScaleBytes + scale_off(r, c8 >> 2)] = (uint8_t)sb;
+  if ((c8 & 3) == 0) sp[tile * kTileScaleBytes + scale_off(r, c8 >> 2)] = (uint8_t)sb;
 }
 
 int launch_quantize_act_packed(const void* x, int64_t M, int64_t K, int64_t ldx, void* qp, void* sp,
                                hipStream_t stream) {
   const int64_t m_pad = (M + kGroupRows - 1) / kGroupRows * kGroupRows;
   const int64_t KS = K / kStepK;
-  const int64_t total = m_pad * (K / 8);    // (m_pad / 128) * KS tiles x 1024 threads
+  const int64_t total = m_pad * (K / 8);    // (m_pad / 2) row pairs x (KS / 4) step quads x 64 lanes
   const int64_t blocks = total / 256;
   if (total < ((int64_t)1 << 32)) {
     hipLaunchKernelGGL(quant_act_packed_kernel<uint32_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
