@@ -38,6 +38,16 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 // ---------------------------------------------------------------------------
 constexpr int kGroupRows = 128;
 constexpr int kStepK = 64;
+constexpr int kXCD = 8;                          // accelerator dies; workgroup b runs on die b % 8
+
+// Bijection from dispatch order to a work order in which XCD x (which gets
+// workgroups x, x+8, x+16, ...) owns one contiguous range of work items, so
+// the items that share operands in one die's L2 run there together.
+__device__ inline int xcd_remap(int bid, int total) {
+  const int xcd = bid % kXCD, k = bid / kXCD;
+  const int per = total / kXCD, rem = total % kXCD;
+  return (xcd < rem) ? xcd * (per + 1) + k : rem * (per + 1) + (xcd - rem) * per + k;
+}
 constexpr int kTileBytes = kGroupRows * kStepK;   // 8192
 constexpr int kTileScaleBytes = kGroupRows * 2;   // 256
 

@@ -46,7 +46,6 @@ constexpr int kOpBytes = 256 * kStepK;                // one operand's 256 rows 
 constexpr int kScaleRegion = 1024;                    // 256 x 2 B weight + 256 x 2 B activation scales
 constexpr int kStage = 2 * kOpBytes + kScaleRegion;   // 33792
 constexpr int kLoadsPerStage = 9;                     // per thread: 4 + 4 data, 1 scale
-constexpr int kXCD = 8;
 
 // Direct global -> LDS copies (each lane moves 16 or 4 bytes to
 // lds_wave_base + lane * size).  Issued from inline assembly so that the
@@ -64,13 +63,7 @@ __device__ inline void g2l_4(const void* g, const uint8_t* lds_wave_base) {
                : "memory", "m0");
 }
 
-// Bijection from dispatch order to a tile order in which XCD x (which gets
-// workgroups x, x+8, x+16, ...) owns one contiguous range of tiles.
-__device__ inline int xcd_remap(int bid, int total) {
-  const int xcd = bid % kXCD, k = bid / kXCD;
-  const int per = total / kXCD, rem = total % kXCD;
-  return (xcd < rem) ? xcd * (per + 1) + k : rem * (per + 1) + (xcd - rem) * per + k;
-}
+using mxfp8::xcd_remap;
 
 template <int N>
 __device__ inline void wait_vmcnt() {
