@@ -176,7 +176,7 @@ int mxfp8_unpack_weight(const void* w_packed, const void* s_packed, int64_t N, i
 int mxfp8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes) {
   if (!bytes) return MXFP8_E_NULLPTR;
   if (M < 0 || N < 1 || K < 256 || K % 256 != 0) return MXFP8_E_SHAPE;
-  *bytes = (M == 0 || use_skinny(M, K)) ? 256 : tile_ws_bytes(M, N, K);
+  *bytes = M == 0 ? 256 : use_skinny(M, K) ? mxfp8::skinny_ws_bytes(M, K) : tile_ws_bytes(M, N, K);
   return MXFP8_OK;
 }
 
@@ -193,13 +193,14 @@ int mxfp8_linear(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, const vo
   if (!aligned(x_bf16, 16)) return MXFP8_E_ALIGN;
   const bool skinny = use_skinny(M, K);
   if (!skinny && (n_pad(M) * (K / 8) + 255) / 256 > INT32_MAX) return MXFP8_E_SHAPE;
-  const size_t need = skinny ? 256 : tile_ws_bytes(M, N, K);
+  const size_t need = skinny ? mxfp8::skinny_ws_bytes(M, K) : tile_ws_bytes(M, N, K);
   if (!workspace || workspace_bytes < need) return MXFP8_E_WORKSPACE;
   if (!aligned(workspace, 256)) return MXFP8_E_ALIGN;
   if (int st = check_device()) return st;
   hipStream_t s = (hipStream_t)stream;
   if (skinny)
-    return mxfp8::launch_gemm_skinny(x_bf16, ldx, M, K, w_packed, s_packed, N, bias_bf16, y_bf16, ldy, s);
+    return mxfp8::launch_gemm_skinny(x_bf16, ldx, M, K, w_packed, s_packed, N, bias_bf16, y_bf16, ldy, s,
+                                     workspace);
   uint8_t* q = (uint8_t*)workspace;
   uint8_t* sc = q + round_up((size_t)n_pad(M) * (size_t)K, 256);
   uint8_t* part = q + tile_ws_act_bytes(M, K);

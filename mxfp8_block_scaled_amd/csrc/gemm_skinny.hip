@@ -9,7 +9,10 @@
 //     while the rest of the prologue works;
 //  2. the workgroup quantizes the M real activation rows (M x K bf16, read
 //     from L2) once, cooperatively, into LDS -- E4M3 bytes and UE8M0 scales
-//     by the MX rule, with gfx950's scaled converter;
+//     by the MX rule, with gfx950's scaled converter.  From kSkinnyPreqM rows
+//     on, every workgroup converting the same M x K activations costs more
+//     than one extra launch: the row-major quantizer (quant.hip) runs first
+//     and the workgroups copy its bytes instead (kPreq);
 //  3. each wave runs one v_mfma_scale_f32_16x16x128_f8f6f4 per K step
 //     (weight rows as the A operand, activation rows as B, from LDS);
 //  4. the 16 per-wave partial sums are reduced through LDS; wave 0 adds the
@@ -34,6 +37,7 @@ constexpr int kBatch = 8;      // activation chunks in flight per thread
 // LDS: activations [16][K + 16] E4M3 bytes (row pitch K + 16 puts the 16
 // rows' fragment reads on distinct banks), scales [16][K/32], partial sums
 // [16 waves][64 lanes] x 16 bytes.
+template <bool kPreq>
 __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int M, int K, const uint8_t* __restrict__ wp,
     const uint8_t* __restrict__ sp, int N, const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
@@ -73,6 +77,19 @@ __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(
     }
   }
 
+  if constexpr (kPreq) {
+    // 2'. Copy the quantized activations (E4M3 [M][K], then UE8M0 [M][K/32],
+    // both row-major at x) into LDS.
+    const uint8_t* xqg = reinterpret_cast<const uint8_t*>(x);
+    const uint8_t* xsg = xqg + (size_t)M * K;
+    const int per_row16 = K / 16;
+    for (int c = tid; c < M * per_row16; c += kThreads) {
+      const int row = c / per_row16, col = (c - row * per_row16) * 16;
+      *reinterpret_cast<uint4*>(xq + row * pitch + col) = *reinterpret_cast<const uint4*>(xqg + (size_t)row * K + col);
+    }
+    for (int c = tid; c < M * (K / 128); c += kThreads)
+      *reinterpret_cast<uint32_t*>(xs + c * 4) = *reinterpret_cast<const uint32_t*>(xsg + (size_t)c * 4);
+  } else {
   // 2. Quantize x[0:M, 0:K] into LDS: four threads per 32-element block,
   // eight elements (16 bytes) each; a thread issues the loads of up to
   // kBatch chunks before converting any, so their L2 latencies overlap.
@@ -107,6 +124,7 @@ __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(
         if ((c8 & 3) == 0) xs[row * (K / 32) + (c8 >> 2)] = (uint8_t)sb;
       }
     }
+  }
   }
   __syncthreads();
 
@@ -162,18 +180,29 @@ __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(
 }
 
 int launch_gemm_skinny(const void* x, int64_t ldx, int64_t M, int64_t K, const void* wp, const void* sp,
-                       int64_t N, const void* bias, void* y, int64_t ldy, hipStream_t stream) {
+                       int64_t N, const void* bias, void* y, int64_t ldy, hipStream_t stream, void* ws) {
   const int blocks = (int)((N + 15) / 16);
   const int vec = (ldy % 4 == 0) && (((uintptr_t)y & 7) == 0);
   const size_t lds = (size_t)16 * (K + 16) + (size_t)16 * (K / 32) + (size_t)kWaves * 64 * 16;
-  static const bool lds_ok = hipFuncSetAttribute((const void*)gemm_skinny_kernel,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 16 * (kSkinnyMaxK + 16) + 16 * (kSkinnyMaxK / 32) +
-                                                     kWaves * 64 * 16) == hipSuccess;
+  constexpr int kMaxLds = 16 * (kSkinnyMaxK + 16) + 16 * (kSkinnyMaxK / 32) + kWaves * 64 * 16;
+  static const bool lds_ok =
+      hipFuncSetAttribute((const void*)gemm_skinny_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          kMaxLds) == hipSuccess &&
+      hipFuncSetAttribute((const void*)gemm_skinny_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          kMaxLds) == hipSuccess;
   if (!lds_ok) return -7;
-  hipLaunchKernelGGL(gemm_skinny_kernel, dim3(blocks), dim3(kThreads), lds, stream, (const uint16_t*)x, ldx,
-                     (int)M, (int)K, (const uint8_t*)wp, (const uint8_t*)sp, (int)N, (const uint16_t*)bias,
-                     (uint16_t*)y, ldy, vec);
+  if (M >= kSkinnyPreqM) {
+    // ws: E4M3 [M][K] then UE8M0 [M][K/32], row-major (skinny_ws_bytes).
+    uint8_t* q = (uint8_t*)ws;
+    if (int st = launch_quantize_act(x, M, K, ldx, q, K, q + M * K, K / 32, stream)) return st;
+    hipLaunchKernelGGL(gemm_skinny_kernel<true>, dim3(blocks), dim3(kThreads), lds, stream, (const uint16_t*)q, K,
+                       (int)M, (int)K, (const uint8_t*)wp, (const uint8_t*)sp, (int)N, (const uint16_t*)bias,
+                       (uint16_t*)y, ldy, vec);
+  } else {
+    hipLaunchKernelGGL(gemm_skinny_kernel<false>, dim3(blocks), dim3(kThreads), lds, stream, (const uint16_t*)x,
+                       ldx, (int)M, (int)K, (const uint8_t*)wp, (const uint8_t*)sp, (int)N,
+                       (const uint16_t*)bias, (uint16_t*)y, ldy, vec);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 

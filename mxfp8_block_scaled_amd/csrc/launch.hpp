@@ -37,12 +37,17 @@ int launch_gemm_tile(const void* qp, const void* sp, int64_t M, int64_t K, const
                      int64_t N, const void* bias, void* y, int64_t ldy, hipStream_t stream, int splits = 1,
                      void* part = nullptr);
 
-// Skinny GEMM with the activation quantization fused in (M <= kSkinnyMaxM,
-// K <= kSkinnyMaxK).
+// Skinny GEMM (M <= kSkinnyMaxM, K <= kSkinnyMaxK) with the activation
+// quantization fused in below kSkinnyPreqM rows, and done once by the
+// row-major quantizer into ws (skinny_ws_bytes) from kSkinnyPreqM rows on.
 constexpr int64_t kSkinnyMaxM = 16;
 constexpr int64_t kSkinnyMaxK = 8192;
+constexpr int64_t kSkinnyPreqM = 9;
+inline size_t skinny_ws_bytes(int64_t M, int64_t K) {
+  return M >= kSkinnyPreqM ? (size_t)(M * K + M * (K / 32) + 255) / 256 * 256 : 256;
+}
 int launch_gemm_skinny(const void* x, int64_t ldx, int64_t M, int64_t K, const void* wp, const void* sp,
-                       int64_t N, const void* bias, void* y, int64_t ldy, hipStream_t stream);
+                       int64_t N, const void* bias, void* y, int64_t ldy, hipStream_t stream, void* ws);
 
 // Mixture of experts (moe.hip).
 constexpr int64_t kGroupRowsHost = 128;   // = kGroupRows of common.hpp
