@@ -18,3 +18,12 @@ from .mx import (  # noqa: F401
     scale_exponent,
 )
 from .moe import moe_ref, route_topk_softmax  # noqa: F401
+from .mxfp4 import (  # noqa: F401
+    dequantize_mxfp4,
+    e2m1_decode,
+    e2m1_encode,
+    linear_w4a8_ref,
+    pack_fp4,
+    quantize_mxfp4,
+    unpack_fp4,
+)

@@ -166,3 +166,79 @@ def check_equivariance(linear, quantize, x_bf16, w_bf16, j):
     qw, sw = quantize(w_bf16.to(torch.float64).numpy())
     x = x_bf16.to(torch.float64).numpy()
     assert np.array_equal(linear(x * 2.0 ** j, qw, sw, None), 2.0 ** j * linear(x, qw, sw, None))
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 (E2M1) pins.  References independent of the oracle's formulas: the
+# format's value table (tests/golden/e2m1_format.txt), a brute-force
+# nearest-value search over that table with ties to the even code, and the
+# MXFP8 oracle (pinned above) for the layer: every E2M1 value is an E4M3
+# value, so the W4A8 layer equals the MXFP8 layer on the widened weight.
+# ---------------------------------------------------------------------------
+
+def e2m1_table(path):
+    codes, vals = [], []
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        c, v, _ = [f.strip() for f in line.split("|")]
+        codes.append(int(c))
+        vals.append(float(v))
+    return np.array(codes), np.array(vals)
+
+
+def check_e2m1_decode(decode, table_path):
+    codes, vals = e2m1_table(table_path)
+    assert np.array_equal(decode(codes.astype(np.uint8)), vals)
+    neg = decode((codes | 8).astype(np.uint8))
+    assert np.array_equal(neg, -vals) and np.all(np.signbit(neg))
+
+
+def bruteforce_e2m1(t, table_path):
+    """Nearest E2M1 magnitude by exhaustive search over the format's table,
+    after saturation to the largest value; exact ties go to the code whose
+    mantissa bit is 0; the sign is kept (also for zero)."""
+    codes, vals = e2m1_table(table_path)
+    t = np.asarray(t, dtype=np.float64)
+    a = np.minimum(np.abs(t), vals.max())
+    d = np.abs(a[:, None] - vals[None, :])
+    best = d.min(axis=1, keepdims=True)
+    cand = d == best
+    # among tied candidates prefer an even code (mantissa bit 0)
+    even = cand & ((codes[None, :] & 1) == 0)
+    pick = np.where(even.any(axis=1), even.argmax(axis=1), cand.argmax(axis=1))
+    out = codes[pick].astype(np.int64)
+    return np.where(np.signbit(t), out | 8, out).astype(np.uint8)
+
+
+def check_e2m1_encode(encode, table_path):
+    """Every finite bf16 value times 2^j for j in [-12, 12], against the
+    brute-force search (about 1.6 M cases)."""
+    base = all_finite_bf16().numpy().astype(np.float64)
+    for j in range(-12, 13):
+        t = np.ldexp(base, j)
+        t = t[np.isfinite(t)]
+        assert np.array_equal(encode(t), bruteforce_e2m1(t, table_path)), j
+
+
+def check_fp4_worked_examples(quantize, rows):
+    for vals, idx, sb, qc, note in rows:
+        q, s = quantize(np.array([vals], dtype=np.float64))
+        assert int(s[0, 0]) == sb, (note, int(s[0, 0]), sb)
+        assert int(q[0, idx]) == qc, (note, int(q[0, idx]), qc)
+
+
+def check_w4a8_vs_mxfp8(linear_w4a8, pack, x_bf16, codes, w_s, decode4, bias=None):
+    """The W4A8 layer on (codes, w_s) equals the pinned MXFP8 layer on the
+    same weight written as E4M3 bytes (torch's cast of the decoded values,
+    exact because every E2M1 value is an E4M3 value), with the same scales."""
+    import oracle
+    vals = decode4(codes)
+    w8 = torch_e4m3_bytes(torch.from_numpy(vals.astype(np.float32)))
+    assert np.array_equal(torch_e4m3_values(w8), vals)
+    x = x_bf16.to(torch.float64).numpy()
+    b = None if bias is None else bias.to(torch.float64).numpy()
+    y4 = linear_w4a8(x, pack(codes), w_s, b)
+    y8 = oracle.linear_ref(x, w8, w_s, b)
+    assert np.array_equal(y4, y8)
