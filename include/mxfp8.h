@@ -126,6 +126,40 @@ int mxfp8_linear(const void* x_bf16, int64_t M, int64_t K, int64_t ldx,
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * W4A8: MXFP4 weights (E2M1 elements, one UE8M0 scale per 32 along K) times
+ * MXFP8 activations -- the "MxE2m1 weights x MxE4m3 activations" mode of
+ * flashinfer's W4A8 exposure PR ("Changes": MXFP4 weights with 32-element
+ * UE8M0 scales, MXFP8 activation preparation).  Same layer as mxfp8_linear
+ * with the weight element format changed; E2M1 is 1 sign, 2 exponent (bias
+ * 1), 1 mantissa bit: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+ *
+ * mxfp8_prepared_weight_fp4_bytes: host-only sizes (N >= 1, K % 256 == 0):
+ *   *w_bytes = N_pad * K / 2, *s_bytes = N_pad * K / 32.
+ * mxfp8_prepare_weight_fp4: one-time pack.
+ *   w_e2m1   [N, K/2] bytes, row stride ldw bytes (ldw >= K/2, ldw % 16 == 0,
+ *            16-byte aligned); element 2j of a row in the low nibble of byte
+ *            j, element 2j + 1 in the high nibble
+ *   w_s_e8m0 [N, >= K/32] row stride ldws (only [:N, :K/32] is read)
+ *   w_packed, s_packed  outputs of the sizes above, 256-byte aligned.  Pad
+ *            rows hold zero elements and scale byte 127.
+ * mxfp8_linear_w4a8_workspace_bytes: host-only.  M <= 16: as mxfp8_linear;
+ *   larger M: mxfp8_linear's workspace plus N_pad * K bytes, where the
+ *   weight is widened (exactly: every E2M1 value is an E4M3 value) to the
+ *   MXFP8 tiles for the MFMA-bound tile GEMM.
+ * mxfp8_linear_w4a8: y[m, n] = bf16( sum_k deq(q(x))[m, k] * deq4(W)[n, k]
+ *   + bias[n] ), fp32 accumulate, one rounding; arguments as mxfp8_linear
+ *   with the packed MXFP4 weight.  M <= 16 streams the 4-bit weight once
+ *   (half the bytes of MXFP8).  Errors as mxfp8_linear.
+ */
+int mxfp8_prepared_weight_fp4_bytes(int64_t N, int64_t K, size_t* w_bytes, size_t* s_bytes);
+int mxfp8_prepare_weight_fp4(const void* w_e2m1, const void* w_s_e8m0, int64_t N, int64_t K, int64_t ldw,
+                             int64_t ldws, void* w_packed, void* s_packed, void* stream);
+int mxfp8_linear_w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes);
+int mxfp8_linear_w4a8(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, const void* w_packed,
+                      const void* s_packed, int64_t N, const void* bias_bf16, void* y_bf16, int64_t ldy,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The two kernels of mxfp8_linear's large-M path, exposed separately (for
  * timing each, and for callers that reuse one quantized activation across
  * several weights).  The packed activation layout is the packed weight

@@ -46,6 +46,10 @@ _SIGNATURES = {
     "mxfp8_moe_grouped": ([_vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
                           ctypes.c_int),
     "mxfp8_moe_debug_capture": ([_vp, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "mxfp8_prepared_weight_fp4_bytes": ([_i64, _i64, ctypes.POINTER(_sz), ctypes.POINTER(_sz)], ctypes.c_int),
+    "mxfp8_prepare_weight_fp4": ([_vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
+    "mxfp8_linear_w4a8_workspace_bytes": ([_i64, _i64, _i64, ctypes.POINTER(_sz)], ctypes.c_int),
+    "mxfp8_linear_w4a8": ([_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _sz, _vp], ctypes.c_int),
 }
 
 
@@ -127,6 +131,27 @@ def mxfp8_linear_workspace_bytes(M, N, K):
 
 def mxfp8_linear(x, M, K, ldx, wp, sp, N, bias, y, ldy, ws, ws_bytes, stream):
     return lib().mxfp8_linear(x, M, K, ldx, wp, sp, N, bias, y, ldy, ws, ws_bytes, stream)
+
+
+def mxfp8_prepared_weight_fp4_bytes(N, K):
+    w, s = _sz(), _sz()
+    _check(lib().mxfp8_prepared_weight_fp4_bytes(N, K, ctypes.byref(w), ctypes.byref(s)),
+           "mxfp8_prepared_weight_fp4_bytes")
+    return w.value, s.value
+
+
+def mxfp8_prepare_weight_fp4(w, ws, N, K, ldw, ldws, wp, sp, stream):
+    return lib().mxfp8_prepare_weight_fp4(w, ws, N, K, ldw, ldws, wp, sp, stream)
+
+
+def mxfp8_linear_w4a8_workspace_bytes(M, N, K):
+    b = _sz()
+    _check(lib().mxfp8_linear_w4a8_workspace_bytes(M, N, K, ctypes.byref(b)), "mxfp8_linear_w4a8_workspace_bytes")
+    return b.value
+
+
+def mxfp8_linear_w4a8(x, M, K, ldx, wp, sp, N, bias, y, ldy, ws, ws_bytes, stream):
+    return lib().mxfp8_linear_w4a8(x, M, K, ldx, wp, sp, N, bias, y, ldy, ws, ws_bytes, stream)
 
 
 def mxfp8_packed_act_bytes(M, K):
@@ -224,7 +249,10 @@ _workspaces = {}
 def workspace(M, N, K, device):
     """A zero-initialised workspace big enough for (M, N, K), cached per
     device and grown on demand (allocation happens here, never in the library)."""
-    need = mxfp8_linear_workspace_bytes(M, N, K)
+    return _workspace_sized(mxfp8_linear_workspace_bytes(M, N, K), device)
+
+
+def _workspace_sized(need, device):
     key = torch.device(device).index if torch.device(device).index is not None else torch.cuda.current_device()
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < need:
@@ -233,10 +261,40 @@ def workspace(M, N, K, device):
     return ws
 
 
+class PreparedWeightFP4(PreparedWeight):
+    """An MXFP4 weight after the one-time preparation (packed E2M1 payload,
+    N_pad * K / 2 bytes, and its UE8M0 scales)."""
+
+    def unpack(self):
+        raise NotImplementedError("no unpack for the MXFP4 layout")
+
+
+def prepare_weight_fp4(w_e2m1, w_s):
+    """MXFP4 weight: ``w_e2m1`` uint8 ``[N, K/2]`` (two E2M1 codes per byte,
+    element 2j in the low nibble) with UE8M0 scales ``w_s`` ``[>= N, >= K/32]``
+    -> PreparedWeightFP4."""
+    w_e2m1 = _as_bytes(w_e2m1)
+    w_s = _as_bytes(w_s)
+    _require_cuda(w_e2m1, "w_e2m1")
+    N, K2 = w_e2m1.shape
+    K = 2 * K2
+    if w_e2m1.stride(-1) != 1 or w_e2m1.stride(0) % 16 != 0:
+        w_e2m1 = w_e2m1.contiguous()
+    if w_s.stride(-1) != 1:
+        w_s = w_s.contiguous()
+    wb, sb = mxfp8_prepared_weight_fp4_bytes(N, K)
+    wp = torch.empty(wb, dtype=torch.uint8, device=w_e2m1.device)
+    sp = torch.empty(sb, dtype=torch.uint8, device=w_e2m1.device)
+    _check(mxfp8_prepare_weight_fp4(_ptr(w_e2m1), _ptr(w_s), N, K, w_e2m1.stride(0), w_s.stride(0), _ptr(wp),
+                                    _ptr(sp), _stream(w_e2m1.device)), "mxfp8_prepare_weight_fp4")
+    return PreparedWeightFP4(wp, sp, N, K)
+
+
 def linear(x, pw, bias=None, out=None):
     """The MXFP8 dense linear layer: ``y = bf16(deq(q(x)) @ deq(W).T + bias)``.
 
-    ``x`` bf16 ``[..., K]`` (GPU), ``pw`` a PreparedWeight, ``bias`` bf16 ``[N]``
+    ``x`` bf16 ``[..., K]`` (GPU), ``pw`` a PreparedWeight (MXFP8) or a
+    PreparedWeightFP4 (MXFP4, the W4A8 layer), ``bias`` bf16 ``[N]``
     or None.  Returns bf16 ``[..., N]`` (contiguous)."""
     assert x.dtype == torch.bfloat16, f"MXFP8 linear requires bfloat16 activations, got {x.dtype}"
     _require_cuda(x, "x")
@@ -251,6 +309,12 @@ def linear(x, pw, bias=None, out=None):
         assert bias.dtype == torch.bfloat16 and bias.numel() == N
         bias = bias.contiguous()
     y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    if isinstance(pw, PreparedWeightFP4):
+        ws = _workspace_sized(mxfp8_linear_w4a8_workspace_bytes(M, N, K), x.device)
+        _check(mxfp8_linear_w4a8(_ptr(x2), M, K, x2.stride(0), _ptr(pw.w_packed), _ptr(pw.s_packed), N,
+                                 _ptr(bias), _ptr(y), y.stride(0), _ptr(ws), ws.numel(), _stream(x.device)),
+               "mxfp8_linear_w4a8")
+        return y.view(*lead, N)
     ws = workspace(M, N, K, x.device)
     _check(mxfp8_linear(_ptr(x2), M, K, x2.stride(0), _ptr(pw.w_packed), _ptr(pw.s_packed), N, _ptr(bias),
                         _ptr(y), y.stride(0), _ptr(ws), ws.numel(), _stream(x.device)), "mxfp8_linear")

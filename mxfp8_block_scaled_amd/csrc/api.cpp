@@ -209,6 +209,68 @@ int mxfp8_linear(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, const vo
                                  mxfp8::gemm_tile_splits(M, N, K), part);
 }
 
+// ---------------------------------------------------------------- W4A8
+int mxfp8_prepared_weight_fp4_bytes(int64_t N, int64_t K, size_t* w_bytes, size_t* s_bytes) {
+  if (!w_bytes || !s_bytes) return MXFP8_E_NULLPTR;
+  if (N < 1 || K < 256 || K % 256 != 0) return MXFP8_E_SHAPE;
+  *w_bytes = (size_t)n_pad(N) * (size_t)(K / 2);
+  *s_bytes = (size_t)n_pad(N) * (size_t)(K / 32);
+  return MXFP8_OK;
+}
+
+int mxfp8_prepare_weight_fp4(const void* w_e2m1, const void* w_s_e8m0, int64_t N, int64_t K, int64_t ldw,
+                             int64_t ldws, void* w_packed, void* s_packed, void* stream) {
+  if (int st = check_packed(w_packed, s_packed, N, K)) return st;
+  if (!w_e2m1 || !w_s_e8m0) return MXFP8_E_NULLPTR;
+  if (ldw < K / 2 || ldw % 16 != 0 || ldws < K / 32) return MXFP8_E_LD;
+  if (!aligned(w_e2m1, 16)) return MXFP8_E_ALIGN;
+  if (int st = check_device()) return st;
+  return mxfp8::launch_pack_weight_fp4(w_e2m1, w_s_e8m0, N, K, ldw, ldws, w_packed, s_packed, (hipStream_t)stream);
+}
+
+int mxfp8_linear_w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes) {
+  if (!bytes) return MXFP8_E_NULLPTR;
+  if (M < 0 || N < 1 || K < 256 || K % 256 != 0) return MXFP8_E_SHAPE;
+  if (M == 0) *bytes = 256;
+  else if (use_skinny(M, K)) *bytes = mxfp8::skinny_ws_bytes(M, K);
+  else *bytes = tile_ws_bytes(M, N, K) + (size_t)n_pad(N) * (size_t)K;
+  return MXFP8_OK;
+}
+
+int mxfp8_linear_w4a8(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, const void* w_packed,
+                      const void* s_packed, int64_t N, const void* bias_bf16, void* y_bf16, int64_t ldy,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (M < 0) return MXFP8_E_SHAPE;
+  if (int st = check_packed(w_packed, s_packed, N, K)) return st;
+  if (M == 0) return MXFP8_OK;
+  if (M > (int64_t)1 << 30) return MXFP8_E_SHAPE;
+  if (!x_bf16) return MXFP8_E_NULLPTR;
+  if (int st = check_output(y_bf16, N, ldy, bias_bf16)) return st;
+  if (ldx < K || ldx % 8 != 0) return MXFP8_E_LD;
+  if (!aligned(x_bf16, 16)) return MXFP8_E_ALIGN;
+  const bool skinny = use_skinny(M, K);
+  if (!skinny && (n_pad(M) * (K / 8) + 255) / 256 > INT32_MAX) return MXFP8_E_SHAPE;
+  size_t need = 0;
+  mxfp8_linear_w4a8_workspace_bytes(M, N, K, &need);
+  if (!workspace || workspace_bytes < need) return MXFP8_E_WORKSPACE;
+  if (!aligned(workspace, 256)) return MXFP8_E_ALIGN;
+  if (int st = check_device()) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (skinny)
+    return mxfp8::launch_gemm_skinny_fp4(x_bf16, ldx, M, K, w_packed, s_packed, N, bias_bf16, y_bf16, ldy, s,
+                                         workspace);
+  // Larger M is MFMA-bound: widen the weight to the MXFP8 tiles (exact) and
+  // run the MXFP8 tile GEMM.
+  uint8_t* q = (uint8_t*)workspace;
+  uint8_t* sc = q + round_up((size_t)n_pad(M) * (size_t)K, 256);
+  uint8_t* part = q + tile_ws_act_bytes(M, K);
+  uint8_t* w8 = q + tile_ws_bytes(M, N, K);
+  if (int st = mxfp8::launch_widen_fp4(w_packed, N, K, w8, s)) return st;
+  if (int st = mxfp8::launch_quantize_act_packed(x_bf16, M, K, ldx, q, sc, s)) return st;
+  return mxfp8::launch_gemm_tile(q, sc, M, K, w8, s_packed, N, bias_bf16, y_bf16, ldy, s,
+                                 mxfp8::gemm_tile_splits(M, N, K), part);
+}
+
 int mxfp8_packed_act_bytes(int64_t M, int64_t K, size_t* q_bytes, size_t* s_bytes) {
   if (!q_bytes || !s_bytes) return MXFP8_E_NULLPTR;
   if (M < 1 || K < 256 || K % 256 != 0) return MXFP8_E_SHAPE;

@@ -37,7 +37,7 @@ constexpr int kBatch = 8;      // activation chunks in flight per thread
 // LDS: activations [16][K + 16] E4M3 bytes (row pitch K + 16 puts the 16
 // rows' fragment reads on distinct banks), scales [16][K/32], partial sums
 // [16 waves][64 lanes] x 16 bytes.
-template <bool kPreq>
+template <bool kPreq, bool kFp4>
 __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int M, int K, const uint8_t* __restrict__ wp,
     const uint8_t* __restrict__ sp, int N, const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
@@ -57,22 +57,29 @@ __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(
   const int n0 = xcd_remap((int)blockIdx.x, (int)gridDim.x) * 16;
   const int grp = n0 / kGroupRows;
   const int r = (n0 % kGroupRows) + i;
-  const int KT = K / kStepK;   // packed tiles along K
-  const int KS = K / 128;      // MFMA steps along K
+  const int KTs = K / kStepK;                      // packed scale tiles along K
+  const int KTw = kFp4 ? K / 128 : K / kStepK;     // packed weight tiles along K
+  const int KS = K / 128;                          // MFMA steps along K
   const int kb = (KS * wave) / kWaves, ke = (KS * (wave + 1)) / kWaves;
 
-  // 1. Weight loads for this wave's steps (tiles 2ks and 2ks+1, chunk g of
-  // row r; this lane's block 4ks + g is block g & 1 of tile 2ks + g/2).
-  const uint8_t* wrow = wp + (size_t)grp * KT * kTileBytes + tile_off(r, g);
-  const uint8_t* srow = sp + (size_t)grp * KT * kTileScaleBytes + scale_off(r, g & 1);
+  // 1. Weight loads for this wave's steps: E4M3, tiles 2ks and 2ks+1, chunk
+  // g of row r; E2M1 (kFp4), tile ks, chunk g = K [32g, 32g + 32) of the step
+  // (16 bytes either way).  This lane's block 4ks + g is block g & 1 of scale
+  // tile 2ks + g/2.
+  const uint8_t* wrow = wp + (size_t)grp * KTw * kTileBytes + tile_off(r, g);
+  const uint8_t* srow = sp + (size_t)grp * KTs * kTileScaleBytes + scale_off(r, g & 1);
   uint4 w0[kMaxSteps], w1[kMaxSteps];
   uint32_t wsd[kMaxSteps];
 #pragma unroll
   for (int u = 0; u < kMaxSteps; ++u) {
     if (kb + u < ke) {
-      const uint8_t* wt = wrow + (size_t)(2 * (kb + u)) * kTileBytes;
-      w0[u] = *reinterpret_cast<const uint4*>(wt);
-      w1[u] = *reinterpret_cast<const uint4*>(wt + kTileBytes);
+      if constexpr (kFp4) {
+        w0[u] = *reinterpret_cast<const uint4*>(wrow + (size_t)(kb + u) * kTileBytes);
+      } else {
+        const uint8_t* wt = wrow + (size_t)(2 * (kb + u)) * kTileBytes;
+        w0[u] = *reinterpret_cast<const uint4*>(wt);
+        w1[u] = *reinterpret_cast<const uint4*>(wt + kTileBytes);
+      }
       wsd[u] = srow[(size_t)(2 * (kb + u) + (g >> 1)) * kTileScaleBytes];
     }
   }
@@ -142,11 +149,16 @@ __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(
       const int xscale = sr[ks * 4];
       v8i wa, xb;
       wa[0] = (int)w0[u].x; wa[1] = (int)w0[u].y; wa[2] = (int)w0[u].z; wa[3] = (int)w0[u].w;
-      wa[4] = (int)w1[u].x; wa[5] = (int)w1[u].y; wa[6] = (int)w1[u].z; wa[7] = (int)w1[u].w;
+      if constexpr (kFp4) {
+        wa[4] = 0; wa[5] = 0; wa[6] = 0; wa[7] = 0;   // an E2M1 operand uses four registers
+      } else {
+        wa[4] = (int)w1[u].x; wa[5] = (int)w1[u].y; wa[6] = (int)w1[u].z; wa[7] = (int)w1[u].w;
+      }
       xb[0] = (int)b0.x; xb[1] = (int)b0.y; xb[2] = (int)b0.z; xb[3] = (int)b0.w;
       xb[4] = (int)b1.x; xb[5] = (int)b1.y; xb[6] = (int)b1.z; xb[7] = (int)b1.w;
       const int wscale = (int)wsd[u];
-      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wa, xb, acc, 0, 0, 0, wscale, 0, xscale);
+      // A format: 0 = E4M3, 4 = E2M1; B (activations) E4M3.
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wa, xb, acc, kFp4 ? 4 : 0, 0, 0, wscale, 0, xscale);
     }
   }
 
@@ -179,31 +191,44 @@ __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(
   }
 }
 
-int launch_gemm_skinny(const void* x, int64_t ldx, int64_t M, int64_t K, const void* wp, const void* sp,
-                       int64_t N, const void* bias, void* y, int64_t ldy, hipStream_t stream, void* ws) {
+namespace {
+template <bool kFp4>
+int launch_skinny(const void* x, int64_t ldx, int64_t M, int64_t K, const void* wp, const void* sp, int64_t N,
+                  const void* bias, void* y, int64_t ldy, hipStream_t stream, void* ws) {
   const int blocks = (int)((N + 15) / 16);
   const int vec = (ldy % 4 == 0) && (((uintptr_t)y & 7) == 0);
   const size_t lds = (size_t)16 * (K + 16) + (size_t)16 * (K / 32) + (size_t)kWaves * 64 * 16;
   constexpr int kMaxLds = 16 * (kSkinnyMaxK + 16) + 16 * (kSkinnyMaxK / 32) + kWaves * 64 * 16;
   static const bool lds_ok =
-      hipFuncSetAttribute((const void*)gemm_skinny_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+      hipFuncSetAttribute((const void*)gemm_skinny_kernel<false, kFp4>, hipFuncAttributeMaxDynamicSharedMemorySize,
                           kMaxLds) == hipSuccess &&
-      hipFuncSetAttribute((const void*)gemm_skinny_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+      hipFuncSetAttribute((const void*)gemm_skinny_kernel<true, kFp4>, hipFuncAttributeMaxDynamicSharedMemorySize,
                           kMaxLds) == hipSuccess;
   if (!lds_ok) return -7;
   if (M >= kSkinnyPreqM) {
     // ws: E4M3 [M][K] then UE8M0 [M][K/32], row-major (skinny_ws_bytes).
     uint8_t* q = (uint8_t*)ws;
     if (int st = launch_quantize_act(x, M, K, ldx, q, K, q + M * K, K / 32, stream)) return st;
-    hipLaunchKernelGGL(gemm_skinny_kernel<true>, dim3(blocks), dim3(kThreads), lds, stream, (const uint16_t*)q, K,
-                       (int)M, (int)K, (const uint8_t*)wp, (const uint8_t*)sp, (int)N, (const uint16_t*)bias,
-                       (uint16_t*)y, ldy, vec);
+    hipLaunchKernelGGL((gemm_skinny_kernel<true, kFp4>), dim3(blocks), dim3(kThreads), lds, stream,
+                       (const uint16_t*)q, K, (int)M, (int)K, (const uint8_t*)wp, (const uint8_t*)sp, (int)N,
+                       (const uint16_t*)bias, (uint16_t*)y, ldy, vec);
   } else {
-    hipLaunchKernelGGL(gemm_skinny_kernel<false>, dim3(blocks), dim3(kThreads), lds, stream, (const uint16_t*)x,
-                       ldx, (int)M, (int)K, (const uint8_t*)wp, (const uint8_t*)sp, (int)N,
+    hipLaunchKernelGGL((gemm_skinny_kernel<false, kFp4>), dim3(blocks), dim3(kThreads), lds, stream,
+                       (const uint16_t*)x, ldx, (int)M, (int)K, (const uint8_t*)wp, (const uint8_t*)sp, (int)N,
                        (const uint16_t*)bias, (uint16_t*)y, ldy, vec);
   }
   return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+}  // namespace
+
+int launch_gemm_skinny(const void* x, int64_t ldx, int64_t M, int64_t K, const void* wp, const void* sp,
+                       int64_t N, const void* bias, void* y, int64_t ldy, hipStream_t stream, void* ws) {
+  return launch_skinny<false>(x, ldx, M, K, wp, sp, N, bias, y, ldy, stream, ws);
+}
+
+int launch_gemm_skinny_fp4(const void* x, int64_t ldx, int64_t M, int64_t K, const void* wp, const void* sp,
+                           int64_t N, const void* bias, void* y, int64_t ldy, hipStream_t stream, void* ws) {
+  return launch_skinny<true>(x, ldx, M, K, wp, sp, N, bias, y, ldy, stream, ws);
 }
 
 }  // namespace mxfp8

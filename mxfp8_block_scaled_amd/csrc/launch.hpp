@@ -48,6 +48,17 @@ inline size_t skinny_ws_bytes(int64_t M, int64_t K) {
 }
 int launch_gemm_skinny(const void* x, int64_t ldx, int64_t M, int64_t K, const void* wp, const void* sp,
                        int64_t N, const void* bias, void* y, int64_t ldy, hipStream_t stream, void* ws);
+// The same with a packed MXFP4 weight (launch_pack_weight_fp4).
+int launch_gemm_skinny_fp4(const void* x, int64_t ldx, int64_t M, int64_t K, const void* wp, const void* sp,
+                           int64_t N, const void* bias, void* y, int64_t ldy, hipStream_t stream, void* ws);
+
+// MXFP4 weights: w [N, K/2] bytes (two E2M1 per byte, element 2j in the low
+// nibble; row stride ldw bytes), ws [N, K/32] UE8M0 -> packed tiles (pack.hip).
+int launch_pack_weight_fp4(const void* w, const void* ws, int64_t N, int64_t K, int64_t ldw, int64_t ldws,
+                           void* wp, void* sp, hipStream_t stream);
+// Packed MXFP4 weight tiles -> packed MXFP8 tiles of the same values (the
+// scales stay as they are), N_pad * K bytes.
+int launch_widen_fp4(const void* w4, int64_t N, int64_t K, void* w8, hipStream_t stream);
 
 // Mixture of experts (moe.hip).
 constexpr int64_t kGroupRowsHost = 128;   // = kGroupRows of common.hpp

@@ -113,6 +113,72 @@ int launch_pack_weight_gate_up(const void* w, const void* ws, int64_t E, int64_t
   return pack(w, ws, E * 2 * I, K, K, K / 32, wp, sp, I, stream);
 }
 
+// MXFP4 weights (two E2M1 elements per byte along K, element 2j in the low
+// nibble): the packed tile of a 128-row group and a 128-element K step is the
+// same 8 KiB geometry as an E4M3 tile of a 64-element step (64 bytes per row,
+// four 16-byte chunks, the same chunk swizzle) -- a lane of the scaled MFMA
+// with an E2M1 operand takes 16 bytes = 32 consecutive K of one row, like the
+// E4M3 lane takes 16 bytes = 16 K -- so the byte packing is pack_w over K / 2
+// bytes per row.  The UE8M0 scales are per 32 elements either way: pack_s
+// unchanged.
+int launch_pack_weight_fp4(const void* w, const void* ws, int64_t N, int64_t K, int64_t ldw, int64_t ldws,
+                           void* wp, void* sp, hipStream_t stream) {
+  const int64_t G = (N + kGroupRows - 1) / kGroupRows;
+  const int64_t KS4 = K / 128, KS = K / kStepK;
+  const int64_t tw = G * KS4 * kChunksPerTile;
+  const int64_t ts = G * KS * kGroupRows;
+  hipLaunchKernelGGL(pack_w_kernel, dim3((unsigned)((tw + 255) / 256)), dim3(256), 0, stream,
+                     (const uint8_t*)w, ldw, N, KS4, tw, (uint8_t*)wp, (int64_t)0);
+  hipLaunchKernelGGL(pack_s_kernel, dim3((unsigned)((ts + 255) / 256)), dim3(256), 0, stream,
+                     (const uint8_t*)ws, ldws, N, KS, ts, (uint8_t*)sp, (int64_t)0);
+  return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+// Packed MXFP4 tiles -> packed MXFP8 tiles of the same values (every E2M1
+// value is an E4M3 value; the scales are unchanged), for the tile GEMM.  One
+// thread per 16-byte E4M3 chunk: chunk c8 (16 elements) of row r in 64-K step
+// s is half (c8 & 1) of E2M1 chunk 2 (s & 1) + c8 / 2 of row r in 128-K step
+// s / 2.  E2M1 magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 are the E4M3 bytes
+// 0x00, 0x30, 0x38, 0x3C, 0x40, 0x44, 0x48, 0x4C; the sign bit moves from
+// bit 3 to bit 7.
+__device__ inline uint32_t e2m1_to_e4m3(uint32_t c) {
+  constexpr uint32_t lo = 0x3C383000u, hi = 0x4C484440u;   // bytes of the 8 magnitudes
+  const uint32_t m = c & 7u;
+  const uint32_t b = ((m < 4 ? lo : hi) >> (8 * (m & 3))) & 0xFFu;
+  return b | ((c & 8u) << 4);
+}
+__global__ __launch_bounds__(256) void widen_fp4_kernel(const uint8_t* __restrict__ w4, int64_t KS, int64_t total,
+                                                        uint8_t* __restrict__ w8) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= total) return;
+  const int64_t tile = t / kChunksPerTile;                 // E4M3 tile: g * KS + s
+  const int slot = (int)(t % kChunksPerTile);
+  const int64_t g = tile / KS, s = tile - g * KS;
+  const int r = slot >> 2;
+  const int c8 = (slot & 3) ^ swz(r);
+  const int c4 = 2 * (int)(s & 1) + (c8 >> 1);
+  const uint8_t* src = w4 + (g * (KS / 2) + (s >> 1)) * kTileBytes + tile_off(r, c4) + (c8 & 1) * 8;
+  const uint2 v = *reinterpret_cast<const uint2*>(src);
+  const uint32_t in[2] = {v.x, v.y};
+  uint32_t out[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t w = in[d >> 1] >> (16 * (d & 1));      // four nibbles = four elements
+    out[d] = e2m1_to_e4m3(w & 0xF) | (e2m1_to_e4m3((w >> 4) & 0xF) << 8) |
+             (e2m1_to_e4m3((w >> 8) & 0xF) << 16) | (e2m1_to_e4m3((w >> 12) & 0xF) << 24);
+  }
+  reinterpret_cast<uint4*>(w8)[t] = make_uint4(out[0], out[1], out[2], out[3]);
+}
+
+int launch_widen_fp4(const void* w4, int64_t N, int64_t K, void* w8, hipStream_t stream) {
+  const int64_t G = (N + kGroupRows - 1) / kGroupRows;
+  const int64_t KS = K / kStepK;
+  const int64_t total = G * KS * kChunksPerTile;
+  hipLaunchKernelGGL(widen_fp4_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+                     (const uint8_t*)w4, KS, total, (uint8_t*)w8);
+  return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
 int launch_unpack_weight(const void* wp, const void* sp, int64_t N, int64_t K, void* w, void* ws,
                          hipStream_t stream) {
   const int64_t KS = K / kStepK;

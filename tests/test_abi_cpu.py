@@ -166,3 +166,31 @@ def test_moe_debug_hook():
     assert api.mxfp8_moe_debug_capture(P + 2, P, P, P, P) == -3
     assert api.mxfp8_moe_debug_capture(P, P, P, P, P) == 0
     assert api.mxfp8_moe_debug_capture(None, None, None, None, None) == 0
+
+
+def test_w4a8_sizes_and_validation():
+    assert api.mxfp8_prepared_weight_fp4_bytes(130, 256) == (256 * 128, 256 * 8)
+    assert api.mxfp8_prepared_weight_fp4_bytes(4096, 4096) == (4096 * 2048, 4096 * 128)
+    with pytest.raises(api.MXFP8Error):
+        api.mxfp8_prepared_weight_fp4_bytes(130, 384)
+    # workspace: decode shapes as the MXFP8 layer; larger M adds the widened weight
+    assert api.mxfp8_linear_w4a8_workspace_bytes(7, 4096, 4096) == api.mxfp8_linear_workspace_bytes(7, 4096, 4096)
+    assert api.mxfp8_linear_w4a8_workspace_bytes(16, 4096, 4096) == api.mxfp8_linear_workspace_bytes(16, 4096, 4096)
+    assert (api.mxfp8_linear_w4a8_workspace_bytes(512, 130, 256)
+            == api.mxfp8_linear_workspace_bytes(512, 130, 256) + 256 * 256)
+    p = api.mxfp8_prepare_weight_fp4
+    assert p(P, P, 130, 256, 128, 8, P, P, None) == -6       # valid (ldw = K/2), no device
+    assert p(P, P, 130, 224, 112, 7, P, P, None) == -2       # K % 256
+    assert p(P, P, 130, 256, 112, 8, P, P, None) == -4       # ldw < K/2
+    assert p(P, P, 130, 256, 136, 8, P, P, None) == -4       # ldw % 16
+    assert p(P + 8, P, 130, 256, 128, 8, P, P, None) == -3
+    assert p(None, P, 130, 256, 128, 8, P, P, None) == -1
+    f = api.mxfp8_linear_w4a8
+    ws = api.mxfp8_linear_w4a8_workspace_bytes(512, 130, 256)
+    ok = (P, 512, 256, 256, P, P, 130, None, P, 130, P, ws, None)
+    assert f(*ok) == -6
+    bad = list(ok); bad[11] = ws - 1; assert f(*bad) == -5   # workspace too small
+    bad = list(ok); bad[2] = 320; assert f(*bad) == -2
+    bad = list(ok); bad[1] = 0; assert f(*bad) == 0
+    bad = list(ok); bad[4] = P + 64; assert f(*bad) == -3
+    bad = list(ok); bad[9] = 100; assert f(*bad) == -4

@@ -1,0 +1,110 @@
+"""The W4A8 layer (MXFP4 weights x MXFP8 activations) on the GPU vs the
+oracle (oracle/mxfp4.py), with the GEMM tolerance of tests/gpu_util.py
+applied to the dequantized MXFP4 weight, plus exact one-hot pins on both
+paths (the 4-bit decode kernel for M <= 16, the widened-weight tile GEMM
+above)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mxfp8_block_scaled_amd import api, synth
+from tests import gpu_util
+
+pytestmark = pytest.mark.gpu
+
+
+def prepare(codes, ws):
+    d = gpu_util.dev()
+    return api.prepare_weight_fp4(torch.from_numpy(oracle.pack_fp4(codes)).to(d), torch.from_numpy(ws).to(d))
+
+
+def tolerance4(x_np, codes, ws, K):
+    qa, sa = oracle.quantize_mx(x_np)
+    A = oracle.dequantize_mx(qa, sa)
+    W = oracle.dequantize_mxfp4(oracle.pack_fp4(codes), ws)
+    acc = (K / 64.0) * 2.0 ** -10 * np.outer(np.abs(A).max(axis=1), np.abs(W).max(axis=1)) \
+        + K * 2.0 ** -23 * (np.abs(A) @ np.abs(W).T)
+    return (1 + 2.0 ** -8) * acc + 2.0 ** -133
+
+
+def run_and_check(M, N, K, seed, bias=True, force_path=0, x_std=1.0, stress=False):
+    g = torch.Generator().manual_seed(seed)
+    x = synth.randn_bf16((M, K), x_std, g)
+    if stress:
+        x = synth.scale_stress(x, seed=seed + 100)
+    w = synth.randn_bf16((N, K), 0.02, g).to(torch.float64).numpy()
+    codes, ws = oracle.quantize_mxfp4(w)
+    b = synth.randn_bf16((N,), 0.1, g) if bias else None
+    label = f"w4a8 M{M} N{N} K{K} path{force_path}"
+    print("CASE", label, flush=True)
+    pw = prepare(codes, ws)
+    prev = api.mxfp8_debug_force_path(force_path)
+    try:
+        y = api.linear(x.to(gpu_util.dev()), pw, None if b is None else b.to(gpu_util.dev()))
+        torch.cuda.synchronize()
+    finally:
+        api.mxfp8_debug_force_path(prev)
+    assert y.shape == (M, N) and y.is_contiguous()
+    xn = x.to(torch.float64).numpy()
+    r = oracle.linear_w4a8_ref(xn, oracle.pack_fp4(codes), ws, None if b is None else b.to(torch.float64).numpy())
+    return gpu_util.compare(y.float().cpu().numpy(), r, tolerance4(xn, codes, ws, K), label)
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (1, 4096, 4096), (7, 4096, 4096), (9, 4096, 4096), (16, 4096, 4096),   # decode (4-bit kernel)
+    (3, 130, 256), (15, 384, 768), (2, 1, 512),                            # ragged N, small K
+])
+def test_decode_parity(M, N, K):
+    run_and_check(M, N, K, seed=M * 7 + N)
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 640, 512), (129, 200, 1024), (128, 4096, 4096), (17, 130, 256)])
+def test_tile_path_parity(M, N, K):
+    """M > 16: the weight is widened to MXFP8 tiles (exact) for the tile GEMM
+    (M = 128, N = 4096 also exercises split-K)."""
+    run_and_check(M, N, K, seed=M + N)
+
+
+@pytest.mark.parametrize("path", [0, 1])
+def test_scale_stress_both_paths(path):
+    run_and_check(13, 256, 512, seed=31, force_path=path, stress=True)
+
+
+@pytest.mark.parametrize("M", [5, 40])
+def test_one_hot_weight_exact(M):
+    """W[n, perm[n]] = 1 (E2M1 code 6 = 4 under scale 2^-2): y[m, n] =
+    bf16(deq(A)[m, perm[n]]) exactly.  Pins the 4-bit operand's nibble order,
+    lane mapping and the weight scale lookup (M = 5: decode kernel), and the
+    widening to E4M3 tiles (M = 40: tile GEMM)."""
+    g = torch.Generator().manual_seed(17)
+    K, N = 512, 200
+    x = synth.scale_stress(synth.randn_bf16((M, K), 1.0, g), seed=9)
+    perm = torch.randint(0, K, (N,), generator=g).numpy()
+    w = np.zeros((N, K))
+    w[np.arange(N), perm] = 1.0
+    codes, ws = oracle.quantize_mxfp4(w)
+    pw = prepare(codes, ws)
+    y = api.linear(x.to(gpu_util.dev()), pw).float().cpu().numpy()
+    qa, sa = oracle.quantize_mx(x.double().numpy())
+    exp = oracle.bf16_round(oracle.dequantize_mx(qa, sa)[:, perm])
+    assert np.array_equal(y, exp)
+
+
+def test_w4a8_matches_mxfp8_on_widened_weight():
+    """The GPU W4A8 layer and the GPU MXFP8 layer fed the same weight (E2M1
+    values written as E4M3 bytes by torch's cast, same scales) agree
+    bit for bit on the tile path (the same GEMM after the exact widening)."""
+    g = torch.Generator().manual_seed(23)
+    M, N, K = 64, 256, 1024
+    x = synth.randn_bf16((M, K), 1.0, g).to(gpu_util.dev())
+    w = synth.randn_bf16((N, K), 0.02, g).to(torch.float64).numpy()
+    codes, ws = oracle.quantize_mxfp4(w)
+    w8 = torch.from_numpy(oracle.e2m1_decode(codes).astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8)
+    pw8 = api.prepare_weight(w8.to(gpu_util.dev()), torch.from_numpy(ws).to(gpu_util.dev()))
+    pw4 = prepare(codes, ws)
+    y8 = api.linear(x, pw8)
+    y4 = api.linear(x, pw4)
+    torch.cuda.synchronize()
+    assert torch.equal(y8, y4)
