@@ -203,15 +203,19 @@ def sweep(api, synth, torch, np, dev, stream):
     rows = []
     sptr = stream.cuda_stream
 
-    def linear_entry(x_list, pw_list, b, M, N, K, y, reps, label, extra=None):
-        ws_t = api.workspace(M, N, K, dev)
+    def linear_entry(x_list, pw_list, b, M, N, K, y, reps, label, extra=None, w4=False):
+        if w4:
+            ws_t = torch.zeros(api.mxfp8_linear_w4a8_workspace_bytes(M, N, K), dtype=torch.uint8, device=dev)
+            entry = api.mxfp8_linear_w4a8
+        else:
+            ws_t = api.workspace(M, N, K, dev)
+            entry = api.mxfp8_linear
 
         def fn(r):
             xx = x_list[r % len(x_list)]
             pp = pw_list[r % len(pw_list)]
-            st = api.mxfp8_linear(xx.data_ptr(), M, K, K, pp.w_packed.data_ptr(), pp.s_packed.data_ptr(), N,
-                                  None if b is None else b.data_ptr(), y.data_ptr(), N, ws_t.data_ptr(),
-                                  ws_t.numel(), sptr)
+            st = entry(xx.data_ptr(), M, K, K, pp.w_packed.data_ptr(), pp.s_packed.data_ptr(), N,
+                       None if b is None else b.data_ptr(), y.data_ptr(), N, ws_t.data_ptr(), ws_t.numel(), sptr)
             if st != 0:
                 raise RuntimeError(st)
         for r in range(5):
@@ -219,7 +223,7 @@ def sweep(api, synth, torch, np, dev, stream):
         torch.cuda.synchronize()
         ms = time_calls(fn, reps, stream, torch)
         flops = 2.0 * M * N * K
-        alg_bytes = M * K * 2 + N * K + N * K / 32 + (0 if b is None else 2 * N) + M * N * 2
+        alg_bytes = M * K * 2 + N * K * (0.5 if w4 else 1.0) + N * K / 32 + (0 if b is None else 2 * N) + M * N * 2
         row = {"workload": label, "M": M, "N": N, "K": K, "us": round(ms * 1e3, 3),
                "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 3),
                "GB/s": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
@@ -252,6 +256,22 @@ def sweep(api, synth, torch, np, dev, stream):
         # per-call time without the host's per-launch cost.
         rows[-1]["graph_replay_us"] = graph_replay_us(api, torch, dev, xs, copies, bd, M, y)
     del copies, pw0
+
+    # W4A8 decode: MXFP4 weights (synthetic: uniformly drawn E2M1 codes, every
+    # scale 2^-6), the same rotation over 48 copies
+    g4 = torch.Generator(device=dev).manual_seed(7)
+    w4 = torch.randint(0, 256, (4096, 2048), generator=g4, device=dev, dtype=torch.int32).to(torch.uint8)
+    s4 = torch.full((4096, 128), 121, dtype=torch.uint8, device=dev)
+    pw4 = api.prepare_weight_fp4(w4, s4)
+    copies4 = [pw4] + [api.PreparedWeightFP4(pw4.w_packed.clone(), pw4.s_packed.clone(), pw4.N, pw4.K)
+                       for _ in range(47)]
+    for M in (1, 7, 16):
+        xm, _, _ = synth.config_inputs(2, M, device=dev)
+        xs = [xm.clone() for _ in range(8)]
+        y = torch.empty((M, 4096), dtype=torch.bfloat16, device=dev)
+        linear_entry(xs, copies4, bd, M, 4096, 4096, y, 480, f"decode W4A8 M={M} N=4096 K=4096",
+                     {"weight_copies_rotated": 48}, w4=True)
+    del copies4, pw4
 
     # prefill QKV shape, M=16384 N=5120 K=2048, no bias
     xd, w, _ = synth.config_inputs(3, device=dev)
