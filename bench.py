@@ -257,11 +257,9 @@ def sweep(api, synth, torch, np, dev, stream):
         rows[-1]["graph_replay_us"] = graph_replay_us(api, torch, dev, xs, copies, bd, M, y)
     del copies, pw0
 
-    # W4A8 decode: MXFP4 weights (synthetic: uniformly drawn E2M1 codes, every
-    # scale 2^-6), the same rotation over 48 copies
-    g4 = torch.Generator(device=dev).manual_seed(7)
-    w4 = torch.randint(0, 256, (4096, 2048), generator=g4, device=dev, dtype=torch.int32).to(torch.uint8)
-    s4 = torch.full((4096, 128), 121, dtype=torch.uint8, device=dev)
+    # W4A8 decode: the same bf16 decode weight quantized to MXFP4 by the
+    # library, the same rotation over 48 copies
+    w4, s4 = api.quantize_fp4(w)
     pw4 = api.prepare_weight_fp4(w4, s4)
     copies4 = [pw4] + [api.PreparedWeightFP4(pw4.w_packed.clone(), pw4.s_packed.clone(), pw4.N, pw4.K)
                        for _ in range(47)]

@@ -151,6 +151,18 @@ int mxfp8_linear(const void* x_bf16, int64_t M, int64_t K, int64_t ldx,
  *   with the packed MXFP4 weight.  M <= 16 streams the 4-bit weight once
  *   (half the bytes of MXFP8).  Errors as mxfp8_linear.
  */
+/*
+ * bf16 -> MXFP4 (the MX rule with E2M1 elements: shared exponent
+ * floor(log2 amax) - 2, RNE, saturate to +-6, all-zero block -> byte 0):
+ *   x_bf16 [M, K] row stride ldx (ldx >= K, ldx % 8 == 0, 16-byte aligned);
+ *   q_e2m1 [M, K/2] bytes, row stride ldq (ldq >= K/2, ldq % 4 == 0, 4-byte
+ *          aligned), element 2j in the low nibble of byte j;
+ *   s_e8m0 [M, K/32] row stride lds.  K % 32 == 0.
+ * For making W4A8 weights from a bf16 checkpoint (the output feeds
+ * mxfp8_prepare_weight_fp4).
+ */
+int mxfp8_quantize_fp4(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, void* q_e2m1, int64_t ldq,
+                       void* s_e8m0, int64_t lds, void* stream);
 int mxfp8_prepared_weight_fp4_bytes(int64_t N, int64_t K, size_t* w_bytes, size_t* s_bytes);
 int mxfp8_prepare_weight_fp4(const void* w_e2m1, const void* w_s_e8m0, int64_t N, int64_t K, int64_t ldw,
                              int64_t ldws, void* w_packed, void* s_packed, void* stream);

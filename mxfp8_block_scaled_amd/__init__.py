@@ -16,7 +16,7 @@ _API = (
     "mxfp8_moe_grouped", "mxfp8_moe_workspace_bytes", "mxfp8_moe_prepared_bytes",
     "mxfp8_moe_prepare_weights", "mxfp8_moe_debug_capture", "MoEWeights", "moe_prepare_weights",
     "moe_debug_capture",
-    "PreparedWeightFP4", "prepare_weight_fp4", "mxfp8_prepared_weight_fp4_bytes", "mxfp8_prepare_weight_fp4",
+    "PreparedWeightFP4", "prepare_weight_fp4", "quantize_fp4", "mxfp8_quantize_fp4", "mxfp8_prepared_weight_fp4_bytes", "mxfp8_prepare_weight_fp4",
     "mxfp8_linear_w4a8_workspace_bytes", "mxfp8_linear_w4a8",
     "mxfp8_status_string", "MXFP8Error",
 )

@@ -46,6 +46,7 @@ _SIGNATURES = {
     "mxfp8_moe_grouped": ([_vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
                           ctypes.c_int),
     "mxfp8_moe_debug_capture": ([_vp, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "mxfp8_quantize_fp4": ([_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp], ctypes.c_int),
     "mxfp8_prepared_weight_fp4_bytes": ([_i64, _i64, ctypes.POINTER(_sz), ctypes.POINTER(_sz)], ctypes.c_int),
     "mxfp8_prepare_weight_fp4": ([_vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
     "mxfp8_linear_w4a8_workspace_bytes": ([_i64, _i64, _i64, ctypes.POINTER(_sz)], ctypes.c_int),
@@ -131,6 +132,25 @@ def mxfp8_linear_workspace_bytes(M, N, K):
 
 def mxfp8_linear(x, M, K, ldx, wp, sp, N, bias, y, ldy, ws, ws_bytes, stream):
     return lib().mxfp8_linear(x, M, K, ldx, wp, sp, N, bias, y, ldy, ws, ws_bytes, stream)
+
+
+def mxfp8_quantize_fp4(x, M, K, ldx, q, ldq, s, lds, stream):
+    return lib().mxfp8_quantize_fp4(x, M, K, ldx, q, ldq, s, lds, stream)
+
+
+def quantize_fp4(x):
+    """bf16 ``[M, K]`` (GPU) -> (uint8 ``[M, K/2]`` packed E2M1, uint8 ``[M, K/32]``
+    UE8M0), the MX rule with E2M1 elements."""
+    assert x.dtype == torch.bfloat16
+    _require_cuda(x, "x")
+    if x.stride(-1) != 1 or x.stride(0) % 8 != 0 or x.data_ptr() % 16 != 0:
+        x = x.contiguous()
+    M, K = x.shape
+    q = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+    s = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+    _check(mxfp8_quantize_fp4(_ptr(x), M, K, x.stride(0), _ptr(q), q.stride(0), _ptr(s), s.stride(0),
+                              _stream(x.device)), "mxfp8_quantize_fp4")
+    return q, s
 
 
 def mxfp8_prepared_weight_fp4_bytes(N, K):

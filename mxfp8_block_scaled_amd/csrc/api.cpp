@@ -210,6 +210,18 @@ int mxfp8_linear(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, const vo
 }
 
 // ---------------------------------------------------------------- W4A8
+int mxfp8_quantize_fp4(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, void* q_e2m1, int64_t ldq,
+                       void* s_e8m0, int64_t lds, void* stream) {
+  if (M < 0 || K < 0 || K % 32 != 0) return MXFP8_E_SHAPE;
+  if (M == 0 || K == 0) return MXFP8_OK;
+  if (!x_bf16 || !q_e2m1 || !s_e8m0) return MXFP8_E_NULLPTR;
+  if (ldx < K || ldx % 8 != 0 || ldq < K / 2 || ldq % 4 != 0 || lds < K / 32) return MXFP8_E_LD;
+  if (!aligned(x_bf16, 16) || !aligned(q_e2m1, 4)) return MXFP8_E_ALIGN;
+  if ((M * (K / 8) + 255) / 256 > INT32_MAX) return MXFP8_E_SHAPE;
+  if (int st = check_device()) return st;
+  return mxfp8::launch_quantize_fp4(x_bf16, M, K, ldx, q_e2m1, ldq, s_e8m0, lds, (hipStream_t)stream);
+}
+
 int mxfp8_prepared_weight_fp4_bytes(int64_t N, int64_t K, size_t* w_bytes, size_t* s_bytes) {
   if (!w_bytes || !s_bytes) return MXFP8_E_NULLPTR;
   if (N < 1 || K < 256 || K % 256 != 0) return MXFP8_E_SHAPE;

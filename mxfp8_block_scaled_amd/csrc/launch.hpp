@@ -59,6 +59,9 @@ int launch_pack_weight_fp4(const void* w, const void* ws, int64_t N, int64_t K, 
 // Packed MXFP4 weight tiles -> packed MXFP8 tiles of the same values (the
 // scales stay as they are), N_pad * K bytes.
 int launch_widen_fp4(const void* w4, int64_t N, int64_t K, void* w8, hipStream_t stream);
+// bf16 [M, K] -> MXFP4: E2M1 [M, K/2] (row stride ldq bytes) + UE8M0 [M, K/32].
+int launch_quantize_fp4(const void* x, int64_t M, int64_t K, int64_t ldx, void* q, int64_t ldq, void* s,
+                        int64_t lds, hipStream_t stream);
 
 // Mixture of experts (moe.hip).
 constexpr int64_t kGroupRowsHost = 128;   // = kGroupRows of common.hpp

@@ -90,6 +90,58 @@ __global__ __launch_bounds__(256) void quant_act_packed_kernel(const uint16_t* _
   if ((c8 & 3) == 0) sp[tile * kTileScaleBytes + scale_off(r, c8 >> 2)] = (uint8_t)sb;
 }
 
+// MXFP4 quantization (bf16 [M, K] -> E2M1 [M, K/2] packed two per byte,
+// element 2j in the low nibble, + UE8M0 [M, K/32]): the MX rule with the
+// E2M1 element type (shared exponent floor(log2 amax) - 2, RNE, saturate to
+// +-6), for preparing W4A8 weights.  Same thread layout as quant_act_kernel;
+// gfx950's v_cvt_scalef32_pk_fp4_bf16 converts two bf16 into the two nibbles
+// of one byte as RNE(x / scale), saturating (E2M1 has no NaN or infinity).
+template <typename Idx>
+__global__ __launch_bounds__(256) void quant_fp4_kernel(const uint16_t* __restrict__ x, int64_t ldx,
+                                                        Idx chunks_per_row, Idx total, uint8_t* __restrict__ q,
+                                                        int64_t ldq, uint8_t* __restrict__ s, int64_t lds) {
+  Idx t = (Idx)blockIdx.x * 256 + threadIdx.x;
+  const bool valid = t < total;
+  if (!valid) t = total - 1;
+  const Idx row = t / chunks_per_row;
+  const Idx c8 = t - row * chunks_per_row;
+  const uint4 v = *reinterpret_cast<const uint4*>(x + (int64_t)row * ldx + (int64_t)c8 * 8);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  u16x2 mp = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) mp = absmax_pk(mp, w[i]);
+  uint32_t m = max((uint32_t)mp[0], (uint32_t)mp[1]);
+  m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+  const uint32_t sb = (uint32_t)max((int)(m >> 7) - 2, 0);    // E2M1 emax = 2
+  const float scale = mx_scale_value(sb);
+  uint32_t d = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, __builtin_bit_cast(bf16x2, w[0]), scale, 0);
+  d = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(d, __builtin_bit_cast(bf16x2, w[1]), scale, 1);
+  d = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(d, __builtin_bit_cast(bf16x2, w[2]), scale, 2);
+  d = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(d, __builtin_bit_cast(bf16x2, w[3]), scale, 3);
+  if (valid) {
+    *reinterpret_cast<uint32_t*>(q + (int64_t)row * ldq + (int64_t)c8 * 4) = d;
+    if ((c8 & 3) == 0) s[(int64_t)row * lds + (int64_t)(c8 >> 2)] = (uint8_t)sb;
+  }
+}
+
+int launch_quantize_fp4(const void* x, int64_t M, int64_t K, int64_t ldx, void* q, int64_t ldq, void* s,
+                        int64_t lds, hipStream_t stream) {
+  const int64_t per_row = K / 8;
+  const int64_t total = M * per_row;
+  const int64_t blocks = (total + 255) / 256;
+  if (total < ((int64_t)1 << 32)) {
+    hipLaunchKernelGGL(quant_fp4_kernel<uint32_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const uint16_t*)x, ldx, (uint32_t)per_row, (uint32_t)total, (uint8_t*)q, ldq,
+                       (uint8_t*)s, lds);
+  } else {
+    hipLaunchKernelGGL(quant_fp4_kernel<uint64_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const uint16_t*)x, ldx, (uint64_t)per_row, (uint64_t)total, (uint8_t*)q, ldq,
+                       (uint8_t*)s, lds);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
 int launch_quantize_act_packed(const void* x, int64_t M, int64_t K, int64_t ldx, void* qp, void* sp,
                                hipStream_t stream) {
   const int64_t m_pad = (M + kGroupRows - 1) / kGroupRows * kGroupRows;

@@ -194,3 +194,14 @@ def test_w4a8_sizes_and_validation():
     bad = list(ok); bad[1] = 0; assert f(*bad) == 0
     bad = list(ok); bad[4] = P + 64; assert f(*bad) == -3
     bad = list(ok); bad[9] = 100; assert f(*bad) == -4
+
+
+def test_quantize_fp4_validation():
+    f = api.mxfp8_quantize_fp4
+    assert f(P, 4, 64, 64, P, 32, P, 2, None) == -6          # valid, no device
+    assert f(P, 4, 48, 48, P, 24, P, 2, None) == -2          # K % 32
+    assert f(P, 0, 64, 64, P, 32, P, 2, None) == 0
+    assert f(P, 4, 64, 64, P, 30, P, 2, None) == -4          # ldq < K/2
+    assert f(P, 4, 64, 64, P, 34, P, 2, None) == -4          # ldq % 4
+    assert f(P, 4, 64, 64, P + 2, 32, P, 2, None) == -3      # q alignment
+    assert f(None, 4, 64, 64, P, 32, P, 2, None) == -1
