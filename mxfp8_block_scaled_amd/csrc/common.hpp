@@ -21,11 +21,15 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 //
 //   data[g][ks]  = 8 KiB tile: 128 rows x 4 chunks of 16 bytes; logical chunk
 //                  c (K bytes [16c, 16c+16) of the step) of row r sits at
-//                  chunk position c ^ swz(r), swz(r) = (r >> 2) & 3, so the
-//                  16-byte fragment reads of 16 consecutive rows at one
-//                  logical chunk cover all 64 LDS banks once (measured on
-//                  gfx950: no bank-conflict cycles; without the swizzle 2.2
-//                  conflict cycles per access);
+//                  chunk position c ^ swz(r), swz(r) = q ^ 2 (q & 1) with
+//                  q = (r >> 2) & 3 (bits 2-3 of the row only).  Measured on
+//                  gfx950 with a 16-wave LDS probe over every swizzle of
+//                  this form: a ds_read_b128 in which lane i + 16 g reads
+//                  row R0 + i, chunk g (16x16x128 operand) or lane i + 32 g
+//                  reads row R0 + i, chunk g (32x32x64 operand) takes 2.1
+//                  cycles with this swizzle for both; the plain (r >> 2) & 3
+//                  is conflict-free only for the second (3.5 cycles for the
+//                  first), no swizzle for neither;
 //   scale[g][ks] = 256 B: 128 rows x 2 UE8M0 bytes (MX blocks 2ks, 2ks+1),
 //                  lane-major: the byte of row r, block b sits at
 //                  (r % 32) * 8 + b * 4 + r / 32, so one 4-byte read gives a
@@ -51,7 +55,10 @@ __device__ inline int xcd_remap(int bid, int total) {
 constexpr int kTileBytes = kGroupRows * kStepK;   // 8192
 constexpr int kTileScaleBytes = kGroupRows * 2;   // 256
 
-__host__ __device__ inline int swz(int r) { return (r >> 2) & 3; }
+__host__ __device__ inline int swz(int r) {
+  const int q = (r >> 2) & 3;
+  return q ^ ((q & 1) << 1);
+}
 // Byte offset of logical chunk c of row r inside a tile.
 __host__ __device__ inline int tile_off(int r, int c) { return r * kStepK + ((c ^ swz(r)) << 4); }
 // Byte offset of the scale of row r (0..127), block b (0..1) inside a scale tile.

@@ -6,7 +6,8 @@
 // with both operands K-major, followed by the slice to the logical N and the
 // bias add of its §Purpose, folded into one epilogue).
 //
-// The K loop is tile_core.hpp's 256 x 256 tile.  Here:
+// The K loop is tile_core.hpp's 256 x 256 tile on 16x16x128 MFMAs
+// (mainloop16).  Here:
 //  * Workgroups are dispatched round-robin over the 8 XCDs; the tile index is
 //    remapped so that each XCD works on a contiguous, M-grouped range of tiles
 //    and its private L2 sees the reuse of weight and activation K-slices.
@@ -58,8 +59,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(
   const int ksl = KS / splits;                           // steps of this slice (multiple of 4)
   const size_t k0 = (size_t)split * ksl * kTileBytes, s0 = (size_t)split * ksl * kTileScaleBytes;
 
-  v16f acc[4][4];
-  tile::mainloop(st0, st1, st2, st3, wp + wa * op_stride + k0, wp + wb * op_stride + k0, qp + xa * op_stride + k0,
+  v4f acc[8][8];
+  tile::mainloop16(st0, st1, st2, st3, wp + wa * op_stride + k0, wp + wb * op_stride + k0, qp + xa * op_stride + k0,
                  qp + xb * op_stride + k0, wsp + wa * sc_stride + s0, wsp + wb * sc_stride + s0,
                  qsp + xa * sc_stride + s0, qsp + xb * sc_stride + s0, ksl, acc);
 

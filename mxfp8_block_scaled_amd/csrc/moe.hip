@@ -321,7 +321,7 @@ __global__ __launch_bounds__(tile::kThreads, 1) void moe_gemm1_kernel(
   tile::GatherX gx;
   {
     const int tid = threadIdx.x;
-    const int chunk = (tid & 3) ^ ((tid >> 4) & 3);
+    const int chunk = (tid & 3) ^ swz(tid >> 2);     // rows tid / 4 + 64 i share one swizzle
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = (tid >> 2) + 64 * i;

@@ -1,8 +1,10 @@
-// The K loop of the 256 x 256 block-scaled MXFP8 tile shared by the dense
-// layer's GEMM and the two grouped GEMMs of the MoE layer: both operands in
-// the packed tile layout of common.hpp, fp32 accumulators in AGPRs.
+// The K loops of the 256 x 256 block-scaled MXFP8 tile: mainloop16 (the
+// dense layer's GEMM, on 16x16x128 MFMAs, described at its definition) and
+// mainloop (the two grouped GEMMs of the MoE layer, on 32x32x64 MFMAs).  Both
+// read operands in the packed tile layout of common.hpp and keep fp32
+// accumulators in AGPRs.
 //
-// Design (gfx950):
+// Design of mainloop (gfx950):
 //  * Workgroup tile 256 (n, weight rows) x 256 (m, activation rows), 4 waves
 //    as 2 x 2, each wave 128 x 128 = 4 x 4 v_mfma_scale_f32_32x32x64_f8f6f4
 //    tiles.  The weight is the MFMA A operand, so lane (li, lg) of wave
@@ -65,12 +67,12 @@ __device__ inline void g2l_4(const void* g, const uint8_t* lds_wave_base) {
 
 using mxfp8::xcd_remap;
 
+// Wait until at most N of this wave's vector memory operations are
+// outstanding (they retire in issue order).
 template <int N>
 __device__ inline void wait_vmcnt() {
-  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else if constexpr (N == kLoadsPerStage) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-  else if constexpr (N == 2 * kLoadsPerStage) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(27)" ::: "memory");
+  static_assert(N >= 0 && N < 64, "vmcnt takes 0..63");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 // Row-gathered activation operand: instead of a packed group, the 16 bytes
@@ -83,55 +85,31 @@ struct GatherX {
   const uint8_t* p[4];
 };
 
-// acc = the tile's product over all KS 64-K steps.  wga / wgb: the packed
-// weight groups of tile rows 0-127 / 128-255 at step 0; xga / xgb: the packed
-// activation groups (kGatherX: unused, gx gives the rows instead); swa, swb,
-// sxa, sxb: the scale tiles of all four at step 0 (always packed).
-// KS must be a multiple of 4 and at least 4.  Every thread of the 256-thread
-// workgroup calls this; st0..st3 are the workgroup's four stage arrays.
-template <bool kGatherX = false>
-__device__ __forceinline__ void mainloop(uint8_t* st0, uint8_t* st1, uint8_t* st2, uint8_t* st3,
-                                         const uint8_t* wga, const uint8_t* wgb, const uint8_t* xga,
-                                         const uint8_t* xgb, const uint8_t* swa, const uint8_t* swb,
-                                         const uint8_t* sxa, const uint8_t* sxb, int KS, v16f (&acc)[4][4],
-                                         GatherX gx = {}) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wn = wave >> 1, wm = wave & 1;
-  const int li = lane & 31, lg = lane >> 5;
-  const uint8_t* w0 = wga + tid * 16;
-  const uint8_t* w1 = wgb + tid * 16;
-  const uint8_t* x0 = xga + tid * 16;
-  const uint8_t* x1 = xgb + tid * 16;
-  // Scale words: wave 0 weight rows 0-127, 1 weight rows 128-255, 2
-  // activation rows 0-127, 3 activation rows 128-255.
-  const uint8_t* ssrc = (wave == 0 ? swa : wave == 1 ? swb : wave == 2 ? sxa : sxb) + lane * 4;
+// This thread's share of one 64-K stage: nine copies, j = 0..3 the weight
+// rows (two 4 KiB runs of each 128-row group), 4..7 the activation rows, 8
+// the wave's 256-byte scale run (wave 0 weight rows 0-127, 1 weight rows
+// 128-255, 2 activation rows 0-127, 3 activation rows 128-255).
+template <bool kGatherX>
+struct StageSrc {
+  const uint8_t *w0, *w1, *x0, *x1, *ssrc;
+  GatherX gx;
+  int wave;
 
+  __device__ __forceinline__ StageSrc(const uint8_t* wga, const uint8_t* wgb, const uint8_t* xga,
+                                      const uint8_t* xgb, const uint8_t* swa, const uint8_t* swb,
+                                      const uint8_t* sxa, const uint8_t* sxb, GatherX g) {
+    const int tid = threadIdx.x;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    w0 = wga + tid * 16;
+    w1 = wgb + tid * 16;
+    x0 = xga + tid * 16;
+    x1 = xgb + tid * 16;
+    ssrc = (wave == 0 ? swa : wave == 1 ? swb : wave == 2 ? sxa : sxb) + (tid & 63) * 4;
+    gx = g;
+  }
 
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
-
-  // Fragments of one 64-deep K step (both operands, with the scale bytes of
-  // the lane's rows: lane group lg supplies MX block lg of the step).
-  struct Frags {
-    v8i a[4], b[4];
-    int sa, sb;     // scale bytes of the lane's 4 rows (byte i: row li + 32 i)
-  };
-  // Lane offsets inside a stage: rows R0 + 32 i share the swizzle of R0
-  // (swz depends on bits 2-3 of the row only), so fragment i is 2048 i bytes
-  // further; the scales of the lane's four rows are one 4-byte word.
-  const int offWa = tile_off(wn * 128 + li, lg), offWb = tile_off(wn * 128 + li, 2 + lg);
-  const int offXa = kOpBytes + tile_off(wm * 128 + li, lg), offXb = kOpBytes + tile_off(wm * 128 + li, 2 + lg);
-  const int offSw = 2 * kOpBytes + wn * kTileScaleBytes + scale_off(li, lg);
-  const int offSx = 2 * kOpBytes + 2 * kTileScaleBytes + wm * kTileScaleBytes + scale_off(li, lg);
-  auto rd16 = [](const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); };
-  // Copy j (0..8) of this thread's share of step ks into stage st.
-  auto dma_one = [&](int j, int ks, uint8_t* st) {
+  // Copy j of step ks into stage st.
+  __device__ __forceinline__ void issue(int j, int ks, uint8_t* st) const {
     uint8_t* base = st + wave * 1024;
     const size_t off = (size_t)ks * kTileBytes;
     switch (j) {
@@ -157,7 +135,50 @@ __device__ __forceinline__ void mainloop(uint8_t* st0, uint8_t* st1, uint8_t* st
         break;
       default: g2l_4(ssrc + (size_t)ks * kTileScaleBytes, st + 2 * kOpBytes + wave * 256); break;
     }
+  }
+};
+
+// acc = the tile's product over all KS 64-K steps.  wga / wgb: the packed
+// weight groups of tile rows 0-127 / 128-255 at step 0; xga / xgb: the packed
+// activation groups (kGatherX: unused, gx gives the rows instead); swa, swb,
+// sxa, sxb: the scale tiles of all four at step 0 (always packed).
+// KS must be a multiple of 4 and at least 4.  Every thread of the 256-thread
+// workgroup calls this; st0..st3 are the workgroup's four stage arrays.
+template <bool kGatherX = false>
+__device__ __forceinline__ void mainloop(uint8_t* st0, uint8_t* st1, uint8_t* st2, uint8_t* st3,
+                                         const uint8_t* wga, const uint8_t* wgb, const uint8_t* xga,
+                                         const uint8_t* xgb, const uint8_t* swa, const uint8_t* swb,
+                                         const uint8_t* sxa, const uint8_t* sxb, int KS, v16f (&acc)[4][4],
+                                         GatherX gx = {}) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave >> 1, wm = wave & 1;
+  const int li = lane & 31, lg = lane >> 5;
+  const StageSrc<kGatherX> src(wga, wgb, xga, xgb, swa, swb, sxa, sxb, gx);
+
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+
+  // Fragments of one 64-deep K step (both operands, with the scale bytes of
+  // the lane's rows: lane group lg supplies MX block lg of the step).
+  struct Frags {
+    v8i a[4], b[4];
+    int sa, sb;     // scale bytes of the lane's 4 rows (byte i: row li + 32 i)
   };
+  // Lane offsets inside a stage: rows R0 + 32 i share the swizzle of R0
+  // (swz depends on bits 2-3 of the row only), so fragment i is 2048 i bytes
+  // further; the scales of the lane's four rows are one 4-byte word.
+  const int offWa = tile_off(wn * 128 + li, lg), offWb = tile_off(wn * 128 + li, 2 + lg);
+  const int offXa = kOpBytes + tile_off(wm * 128 + li, lg), offXb = kOpBytes + tile_off(wm * 128 + li, 2 + lg);
+  const int offSw = 2 * kOpBytes + wn * kTileScaleBytes + scale_off(li, lg);
+  const int offSx = 2 * kOpBytes + 2 * kTileScaleBytes + wm * kTileScaleBytes + scale_off(li, lg);
+  auto rd16 = [](const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); };
+  auto dma_one = [&](int j, int ks, uint8_t* st) { src.issue(j, ks, st); };
   // Part j (0..15) of the fragment reads of a stage (parts 8..15 are empty).
   // The scale words go first: read after the fragments (parts 8, 9) they
   // cost the loop about 12 % (measured).
@@ -241,12 +262,223 @@ __device__ __forceinline__ void mainloop(uint8_t* st0, uint8_t* st1, uint8_t* st
 }
 
 
+// c += A x B on v_mfma_scale_f32_16x16x128_f8f6f4 with E4M3 operands, the
+// accumulator updated in place in AGPRs.  Written as inline assembly because
+// the compiler, given the builtin in this loop, gives most of the 64
+// accumulators a new destination on every MFMA and then shuffles them with
+// hundreds of AGPR/VGPR copies per step.  op_sel / op_sel_hi carry bit 0 /
+// bit 1 of the byte each scale operand is taken from.  The assembly is
+// opaque to the compiler's hazard checks, so it carries its own: two wait
+// states in front (a VALU write of a source register needs them before an
+// MFMA reads it; the operands normally come straight from LDS reads, which
+// the compiler's lgkmcnt waits cover); an accumulator is read again only 64
+// MFMAs later inside the loop, and the loop ends with enough wait states
+// before the epilogue reads the accumulators.
+template <int kSelA, int kSelB>
+__device__ __forceinline__ void mfma16(v4f& c, const v8i& a, const v8i& b, int sa, int sb) {
+  asm volatile("s_nop 1\n\tv_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[%5,%6,0] op_sel_hi:[%7,%8,0]"
+               : "+a"(c)
+               : "v"(a), "v"(b), "v"(sa), "v"(sb), "n"(kSelA & 1), "n"(kSelB & 1), "n"(kSelA >> 1), "n"(kSelB >> 1));
+}
+
+// The same 256 x 256 tile on v_mfma_scale_f32_16x16x128_f8f6f4.  A 16x16x128
+// MFMA does the work of half a 32x32x64 one with the same operand bytes per
+// flop and a quarter of the accumulator traffic, and on gfx950 the chip
+// sustains a higher clock on it under a full MFMA load (measured: 8 % more
+// MFMA throughput than 32x32x64 at the power limit).
+//
+//  * Each wave's 128 x 128 block is 8 x 8 MFMA tiles of 16 x 16; lane (i, g)
+//    (i = lane % 16, g = lane / 16) ends with acc[a][b][j] =
+//    D[n = wn*128 + 16a + 4g + j][m = wm*128 + 16b + i].
+//  * One MFMA consumes 128 K: bytes K [16g, 16g+16) come from chunk g of the
+//    even 64-K tile and K [64+16g, ...) from chunk g of the odd one, so a
+//    128-K step reads a pair of the 64-K stages (st0, st1 or st2, st3); the
+//    global layout and the copies are those of the 64-K loop.
+//  * Per step: all eight weight fragments (64 registers) and the scale words
+//    stay in registers for the whole step; the activation fragment of tile
+//    column b + 2 is read from LDS during the eight MFMAs of column b.  So the
+//    weight half and the scales of a stage pair are consumed at the end of
+//    the previous step, the activation half only during the step: the
+//    weight-and-scale copies of step p + 2 go out after a barrier early in
+//    step p (after its first column), the activation copies after a second
+//    barrier before column 6, once every wave holds its last activation
+//    fragment of the pair.
+//  * Scale words: lane (i, g) supplies MX block g of the step, i.e. block
+//    g % 2 of tile g / 2; word e holds rows 16e + i + 32k (byte k), so tile a
+//    uses word a % 2, op_sel a / 2.
+template <bool kGatherX = false>
+__device__ __forceinline__ void mainloop16(uint8_t* st0, uint8_t* st1, uint8_t* st2, uint8_t* st3,
+                                           const uint8_t* wga, const uint8_t* wgb, const uint8_t* xga,
+                                           const uint8_t* xgb, const uint8_t* swa, const uint8_t* swb,
+                                           const uint8_t* sxa, const uint8_t* sxb, int KS, v4f (&acc)[8][8],
+                                           GatherX gx = {}) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = wave >> 1, wm = wave & 1;
+  const int li = lane & 15, lg = lane >> 4;
+  const StageSrc<kGatherX> src(wga, wgb, xga, xgb, swa, swb, sxa, sxb, gx);
+
+#pragma unroll
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int b = 0; b < 8; ++b) acc[a][b] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // Registers carried from step to step: the eight weight fragments and the
+  // scale words of the current step, and four activation fragment buffers
+  // (column b in buffer b % 4; columns 0 and 1 are in place at the start of
+  // a step).  A weight fragment is overwritten with the next step's right
+  // after its last MFMA.
+  struct State {
+    v8i a[8];
+    v8i bf[4];
+    int sa[2], sb[2];
+  };
+  // Rows R0 + 16 a share the swizzle of R0, so tile a is 1024 a bytes further.
+  const int offA = tile_off(wn * 128 + li, lg);
+  const int offB = kOpBytes + tile_off(wm * 128 + li, lg);
+  // Scale word e of the lane: tile lg / 2 of the pair, block lg % 2.
+  const int offS = 2 * kOpBytes + scale_off(li, lg & 1);
+  const int swA = wn * kTileScaleBytes, swB = 2 * kTileScaleBytes + wm * kTileScaleBytes;
+  auto rd16 = [](const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); };
+  auto frag = [&](const uint8_t* ev, const uint8_t* od, int off) {
+    const uint4 lo = rd16(ev + off), hi = rd16(od + off);
+    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  };
+  auto rd_scale = [&](const uint8_t* ev, const uint8_t* od, int base, int e) {
+    const uint8_t* st = (lg >> 1) ? od : ev;
+    return *reinterpret_cast<const int*>(st + offS + base + 128 * e);
+  };
+  // Weight-and-scale copies of step q into pair (ev, od): ten per thread;
+  // activation copies: eight.
+  auto issue_w = [&](int k, int q, uint8_t* ev, uint8_t* od) {
+    const int t = k / 5, c = k % 5;
+    src.issue(c < 4 ? c : 8, 2 * q + t, t ? od : ev);
+  };
+  auto issue_x = [&](int k, int q, uint8_t* ev, uint8_t* od) {
+    const int t = k >> 2;
+    src.issue(4 + (k & 3), 2 * q + t, t ? od : ev);
+  };
+
+  // One 128-K step p on pair (ev, od); (nev, nod) holds step p + 1.  No
+  // LDS wait sits at a step boundary: the reads of step p + 1 issued in the
+  // last columns have at least eight MFMAs to land before their first use,
+  // and activation column b + 2 is read during column b.
+  auto step = [&](auto do_issue, auto do_next, int p, uint8_t* ev, uint8_t* od, const uint8_t* nev,
+                  const uint8_t* nod, State& S) {
+    int nsa[2], nsb[2];
+    static_for<0, 64>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      constexpr int b = j >> 3, a = j & 7;
+      if constexpr (j == 8) {
+        // Every wave has read this pair's weight half and scales (end of the
+        // previous step): the copies of step p + 2 may overwrite them.
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (j == 48) {
+        // Columns 6 and 7: every wave holds its last activation fragment of
+        // this pair, and step p + 1 has landed (the only copies issued since
+        // are the ten weight-and-scale copies of step p + 2).
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        wait_vmcnt<decltype(do_issue)::value ? 10 : 0>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      mfma16<(a >> 1), (b >> 1)>(acc[a][b], S.a[a], S.bf[b & 3], S.sa[a & 1], S.sb[b & 1]);
+      if constexpr (decltype(do_issue)::value) {
+        if constexpr (j >= 8 && j < 18) issue_w(j - 8, p + 2, ev, od);
+        if constexpr (j >= 48 && j < 56) issue_x(j - 48, p + 2, ev, od);
+      }
+      if constexpr (a == 0 && b < 6) S.bf[(b + 2) & 3] = frag(ev, od, offB + 1024 * (b + 2));
+      if constexpr (decltype(do_next)::value) {
+        if constexpr (j == 48) {
+          nsa[0] = rd_scale(nev, nod, swA, 0);
+          nsa[1] = rd_scale(nev, nod, swA, 1);
+          S.bf[0] = frag(nev, nod, offB);              // column 4 was the last user
+        }
+        if constexpr (j == 49) { nsb[0] = rd_scale(nev, nod, swB, 0); nsb[1] = rd_scale(nev, nod, swB, 1); }
+        if constexpr (j == 56) S.bf[1] = frag(nev, nod, offB + 1024);   // column 5 was the last user
+        if constexpr (j >= 56) S.a[a] = frag(nev, nod, offA + 1024 * a);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if constexpr (decltype(do_next)::value) {
+      S.sa[0] = nsa[0]; S.sa[1] = nsa[1];
+      S.sb[0] = nsb[0]; S.sb[1] = nsb[1];
+    }
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+
+  const int P = KS / 2;      // 128-K steps: even, at least 2
+  State S;
+  // Issue order: weights+scales of step 0, activations of step 0, then step 1.
+#pragma unroll
+  for (int k = 0; k < 10; ++k) issue_w(k, 0, st0, st1);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) issue_x(k, 0, st0, st1);
+#pragma unroll
+  for (int k = 0; k < 10; ++k) issue_w(k, 1, st2, st3);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) issue_x(k, 1, st2, st3);
+  asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  S.sa[0] = rd_scale(st0, st1, swA, 0);
+  S.sa[1] = rd_scale(st0, st1, swA, 1);
+  S.sb[0] = rd_scale(st0, st1, swB, 0);
+  S.sb[1] = rd_scale(st0, st1, swB, 1);
+#pragma unroll
+  for (int a = 0; a < 8; ++a) S.a[a] = frag(st0, st1, offA + 1024 * a);
+  S.bf[0] = frag(st0, st1, offB);
+  S.bf[1] = frag(st0, st1, offB + 1024);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  int p = 0;
+  for (; p + 4 <= P; p += 2) {
+    step(T{}, T{}, p, st0, st1, st2, st3, S);
+    step(T{}, T{}, p + 1, st2, st3, st0, st1, S);
+  }
+  step(F{}, T{}, p, st0, st1, st2, st3, S);
+  step(F{}, F{}, p + 1, st2, st3, st0, st1, S);
+  // The last MFMAs must retire before anything reads the accumulators.
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+}
+
+// Staging of one 64-row half (m = 64 h .. 64 h + 63 of the wave's block) into
+// the wave's LDS buffer as rows of 128 fp32 n values, pitch kEpiPitch.
+template <int kPitch>
+__device__ __forceinline__ void stage_half(float* stage, const v16f (&acc)[4][4], int h, int lane) {
+  const int li = lane & 31, lg = lane >> 5;
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const v16f& v = acc[a][2 * h + b2];
+        float4 f = make_float4(v[4 * rr], v[4 * rr + 1], v[4 * rr + 2], v[4 * rr + 3]);
+        *reinterpret_cast<float4*>(stage + (32 * b2 + li) * kPitch + 32 * a + 8 * rr + 4 * lg) = f;
+      }
+}
+template <int kPitch>
+__device__ __forceinline__ void stage_half(float* stage, const v4f (&acc)[8][8], int h, int lane) {
+  const int li = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int b2 = 0; b2 < 4; ++b2) {
+      const v4f& v = acc[a][4 * h + b2];
+      *reinterpret_cast<float4*>(stage + (16 * b2 + li) * kPitch + 16 * a + 4 * lg) =
+          make_float4(v[0], v[1], v[2], v[3]);
+    }
+}
+
 constexpr int kEpiPitch = 132;                        // floats per staged row (128 + 4 pad)
 
 // The layer's epilogue for one tile: y[m][n] = bf16(acc + bias[n]) for tile
 // rows m with row0 + m < row_end and columns col0 + n < N (bias may be null).
-// Lane (li, lg) holds n = 32a + 8(r/4) + 4lg + r%4, m = 32b + li of its
-// wave's 128 x 128 block.  Each wave stages 64 rows (b = 2h, 2h+1) at a time
+// acc is either loop's accumulator set (v16f[4][4] of the 32x32x64 loop or
+// v4f[8][8] of the 16x16x128 one).  Each wave stages 64 rows at a time
 // in its own LDS stage buffer, then reads them back as 4 consecutive n per
 // lane (a wave instruction covers two whole 256-byte output row segments),
 // adds the bias in fp32 and rounds once to bf16.  vec_store: y is 8-byte
@@ -258,20 +490,19 @@ constexpr int kEpiPitch = 132;                        // floats per staged row (
 // tile row m goes to output row row_map[m] (an LDS array of 256 ints; a
 // negative entry is not stored) instead of row0 + m, row_end is not used,
 // and every column of the tile must be < N with vec_store set.
-template <bool kRowScale = false, typename OutT = uint16_t, bool kRowMap = false>
+template <bool kRowScale = false, typename OutT = uint16_t, bool kRowMap = false, typename Acc>
 __device__ __forceinline__ void store_bf16(uint8_t* st0, uint8_t* st1, uint8_t* st2, uint8_t* st3,
-                                           const v16f (&acc)[4][4], OutT* __restrict__ y, int64_t ldy,
+                                           const Acc& acc, OutT* __restrict__ y, int64_t ldy,
                                            int row0, int row_end, int col0, int N,
                                            const uint16_t* __restrict__ bias, int vec_store,
                                            const float* row_scale = nullptr, const int* row_map = nullptr) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wave >> 1, wm = wave & 1;
-  const int li = lane & 31, lg = lane >> 5;
-  // Lane (li, lg) holds n = 32a + 8(r/4) + 4lg + r%4, m = 32b + li of the
-  // wave's 128 x 128 block.  Stage 64 rows (b = 2h, 2h+1) at a time in this
-  // wave's own LDS buffer, then read them back as 4 consecutive n per lane
-  // (a wave instruction covers two whole 256-byte output row segments).
+  // Stage 64 rows of the wave's 128 x 128 block at a time in this wave's own
+  // LDS buffer (stage_half, for either accumulator layout), then read them
+  // back as 4 consecutive n per lane (a wave instruction covers two whole
+  // 256-byte output row segments).
   float* stage = reinterpret_cast<float*>(wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3);
   const int n4 = lane & 31;
   const int rsub = lane >> 5;
@@ -287,16 +518,7 @@ __device__ __forceinline__ void store_bf16(uint8_t* st0, uint8_t* st1, uint8_t* 
   const bool full_n = nl + 3 < N;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const v16f& v = acc[a][2 * h + b2];
-          float4 f = make_float4(v[4 * rr], v[4 * rr + 1], v[4 * rr + 2], v[4 * rr + 3]);
-          *reinterpret_cast<float4*>(stage + (32 * b2 + li) * kEpiPitch + 32 * a + 8 * rr + 4 * lg) = f;
-        }
+    stage_half<kEpiPitch>(stage, acc, h, lane);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     const int m_first = row0 + wm * 128 + 64 * h + rsub;
     const int rows_left = row_end - m_first;          // this lane's rows are m_first + 2 it
