@@ -67,6 +67,34 @@ __device__ inline void g2l_4(const void* g, const uint8_t* lds_wave_base) {
 
 using mxfp8::xcd_remap;
 
+typedef int i4v __attribute__((ext_vector_type(4)));
+
+// Buffer resource (raw, untyped) over [base, base + bytes): loads past the
+// end return zeros instead of touching memory.
+__device__ inline i4v buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  i4v r;
+  r[0] = (int)(uint32_t)b;
+  r[1] = (int)(uint32_t)(b >> 32);     // stride 0
+  r[2] = (int)bytes;
+  r[3] = 0x00020000;                   // 32-bit data format, no swizzle
+  return r;
+}
+// Buffer -> LDS copies: lane l moves 16 (or 4) bytes from base + voff + soff
+// to lds_wave_base + 16 l (or 4 l).  The per-lane offset is fixed for the
+// whole loop and the step advances in the scalar offset, so a copy costs no
+// vector address arithmetic.
+__device__ inline void b2l_16(uint32_t voff, i4v rsrc, uint32_t soff, const uint8_t* lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc),
+               "s"(soff), "s"(lds_addr(lds_wave_base))
+               : "memory", "m0");
+}
+__device__ inline void b2l_4(uint32_t voff, i4v rsrc, uint32_t soff, const uint8_t* lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc),
+               "s"(soff), "s"(lds_addr(lds_wave_base))
+               : "memory", "m0");
+}
+
 // Wait until at most N of this wave's vector memory operations are
 // outstanding (they retire in issue order).
 template <int N>
@@ -134,6 +162,45 @@ struct StageSrc {
         else g2l_16(x1 + off + 4096, base + kOpBytes + 12288);
         break;
       default: g2l_4(ssrc + (size_t)ks * kTileScaleBytes, st + 2 * kOpBytes + wave * 256); break;
+    }
+  }
+};
+
+// The same nine copies per 64-K stage as StageSrc, as buffer loads over the
+// KS steps of each operand group (packed operands only).
+struct BufSrc {
+  i4v w0, w1, x0, x1, sc;
+  uint32_t voff, soff_lane;
+  int wave;
+
+  __device__ __forceinline__ BufSrc(const uint8_t* wga, const uint8_t* wgb, const uint8_t* xga,
+                                    const uint8_t* xgb, const uint8_t* swa, const uint8_t* swb,
+                                    const uint8_t* sxa, const uint8_t* sxb, int KS) {
+    const int tid = threadIdx.x;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t data = (uint32_t)KS * kTileBytes, scales = (uint32_t)KS * kTileScaleBytes;
+    w0 = buffer_rsrc(wga, data);
+    w1 = buffer_rsrc(wgb, data);
+    x0 = buffer_rsrc(xga, data);
+    x1 = buffer_rsrc(xgb, data);
+    sc = buffer_rsrc(wave == 0 ? swa : wave == 1 ? swb : wave == 2 ? sxa : sxb, scales);
+    voff = (uint32_t)tid * 16;
+    soff_lane = (uint32_t)(tid & 63) * 4;
+  }
+
+  __device__ __forceinline__ void issue(int j, int ks, uint8_t* st) const {
+    uint8_t* base = st + wave * 1024;
+    const uint32_t off = (uint32_t)ks * kTileBytes;
+    switch (j) {
+      case 0: b2l_16(voff, w0, off, base); break;
+      case 1: b2l_16(voff + 4096, w0, off, base + 4096); break;
+      case 2: b2l_16(voff, w1, off, base + 8192); break;
+      case 3: b2l_16(voff + 4096, w1, off, base + 12288); break;
+      case 4: b2l_16(voff, x0, off, base + kOpBytes); break;
+      case 5: b2l_16(voff + 4096, x0, off, base + kOpBytes + 4096); break;
+      case 6: b2l_16(voff, x1, off, base + kOpBytes + 8192); break;
+      case 7: b2l_16(voff + 4096, x1, off, base + kOpBytes + 12288); break;
+      default: b2l_4(soff_lane, sc, (uint32_t)ks * kTileScaleBytes, st + 2 * kOpBytes + wave * 256); break;
     }
   }
 };
@@ -306,17 +373,15 @@ __device__ __forceinline__ void mfma16(v4f& c, const v8i& a, const v8i& b, int s
 //  * Scale words: lane (i, g) supplies MX block g of the step, i.e. block
 //    g % 2 of tile g / 2; word e holds rows 16e + i + 32k (byte k), so tile a
 //    uses word a % 2, op_sel a / 2.
-template <bool kGatherX = false>
 __device__ __forceinline__ void mainloop16(uint8_t* st0, uint8_t* st1, uint8_t* st2, uint8_t* st3,
                                            const uint8_t* wga, const uint8_t* wgb, const uint8_t* xga,
                                            const uint8_t* xgb, const uint8_t* swa, const uint8_t* swb,
-                                           const uint8_t* sxa, const uint8_t* sxb, int KS, v4f (&acc)[8][8],
-                                           GatherX gx = {}) {
+                                           const uint8_t* sxa, const uint8_t* sxb, int KS, v4f (&acc)[8][8]) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wave >> 1, wm = wave & 1;
   const int li = lane & 15, lg = lane >> 4;
-  const StageSrc<kGatherX> src(wga, wgb, xga, xgb, swa, swb, sxa, sxb, gx);
+  const BufSrc src(wga, wgb, xga, xgb, swa, swb, sxa, sxb, KS);
 
 #pragma unroll
   for (int a = 0; a < 8; ++a)
