@@ -16,6 +16,8 @@ namespace {
 constexpr int kMaxDevices = 64;
 // Per-device cached answer to "is this a gfx950": 0 unknown, 1 yes, 2 no.
 std::atomic<int> g_dev_ok[kMaxDevices];
+// Per-device compute-unit count (0 = not yet queried).
+std::atomic<int> g_dev_cus[kMaxDevices];
 std::atomic<int> g_force_path{0};
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -28,6 +30,7 @@ int check_device() {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MXFP8_E_DEVICE;
     s = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_dev_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
     g_dev_ok[dev].store(s, std::memory_order_relaxed);
   }
   return s == 1 ? MXFP8_OK : MXFP8_E_DEVICE;
@@ -117,6 +120,21 @@ bool use_skinny(int64_t M, int64_t K) {
 }
 
 }  // namespace
+
+// Compute units of the current device (the persistent GEMM's grid); the
+// device check caches it on the first call of any entry point.
+int mxfp8::device_cu_count() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int n = g_dev_cus[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    hipDeviceProp_t prop;
+    n = (hipGetDeviceProperties(&prop, dev) == hipSuccess && prop.multiProcessorCount > 0) ? prop.multiProcessorCount
+                                                                                         : 256;
+    g_dev_cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 extern "C" {
 

@@ -11,8 +11,9 @@
 //  * Workgroups are dispatched round-robin over the 8 XCDs; the tile index is
 //    remapped so that each XCD works on a contiguous, M-grouped range of tiles
 //    and its private L2 sees the reuse of weight and activation K-slices.
-//  * Epilogue (tile::store_bf16): fp32 staged through LDS, bias added in fp32,
-//    one rounding to bf16, 8-byte stores covering whole 256-byte row segments.
+//  * Epilogue (tile::store16): fp32 staged through LDS, bias added in fp32,
+//    one rounding to bf16, 16-byte non-temporal stores covering whole
+//    256-byte row segments.
 #include "common.hpp"
 #include "launch.hpp"
 #include "tile_core.hpp"
@@ -65,12 +66,60 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(
                  qsp + xa * sc_stride + s0, qsp + xb * sc_stride + s0, ksl, acc);
 
   if (splits == 1) {
-    tile::store_bf16(st0, st1, st2, st3, acc, y, ldy, tm * 256, M, tn * 256, N, bias, vec_store);
+    tile::store16(st0, st1, st2, st3, acc, y, ldy, tm * 256, M, tn * 256, N, bias, vec_store);
   } else {
     // fp32 partial of this slice: part[split][m][n], row stride ldp (% 4 == 0).
-    tile::store_bf16<false, float>(st0, st1, st2, st3, acc, part + (size_t)split * M * ldp, ldp, tm * 256, M,
-                                   tn * 256, N, nullptr, 1);
+    tile::store16(st0, st1, st2, st3, acc, part + (size_t)split * M * ldp, ldp, tm * 256, M, tn * 256, N,
+                  (const uint16_t*)nullptr, 1);
   }
+}
+
+// The same GEMM as a persistent kernel (no split-K): workgroup w runs tiles
+// w, w + G, w + 2G, ... of the same XCD-contiguous, M-grouped order, with the
+// copies of each next tile overlapping the end of the current one
+// (tile::persistent16).  G is a multiple of 8, so dispatch index i G + w
+// lands on the XCD that xcd_remap assigns to it.
+__global__ __launch_bounds__(kThreads, 1) void gemm_persistent_kernel(
+    const uint8_t* __restrict__ qp, const uint8_t* __restrict__ qsp, int M, int K,
+    const uint8_t* __restrict__ wp, const uint8_t* __restrict__ wsp, int N, int GN, int GM,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int64_t ldy, int tiles_m, int tiles_n,
+    int vec_store) {
+  __shared__ __attribute__((aligned(16))) uint8_t st0[kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t st3[kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t epi[tile::kEpiBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t blds[tile::kBiasBytes];
+
+  const int total = tiles_m * tiles_n;
+  const int KS = K / kStepK;
+  const size_t op_stride = (size_t)KS * kTileBytes;
+  const size_t sc_stride = (size_t)KS * kTileScaleBytes;
+  auto decode = [&](int bidx) {
+    const int logical = tile::xcd_remap(bidx, total);
+    const int per_group = kGroupM * tiles_n;
+    const int group = logical / per_group;
+    const int first_m = group * kGroupM;
+    const int gm = min(tiles_m - first_m, kGroupM);
+    const int in_group = logical - group * per_group;
+    const int tm = first_m + in_group % gm;
+    const int tn = in_group / gm;
+    const int wa = min(2 * tn, GN - 1), wb = min(2 * tn + 1, GN - 1);
+    const int xa = min(2 * tm, GM - 1), xb = min(2 * tm + 1, GM - 1);
+    tile::Job16 j;
+    j.wga = wp + wa * op_stride;
+    j.wgb = wp + wb * op_stride;
+    j.xga = qp + xa * op_stride;
+    j.xgb = qp + xb * op_stride;
+    j.swa = wsp + wa * sc_stride;
+    j.swb = wsp + wb * sc_stride;
+    j.sxa = qsp + xa * sc_stride;
+    j.sxb = qsp + xb * sc_stride;
+    j.row0 = tm * 256;
+    j.col0 = tn * 256;
+    return j;
+  };
+  tile::persistent16(st0, st1, st2, st3, epi, blds, total, KS, decode, y, ldy, M, N, bias, vec_store);
 }
 
 // y[m][n] = bf16( sum_s part[s][m][n] + bias[n] ), slices added in order.
@@ -113,8 +162,17 @@ int launch_gemm_tile(const void* qp, const void* sp, int64_t M, int64_t K, const
   const int64_t GM = (M + kGroupRows - 1) / kGroupRows;
   const int tiles_n = (int)((GN + 1) / 2);
   const int tiles_m = (int)((GM + 1) / 2);
-  const int vec = (ldy % 4 == 0) && (((uintptr_t)y & 7) == 0);
+  const int vec = (ldy % 8 == 0 && ((uintptr_t)y & 15) == 0) ? 2 : (ldy % 4 == 0 && ((uintptr_t)y & 7) == 0) ? 1 : 0;
   const int64_t ldp = (N + 3) / 4 * 4;
+  if (splits == 1) {
+    const int total = tiles_m * tiles_n;
+    const int cus = device_cu_count();
+    const int grid = total <= cus ? total : (cus >= 8 ? cus - cus % 8 : cus);
+    hipLaunchKernelGGL(gemm_persistent_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, (const uint8_t*)qp,
+                       (const uint8_t*)sp, (int)M, (int)K, (const uint8_t*)wp, (const uint8_t*)wsp, (int)N, (int)GN,
+                       (int)GM, (const uint16_t*)bias, (uint16_t*)y, ldy, tiles_m, tiles_n, vec);
+    return hipGetLastError() == hipSuccess ? 0 : -7;
+  }
   hipLaunchKernelGGL(gemm_tile_kernel, dim3((unsigned)(tiles_m * tiles_n * splits)), dim3(kThreads), 0, stream,
                      (const uint8_t*)qp, (const uint8_t*)sp, (int)M, (int)K, (const uint8_t*)wp,
                      (const uint8_t*)wsp, (int)N, (int)GN, (int)GM, (const uint16_t*)bias, (uint16_t*)y, ldy,

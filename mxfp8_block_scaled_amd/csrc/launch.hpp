@@ -32,6 +32,7 @@ int launch_unpack_weight(const void* wp, const void* sp, int64_t N, int64_t K, v
 // workgroups per tile: fp32 partials go to part (splits * M * round_up(N, 4)
 // floats), then one reduce kernel adds them with the bias into y.
 constexpr int kMaxSplitK = 8;
+int device_cu_count();
 int gemm_tile_splits(int64_t M, int64_t N, int64_t K);
 int launch_gemm_tile(const void* qp, const void* sp, int64_t M, int64_t K, const void* wp, const void* wsp,
                      int64_t N, const void* bias, void* y, int64_t ldy, hipStream_t stream, int splits = 1,

@@ -73,10 +73,12 @@ typedef int i4v __attribute__((ext_vector_type(4)));
 // end return zeros instead of touching memory.
 __device__ inline i4v buffer_rsrc(const void* base, uint32_t bytes) {
   const uint64_t b = (uint64_t)(uintptr_t)base;
+  // The descriptor lives in scalar registers: every lane holds the same
+  // value, and readfirstlane says so to the compiler.
   i4v r;
-  r[0] = (int)(uint32_t)b;
-  r[1] = (int)(uint32_t)(b >> 32);     // stride 0
-  r[2] = (int)bytes;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));     // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
   r[3] = 0x00020000;                   // 32-bit data format, no swizzle
   return r;
 }
@@ -172,6 +174,8 @@ struct BufSrc {
   i4v w0, w1, x0, x1, sc;
   uint32_t voff, soff_lane;
   int wave;
+
+  BufSrc() = default;
 
   __device__ __forceinline__ BufSrc(const uint8_t* wga, const uint8_t* wgb, const uint8_t* xga,
                                     const uint8_t* xgb, const uint8_t* swa, const uint8_t* swb,
@@ -650,6 +654,362 @@ __device__ __forceinline__ void store_bf16(uint8_t* st0, uint8_t* st1, uint8_t* 
     }
     // The next half overwrites the same rows: finish the reads first.
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+}
+
+// Epilogue of the 16x16x128 loop (the dense layer): y[m][n] = OutT(acc +
+// bias[n]) for tile rows m with row0 + m < row_end and columns col0 + n < N.
+// OutT = uint16_t: bf16 (one rounding after the fp32 bias add), written with
+// non-temporal stores (the output is not read again, so it need not displace
+// operand tiles in L2); OutT = float: the fp32 values (split-K partials; bias
+// must be null).  Each wave stages 64 rows of its 128 x 128 block at a time in
+// its own LDS stage buffer and reads them back so that a lane holds 8
+// consecutive columns of one row: lanes 16G + 8r + q (G = 0..3, r = 0..1,
+// q = 0..7) take row 2 (G / 2) + r of a 4-row pass and columns
+// 64 (G % 2) + 8 q ..+7; a store instruction then covers 4 whole 256-byte
+// row segments (bf16), and the 16 lanes of a read group hit 16 distinct LDS
+// bank quads (the pitch of 132 floats shifts the second row by one quad).
+// Reads are batched eight passes at a time before one wait.  vec_store: 2 =
+// y 16-byte aligned and ldy % 8 == 0, 1 = 8-byte aligned and ldy % 4 == 0,
+// 0 = neither.  The stage buffers must be free (the K loop is over in every
+// wave).
+template <typename OutT>
+__device__ __forceinline__ void store16(uint8_t* st0, uint8_t* st1, uint8_t* st2, uint8_t* st3,
+                                        const v4f (&acc)[8][8], OutT* __restrict__ y, int64_t ldy, int row0,
+                                        int row_end, int col0, int N, const uint16_t* __restrict__ bias,
+                                        int vec_store) {
+  typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = wave >> 1, wm = wave & 1;
+  float* stage = reinterpret_cast<float*>(wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3);
+  const int G = lane >> 4, r = (lane >> 3) & 1, q = lane & 7;
+  const int prow = 2 * (G >> 1) + r;
+  const int nloc = 64 * (G & 1) + 8 * q;
+  const int nl = col0 + wn * 128 + nloc;
+  const bool full8 = nl + 7 < N;
+  float bv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float b = 0.0f;
+    if (bias != nullptr) b = __uint_as_float((uint32_t)bias[min(nl + e, N - 1)] << 16);
+    bv[e] = (nl + e < N) ? b : 0.0f;
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    stage_half<kEpiPitch>(stage, acc, h, lane);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int mbase = row0 + wm * 128 + 64 * h + prow;     // this lane's rows: mbase + 4 it
+#pragma unroll
+    for (int batch = 0; batch < 2; ++batch) {
+      float4 lo[8], hi[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float* src = stage + (prow + 4 * (8 * batch + k)) * kEpiPitch + nloc;
+        lo[k] = *reinterpret_cast<const float4*>(src);
+        hi[k] = *reinterpret_cast<const float4*>(src + 4);
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int m = mbase + 4 * (8 * batch + k);
+        if (m >= row_end || nl >= N) continue;
+        const float v[8] = {lo[k].x + bv[0], lo[k].y + bv[1], lo[k].z + bv[2], lo[k].w + bv[3],
+                            hi[k].x + bv[4], hi[k].y + bv[5], hi[k].z + bv[6], hi[k].w + bv[7]};
+        OutT* d = y + (size_t)m * ldy + nl;
+        if constexpr (sizeof(OutT) == 4) {
+          if (vec_store && full8) {
+            *reinterpret_cast<float4*>(d) = make_float4(v[0], v[1], v[2], v[3]);
+            *reinterpret_cast<float4*>(d + 4) = make_float4(v[4], v[5], v[6], v[7]);
+          } else {
+            for (int e = 0; e < 8; ++e)
+              if (nl + e < N) d[e] = v[e];
+          }
+        } else {
+          const u4v w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                         pack_bf16x2(v[6], v[7])};
+          if (vec_store == 2 && full8) {
+            __builtin_nontemporal_store(w, reinterpret_cast<u4v*>(d));
+          } else if (vec_store == 1 && full8) {
+            *reinterpret_cast<uint2*>(d) = make_uint2(w[0], w[1]);
+            *reinterpret_cast<uint2*>(d + 4) = make_uint2(w[2], w[3]);
+          } else {
+            for (int e = 0; e < 8; ++e)
+              if (nl + e < N) d[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Persistent form of the 16x16x128 loop for the dense layer.  A workgroup
+// runs tiles blockIdx.x, blockIdx.x + gridDim.x, ... and the copy stream
+// never stops at a tile boundary: the last two steps of a tile copy the next
+// tile's first two steps (the same slots and stage pairs as inside a tile),
+// and the last step reads the next tile's first fragments.  The epilogue then
+// runs with the next tile's data already in LDS and in registers, so no tile
+// after the first waits for its prologue copies.  The epilogue stages through
+// its own small LDS region (bf16, 16 rows per pass) instead of the stage
+// buffers, which hold the next tile by then.  The bias of a tile (its 256
+// columns, zeros past N) is copied into one of two LDS slots together with
+// the tile's second step.
+// ---------------------------------------------------------------------------
+constexpr int kEpiRows = 16;                          // rows per staging pass
+constexpr int kEpiPitchH = 136;                       // bf16 per staged row (128 + 8 pad)
+constexpr int kEpiWaveBytes = kEpiRows * kEpiPitchH * 2;   // 4352
+constexpr int kEpiBytes = 4 * kEpiWaveBytes;          // 17408
+constexpr int kBiasSlot = 4 * 256;                    // one tile's bias: 256 B per wave
+constexpr int kBiasBytes = 2 * kBiasSlot;
+
+struct Job16 {
+  const uint8_t *wga, *wgb, *xga, *xgb, *swa, *swb, *sxa, *sxb;
+  int row0, col0;
+};
+
+// Resource over the bias of columns [col0, col0 + 256) that exist (none if
+// bias is null): loads past the end read zeros.
+__device__ inline i4v bias_rsrc(const uint16_t* bias, int col0, int N) {
+  if (bias == nullptr) return buffer_rsrc(nullptr, 0);
+  const int valid = max(0, min(256, N - col0));
+  return buffer_rsrc(reinterpret_cast<const uint8_t*>(bias) + 2 * (size_t)col0, (uint32_t)valid * 2);
+}
+
+// Epilogue of one tile of the persistent loop: y = bf16(acc + bias) for rows
+// < row_end and columns < N.  Wave (wn, wm) stages its 128 x 128 block 16
+// rows at a time as bf16 in its own kEpiWaveBytes region (lane (i, g) writes
+// columns 16a + 4g .. +3 of row i for a = 0..7), reads each pass back as 8
+// consecutive columns per lane (4 rows per read) and writes 16-byte
+// non-temporal stores covering whole 256-byte row segments.  bias_slot: the
+// wave's 256-byte bias slice (columns wn * 128 ..).  Returns true when the
+// wave issued exactly 32 stores (block fully in range, vec_store == 2).
+__device__ __forceinline__ bool epi16(uint8_t* epi, const uint8_t* bias_slot, const v4f (&acc)[8][8],
+                                      uint16_t* __restrict__ y, int64_t ldy, int row0, int row_end, int col0,
+                                      int N, int vec_store) {
+  typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = wave >> 1, wm = wave & 1;
+  const int li = lane & 15, lg = lane >> 4;
+  uint8_t* reg = epi + wave * kEpiWaveBytes;
+  uint2 bw[8];
+#pragma unroll
+  for (int a = 0; a < 8; ++a) bw[a] = *reinterpret_cast<const uint2*>(bias_slot + (16 * a + 4 * lg) * 2);
+  const int nw = col0 + wn * 128, mw = row0 + wm * 128;
+  const bool full = vec_store == 2 && mw + 128 <= row_end && nw + 128 <= N;
+  const int rr = lane >> 4, cc = (lane & 15) * 8;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+      const v4f v = acc[a][k];
+      const uint2 w = make_uint2(pack_bf16x2(v[0] + bf16_lo(bw[a].x), v[1] + bf16_hi(bw[a].x)),
+                                 pack_bf16x2(v[2] + bf16_lo(bw[a].y), v[3] + bf16_hi(bw[a].y)));
+      *reinterpret_cast<uint2*>(reg + (li * kEpiPitchH + 16 * a + 4 * lg) * 2) = w;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    u4v t[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) t[r] = *reinterpret_cast<const u4v*>(reg + ((rr + 4 * r) * kEpiPitchH + cc) * 2);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = mw + 16 * k + rr + 4 * r, n = nw + cc;
+      uint16_t* d = y + (size_t)m * ldy + n;
+      if (full) {
+        __builtin_nontemporal_store(t[r], reinterpret_cast<u4v*>(d));
+      } else if (m < row_end && n < N) {
+        if (vec_store == 2 && n + 7 < N) {
+          *reinterpret_cast<u4v*>(d) = t[r];
+        } else {
+          for (int e = 0; e < 8; ++e)
+            if (n + e < N) d[e] = (uint16_t)(t[r][e >> 1] >> (16 * (e & 1)));
+        }
+      }
+    }
+  }
+  return full;
+}
+
+template <typename Decode>
+__device__ __forceinline__ void persistent16(uint8_t* st0, uint8_t* st1, uint8_t* st2, uint8_t* st3, uint8_t* epi,
+                                             uint8_t* bias_lds, int total, int KS, Decode decode,
+                                             uint16_t* __restrict__ y, int64_t ldy, int M, int N,
+                                             const uint16_t* __restrict__ bias, int vec_store) {
+  int b = blockIdx.x;
+  if (b >= total) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = wave >> 1, wm = wave & 1;
+  const int li = lane & 15, lg = lane >> 4;
+
+  struct State {
+    v8i a[8];
+    v8i bf[4];
+    int sa[2], sb[2];
+  };
+  const int offA = tile_off(wn * 128 + li, lg);
+  const int offB = kOpBytes + tile_off(wm * 128 + li, lg);
+  const int offS = 2 * kOpBytes + scale_off(li, lg & 1);
+  const int swA = wn * kTileScaleBytes, swB = 2 * kTileScaleBytes + wm * kTileScaleBytes;
+  auto rd16 = [](const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); };
+  auto frag = [&](const uint8_t* ev, const uint8_t* od, int off) {
+    const uint4 lo = rd16(ev + off), hi = rd16(od + off);
+    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  };
+  auto rd_scale = [&](const uint8_t* ev, const uint8_t* od, int base, int e) {
+    const uint8_t* st = (lg >> 1) ? od : ev;
+    return *reinterpret_cast<const int*>(st + offS + base + 128 * e);
+  };
+  auto issue_w = [&](const BufSrc& sr, int k, int q, uint8_t* ev, uint8_t* od) {
+    const int t = k / 5, c = k % 5;
+    sr.issue(c < 4 ? c : 8, 2 * q + t, t ? od : ev);
+  };
+  auto issue_x = [&](const BufSrc& sr, int k, int q, uint8_t* ev, uint8_t* od) {
+    const int t = k >> 2;
+    sr.issue(4 + (k & 3), 2 * q + t, t ? od : ev);
+  };
+  auto issue_bias = [&](i4v r, int buf) {
+    b2l_4((uint32_t)(wn * 256 + lane * 4), r, 0u, bias_lds + buf * kBiasSlot + wave * 256);
+  };
+  auto make_src = [&](const Job16& j) { return BufSrc(j.wga, j.wgb, j.xga, j.xgb, j.swa, j.swb, j.sxa, j.sxb, KS); };
+
+  v4f acc[8][8];
+  State S;
+  // One 128-K step on pair (ev, od); (nev, nod) holds the next step (of this
+  // tile or the next).  Copies step q of sr into this pair when kIssue, or
+  // (kRtIssue) when the runtime flag rt_issue is set: weights and scales
+  // after column 1, activations after column 6, and with with_bias also the
+  // bias of sr's tile into slot bbuf.  The wait before column 6 needs the
+  // next step's copies: besides the ten weight copies issued in this step (if
+  // any), vm_extra stores of the previous epilogue may still be in flight
+  // after them (32, or 0 when unknown).  The next step's fragments are always
+  // read (after the last tile they are stale and unused).
+  auto step = [&](auto kIssue, auto kRtIssue, auto with_bias, auto kVm, bool rt_issue, uint8_t* ev, uint8_t* od,
+                  const uint8_t* nev, const uint8_t* nod, const BufSrc& sr, int q, int vm_extra, i4v brs, int bbuf) {
+    constexpr bool kI = decltype(kIssue)::value, kR = decltype(kRtIssue)::value;
+    const bool issue = kI || (kR && rt_issue);
+    int nsa[2], nsb[2];
+    static_for<0, 64>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      constexpr int bb = j >> 3, a = j & 7;
+      if constexpr (j == 8) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (j == 48) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const bool extra = decltype(kVm)::value && vm_extra == 32;
+        if constexpr (kI) {
+          if (extra) wait_vmcnt<42>();
+          else wait_vmcnt<10>();
+        } else {
+          if (issue) {
+            if (extra) wait_vmcnt<42>();
+            else wait_vmcnt<10>();
+          } else {
+            if (extra) wait_vmcnt<32>();
+            else wait_vmcnt<0>();
+          }
+        }
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      mfma16<(a >> 1), (bb >> 1)>(acc[a][bb], S.a[a], S.bf[bb & 3], S.sa[a & 1], S.sb[bb & 1]);
+      if constexpr (kI || kR) {
+        if (issue) {
+          if constexpr (j >= 8 && j < 18) issue_w(sr, j - 8, q, ev, od);
+          if constexpr (j >= 48 && j < 56) issue_x(sr, j - 48, q, ev, od);
+          if constexpr (decltype(with_bias)::value && j == 56) issue_bias(brs, bbuf);
+        }
+      }
+      if constexpr (a == 0 && bb < 6) S.bf[(bb + 2) & 3] = frag(ev, od, offB + 1024 * (bb + 2));
+      if constexpr (j == 48) {
+        nsa[0] = rd_scale(nev, nod, swA, 0);
+        nsa[1] = rd_scale(nev, nod, swA, 1);
+        S.bf[0] = frag(nev, nod, offB);
+      }
+      if constexpr (j == 49) { nsb[0] = rd_scale(nev, nod, swB, 0); nsb[1] = rd_scale(nev, nod, swB, 1); }
+      if constexpr (j == 56) S.bf[1] = frag(nev, nod, offB + 1024);
+      if constexpr (j >= 56) S.a[a] = frag(nev, nod, offA + 1024 * a);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    S.sa[0] = nsa[0]; S.sa[1] = nsa[1];
+    S.sb[0] = nsb[0]; S.sb[1] = nsb[1];
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+
+  BufSrc src;
+  int row0, col0;
+  {
+    const Job16 first = decode(b);
+    src = make_src(first);
+    row0 = first.row0;
+    col0 = first.col0;
+  }
+  // First tile: its two first steps and its bias, then its first fragments.
+#pragma unroll
+  for (int k = 0; k < 10; ++k) issue_w(src, k, 0, st0, st1);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) issue_x(src, k, 0, st0, st1);
+#pragma unroll
+  for (int k = 0; k < 10; ++k) issue_w(src, k, 1, st2, st3);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) issue_x(src, k, 1, st2, st3);
+  issue_bias(bias_rsrc(bias, col0, N), 0);
+  wait_vmcnt<19>();
+  __builtin_amdgcn_s_barrier();
+  S.sa[0] = rd_scale(st0, st1, swA, 0);
+  S.sa[1] = rd_scale(st0, st1, swA, 1);
+  S.sb[0] = rd_scale(st0, st1, swB, 0);
+  S.sb[1] = rd_scale(st0, st1, swB, 1);
+#pragma unroll
+  for (int a = 0; a < 8; ++a) S.a[a] = frag(st0, st1, offA + 1024 * a);
+  S.bf[0] = frag(st0, st1, offB);
+  S.bf[1] = frag(st0, st1, offB + 1024);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+
+  const int P = KS / 2;       // 128-K steps per tile: even, at least 2
+  const i4v nob = buffer_rsrc(nullptr, 0);
+  int vm_extra = 0, buf = 0;
+  for (;;) {
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[a][c] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    int p = 0;
+    if (P >= 4) {
+      // The first step alone may find the previous epilogue's stores in
+      // flight (see step).
+      step(T{}, F{}, F{}, T{}, true, st0, st1, st2, st3, src, 2, vm_extra, nob, 0);
+      step(T{}, F{}, F{}, F{}, true, st2, st3, st0, st1, src, 3, 0, nob, 0);
+      for (p = 2; p + 4 <= P; p += 2) {
+        step(T{}, F{}, F{}, F{}, true, st0, st1, st2, st3, src, p + 2, 0, nob, 0);
+        step(T{}, F{}, F{}, F{}, true, st2, st3, st0, st1, src, p + 3, 0, nob, 0);
+      }
+      vm_extra = 0;
+    }
+    // The next tile is decoded only now, so its sources do not occupy
+    // registers during the loop above.
+    const int nb = b + (int)gridDim.x;
+    const bool has_next = nb < total;
+    const Job16 nxt = decode(has_next ? nb : b);
+    const BufSrc nsrc = make_src(nxt);
+    step(F{}, T{}, F{}, T{}, has_next, st0, st1, st2, st3, nsrc, 0, vm_extra, nob, 0);
+    step(F{}, T{}, T{}, F{}, has_next, st2, st3, st0, st1, nsrc, 1, 0, bias_rsrc(bias, nxt.col0, N), buf ^ 1);
+    // The last MFMAs must retire before the epilogue reads the accumulators.
+    asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+    const bool full = epi16(epi, bias_lds + buf * kBiasSlot + wave * 256, acc, y, ldy, row0, M, col0, N, vec_store);
+    if (!has_next) break;
+    vm_extra = full ? 32 : 0;
+    src = nsrc;
+    row0 = nxt.row0;
+    col0 = nxt.col0;
+    b = nb;
+    buf ^= 1;
   }
 }
 
