@@ -168,7 +168,7 @@ def main():
                       "pct_hbm": round(100 * quant_bytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_MFMA_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_MFMA_FP8_TFLOPS, 4),
-                     "traffic": measured_traffic(None), "kernel": "gemm_tile_kernel"},
+                     "traffic": measured_traffic(None), "kernel": "gemm_persistent_kernel"},
     }
     del q, s, y, x
 
