@@ -431,11 +431,11 @@ __global__ __launch_bounds__(tile::kThreads, 1) void moe_gemm2_kernel(
   const size_t op_stride = (size_t)KS * kTileBytes, sc_stride = (size_t)KS * kTileScaleBytes;
   const uint8_t* we = w2p + (size_t)e * (size_t)H * (size_t)I;
   const uint8_t* se = s2p + (size_t)e * (size_t)H * (size_t)(I / 32);
-  v16f acc[4][4];
-  tile::mainloop(st0, st1, st2, st3, we + (2 * nt) * op_stride, we + (2 * nt + 1) * op_stride,
-                 a2q + (size_t)g0 * op_stride, a2q + (size_t)(g0 + 1) * op_stride, se + (2 * nt) * sc_stride,
-                 se + (2 * nt + 1) * sc_stride, a2s + (size_t)g0 * sc_stride, a2s + (size_t)(g0 + 1) * sc_stride,
-                 KS, acc);
+  v4f acc[8][8];
+  tile::mainloop16(st0, st1, st2, st3, we + (2 * nt) * op_stride, we + (2 * nt + 1) * op_stride,
+                   a2q + (size_t)g0 * op_stride, a2q + (size_t)(g0 + 1) * op_stride, se + (2 * nt) * sc_stride,
+                   se + (2 * nt + 1) * sc_stride, a2s + (size_t)g0 * sc_stride, a2s + (size_t)(g0 + 1) * sc_stride,
+                   KS, acc);
 
   // Routing weight and slot (t * k + j) of each tile row; pad rows and the
   // rows past the tile's groups are not stored.
