@@ -227,3 +227,28 @@ def test_full_size_sampled(cfg):
     bn = None if b is None else b[cols].to(torch.float64).numpy()
     r = oracle.linear_ref(xn, wq, ws, bn)
     gpu_util.compare(ys, r, gpu_util.tolerance(xn, wq, ws, len(cols), K), f"config{cfg} sampled")
+
+
+@pytest.mark.parametrize("M,N,K", [(4100, 16500, 256), (2000, 9000, 768), (1031, 32768, 512)])
+def test_persistent_ragged_sampled(M, N, K):
+    """More tiles than workgroups with ragged M and N: every workgroup of the
+    persistent GEMM runs several tiles, edge tiles sit between full ones (the
+    next tile's first wait then covers an unknown number of stores), the bias
+    copy is cut at N, and K = 256 has a single pair of steps per tile.
+    Sampled rows x columns, including the first and last row and column,
+    against the oracle."""
+    g = torch.Generator().manual_seed(M + N + K)
+    x = synth.randn_bf16((M, K), 1.0, g)
+    w = synth.randn_bf16((N, K), 0.02, g)
+    b = synth.randn_bf16((N,), 0.1, g)
+    print("CASE persistent", M, N, K, flush=True)
+    pw = gpu_util.gpu_prepare(w)
+    y = api.linear(x.to(gpu_util.dev()), pw, b.to(gpu_util.dev()))
+    torch.cuda.synchronize()
+    rows = torch.cat([torch.randperm(M, generator=g)[:96], torch.tensor([0, M - 1])])
+    cols = torch.cat([torch.randperm(N, generator=g)[:96], torch.tensor([0, N - 1])])
+    ys = y[rows.to(y.device)][:, cols.to(y.device)].float().cpu().numpy()
+    wq, ws = gpu_util.oracle_weight(w[cols])
+    xn = x[rows].to(torch.float64).numpy()
+    r = oracle.linear_ref(xn, wq, ws, b[cols].to(torch.float64).numpy())
+    gpu_util.compare(ys, r, gpu_util.tolerance(xn, wq, ws, len(cols), K), f"persistent {M}x{N}x{K} sampled")
