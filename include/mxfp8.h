@@ -40,7 +40,8 @@ extern "C" {
 typedef enum {
   MXFP8_OK = 0,
   MXFP8_E_NULLPTR = -1,   /* a required pointer is NULL */
-  MXFP8_E_SHAPE = -2,     /* a size is negative / zero where it must not be, or breaks K % 32, K % 256 */
+  MXFP8_E_SHAPE = -2,     /* a size is negative / zero where it must not be, breaks K % 32, K % 256,
+                             or exceeds a limit (K <= 2^24 for the packed operands of the GEMM) */
   MXFP8_E_ALIGN = -3,     /* a pointer is not aligned as documented */
   MXFP8_E_LD = -4,        /* a leading dimension is too small or not a documented multiple */
   MXFP8_E_WORKSPACE = -5, /* workspace NULL or smaller than the *_workspace_bytes query */

@@ -41,7 +41,9 @@ int64_t n_pad(int64_t N) { return (N + 127) / 128 * 128; }
 int check_packed(const void* wp, const void* sp, int64_t N, int64_t K) {
   if (!wp || !sp) return MXFP8_E_NULLPTR;
   if (N < 1 || K < 256 || K % 256 != 0) return MXFP8_E_SHAPE;
-  if (N > (int64_t)1 << 30 || K > (int64_t)1 << 30) return MXFP8_E_SHAPE;
+  // A packed 128-row group (128 K bytes) must stay below 2^32 bytes: the GEMM
+  // addresses it with 32-bit buffer offsets.
+  if (N > (int64_t)1 << 30 || K > (int64_t)1 << 24) return MXFP8_E_SHAPE;
   if (!aligned(wp, 256) || !aligned(sp, 256)) return MXFP8_E_ALIGN;
   return MXFP8_OK;
 }
@@ -313,7 +315,7 @@ int mxfp8_quantize_act_packed(const void* x_bf16, int64_t M, int64_t K, int64_t 
                               void* s_packed, void* stream) {
   if (M < 0 || K < 256 || K % 256 != 0) return MXFP8_E_SHAPE;
   if (M == 0) return MXFP8_OK;
-  if (M > (int64_t)1 << 30 || K > (int64_t)1 << 30) return MXFP8_E_SHAPE;
+  if (M > (int64_t)1 << 30 || K > (int64_t)1 << 24) return MXFP8_E_SHAPE;
   if (!x_bf16 || !q_packed || !s_packed) return MXFP8_E_NULLPTR;
   if (ldx < K || ldx % 8 != 0) return MXFP8_E_LD;
   if (!aligned(x_bf16, 16) || !aligned(q_packed, 256) || !aligned(s_packed, 256)) return MXFP8_E_ALIGN;

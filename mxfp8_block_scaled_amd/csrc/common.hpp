@@ -17,11 +17,17 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 // in place of N), so both GEMM operands are read the same way.  Rows are
 // padded to a multiple of 128 ("pad N to 128" in the weight preparation step
 // of vLLM PR #52204); K is a multiple of 256.  Rows are cut into 128-row
-// groups and K into 64-byte steps:
+// groups, each group into eight 16-row bands, and K into 64-byte steps:
 //
-//   data[g][ks]  = 8 KiB tile: 128 rows x 4 chunks of 16 bytes; logical chunk
-//                  c (K bytes [16c, 16c+16) of the step) of row r sits at
-//                  chunk position c ^ swz(r), swz(r) = q ^ 2 (q & 1) with
+//   data[g]      = KS * 8 KiB, band-major: the 1 KiB piece of band b (rows
+//                  16b .. 16b+15 of the group) and step ks sits at
+//                  (b * KS + ks) * 1024, so one band is a contiguous run over
+//                  the whole K (a decode workgroup that owns 16 rows streams
+//                  one run: measured 4.1 us for a 16 MiB weight against
+//                  4.7 us when each band is 1 KiB pieces at an 8 KiB stride).
+//                  Inside a piece, row r at (r % 16) * 64 has 4 chunks of 16
+//                  bytes; logical chunk c (K bytes [16c, 16c+16) of the step)
+//                  sits at chunk position c ^ swz(r), swz(r) = q ^ 2 (q & 1) with
 //                  q = (r >> 2) & 3 (bits 2-3 of the row only).  Measured on
 //                  gfx950 with a 16-wave LDS probe over every swizzle of
 //                  this form: a ds_read_b128 in which lane i + 16 g reads
@@ -37,8 +43,9 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 //                  rows r % 32 + 32 i, i = 0..3 (the MFMA picks byte i with
 //                  the scale operand's op_sel).
 //
-// A tile is one contiguous run of bytes, so a GEMM workgroup copies it to LDS
-// unchanged with direct global->LDS loads.
+// A GEMM stage (128 rows x one step) is eight 1 KiB pieces; a workgroup
+// copies each to LDS unchanged with one direct global->LDS load per wave, so
+// in LDS the stage is the 8 KiB tile of rows 0..127 at r * 64 (tile_off).
 // ---------------------------------------------------------------------------
 constexpr int kGroupRows = 128;
 constexpr int kStepK = 64;
@@ -59,8 +66,15 @@ __host__ __device__ inline int swz(int r) {
   const int q = (r >> 2) & 3;
   return q ^ ((q & 1) << 1);
 }
-// Byte offset of logical chunk c of row r inside a tile.
+// Byte offset of logical chunk c of row r inside a tile (128 rows x 64 bytes,
+// rows consecutive: one stage in LDS).
 __host__ __device__ inline int tile_off(int r, int c) { return r * kStepK + ((c ^ swz(r)) << 4); }
+constexpr int kPieceBytes = 16 * kStepK;         // 1024: one 16-row band x one step
+// Byte offset, inside the data of a 128-row group with KS steps, of logical
+// chunk c of row r (0..127) in step ks.
+__host__ __device__ inline int64_t packed_off(int r, int64_t ks, int c, int64_t KS) {
+  return ((int64_t)(r >> 4) * KS + ks) * kPieceBytes + (r & 15) * kStepK + ((c ^ swz(r)) << 4);
+}
 // Byte offset of the scale of row r (0..127), block b (0..1) inside a scale tile.
 __host__ __device__ inline int scale_off(int r, int b) { return (r & 31) * 8 + b * 4 + (r >> 5); }
 

@@ -62,11 +62,13 @@ __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(
   const int KS = K / 128;                          // MFMA steps along K
   const int kb = (KS * wave) / kWaves, ke = (KS * (wave + 1)) / kWaves;
 
-  // 1. Weight loads for this wave's steps: E4M3, tiles 2ks and 2ks+1, chunk
-  // g of row r; E2M1 (kFp4), tile ks, chunk g = K [32g, 32g + 32) of the step
-  // (16 bytes either way).  This lane's block 4ks + g is block g & 1 of scale
-  // tile 2ks + g/2.
-  const uint8_t* wrow = wp + (size_t)grp * KTw * kTileBytes + tile_off(r, g);
+  // 1. Weight loads for this wave's steps: E4M3, pieces 2ks and 2ks+1 of the
+  // workgroup's 16-row band, chunk g of row r; E2M1 (kFp4), piece ks, chunk
+  // g = K [32g, 32g + 32) of the step (16 bytes either way).  The band is one
+  // contiguous run over K, so the workgroup streams one 64 KiB run (at
+  // K = 4096).  This lane's block 4ks + g is block g & 1 of scale tile
+  // 2ks + g/2.
+  const uint8_t* wrow = wp + (size_t)grp * KTw * kTileBytes + packed_off(r, 0, g, KTw);
   const uint8_t* srow = sp + (size_t)grp * KTs * kTileScaleBytes + scale_off(r, g & 1);
   uint4 w0[kMaxSteps], w1[kMaxSteps];
   uint32_t wsd[kMaxSteps];
@@ -74,11 +76,11 @@ __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(
   for (int u = 0; u < kMaxSteps; ++u) {
     if (kb + u < ke) {
       if constexpr (kFp4) {
-        w0[u] = *reinterpret_cast<const uint4*>(wrow + (size_t)(kb + u) * kTileBytes);
+        w0[u] = *reinterpret_cast<const uint4*>(wrow + (size_t)(kb + u) * kPieceBytes);
       } else {
-        const uint8_t* wt = wrow + (size_t)(2 * (kb + u)) * kTileBytes;
+        const uint8_t* wt = wrow + (size_t)(2 * (kb + u)) * kPieceBytes;
         w0[u] = *reinterpret_cast<const uint4*>(wt);
-        w1[u] = *reinterpret_cast<const uint4*>(wt + kTileBytes);
+        w1[u] = *reinterpret_cast<const uint4*>(wt + kPieceBytes);
       }
       wsd[u] = srow[(size_t)(2 * (kb + u) + (g >> 1)) * kTileScaleBytes];
     }

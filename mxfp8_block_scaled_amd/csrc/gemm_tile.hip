@@ -58,12 +58,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(
   const int xa = min(2 * tm, GM - 1), xb = min(2 * tm + 1, GM - 1);
 
   const int ksl = KS / splits;                           // steps of this slice (multiple of 4)
-  const size_t k0 = (size_t)split * ksl * kTileBytes, s0 = (size_t)split * ksl * kTileScaleBytes;
+  // The slice starts at step split * ksl of every band (data) and of the
+  // scale tiles; bands stay KS pieces apart.
+  const size_t k0 = (size_t)split * ksl * kPieceBytes, s0 = (size_t)split * ksl * kTileScaleBytes;
 
   v4f acc[8][8];
   tile::mainloop16(st0, st1, st2, st3, wp + wa * op_stride + k0, wp + wb * op_stride + k0, qp + xa * op_stride + k0,
                  qp + xb * op_stride + k0, wsp + wa * sc_stride + s0, wsp + wb * sc_stride + s0,
-                 qsp + xa * sc_stride + s0, qsp + xb * sc_stride + s0, ksl, acc);
+                 qsp + xa * sc_stride + s0, qsp + xb * sc_stride + s0, ksl, acc, KS);
 
   if (splits == 1) {
     tile::store16(st0, st1, st2, st3, acc, y, ldy, tm * 256, M, tn * 256, N, bias, vec_store);

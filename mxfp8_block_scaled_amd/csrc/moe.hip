@@ -382,12 +382,12 @@ __global__ __launch_bounds__(tile::kThreads, 1) void moe_gemm1_kernel(
       cvt8s(w + 4, scale, q + 2);
       const int iblk = nt * 128 + wn * 64 + 32 * a;   // first intermediate index of the block
       const int ks = iblk / kStepK;
-      uint8_t* tbase = a2q + ((size_t)g * KS2 + ks) * kTileBytes;
+      uint8_t* gbase = a2q + (size_t)g * KS2 * kTileBytes;
       if (row_ok) {
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
           const int k = (iblk % kStepK) + 8 * s4 + 4 * lg;  // within the 64-K step
-          *reinterpret_cast<uint32_t*>(tbase + tile_off(rr, k >> 4) + (k & 15)) = q[s4];
+          *reinterpret_cast<uint32_t*>(gbase + packed_off(rr, ks, k >> 4, KS2) + (k & 15)) = q[s4];
         }
         if (lg == 0) a2s[((size_t)g * KS2 + ks) * kTileScaleBytes + scale_off(rr, (iblk >> 5) & 1)] = (uint8_t)sb;
       }

@@ -25,17 +25,36 @@ __device__ inline int64_t src_row(int64_t n, int64_t gate_up_I) {
   return e * per + row;
 }
 
+// Packed chunk t (16 bytes, in storage order) -> its 128-row group g, step
+// ks, row r inside the group and logical chunk c: group-major, then 16-row
+// band, then step, then (row in band, chunk position).
+struct ChunkPos {
+  int64_t g, ks;
+  int r, c;
+};
+__device__ inline ChunkPos chunk_pos(int64_t t, int64_t KS) {
+  const int64_t per_group = KS * kChunksPerTile;
+  ChunkPos p;
+  p.g = t / per_group;
+  const int64_t rem = t - p.g * per_group;
+  const int64_t band = rem / (KS * 64);
+  const int64_t rem2 = rem - band * (KS * 64);
+  p.ks = rem2 >> 6;
+  const int slot = (int)(rem2 & 63);
+  p.r = (int)band * 16 + (slot >> 2);
+  p.c = (slot & 3) ^ swz(p.r);
+  return p;
+}
+
 // One thread per 16-byte chunk of the packed data.
 __global__ __launch_bounds__(256) void pack_w_kernel(const uint8_t* __restrict__ w, int64_t ldw, int64_t N,
                                                      int64_t KS, int64_t total, uint8_t* __restrict__ wp,
                                                      int64_t gate_up_I) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= total) return;
-  const int64_t tile = t / kChunksPerTile;
-  const int slot = (int)(t % kChunksPerTile);
-  const int64_t g = tile / KS, ks = tile - g * KS;
-  const int r = slot >> 2;
-  const int c = (slot & 3) ^ swz(r);
+  const ChunkPos cp = chunk_pos(t, KS);
+  const int64_t g = cp.g, ks = cp.ks;
+  const int r = cp.r, c = cp.c;
   const int64_t n = g * kGroupRows + r;
   uint4 v = make_uint4(0u, 0u, 0u, 0u);
   if (n < N) v = *reinterpret_cast<const uint4*>(w + src_row(n, gate_up_I) * ldw + ks * kStepK + c * 16);
@@ -67,13 +86,9 @@ __global__ __launch_bounds__(256) void unpack_w_kernel(const uint8_t* __restrict
                                                        int64_t total, uint8_t* __restrict__ w) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= total) return;
-  const int64_t tile = t / kChunksPerTile;
-  const int slot = (int)(t % kChunksPerTile);
-  const int64_t g = tile / KS, ks = tile - g * KS;
-  const int r = slot >> 2;
-  const int c = (slot & 3) ^ swz(r);
-  const int64_t n = g * kGroupRows + r;
-  *reinterpret_cast<uint4*>(w + n * K + ks * kStepK + c * 16) = reinterpret_cast<const uint4*>(wp)[t];
+  const ChunkPos cp = chunk_pos(t, KS);
+  const int64_t n = cp.g * kGroupRows + cp.r;
+  *reinterpret_cast<uint4*>(w + n * K + cp.ks * kStepK + cp.c * 16) = reinterpret_cast<const uint4*>(wp)[t];
 }
 
 __global__ __launch_bounds__(256) void unpack_s_kernel(const uint8_t* __restrict__ sp, int64_t K, int64_t KS,
@@ -114,13 +129,13 @@ int launch_pack_weight_gate_up(const void* w, const void* ws, int64_t E, int64_t
 }
 
 // MXFP4 weights (two E2M1 elements per byte along K, element 2j in the low
-// nibble): the packed tile of a 128-row group and a 128-element K step is the
-// same 8 KiB geometry as an E4M3 tile of a 64-element step (64 bytes per row,
-// four 16-byte chunks, the same chunk swizzle) -- a lane of the scaled MFMA
-// with an E2M1 operand takes 16 bytes = 32 consecutive K of one row, like the
-// E4M3 lane takes 16 bytes = 16 K -- so the byte packing is pack_w over K / 2
-// bytes per row.  The UE8M0 scales are per 32 elements either way: pack_s
-// unchanged.
+// nibble): a 128-element K step of a 16-row band is the same 1 KiB piece as an
+// E4M3 piece of a 64-element step (64 bytes per row, four 16-byte chunks, the
+// same chunk swizzle, bands KS4 = K / 128 pieces long) -- a lane of the scaled
+// MFMA with an E2M1 operand takes 16 bytes = 32 consecutive K of one row,
+// like the E4M3 lane takes 16 bytes = 16 K -- so the byte packing is pack_w
+// over K / 2 bytes per row.  The UE8M0 scales are per 32 elements either way:
+// pack_s unchanged.
 int launch_pack_weight_fp4(const void* w, const void* ws, int64_t N, int64_t K, int64_t ldw, int64_t ldws,
                            void* wp, void* sp, hipStream_t stream) {
   const int64_t G = (N + kGroupRows - 1) / kGroupRows;
@@ -151,13 +166,12 @@ __global__ __launch_bounds__(256) void widen_fp4_kernel(const uint8_t* __restric
                                                         uint8_t* __restrict__ w8) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= total) return;
-  const int64_t tile = t / kChunksPerTile;                 // E4M3 tile: g * KS + s
-  const int slot = (int)(t % kChunksPerTile);
-  const int64_t g = tile / KS, s = tile - g * KS;
-  const int r = slot >> 2;
-  const int c8 = (slot & 3) ^ swz(r);
+  const ChunkPos cp = chunk_pos(t, KS);                    // E4M3 chunk: 64-K step s
+  const int64_t g = cp.g, s = cp.ks;
+  const int r = cp.r, c8 = cp.c;
   const int c4 = 2 * (int)(s & 1) + (c8 >> 1);
-  const uint8_t* src = w4 + (g * (KS / 2) + (s >> 1)) * kTileBytes + tile_off(r, c4) + (c8 & 1) * 8;
+  const int64_t KS4 = KS / 2;                              // E2M1 steps of 128 K
+  const uint8_t* src = w4 + g * KS4 * kTileBytes + packed_off(r, s >> 1, c4, KS4) + (c8 & 1) * 8;
   const uint2 v = *reinterpret_cast<const uint2*>(src);
   const uint32_t in[2] = {v.x, v.y};
   uint32_t out[4];

@@ -85,8 +85,8 @@ __global__ __launch_bounds__(256) void quant_act_packed_kernel(const uint16_t* _
   uint32_t qd[2];
   cvt8s(v4, mx_scale_value(sb), qd);
   const int64_t tile = g * KS + ks;
-  uint8_t* dst = qp + tile * kTileBytes;
-  *reinterpret_cast<uint2*>(dst + tile_off(r, c8 >> 1) + (c8 & 1) * 8) = make_uint2(qd[0], qd[1]);
+  uint8_t* dst = qp + g * KS * kTileBytes + packed_off(r, ks, c8 >> 1, KS) + (c8 & 1) * 8;
+  *reinterpret_cast<uint2*>(dst) = make_uint2(qd[0], qd[1]);
   if ((c8 & 3) == 0) sp[tile * kTileScaleBytes + scale_off(r, c8 >> 2)] = (uint8_t)sb;
 }
 

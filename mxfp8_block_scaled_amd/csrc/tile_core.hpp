@@ -116,24 +116,29 @@ struct GatherX {
 };
 
 // This thread's share of one 64-K stage: nine copies, j = 0..3 the weight
-// rows (two 4 KiB runs of each 128-row group), 4..7 the activation rows, 8
-// the wave's 256-byte scale run (wave 0 weight rows 0-127, 1 weight rows
-// 128-255, 2 activation rows 0-127, 3 activation rows 128-255).
+// rows (bands 0-3 and 4-7 of each 128-row group: wave w copies the 1 KiB
+// piece of band w, resp. w + 4), 4..7 the activation rows, 8 the wave's
+// 256-byte scale run (wave 0 weight rows 0-127, 1 weight rows 128-255, 2
+// activation rows 0-127, 3 activation rows 128-255).  KSband: the steps of
+// the operand's full K (the distance between bands is KSband pieces).
 template <bool kGatherX>
 struct StageSrc {
   const uint8_t *w0, *w1, *x0, *x1, *ssrc;
+  size_t hi;                 // from band w to band w + 4
   GatherX gx;
   int wave;
 
   __device__ __forceinline__ StageSrc(const uint8_t* wga, const uint8_t* wgb, const uint8_t* xga,
                                       const uint8_t* xgb, const uint8_t* swa, const uint8_t* swb,
-                                      const uint8_t* sxa, const uint8_t* sxb, GatherX g) {
+                                      const uint8_t* sxa, const uint8_t* sxb, GatherX g, int KSband) {
     const int tid = threadIdx.x;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    w0 = wga + tid * 16;
-    w1 = wgb + tid * 16;
-    x0 = xga + tid * 16;
-    x1 = xgb + tid * 16;
+    const size_t lo = (size_t)wave * KSband * kPieceBytes + (tid & 63) * 16;
+    hi = (size_t)4 * KSband * kPieceBytes;
+    w0 = wga + lo;
+    w1 = wgb + lo;
+    x0 = xga + lo;
+    x1 = xgb + lo;
     ssrc = (wave == 0 ? swa : wave == 1 ? swb : wave == 2 ? sxa : sxb) + (tid & 63) * 4;
     gx = g;
   }
@@ -141,19 +146,19 @@ struct StageSrc {
   // Copy j of step ks into stage st.
   __device__ __forceinline__ void issue(int j, int ks, uint8_t* st) const {
     uint8_t* base = st + wave * 1024;
-    const size_t off = (size_t)ks * kTileBytes;
+    const size_t off = (size_t)ks * kPieceBytes;
     switch (j) {
       case 0: g2l_16(w0 + off, base); break;
-      case 1: g2l_16(w0 + off + 4096, base + 4096); break;
+      case 1: g2l_16(w0 + hi + off, base + 4096); break;
       case 2: g2l_16(w1 + off, base + 8192); break;
-      case 3: g2l_16(w1 + off + 4096, base + 12288); break;
+      case 3: g2l_16(w1 + hi + off, base + 12288); break;
       case 4:
         if constexpr (kGatherX) g2l_16(gx.p[0] + (size_t)ks * kStepK, base + kOpBytes);
         else g2l_16(x0 + off, base + kOpBytes);
         break;
       case 5:
         if constexpr (kGatherX) g2l_16(gx.p[1] + (size_t)ks * kStepK, base + kOpBytes + 4096);
-        else g2l_16(x0 + off + 4096, base + kOpBytes + 4096);
+        else g2l_16(x0 + hi + off, base + kOpBytes + 4096);
         break;
       case 6:
         if constexpr (kGatherX) g2l_16(gx.p[2] + (size_t)ks * kStepK, base + kOpBytes + 8192);
@@ -161,49 +166,52 @@ struct StageSrc {
         break;
       case 7:
         if constexpr (kGatherX) g2l_16(gx.p[3] + (size_t)ks * kStepK, base + kOpBytes + 12288);
-        else g2l_16(x1 + off + 4096, base + kOpBytes + 12288);
+        else g2l_16(x1 + hi + off, base + kOpBytes + 12288);
         break;
       default: g2l_4(ssrc + (size_t)ks * kTileScaleBytes, st + 2 * kOpBytes + wave * 256); break;
     }
   }
 };
 
-// The same nine copies per 64-K stage as StageSrc, as buffer loads over the
-// KS steps of each operand group (packed operands only).
+// The same nine copies per 64-K stage as StageSrc, as buffer loads (packed
+// operands only).  The group pointers may start inside the group's K (a
+// split-K slice: step ks0 of every band); KSband is the full K's step count,
+// the distance between bands.  A group holds at most 2^32 bytes (K < 2^25).
 struct BufSrc {
   i4v w0, w1, x0, x1, sc;
-  uint32_t voff, soff_lane;
+  uint32_t vlo, vhi, soff_lane;
   int wave;
 
   BufSrc() = default;
 
   __device__ __forceinline__ BufSrc(const uint8_t* wga, const uint8_t* wgb, const uint8_t* xga,
                                     const uint8_t* xgb, const uint8_t* swa, const uint8_t* swb,
-                                    const uint8_t* sxa, const uint8_t* sxb, int KS) {
+                                    const uint8_t* sxa, const uint8_t* sxb, int KS, int KSband) {
     const int tid = threadIdx.x;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const uint32_t data = (uint32_t)KS * kTileBytes, scales = (uint32_t)KS * kTileScaleBytes;
+    const uint32_t data = (uint32_t)KSband * kTileBytes, scales = (uint32_t)KS * kTileScaleBytes;
     w0 = buffer_rsrc(wga, data);
     w1 = buffer_rsrc(wgb, data);
     x0 = buffer_rsrc(xga, data);
     x1 = buffer_rsrc(xgb, data);
     sc = buffer_rsrc(wave == 0 ? swa : wave == 1 ? swb : wave == 2 ? sxa : sxb, scales);
-    voff = (uint32_t)tid * 16;
+    vlo = (uint32_t)wave * KSband * kPieceBytes + (uint32_t)(tid & 63) * 16;
+    vhi = vlo + 4u * KSband * kPieceBytes;
     soff_lane = (uint32_t)(tid & 63) * 4;
   }
 
   __device__ __forceinline__ void issue(int j, int ks, uint8_t* st) const {
     uint8_t* base = st + wave * 1024;
-    const uint32_t off = (uint32_t)ks * kTileBytes;
+    const uint32_t off = (uint32_t)ks * kPieceBytes;
     switch (j) {
-      case 0: b2l_16(voff, w0, off, base); break;
-      case 1: b2l_16(voff + 4096, w0, off, base + 4096); break;
-      case 2: b2l_16(voff, w1, off, base + 8192); break;
-      case 3: b2l_16(voff + 4096, w1, off, base + 12288); break;
-      case 4: b2l_16(voff, x0, off, base + kOpBytes); break;
-      case 5: b2l_16(voff + 4096, x0, off, base + kOpBytes + 4096); break;
-      case 6: b2l_16(voff, x1, off, base + kOpBytes + 8192); break;
-      case 7: b2l_16(voff + 4096, x1, off, base + kOpBytes + 12288); break;
+      case 0: b2l_16(vlo, w0, off, base); break;
+      case 1: b2l_16(vhi, w0, off, base + 4096); break;
+      case 2: b2l_16(vlo, w1, off, base + 8192); break;
+      case 3: b2l_16(vhi, w1, off, base + 12288); break;
+      case 4: b2l_16(vlo, x0, off, base + kOpBytes); break;
+      case 5: b2l_16(vhi, x0, off, base + kOpBytes + 4096); break;
+      case 6: b2l_16(vlo, x1, off, base + kOpBytes + 8192); break;
+      case 7: b2l_16(vhi, x1, off, base + kOpBytes + 12288); break;
       default: b2l_4(soff_lane, sc, (uint32_t)ks * kTileScaleBytes, st + 2 * kOpBytes + wave * 256); break;
     }
   }
@@ -226,7 +234,7 @@ __device__ __forceinline__ void mainloop(uint8_t* st0, uint8_t* st1, uint8_t* st
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave >> 1, wm = wave & 1;
   const int li = lane & 31, lg = lane >> 5;
-  const StageSrc<kGatherX> src(wga, wgb, xga, xgb, swa, swb, sxa, sxb, gx);
+  const StageSrc<kGatherX> src(wga, wgb, xga, xgb, swa, swb, sxa, sxb, gx, KS);
 
 #pragma unroll
   for (int a = 0; a < 4; ++a)
@@ -380,12 +388,13 @@ __device__ __forceinline__ void mfma16(v4f& c, const v8i& a, const v8i& b, int s
 __device__ __forceinline__ void mainloop16(uint8_t* st0, uint8_t* st1, uint8_t* st2, uint8_t* st3,
                                            const uint8_t* wga, const uint8_t* wgb, const uint8_t* xga,
                                            const uint8_t* xgb, const uint8_t* swa, const uint8_t* swb,
-                                           const uint8_t* sxa, const uint8_t* sxb, int KS, v4f (&acc)[8][8]) {
+                                           const uint8_t* sxa, const uint8_t* sxb, int KS, v4f (&acc)[8][8],
+                                           int KSband = 0) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wave >> 1, wm = wave & 1;
   const int li = lane & 15, lg = lane >> 4;
-  const BufSrc src(wga, wgb, xga, xgb, swa, swb, sxa, sxb, KS);
+  const BufSrc src(wga, wgb, xga, xgb, swa, swb, sxa, sxb, KS, KSband > 0 ? KSband : KS);
 
 #pragma unroll
   for (int a = 0; a < 8; ++a)
@@ -873,7 +882,7 @@ __device__ __forceinline__ void persistent16(uint8_t* st0, uint8_t* st1, uint8_t
   auto issue_bias = [&](i4v r, int buf) {
     b2l_4((uint32_t)(wn * 256 + lane * 4), r, 0u, bias_lds + buf * kBiasSlot + wave * 256);
   };
-  auto make_src = [&](const Job16& j) { return BufSrc(j.wga, j.wgb, j.xga, j.xgb, j.swa, j.swb, j.sxa, j.sxb, KS); };
+  auto make_src = [&](const Job16& j) { return BufSrc(j.wga, j.wgb, j.xga, j.xgb, j.swa, j.swb, j.sxa, j.sxb, KS, KS); };
 
   v4f acc[8][8];
   State S;
