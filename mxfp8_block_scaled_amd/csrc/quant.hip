@@ -51,8 +51,9 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
 // zero elements with scale byte 0, so every byte the GEMM reads is defined).
 // A wave owns two adjacent rows of a 128-row group and four consecutive
 // 64-K steps: it reads 512 contiguous bytes of each row (consecutive waves
-// continue along the same rows) and writes, in each of its four packed tiles,
-// the two rows' 128 contiguous bytes (one whole cache line).
+// continue along the same rows) and writes, in each of its four 1 KiB pieces
+// (the rows' band, consecutive steps), the two rows' 128 contiguous bytes
+// (one whole cache line).
 template <typename Idx>
 __global__ __launch_bounds__(256) void quant_act_packed_kernel(const uint16_t* __restrict__ x, int64_t ldx, int M,
                                                                Idx total, int64_t KS,

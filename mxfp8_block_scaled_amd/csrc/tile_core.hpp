@@ -10,9 +10,9 @@
 //    tiles.  The weight is the MFMA A operand, so lane (li, lg) of wave
 //    (wn, wm) ends with acc[a][b][r] = D[n = wn*128 + 32a + 8(r/4) + 4lg + r%4]
 //    [m = wm*128 + 32b + li].
-//  * A stage is four contiguous 4 KiB runs (two 128-row groups per operand)
-//    and four 256-byte scale runs, copied straight into LDS by
-//    global_load_lds_dwordx4 / _dword (no VGPR staging).
+//  * A stage is sixteen 1 KiB pieces (two 128-row groups per operand, eight
+//    16-row bands each) and four 256-byte scale runs, copied straight into
+//    LDS by global_load_lds_dwordx4 / _dword (no VGPR staging).
 //  * K advances 64 per stage; four LDS stages (4 x 33 KiB).  Each stage lives
 //    in its own __shared__ array and the loop is unrolled by four, so every
 //    LDS access names a distinct array: the compiler then needs no blanket
