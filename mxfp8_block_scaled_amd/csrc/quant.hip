@@ -49,46 +49,53 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
 // Same quantization, written in the packed operand layout of common.hpp for
 // the large-M GEMM (rows padded to a multiple of 128; pad rows are written as
 // zero elements with scale byte 0, so every byte the GEMM reads is defined).
-// A wave owns two adjacent rows of a 128-row group and four consecutive
-// 64-K steps: it reads 512 contiguous bytes of each row (consecutive waves
-// continue along the same rows) and writes, in each of its four 1 KiB pieces
-// (the rows' band, consecutive steps), the two rows' 128 contiguous bytes
-// (one whole cache line).
-template <typename Idx>
+// A workgroup owns one 16-row band and SPW consecutive 64-K steps, i.e. SPW
+// consecutive 1 KiB pieces, one contiguous run of the packed data.  Its
+// waves read whole row segments (SPW * 128 contiguous bytes per row, four
+// lanes per 32-block as in quant_act_kernel), write the E4M3 bytes into the
+// pieces' layout in LDS, and the workgroup then copies the SPW KiB out with
+// 16-byte stores; the scale bytes go straight to the scale tiles.
+template <int SPW>
 __global__ __launch_bounds__(256) void quant_act_packed_kernel(const uint16_t* __restrict__ x, int64_t ldx, int M,
-                                                               Idx total, int64_t KS,
-                                                               uint8_t* __restrict__ qp, uint8_t* __restrict__ sp) {
-  const Idx t = (Idx)blockIdx.x * 256 + threadIdx.x;
-  if (t >= total) return;  // total is a multiple of 64: whole waves leave
-  const Idx w = t >> 6;                     // wave: (g * 64 + row pair) * (KS / 4) + step quad
-  const int lane = (int)(t & 63);
-  const Idx nq = (Idx)(KS >> 2);
-  const Idx gp = w / nq;
-  const int64_t quad = (int64_t)(w - gp * nq);
-  const int64_t g = (int64_t)(gp >> 6);
-  const int r = (int)((gp & 63) * 2) + (lane >> 5);   // row inside the 128-row group
-  const int c = lane & 31;                            // 8-element chunk inside the 4 steps
-  const int64_t ks = quad * 4 + (c >> 3);
-  const int c8 = c & 7;                               // chunk inside the 64-K step
-  const int64_t row = g * kGroupRows + r;
-  uint32_t v4[4] = {0u, 0u, 0u, 0u};
-  if (row < M) {
-    const uint4 v = *reinterpret_cast<const uint4*>(x + row * ldx + ks * kStepK + c8 * 8);
-    v4[0] = v.x; v4[1] = v.y; v4[2] = v.z; v4[3] = v.w;
-  }
-  u16x2 mp = {0, 0};
+                                                               int64_t KS, int64_t nsg, uint8_t* __restrict__ qp,
+                                                               uint8_t* __restrict__ sp) {
+  constexpr int kLanesPerRow = SPW * 8;            // 8 elements per lane
+  constexpr int kRowsPerWave = 64 / kLanesPerRow;
+  __shared__ __attribute__((aligned(16))) uint8_t buf[SPW * kPieceBytes];
+  const int64_t band = (int64_t)blockIdx.x / nsg;  // global 16-row band
+  const int64_t s0 = ((int64_t)blockIdx.x - band * nsg) * SPW;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l = lane % kLanesPerRow;
+  const int s = l >> 3, c16 = (l & 7) >> 1, half = l & 1;   // step, chunk, half of the lane's 8 bytes
+  const int64_t g = band >> 3;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) mp = absmax_pk(mp, v4[i]);
-  uint32_t m = max((uint32_t)mp[0], (uint32_t)mp[1]);
-  m = max(m, (uint32_t)__shfl_xor((int)m, 1));
-  m = max(m, (uint32_t)__shfl_xor((int)m, 2));
-  const uint32_t sb = (uint32_t)max((int)(m >> 7) - 8, 0);
-  uint32_t qd[2];
-  cvt8s(v4, mx_scale_value(sb), qd);
-  const int64_t tile = g * KS + ks;
-  uint8_t* dst = qp + g * KS * kTileBytes + packed_off(r, ks, c8 >> 1, KS) + (c8 & 1) * 8;
-  *reinterpret_cast<uint2*>(dst) = make_uint2(qd[0], qd[1]);
-  if ((c8 & 3) == 0) sp[tile * kTileScaleBytes + scale_off(r, c8 >> 2)] = (uint8_t)sb;
+  for (int pass = 0; pass < 16 / (4 * kRowsPerWave); ++pass) {
+    const int rb = (pass * 4 + wave) * kRowsPerWave + lane / kLanesPerRow;   // row in the band
+    const int64_t row = band * 16 + rb;
+    const int r = (int)(row & (kGroupRows - 1));                           // row in the group
+    uint32_t v4[4] = {0u, 0u, 0u, 0u};
+    if (row < M) {
+      const uint4 v = *reinterpret_cast<const uint4*>(x + row * ldx + s0 * kStepK + l * 8);
+      v4[0] = v.x; v4[1] = v.y; v4[2] = v.z; v4[3] = v.w;
+    }
+    u16x2 mp = {0, 0};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mp = absmax_pk(mp, v4[i]);
+    uint32_t m = max((uint32_t)mp[0], (uint32_t)mp[1]);
+    m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+    const uint32_t sb = (uint32_t)max((int)(m >> 7) - 8, 0);
+    uint32_t qd[2];
+    cvt8s(v4, mx_scale_value(sb), qd);
+    *reinterpret_cast<uint2*>(buf + s * kPieceBytes + rb * kStepK + ((c16 ^ swz(r)) << 4) + half * 8) =
+        make_uint2(qd[0], qd[1]);
+    if ((l & 3) == 0) sp[(g * KS + s0 + s) * kTileScaleBytes + scale_off(r, (l >> 2) & 1)] = (uint8_t)sb;
+  }
+  __syncthreads();
+  uint8_t* dst = qp + g * KS * kTileBytes + ((band & 7) * KS + s0) * kPieceBytes;
+#pragma unroll
+  for (int o = tid * 16; o < SPW * kPieceBytes; o += 256 * 16)
+    *reinterpret_cast<uint4*>(dst + o) = *reinterpret_cast<const uint4*>(buf + o);
 }
 
 // MXFP4 quantization (bf16 [M, K] -> E2M1 [M, K/2] packed two per byte,
@@ -146,15 +153,16 @@ int launch_quantize_fp4(const void* x, int64_t M, int64_t K, int64_t ldx, void* 
 int launch_quantize_act_packed(const void* x, int64_t M, int64_t K, int64_t ldx, void* qp, void* sp,
                                hipStream_t stream) {
   const int64_t m_pad = (M + kGroupRows - 1) / kGroupRows * kGroupRows;
-  const int64_t KS = K / kStepK;
-  const int64_t total = m_pad * (K / 8);    // (m_pad / 2) row pairs x (KS / 4) step quads x 64 lanes
-  const int64_t blocks = total / 256;
-  if (total < ((int64_t)1 << 32)) {
-    hipLaunchKernelGGL(quant_act_packed_kernel<uint32_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       (const uint16_t*)x, ldx, (int)M, (uint32_t)total, KS, (uint8_t*)qp, (uint8_t*)sp);
+  const int64_t KS = K / kStepK;            // a multiple of 4 (K % 256 == 0)
+  const int64_t bands = m_pad / 16;
+  if (KS % 8 == 0) {
+    const int64_t nsg = KS / 8;
+    hipLaunchKernelGGL(quant_act_packed_kernel<8>, dim3((unsigned)(bands * nsg)), dim3(256), 0, stream,
+                       (const uint16_t*)x, ldx, (int)M, KS, nsg, (uint8_t*)qp, (uint8_t*)sp);
   } else {
-    hipLaunchKernelGGL(quant_act_packed_kernel<uint64_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       (const uint16_t*)x, ldx, (int)M, (uint64_t)total, KS, (uint8_t*)qp, (uint8_t*)sp);
+    const int64_t nsg = KS / 4;
+    hipLaunchKernelGGL(quant_act_packed_kernel<4>, dim3((unsigned)(bands * nsg)), dim3(256), 0, stream,
+                       (const uint16_t*)x, ldx, (int)M, KS, nsg, (uint8_t*)qp, (uint8_t*)sp);
   }
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
