@@ -17,32 +17,47 @@
 
 namespace mxfp8 {
 
-template <typename Idx>
+// Each thread converts CPT chunks 256 apart (every pass of the workgroup
+// covers 256 consecutive chunks, 4 KiB of bf16) and issues all their loads
+// before converting any, so several loads per lane are in flight.  CPT = 4
+// for large inputs (measured 3-5 % faster from 16384 x 2048 up); CPT = 1
+// keeps enough workgroups for small ones.
+template <typename Idx, int CPT>
 __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restrict__ x, int64_t ldx,
                                                         Idx chunks_per_row, Idx total,
                                                         uint8_t* __restrict__ q, int64_t ldq,
                                                         uint8_t* __restrict__ s, int64_t lds) {
-  Idx t = (Idx)blockIdx.x * 256 + threadIdx.x;
-  const bool valid = t < total;
-  // Threads past the end come in whole groups of four (total and the block
-  // size are multiples of 4), so they only exchange among themselves.
-  if (!valid) t = total - 1;
-  const Idx row = t / chunks_per_row;
-  const Idx c8 = t - row * chunks_per_row;
-  const uint4 v = *reinterpret_cast<const uint4*>(x + (int64_t)row * ldx + (int64_t)c8 * 8);
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  u16x2 mp = {0, 0};
+  const Idx t0 = (Idx)blockIdx.x * (256 * CPT) + threadIdx.x;
+  uint4 v[CPT];
+  Idx rows[CPT], c8s[CPT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) mp = absmax_pk(mp, w[i]);
-  uint32_t m = max((uint32_t)mp[0], (uint32_t)mp[1]);
-  m = max(m, (uint32_t)__shfl_xor((int)m, 1));
-  m = max(m, (uint32_t)__shfl_xor((int)m, 2));
-  const uint32_t sb = (uint32_t)max((int)(m >> 7) - 8, 0);
-  uint32_t qd[2];
-  cvt8s(w, mx_scale_value(sb), qd);
-  if (valid) {
-    *reinterpret_cast<uint2*>(q + (int64_t)row * ldq + (int64_t)c8 * 8) = make_uint2(qd[0], qd[1]);
-    if ((c8 & 3) == 0) s[(int64_t)row * lds + (int64_t)(c8 >> 2)] = (uint8_t)sb;
+  for (int k = 0; k < CPT; ++k) {
+    Idx t = t0 + (Idx)k * 256;
+    // Threads past the end come in whole groups of four (total and the
+    // pass size are multiples of 4), so they only exchange among themselves.
+    if (t >= total) t = total - 1;
+    rows[k] = t / chunks_per_row;
+    c8s[k] = t - rows[k] * chunks_per_row;
+    v[k] = *reinterpret_cast<const uint4*>(x + (int64_t)rows[k] * ldx + (int64_t)c8s[k] * 8);
+  }
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    const bool valid = t0 + (Idx)k * 256 < total;
+    const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+    u16x2 mp = {0, 0};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mp = absmax_pk(mp, w[i]);
+    uint32_t m = max((uint32_t)mp[0], (uint32_t)mp[1]);
+    m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+    const uint32_t sb = (uint32_t)max((int)(m >> 7) - 8, 0);
+    uint32_t qd[2];
+    cvt8s(w, mx_scale_value(sb), qd);
+    if (valid) {
+      const Idx row = rows[k], c8 = c8s[k];
+      *reinterpret_cast<uint2*>(q + (int64_t)row * ldq + (int64_t)c8 * 8) = make_uint2(qd[0], qd[1]);
+      if ((c8 & 3) == 0) s[(int64_t)row * lds + (int64_t)(c8 >> 2)] = (uint8_t)sb;
+    }
   }
 }
 
@@ -171,15 +186,19 @@ int launch_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx, void* 
                         int64_t lds, hipStream_t stream) {
   const int64_t per_row = K / 8;
   const int64_t total = M * per_row;
-  const int64_t blocks = (total + 255) / 256;
+  const bool wide = total >= (int64_t)256 * 4 * 2048;       // still >= 2048 workgroups at 4 chunks
+  const int cpt = wide ? 4 : 1;
+  const int64_t blocks = (total + 256 * cpt - 1) / (256 * cpt);
+  auto go = [&](auto kern, auto idx) {
+    using Idx = decltype(idx);
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, stream, (const uint16_t*)x, ldx, (Idx)per_row,
+                       (Idx)total, (uint8_t*)q, ldq, (uint8_t*)s, lds);
+  };
   if (total < ((int64_t)1 << 32)) {
-    hipLaunchKernelGGL(quant_act_kernel<uint32_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       (const uint16_t*)x, ldx, (uint32_t)per_row, (uint32_t)total, (uint8_t*)q, ldq,
-                       (uint8_t*)s, lds);
+    if (wide) go(quant_act_kernel<uint32_t, 4>, uint32_t{});
+    else go(quant_act_kernel<uint32_t, 1>, uint32_t{});
   } else {
-    hipLaunchKernelGGL(quant_act_kernel<uint64_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       (const uint16_t*)x, ldx, (uint64_t)per_row, (uint64_t)total, (uint8_t*)q, ldq,
-                       (uint8_t*)s, lds);
+    go(quant_act_kernel<uint64_t, 4>, uint64_t{});
   }
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
