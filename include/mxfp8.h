@@ -101,9 +101,8 @@ int mxfp8_unpack_weight(const void* w_packed, const void* s_packed, int64_t N, i
  * Workspace bytes mxfp8_linear needs for this shape (host-only).  For M > 16
  * the workspace holds the activations quantized into the packed layout
  * (M padded to 128 rows, plus their scales; plus fp32 split-K partials when
- * the shape has few tiles); for 9 <= M <= 16 the activations quantized
- * row-major (M*K + M*K/32 bytes); for M <= 8 nothing is stored there (a
- * 256-byte minimum is still required).  Its contents need no
+ * the shape has few tiles); for M <= 16 (K <= 8192) nothing is stored
+ * there (a 256-byte minimum is still required).  Its contents need no
  * initialization.  Calls that share one workspace must be ordered on one
  * stream (concurrent calls on one workspace race).
  */

@@ -39,14 +39,11 @@ int launch_gemm_tile(const void* qp, const void* sp, int64_t M, int64_t K, const
                      void* part = nullptr);
 
 // Skinny GEMM (M <= kSkinnyMaxM, K <= kSkinnyMaxK) with the activation
-// quantization fused in below kSkinnyPreqM rows, and done once by the
-// row-major quantizer into ws (skinny_ws_bytes) from kSkinnyPreqM rows on.
+// quantization fused in; it needs no workspace (skinny_ws_bytes is the
+// minimum the entry points ask for).
 constexpr int64_t kSkinnyMaxM = 16;
 constexpr int64_t kSkinnyMaxK = 8192;
-constexpr int64_t kSkinnyPreqM = 9;
-inline size_t skinny_ws_bytes(int64_t M, int64_t K) {
-  return M >= kSkinnyPreqM ? (size_t)(M * K + M * (K / 32) + 255) / 256 * 256 : 256;
-}
+inline size_t skinny_ws_bytes(int64_t, int64_t) { return 256; }
 int launch_gemm_skinny(const void* x, int64_t ldx, int64_t M, int64_t K, const void* wp, const void* sp,
                        int64_t N, const void* bias, void* y, int64_t ldy, hipStream_t stream, void* ws);
 // The same with a packed MXFP4 weight (launch_pack_weight_fp4).

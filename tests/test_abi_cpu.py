@@ -176,6 +176,8 @@ def test_w4a8_sizes_and_validation():
     # workspace: decode shapes as the MXFP8 layer; larger M adds the widened weight
     assert api.mxfp8_linear_w4a8_workspace_bytes(7, 4096, 4096) == api.mxfp8_linear_workspace_bytes(7, 4096, 4096)
     assert api.mxfp8_linear_w4a8_workspace_bytes(16, 4096, 4096) == api.mxfp8_linear_workspace_bytes(16, 4096, 4096)
+    # M <= 16 (K <= 8192) stores nothing in the workspace: the 256-byte minimum
+    assert api.mxfp8_linear_workspace_bytes(16, 4096, 8192) == 256
     assert (api.mxfp8_linear_w4a8_workspace_bytes(512, 130, 256)
             == api.mxfp8_linear_workspace_bytes(512, 130, 256) + 256 * 256)
     p = api.mxfp8_prepare_weight_fp4
