@@ -98,12 +98,12 @@ int mxfp8_unpack_weight(const void* w_packed, const void* s_packed, int64_t N, i
                         void* w_e4m3, void* w_s_e8m0, void* stream);
 
 /*
- * Workspace bytes mxfp8_linear needs for this shape (host-only).  For M > 16
- * the workspace holds the activations quantized into the packed layout
- * (M padded to 128 rows, plus their scales; plus fp32 split-K partials when
- * the shape has few tiles); for M <= 16 (K <= 8192) nothing is stored
- * there (a 256-byte minimum is still required).  Its contents need no
- * initialization.  Calls that share one workspace must be ordered on one
+ * Workspace bytes mxfp8_linear needs for this shape (host-only).  For
+ * M <= 16 (K <= 8192) nothing is stored there (a 256-byte minimum is still
+ * required); otherwise it holds the activations quantized into the packed
+ * layout (M padded to 128 rows, plus their scales; for M > 128 also the
+ * fp32 split-K partials when the shape has few tiles).  Its
+ * contents need no initialization.  Calls that share one workspace must be ordered on one
  * stream (concurrent calls on one workspace race).
  */
 int mxfp8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes);
@@ -142,13 +142,13 @@ int mxfp8_linear(const void* x_bf16, int64_t M, int64_t K, int64_t ldx,
  *   w_s_e8m0 [N, >= K/32] row stride ldws (only [:N, :K/32] is read)
  *   w_packed, s_packed  outputs of the sizes above, 256-byte aligned.  Pad
  *            rows hold zero elements and scale byte 127.
- * mxfp8_linear_w4a8_workspace_bytes: host-only.  M <= 16: as mxfp8_linear;
- *   larger M: mxfp8_linear's workspace plus N_pad * K bytes, where the
- *   weight is widened (exactly: every E2M1 value is an E4M3 value) to the
- *   MXFP8 tiles for the MFMA-bound tile GEMM.
+ * mxfp8_linear_w4a8_workspace_bytes: host-only.  M <= 128 (K <= 8192): as
+ *   mxfp8_linear; larger M: mxfp8_linear's workspace plus N_pad * K bytes,
+ *   where the weight is widened (exactly: every E2M1 value is an E4M3
+ *   value) to the MXFP8 tiles for the MFMA-bound tile GEMM.
  * mxfp8_linear_w4a8: y[m, n] = bf16( sum_k deq(q(x))[m, k] * deq4(W)[n, k]
  *   + bias[n] ), fp32 accumulate, one rounding; arguments as mxfp8_linear
- *   with the packed MXFP4 weight.  M <= 16 streams the 4-bit weight once
+ *   with the packed MXFP4 weight.  M <= 128 streams the 4-bit weight once
  *   (half the bytes of MXFP8).  Errors as mxfp8_linear.
  */
 /*
@@ -268,9 +268,11 @@ int mxfp8_moe_grouped(const void* x_bf16, const float* logits_f32, int64_t T, in
 int mxfp8_moe_debug_capture(void* act_bf16, void* act_e4m3, void* act_e8m0, void* ids_i32, void* wts_f32);
 
 /*
- * Test hook: force the GEMM path of mxfp8_linear (0 = automatic by shape,
- * 1 = large-tile path, 2 = skinny path).  Process-wide; returns the previous
- * value, or MXFP8_E_SHAPE for an unknown path.
+ * Test hook: force the GEMM path of mxfp8_linear and mxfp8_linear_w4a8
+ * (0 or 2 = automatic by shape: decode kernel for M <= 16, mid-M kernel for
+ * M <= 128, both for K <= 8192, large-tile GEMM otherwise; 1 = large-tile
+ * path; 3 = mid-M kernel for every M <= 128).  Process-wide; returns the
+ * previous value, or MXFP8_E_SHAPE for an unknown path.
  */
 int mxfp8_debug_force_path(int path);
 

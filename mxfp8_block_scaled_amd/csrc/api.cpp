@@ -116,9 +116,16 @@ size_t moe_layout(int64_t T, int64_t H, int64_t E, int64_t topk, int64_t I, uint
   return off;
 }
 
-bool use_skinny(int64_t M, int64_t K) {
-  if (g_force_path.load(std::memory_order_relaxed) == 1) return false;
-  return M <= mxfp8::kSkinnyMaxM && K <= mxfp8::kSkinnyMaxK;
+// GEMM path of a linear call: the decode kernel (M <= 16), the mid-M kernel
+// (M <= 128) or the large-tile GEMM; mxfp8_debug_force_path can pin it.
+enum class Path { kTile, kSkinny, kMid };
+Path linear_path(int64_t M, int64_t K) {
+  const int force = g_force_path.load(std::memory_order_relaxed);
+  const bool small_k = K <= mxfp8::kSkinnyMaxK;
+  if (force == 1 || !small_k) return Path::kTile;
+  if (force == 3) return M <= mxfp8::kMidMaxM ? Path::kMid : Path::kTile;
+  if (M <= mxfp8::kSkinnyMaxM) return Path::kSkinny;
+  return M <= mxfp8::kMidMaxM ? Path::kMid : Path::kTile;
 }
 
 }  // namespace
@@ -196,7 +203,15 @@ int mxfp8_unpack_weight(const void* w_packed, const void* s_packed, int64_t N, i
 int mxfp8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes) {
   if (!bytes) return MXFP8_E_NULLPTR;
   if (M < 0 || N < 1 || K < 256 || K % 256 != 0) return MXFP8_E_SHAPE;
-  *bytes = M == 0 ? 256 : use_skinny(M, K) ? mxfp8::skinny_ws_bytes(M, K) : tile_ws_bytes(M, N, K);
+  if (M == 0) {
+    *bytes = 256;
+    return MXFP8_OK;
+  }
+  switch (linear_path(M, K)) {
+    case Path::kSkinny: *bytes = mxfp8::skinny_ws_bytes(M, K); break;
+    case Path::kMid: *bytes = mxfp8::mid_ws_bytes(M, K); break;
+    default: *bytes = tile_ws_bytes(M, N, K);
+  }
   return MXFP8_OK;
 }
 
@@ -211,16 +226,19 @@ int mxfp8_linear(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, const vo
   if (int st = check_output(y_bf16, N, ldy, bias_bf16)) return st;
   if (ldx < K || ldx % 8 != 0) return MXFP8_E_LD;
   if (!aligned(x_bf16, 16)) return MXFP8_E_ALIGN;
-  const bool skinny = use_skinny(M, K);
-  if (!skinny && (n_pad(M) * (K / 8) + 255) / 256 > INT32_MAX) return MXFP8_E_SHAPE;
-  const size_t need = skinny ? mxfp8::skinny_ws_bytes(M, K) : tile_ws_bytes(M, N, K);
+  const Path path = linear_path(M, K);
+  if (path == Path::kTile && (n_pad(M) * (K / 8) + 255) / 256 > INT32_MAX) return MXFP8_E_SHAPE;
+  size_t need = 0;
+  mxfp8_linear_workspace_bytes(M, N, K, &need);
   if (!workspace || workspace_bytes < need) return MXFP8_E_WORKSPACE;
   if (!aligned(workspace, 256)) return MXFP8_E_ALIGN;
   if (int st = check_device()) return st;
   hipStream_t s = (hipStream_t)stream;
-  if (skinny)
+  if (path == Path::kSkinny)
     return mxfp8::launch_gemm_skinny(x_bf16, ldx, M, K, w_packed, s_packed, N, bias_bf16, y_bf16, ldy, s,
                                      workspace);
+  if (path == Path::kMid)
+    return mxfp8::launch_gemm_mid(x_bf16, ldx, M, K, w_packed, s_packed, N, bias_bf16, y_bf16, ldy, s, workspace);
   uint8_t* q = (uint8_t*)workspace;
   uint8_t* sc = q + round_up((size_t)n_pad(M) * (size_t)K, 256);
   uint8_t* part = q + tile_ws_act_bytes(M, K);
@@ -263,9 +281,15 @@ int mxfp8_prepare_weight_fp4(const void* w_e2m1, const void* w_s_e8m0, int64_t N
 int mxfp8_linear_w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes) {
   if (!bytes) return MXFP8_E_NULLPTR;
   if (M < 0 || N < 1 || K < 256 || K % 256 != 0) return MXFP8_E_SHAPE;
-  if (M == 0) *bytes = 256;
-  else if (use_skinny(M, K)) *bytes = mxfp8::skinny_ws_bytes(M, K);
-  else *bytes = tile_ws_bytes(M, N, K) + (size_t)n_pad(N) * (size_t)K;
+  if (M == 0) {
+    *bytes = 256;
+    return MXFP8_OK;
+  }
+  switch (linear_path(M, K)) {
+    case Path::kSkinny: *bytes = mxfp8::skinny_ws_bytes(M, K); break;
+    case Path::kMid: *bytes = mxfp8::mid_ws_bytes(M, K); break;
+    default: *bytes = tile_ws_bytes(M, N, K) + (size_t)n_pad(N) * (size_t)K;
+  }
   return MXFP8_OK;
 }
 
@@ -280,17 +304,20 @@ int mxfp8_linear_w4a8(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, con
   if (int st = check_output(y_bf16, N, ldy, bias_bf16)) return st;
   if (ldx < K || ldx % 8 != 0) return MXFP8_E_LD;
   if (!aligned(x_bf16, 16)) return MXFP8_E_ALIGN;
-  const bool skinny = use_skinny(M, K);
-  if (!skinny && (n_pad(M) * (K / 8) + 255) / 256 > INT32_MAX) return MXFP8_E_SHAPE;
+  const Path path = linear_path(M, K);
+  if (path == Path::kTile && (n_pad(M) * (K / 8) + 255) / 256 > INT32_MAX) return MXFP8_E_SHAPE;
   size_t need = 0;
   mxfp8_linear_w4a8_workspace_bytes(M, N, K, &need);
   if (!workspace || workspace_bytes < need) return MXFP8_E_WORKSPACE;
   if (!aligned(workspace, 256)) return MXFP8_E_ALIGN;
   if (int st = check_device()) return st;
   hipStream_t s = (hipStream_t)stream;
-  if (skinny)
+  if (path == Path::kSkinny)
     return mxfp8::launch_gemm_skinny_fp4(x_bf16, ldx, M, K, w_packed, s_packed, N, bias_bf16, y_bf16, ldy, s,
                                          workspace);
+  if (path == Path::kMid)
+    return mxfp8::launch_gemm_mid_fp4(x_bf16, ldx, M, K, w_packed, s_packed, N, bias_bf16, y_bf16, ldy, s,
+                                      workspace);
   // Larger M is MFMA-bound: widen the weight to the MXFP8 tiles (exact) and
   // run the MXFP8 tile GEMM.
   uint8_t* q = (uint8_t*)workspace;
@@ -425,7 +452,7 @@ int mxfp8_moe_debug_capture(void* act_bf16, void* act_e4m3, void* act_e8m0, void
 }
 
 int mxfp8_debug_force_path(int path) {
-  if (path < 0 || path > 2) return MXFP8_E_SHAPE;
+  if (path < 0 || path > 3) return MXFP8_E_SHAPE;
   return g_force_path.exchange(path);
 }
 

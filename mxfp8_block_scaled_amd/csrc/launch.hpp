@@ -44,6 +44,18 @@ int launch_gemm_tile(const void* qp, const void* sp, int64_t M, int64_t K, const
 constexpr int64_t kSkinnyMaxM = 16;
 constexpr int64_t kSkinnyMaxK = 8192;
 inline size_t skinny_ws_bytes(int64_t, int64_t) { return 256; }
+
+// Mid-M GEMM (kSkinnyMaxM < M <= kMidMaxM, K <= kSkinnyMaxK): the packed
+// quantizer writes one 128-row group of activation tiles (E4M3 128 * K bytes,
+// then the scale tiles, 128 * K / 32) into ws (mid_ws_bytes), then
+// gemm_mid.hip's kernel reads them with the packed weight.
+constexpr int64_t kMidMaxM = 128;
+inline size_t mid_ws_bytes(int64_t, int64_t K) { return (size_t)(128 * K + 128 * (K / 32) + 255) / 256 * 256; }
+int launch_gemm_mid(const void* x, int64_t ldx, int64_t M, int64_t K, const void* wp, const void* sp, int64_t N,
+                    const void* bias, void* y, int64_t ldy, hipStream_t stream, void* ws);
+// The same with a packed MXFP4 weight (launch_pack_weight_fp4).
+int launch_gemm_mid_fp4(const void* x, int64_t ldx, int64_t M, int64_t K, const void* wp, const void* sp,
+                        int64_t N, const void* bias, void* y, int64_t ldy, hipStream_t stream, void* ws);
 int launch_gemm_skinny(const void* x, int64_t ldx, int64_t M, int64_t K, const void* wp, const void* sp,
                        int64_t N, const void* bias, void* y, int64_t ldy, hipStream_t stream, void* ws);
 // The same with a packed MXFP4 weight (launch_pack_weight_fp4).

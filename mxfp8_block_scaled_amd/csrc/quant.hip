@@ -170,14 +170,18 @@ int launch_quantize_act_packed(const void* x, int64_t M, int64_t K, int64_t ldx,
   const int64_t m_pad = (M + kGroupRows - 1) / kGroupRows * kGroupRows;
   const int64_t KS = K / kStepK;            // a multiple of 4 (K % 256 == 0)
   const int64_t bands = m_pad / 16;
-  if (KS % 8 == 0) {
-    const int64_t nsg = KS / 8;
-    hipLaunchKernelGGL(quant_act_packed_kernel<8>, dim3((unsigned)(bands * nsg)), dim3(256), 0, stream,
-                       (const uint16_t*)x, ldx, (int)M, KS, nsg, (uint8_t*)qp, (uint8_t*)sp);
+  // Eight steps per workgroup (one 8 KiB run) where that still gives the
+  // chip over a thousand workgroups; fewer for small inputs (a 128-row group
+  // at K = 4096 gets 256 workgroups of two steps instead of 64 of eight).
+  if (KS % 8 == 0 && bands * (KS / 8) >= 1024) {
+    hipLaunchKernelGGL(quant_act_packed_kernel<8>, dim3((unsigned)(bands * (KS / 8))), dim3(256), 0, stream,
+                       (const uint16_t*)x, ldx, (int)M, KS, KS / 8, (uint8_t*)qp, (uint8_t*)sp);
+  } else if (bands * (KS / 4) >= 1024) {
+    hipLaunchKernelGGL(quant_act_packed_kernel<4>, dim3((unsigned)(bands * (KS / 4))), dim3(256), 0, stream,
+                       (const uint16_t*)x, ldx, (int)M, KS, KS / 4, (uint8_t*)qp, (uint8_t*)sp);
   } else {
-    const int64_t nsg = KS / 4;
-    hipLaunchKernelGGL(quant_act_packed_kernel<4>, dim3((unsigned)(bands * nsg)), dim3(256), 0, stream,
-                       (const uint16_t*)x, ldx, (int)M, KS, nsg, (uint8_t*)qp, (uint8_t*)sp);
+    hipLaunchKernelGGL(quant_act_packed_kernel<2>, dim3((unsigned)(bands * (KS / 2))), dim3(256), 0, stream,
+                       (const uint16_t*)x, ldx, (int)M, KS, KS / 2, (uint8_t*)qp, (uint8_t*)sp);
   }
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }

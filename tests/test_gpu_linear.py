@@ -99,6 +99,20 @@ def test_edge_grid(M, N, K):
     gpu_util.run_linear_and_check(x, w, b, f"edge {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(5, 130, 512), (17, 1, 256), (48, 255, 768), (100, 384, 8192),
+                                   (128, 4096, 4096), (113, 200, 6144)])
+def test_mid_path(M, N, K):
+    """The mid-M kernel (automatic for 16 < M <= 128; path 3 forces it at
+    M = 5): 1..4 K steps per wave (K = 6144 leaves one of four empty), 1..8
+    row groups with a ragged last one, ragged N, bias on and off."""
+    g = torch.Generator().manual_seed(M * 31 + N + K)
+    x = synth.scale_stress(synth.randn_bf16((M, K), 1.0, g), seed=M + 5)
+    w = synth.scale_stress(synth.randn_bf16((N, K), 0.02, g), seed=N + 6)
+    b = synth.randn_bf16((N,), 0.1, g) if M % 2 == 0 else None
+    st = gpu_util.run_linear_and_check(x, w, b, f"mid {M}x{N}x{K}", force_path=3)
+    assert st["over_bound"] == 0
+
+
 def test_skinny_and_tile_paths_agree():
     """Same inputs through both GEMM paths: each within the bound of the
     oracle; their difference stays within the sum of the two bounds."""

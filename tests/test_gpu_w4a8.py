@@ -62,9 +62,16 @@ def test_decode_parity(M, N, K):
 
 @pytest.mark.parametrize("M,N,K", [(300, 640, 512), (129, 200, 1024), (128, 4096, 4096), (17, 130, 256)])
 def test_tile_path_parity(M, N, K):
-    """M > 16: the weight is widened to MXFP8 tiles (exact) for the tile GEMM
-    (M = 128, N = 4096 also exercises split-K)."""
-    run_and_check(M, N, K, seed=M + N)
+    """The weight widened to MXFP8 tiles (exact) for the tile GEMM: automatic
+    above M = 128, forced below (M = 128, N = 4096 also exercises split-K)."""
+    run_and_check(M, N, K, seed=M + N, force_path=1 if M <= 128 else 0)
+
+
+@pytest.mark.parametrize("M,N,K", [(17, 130, 256), (40, 384, 768), (128, 4096, 4096), (100, 200, 8192), (5, 256, 512)])
+def test_mid_path_parity(M, N, K):
+    """16 < M <= 128 streams the 4-bit weight once through the mid-M kernel
+    (path 3 forces it at M = 5; K = 8192 gives four steps per wave)."""
+    run_and_check(M, N, K, seed=M + 3 * N, force_path=3)
 
 
 @pytest.mark.parametrize("path", [0, 1])
@@ -104,7 +111,11 @@ def test_w4a8_matches_mxfp8_on_widened_weight():
     w8 = torch.from_numpy(oracle.e2m1_decode(codes).astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8)
     pw8 = api.prepare_weight(w8.to(gpu_util.dev()), torch.from_numpy(ws).to(gpu_util.dev()))
     pw4 = prepare(codes, ws)
-    y8 = api.linear(x, pw8)
-    y4 = api.linear(x, pw4)
-    torch.cuda.synchronize()
+    prev = api.mxfp8_debug_force_path(1)
+    try:
+        y8 = api.linear(x, pw8)
+        y4 = api.linear(x, pw4)
+        torch.cuda.synchronize()
+    finally:
+        api.mxfp8_debug_force_path(prev)
     assert torch.equal(y8, y4)
