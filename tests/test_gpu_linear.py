@@ -99,8 +99,9 @@ def test_edge_grid(M, N, K):
     gpu_util.run_linear_and_check(x, w, b, f"edge {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(5, 130, 512), (17, 1, 256), (48, 255, 768), (100, 384, 8192),
-                                   (128, 4096, 4096), (113, 200, 6144)])
+@pytest.mark.parametrize("M,N,K", [(5, 130, 512), (17, 1, 256), (48, 255, 768), (64, 130, 1024),
+                                   (80, 384, 2048), (90, 255, 512), (100, 384, 8192), (128, 4096, 4096),
+                                   (113, 200, 6144)])
 def test_mid_path(M, N, K):
     """The mid-M kernel (automatic for 16 < M <= 128; path 3 forces it at
     M = 5): 1..4 K steps per wave (K = 6144 leaves one of four empty), 1..8
@@ -138,10 +139,14 @@ def test_packed_entries_match_linear():
     assert torch.equal(y1, y2)
 
 
-@pytest.mark.parametrize("M,K", [(1, 256), (130, 512), (300, 768), (256, 1024)])
+@pytest.mark.parametrize("M,K", [(1, 256), (130, 512), (300, 768), (256, 1024),
+                                 (4096, 2048), (2048, 2048), (5504, 768)])
 def test_packed_activation_quantizer_bit_exact(M, K):
     """The packed-layout quantizer writes exactly the oracle's bytes (checked
-    after unpacking), with zero pad rows and zero scales."""
+    after unpacking), with zero pad rows and zero scales.  The launch takes
+    two, four or eight 64-K steps per workgroup by grid size: the small
+    shapes take two, (2048, 2048) and (5504, 768) four (the latter because
+    its step count is not a multiple of eight), (4096, 2048) eight."""
     g = torch.Generator().manual_seed(M + K)
     x = synth.scale_stress(synth.activations(M, K, 1.0, g, 0.01, 50.0), seed=M)
     pa = api.quantize_act_packed(x.to(gpu_util.dev()))
