@@ -7,7 +7,7 @@ M=8192, N=28672, K=8192 (x ~ N(0,1), W ~ N(0,0.01) MXFP8, bf16 bias): a step is
 one pass of the whole hot path over that batch -- activation quantization
 into the GEMM's packed layout (mxfp8_quantize_act_packed) then the
 block-scaled GEMM with its bias/bf16 epilogue (mxfp8_gemm_packed), the same
-two kernels mxfp8_linear launches for M > 16.
+two kernels mxfp8_linear launches for M > 128 (and for any M when K > 8192).
 The one-time weight preparation runs before the timed region.  ``value`` is
 2*M*N*K / step time in TFLOP/s, inputs resident in HBM.
 
