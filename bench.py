@@ -134,16 +134,17 @@ def main():
 
     # Same shape through the single product entry point, for reference.
     ws_t = api.workspace(M, N, K, dev)
-    for _ in range(2):
+    for _ in range(10):
         api.linear(x, pw, bias, out=y)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        api.linear(x, pw, bias, out=y)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    linear_ms = e0.elapsed_time(e1) / args.steps
+    for _ in range(3):   # the last of three repeats (first-use transient of the new workspace)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            api.linear(x, pw, bias, out=y)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        linear_ms = e0.elapsed_time(e1) / args.steps
     del ws_t
 
     out = {
@@ -218,10 +219,16 @@ def sweep(api, synth, torch, np, dev, stream):
                        None if b is None else b.data_ptr(), y.data_ptr(), N, ws_t.data_ptr(), ws_t.numel(), sptr)
             if st != 0:
                 raise RuntimeError(st)
-        for r in range(5):
+        # Untimed warm-up, then three timed repeats; the last is reported.  A
+        # shape's first calls on freshly allocated buffers run slower for a
+        # few milliseconds (prefill: 163 us in the first repeat, 153-155 us
+        # after), longer than a warm-up of a few calls covers.
+        for r in range(max(5, reps // 2)):
             fn(r)
         torch.cuda.synchronize()
-        ms = time_calls(fn, reps, stream, torch)
+        tries = [time_calls(fn, reps, stream, torch) for _ in range(3)]
+        print(f"{label}: " + " ".join(f"{t * 1e3:.2f}" for t in tries) + " us", file=sys.stderr, flush=True)
+        ms = tries[-1]
         flops = 2.0 * M * N * K
         alg_bytes = M * K * 2 + N * K * (0.5 if w4 else 1.0) + N * K / 32 + (0 if b is None else 2 * N) + M * N * 2
         row = {"workload": label, "M": M, "N": N, "K": K, "us": round(ms * 1e3, 3),
@@ -288,8 +295,9 @@ def sweep(api, synth, torch, np, dev, stream):
     def qf(r):
         api.mxfp8_quantize_act(xd.data_ptr(), 16384, 2048, 2048, q.data_ptr(), 2048, s.data_ptr(), 64,
                                stream.cuda_stream)
-    qf(0)
-    ms = time_calls(qf, 100, stream, torch)
+    for r in range(50):
+        qf(r)
+    ms = [time_calls(qf, 100, stream, torch) for _ in range(3)][-1]
     nb = 16384 * 2048 * (2 + 1 + 1 / 32)
     rows.append({"workload": "act-quant M=16384 K=2048", "us": round(ms * 1e3, 3),
                  "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
@@ -342,10 +350,13 @@ def moe_row(api, synth, torch, dev, stream):
                                  q2.view(E, H, inter), s2.view(E, H, inter // 32))
     del q13, s13, q2, s2
     y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    for _ in range(3):
+    for _ in range(10):
         api.moe_grouped(x, logits, mw, k, out=y)
     torch.cuda.synchronize()
-    ms = time_calls(lambda r: api.moe_grouped(x, logits, mw, k, out=y), 20, stream, torch)
+    # the last of three repeats, as for the linear shapes
+    tries = [time_calls(lambda r: api.moe_grouped(x, logits, mw, k, out=y), 20, stream, torch) for _ in range(3)]
+    print("moe: " + " ".join(f"{t * 1e3:.2f}" for t in tries) + " us", file=sys.stderr, flush=True)
+    ms = tries[-1]
     flops = 2.0 * T * k * (2 * inter * H + H * inter)
     nbytes = E * (2 * inter * H + H * inter) * (1 + 1 / 32) + T * H * 2 * 2 + T * E * 4
     return {"workload": f"moe T={T} H={H} E={E} top{k} I={inter}", "us": round(ms * 1e3, 3),
