@@ -114,6 +114,19 @@ def test_mid_path(M, N, K):
     assert st["over_bound"] == 0
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 130, 8192), (7, 384, 6144), (16, 255, 8192), (4, 256, 8448)])
+def test_decode_large_k(M, N, K):
+    """The decode kernel with four K steps per wave (K = 6144: one of them
+    empty; K = 8192: the largest K it takes) and, at K = 8448, the shape
+    falling back to the tile GEMM."""
+    g = torch.Generator().manual_seed(M * 7 + N + K)
+    x = synth.scale_stress(synth.randn_bf16((M, K), 1.0, g), seed=M + 11)
+    w = synth.scale_stress(synth.randn_bf16((N, K), 0.02, g), seed=N + 12)
+    b = synth.randn_bf16((N,), 0.1, g) if M % 2 == 0 else None
+    st = gpu_util.run_linear_and_check(x, w, b, f"decode {M}x{N}x{K}")
+    assert st["over_bound"] == 0
+
+
 def test_skinny_and_tile_paths_agree():
     """Same inputs through both GEMM paths: each within the bound of the
     oracle; their difference stays within the sum of the two bounds."""

@@ -55,6 +55,7 @@ def run_and_check(M, N, K, seed, bias=True, force_path=0, x_std=1.0, stress=Fals
 @pytest.mark.parametrize("M,N,K", [
     (1, 4096, 4096), (7, 4096, 4096), (9, 4096, 4096), (16, 4096, 4096),   # decode (4-bit kernel)
     (3, 130, 256), (15, 384, 768), (2, 1, 512),                            # ragged N, small K
+    (5, 200, 8192), (12, 256, 6144),                                       # four K steps per wave
 ])
 def test_decode_parity(M, N, K):
     run_and_check(M, N, K, seed=M * 7 + N)
