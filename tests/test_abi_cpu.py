@@ -92,6 +92,36 @@ def test_linear_validation():
     bad = list(ok); bad[0] = P + 2; assert f(*bad) == -3
 
 
+def test_linear_paths_workspace():
+    """Workspace per path: nothing stored for M <= 16; one 128-row group of
+    packed activations (E4M3 tiles, then scale tiles) for 16 < M <= 128; the
+    tile path's padded packed activations above; K > 8192 always takes the
+    tile path.  The forced paths move the M = 64 shape between them."""
+    ws = api.mxfp8_linear_workspace_bytes
+    assert ws(16, 4096, 4096) == 256
+    assert ws(17, 4096, 4096) == ws(128, 4096, 4096) == 128 * 4096 + 128 * 128
+    assert ws(129, 4096, 4096) >= 256 * 4096 + 256 * 128
+    assert ws(8, 4096, 8448) >= 128 * 8448 + 128 * 264          # K > 8192: tile path
+    prev = api.mxfp8_debug_force_path(1)
+    try:
+        assert ws(64, 4096, 4096) >= 128 * 4096 + 128 * 128      # tile path (split-K partials on top)
+        assert ws(8, 4096, 4096) >= 128 * 4096 + 128 * 128
+        api.mxfp8_debug_force_path(3)
+        assert ws(8, 4096, 4096) == 128 * 4096 + 128 * 128       # mid path forced at M = 8
+        assert ws(200, 4096, 4096) >= 256 * 4096 + 256 * 128     # above 128: still the tile path
+    finally:
+        api.mxfp8_debug_force_path(prev)
+    f = api.mxfp8_linear
+    need = ws(64, 256, 512)
+    ok = (P, 64, 512, 512, P, P, 256, None, P, 256, P, need, None)
+    assert f(*ok) == -6                                           # valid, but no gfx950 device here
+    bad = list(ok); bad[11] = need - 1; assert f(*bad) == -5
+    bad = list(ok); bad[10] = P + 128; assert f(*bad) == -3       # workspace 256-byte alignment
+    g = api.mxfp8_linear_w4a8
+    assert api.mxfp8_linear_w4a8_workspace_bytes(64, 256, 512) == need   # no widened weight on this path
+    assert g(*ok) == -6
+
+
 def test_packed_entries_validation():
     assert api.mxfp8_packed_act_bytes(300, 512) == (384 * 512, 384 * 16)
     f = api.mxfp8_quantize_act_packed
