@@ -264,20 +264,38 @@ def prepare_weight(w_q, w_s):
 
 
 _workspaces = {}
+# Buffers a larger shape replaced.  They are never freed: a HIP graph captured
+# earlier, or work still queued on the stream, may hold their addresses.
+_retired = []
+
+
+def _cache_key(device, stream):
+    d = torch.device(device)
+    idx = d.index if d.index is not None else torch.cuda.current_device()
+    return idx, int(stream.cuda_stream)
 
 
 def workspace(M, N, K, device):
-    """A zero-initialised workspace big enough for (M, N, K), cached per
-    device and grown on demand (allocation happens here, never in the library)."""
+    """A zero-initialised workspace big enough for mxfp8_linear at (M, N, K),
+    cached per (device, current stream) and grown on demand (allocation
+    happens here, never in the library).  Calls sharing a workspace must be
+    ordered on one stream, hence one buffer per stream; a buffer that a
+    larger shape replaces stays allocated for the life of the process, so a
+    captured graph or queued work that still uses it never sees freed memory."""
     return _workspace_sized(mxfp8_linear_workspace_bytes(M, N, K), device)
 
 
-def _workspace_sized(need, device):
-    key = torch.device(device).index if torch.device(device).index is not None else torch.cuda.current_device()
-    ws = _workspaces.get(key)
+def _workspace_sized(need, device, cache=None, zero=True):
+    cache = _workspaces if cache is None else cache
+    key = _cache_key(device, torch.cuda.current_stream(device))
+    ws = cache.get(key)
     if ws is None or ws.numel() < need:
-        ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=device)
-        _workspaces[key] = ws
+        if ws is not None:
+            _retired.append(ws)
+        size = max(need, 256)
+        ws = torch.zeros(size, dtype=torch.uint8, device=device) if zero else \
+            torch.empty(size, dtype=torch.uint8, device=device)
+        cache[key] = ws
     return ws
 
 
@@ -310,12 +328,16 @@ def prepare_weight_fp4(w_e2m1, w_s):
     return PreparedWeightFP4(wp, sp, N, K)
 
 
-def linear(x, pw, bias=None, out=None):
+def linear(x, pw, bias=None, out=None, workspace=None):
     """The MXFP8 dense linear layer: ``y = bf16(deq(q(x)) @ deq(W).T + bias)``.
 
     ``x`` bf16 ``[..., K]`` (GPU), ``pw`` a PreparedWeight (MXFP8) or a
     PreparedWeightFP4 (MXFP4, the W4A8 layer), ``bias`` bf16 ``[N]``
-    or None.  Returns bf16 ``[..., N]`` (contiguous)."""
+    or None.  Returns bf16 ``[..., N]`` (contiguous).  ``workspace``: an
+    optional uint8 GPU tensor of at least ``mxfp8_linear_workspace_bytes``
+    (``mxfp8_linear_w4a8_workspace_bytes`` for MXFP4) bytes, 256-byte
+    aligned, owned by the caller; by default a cached buffer per (device,
+    stream) is used."""
     assert x.dtype == torch.bfloat16, f"MXFP8 linear requires bfloat16 activations, got {x.dtype}"
     _require_cuda(x, "x")
     K = pw.K
@@ -330,12 +352,13 @@ def linear(x, pw, bias=None, out=None):
         bias = bias.contiguous()
     y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     if isinstance(pw, PreparedWeightFP4):
-        ws = _workspace_sized(mxfp8_linear_w4a8_workspace_bytes(M, N, K), x.device)
+        ws = workspace if workspace is not None else \
+            _workspace_sized(mxfp8_linear_w4a8_workspace_bytes(M, N, K), x.device)
         _check(mxfp8_linear_w4a8(_ptr(x2), M, K, x2.stride(0), _ptr(pw.w_packed), _ptr(pw.s_packed), N,
                                  _ptr(bias), _ptr(y), y.stride(0), _ptr(ws), ws.numel(), _stream(x.device)),
                "mxfp8_linear_w4a8")
         return y.view(*lead, N)
-    ws = workspace(M, N, K, x.device)
+    ws = workspace if workspace is not None else _workspace_sized(mxfp8_linear_workspace_bytes(M, N, K), x.device)
     _check(mxfp8_linear(_ptr(x2), M, K, x2.stride(0), _ptr(pw.w_packed), _ptr(pw.s_packed), N, _ptr(bias),
                         _ptr(y), y.stride(0), _ptr(ws), ws.numel(), _stream(x.device)), "mxfp8_linear")
     return y.view(*lead, N)
@@ -445,13 +468,9 @@ _moe_workspaces = {}
 
 
 def moe_workspace(T, H, I, E, topk, device):
-    need = mxfp8_moe_workspace_bytes(T, H, I, E, topk)
-    key = torch.device(device).index if torch.device(device).index is not None else torch.cuda.current_device()
-    ws = _moe_workspaces.get(key)
-    if ws is None or ws.numel() < need:
-        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
-        _moe_workspaces[key] = ws
-    return ws
+    """The MoE layer's workspace, cached per (device, current stream) like
+    ``workspace`` (superseded buffers are kept, never freed)."""
+    return _workspace_sized(mxfp8_moe_workspace_bytes(T, H, I, E, topk), device, cache=_moe_workspaces, zero=False)
 
 
 def moe_grouped(x, logits, mw, topk, out=None):

@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kMaxDevices = 64;
+using mxfp8::kMaxDevices;
 // Per-device cached answer to "is this a gfx950": 0 unknown, 1 yes, 2 no.
 std::atomic<int> g_dev_ok[kMaxDevices];
 // Per-device compute-unit count (0 = not yet queried).
@@ -143,6 +143,18 @@ int mxfp8::device_cu_count() {
     g_dev_cus[dev].store(n, std::memory_order_relaxed);
   }
   return n;
+}
+
+bool mxfp8::set_lds_limit_once(const void* fn, int bytes, std::atomic<int>* flags) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return false;
+  int st = flags[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    // Two threads may both set it; the call is idempotent.
+    st = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) == hipSuccess ? 1 : 2;
+    flags[dev].store(st, std::memory_order_release);
+  }
+  return st == 1;
 }
 
 extern "C" {

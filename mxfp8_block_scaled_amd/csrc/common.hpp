@@ -59,6 +59,14 @@ __device__ inline int xcd_remap(int bid, int total) {
   const int per = total / kXCD, rem = total % kXCD;
   return (xcd < rem) ? xcd * (per + 1) + k : rem * (per + 1) + (xcd - rem) * per + k;
 }
+// Raw buffer resource over [base, base + bytes) for compiler-tracked buffer
+// loads (__builtin_amdgcn_raw_buffer_load_*): a load at or past `bytes`
+// returns zero without touching memory, so a null base with bytes = 0 reads
+// zeros.  Word 3 selects the 32-bit data format, no swizzle.
+__device__ inline __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 constexpr int kTileBytes = kGroupRows * kStepK;   // 8192
 constexpr int kTileScaleBytes = kGroupRows * 2;   // 256
 

@@ -65,16 +65,17 @@ __global__ __launch_bounds__(kThreads) void gemm_mid_kernel(
   for (int u = 0; u < kSteps; ++u) ks_of[u] = min(kb + u, KS - 1);
 
   // 1. The reducing waves' bias values (columns n0 + 4g .. + 3, index clamped
-  // to N - 1; those past N are never stored), issued first from asm so the
-  // compiler cannot sink them into the epilogue; they are older than every
-  // load the compiler issues, so its own wait counts stay safe.
+  // to N - 1; those past N are never stored), issued first as unconditional
+  // buffer loads (above the scheduling barrier below, so the compiler cannot
+  // sink them into the epilogue); the other waves' buffer is empty and reads
+  // zeros without a memory access.  Compiler-tracked: its own wait covers
+  // the first use.
   const bool has_bias = bias != nullptr;
-  uint32_t braw[4] = {0u, 0u, 0u, 0u};
-  if (wave < kMG && has_bias) {
+  const __amdgpu_buffer_rsrc_t brsrc = raw_rsrc(bias, (has_bias && wave < kMG) ? (uint32_t)N * 2u : 0u);
+  uint32_t braw[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      asm volatile("global_load_ushort %0, %1, off" : "=v"(braw[e]) : "v"(bias + min(n0 + 4 * g + e, N - 1)) : "memory");
-  }
+  for (int e = 0; e < 4; ++e)
+    braw[e] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(brsrc, (uint32_t)min(n0 + 4 * g + e, N - 1) * 2u, 0, 0);
 
   // 2. Weight loads of the wave's steps (the decode kernel's addressing):
   // E4M3 pieces 2ks and 2ks+1 of the workgroup's 16-row band, chunk g of row
@@ -163,10 +164,9 @@ __global__ __launch_bounds__(kThreads) void gemm_mid_kernel(
   const int m = 16 * mg + i;
   const int n = n0 + 4 * g;
   if (m >= M || n >= N) return;
-  asm volatile("s_waitcnt vmcnt(0)" : "+v"(braw[0]), "+v"(braw[1]), "+v"(braw[2]), "+v"(braw[3]));
   float v[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) v[e] = has_bias ? s[e] + __uint_as_float(braw[e] << 16) : s[e];
+  for (int e = 0; e < 4; ++e) v[e] = s[e] + __uint_as_float(braw[e] << 16);
   uint16_t* yrow = y + (size_t)m * ldy;
   const uint32_t lo = pack_bf16x2(v[0], v[1]);
   const uint32_t hi = pack_bf16x2(v[2], v[3]);
@@ -185,9 +185,8 @@ template <bool kFp4, int kSteps, int kMG>
 int launch_mid_k(const uint8_t* xp, const uint8_t* xsp, int64_t M, int64_t K, const void* wp, const void* sp,
                  int64_t N, const void* bias, void* y, int64_t ldy, hipStream_t stream) {
   constexpr int lds = kMG * kWaves * 64 * 16;
-  static const bool lds_ok = hipFuncSetAttribute((const void*)gemm_mid_kernel<kFp4, kSteps, kMG>,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, lds) == hipSuccess;
-  if (!lds_ok) return -7;
+  static std::atomic<int> lds_set[kMaxDevices];
+  if (!set_lds_limit_once((const void*)gemm_mid_kernel<kFp4, kSteps, kMG>, lds, lds_set)) return -7;
   const int blocks = (int)((N + 15) / 16);
   const int vec = (ldy % 4 == 0) && (((uintptr_t)y & 7) == 0);
   hipLaunchKernelGGL((gemm_mid_kernel<kFp4, kSteps, kMG>), dim3(blocks), dim3(kThreads), lds, stream, xp, xsp,

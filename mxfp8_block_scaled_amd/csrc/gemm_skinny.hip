@@ -78,17 +78,18 @@ __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(
 
   // 1. Wave 0's bias values (columns n0 + 4g .. + 3, index clamped to N - 1;
   // those past N are never stored), issued first so their latency hides
-  // under the weight stream.  Issued from asm because the compiler would
-  // sink them into the epilogue, where each would cost a full memory
-  // latency; they are older than every load the compiler issues, so its own
-  // wait counts stay safe.
+  // under the weight stream.  The loads are unconditional buffer loads, so
+  // they sit above the scheduling barrier below and cannot be sunk into the
+  // epilogue, where each would cost a full memory latency; for the other
+  // waves (and a null bias) the buffer is empty and they return 0 without a
+  // memory access.  They are ordinary compiler-tracked loads: the
+  // compiler's own wait covers their first use.
   const bool has_bias = bias != nullptr;
-  uint32_t braw[4] = {0u, 0u, 0u, 0u};
-  if (wave == 0 && has_bias) {
+  const __amdgpu_buffer_rsrc_t brsrc = raw_rsrc(bias, (has_bias && wave == 0) ? (uint32_t)N * 2u : 0u);
+  uint32_t braw[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      asm volatile("global_load_ushort %0, %1, off" : "=v"(braw[e]) : "v"(bias + min(n0 + 4 * g + e, N - 1)) : "memory");
-  }
+  for (int e = 0; e < 4; ++e)
+    braw[e] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(brsrc, (uint32_t)min(n0 + 4 * g + e, N - 1) * 2u, 0, 0);
 
   // 2. The wave's activation slice, coalesced: M rows x kSteps steps of bf16,
   // chunk c = lane + 64 q is 16 bytes of row c / kChunksRow.  Loads return in
@@ -208,10 +209,9 @@ __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(
   if (i >= M) return;
   const int n = n0 + 4 * g;
   if (n >= N) return;
-  asm volatile("s_waitcnt vmcnt(0)" : "+v"(braw[0]), "+v"(braw[1]), "+v"(braw[2]), "+v"(braw[3]));
   float v[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) v[e] = has_bias ? acc[e] + __uint_as_float(braw[e] << 16) : acc[e];
+  for (int e = 0; e < 4; ++e) v[e] = acc[e] + __uint_as_float(braw[e] << 16);
   uint16_t* yrow = y + (size_t)i * ldy;
   const uint32_t lo = pack_bf16x2(v[0], v[1]);
   const uint32_t hi = pack_bf16x2(v[2], v[3]);
@@ -230,9 +230,8 @@ template <bool kFp4, int kSteps>
 int launch_skinny_k(const void* x, int64_t ldx, int64_t M, int64_t K, const void* wp, const void* sp, int64_t N,
                     const void* bias, void* y, int64_t ldy, hipStream_t stream) {
   constexpr int lds = SkinnyLds<kSteps>::kBytes;
-  static const bool lds_ok = hipFuncSetAttribute((const void*)gemm_skinny_kernel<kFp4, kSteps>,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, lds) == hipSuccess;
-  if (!lds_ok) return -7;
+  static std::atomic<int> lds_set[kMaxDevices];
+  if (!set_lds_limit_once((const void*)gemm_skinny_kernel<kFp4, kSteps>, lds, lds_set)) return -7;
   const int blocks = (int)((N + 15) / 16);
   const int vec = (ldy % 4 == 0) && (((uintptr_t)y & 7) == 0);
   hipLaunchKernelGGL((gemm_skinny_kernel<kFp4, kSteps>), dim3(blocks), dim3(kThreads), lds, stream,

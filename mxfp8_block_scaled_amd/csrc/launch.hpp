@@ -5,7 +5,18 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace mxfp8 {
+
+// Devices the per-device caches of the library cover (device ids 0..63).
+constexpr int kMaxDevices = 64;
+
+// Raises the dynamic LDS limit of kernel fn to `bytes` on the current device,
+// once per device (the attribute belongs to a device's copy of the kernel):
+// flags[dev] is 0 before, 1 after a successful call, 2 after a failed one.
+// Returns false if the device is out of range or the runtime refused.
+bool set_lds_limit_once(const void* fn, int bytes, std::atomic<int>* flags);
 
 int launch_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx, void* q, int64_t ldq, void* s,
                         int64_t lds, hipStream_t stream);

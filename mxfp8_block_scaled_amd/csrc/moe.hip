@@ -70,6 +70,10 @@ __global__ __launch_bounds__(1024) void moe_route_kernel(const float* __restrict
       const int e = lane + 64 * c;
       ok[c] = e < E;
       v[c] = ok[c] ? logits[(int64_t)t * E + e] : 0.0f;
+      // NaN compares false both ways: read it as -inf, so every round still
+      // finds a candidate (topk <= E) and every selected id is an expert.
+      // The routing of such a token is meaningless, but stays in bounds.
+      if (v[c] != v[c]) v[c] = -INFINITY;
     }
     float selv = 0.0f;
     int seli = 0;
@@ -96,7 +100,7 @@ __global__ __launch_bounds__(1024) void moe_route_kernel(const float* __restrict
         if (lane + 64 * c == bi) ok[c] = false;
       if (lane == j) {
         selv = bv;
-        seli = bi;
+        seli = min(max(bi, 0), E - 1);   // always an expert id (see the NaN note above)
       }
     }
     // Selection 0 is the largest logit.

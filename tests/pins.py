@@ -242,3 +242,25 @@ def check_w4a8_vs_mxfp8(linear_w4a8, pack, x_bf16, codes, w_s, decode4, bias=Non
     y4 = linear_w4a8(x, pack(codes), w_s, b)
     y8 = oracle.linear_ref(x, w8, w_s, b)
     assert np.array_equal(y4, y8)
+
+
+def check_silu(silu):
+    """SiLU, z * sigmoid(z) (the gate activation of the routed MoE layer),
+    against three things that do not share its formula:
+      * torch.nn.functional.silu in float64 over z in [-100, 100] and at
+        magnitudes where exp overflows (|z| up to 1e4);
+      * the identity silu(z) - silu(-z) = z (z sigmoid(z) + z sigmoid(-z) = z),
+        which fixes the sign convention of the exponent;
+      * the closed form silu(ln 3) = (3/4) ln 3 and silu(0) = 0."""
+    z = np.concatenate([np.linspace(-100.0, 100.0, 20001), [-1e4, -745.0, -700.0, 700.0, 745.0, 1e4]])
+    with np.errstate(over="ignore"):
+        got = np.asarray(silu(z), dtype=np.float64)
+        mirror = np.asarray(silu(-z), dtype=np.float64)
+    ref = torch.nn.functional.silu(torch.from_numpy(z)).numpy()
+    assert np.all(np.isfinite(got)), "silu must stay finite where exp overflows"
+    assert np.allclose(got, ref, rtol=1e-13, atol=1e-300), float(np.max(np.abs(got - ref)))
+    core = np.abs(z) <= 100
+    assert np.allclose((got - mirror)[core], z[core], rtol=1e-13, atol=1e-13)
+    ln3 = np.log(3.0)
+    assert abs(float(silu(np.array([ln3]))[0]) - 0.75 * ln3) <= 1e-15
+    assert float(silu(np.array([0.0]))[0]) == 0.0

@@ -211,3 +211,29 @@ def test_moe_full_config_sampled():
     g = np.random.default_rng(5)
     tokens = np.sort(g.choice(c["T"], size=24, replace=False))
     check_moe(x, logits, w13q, w13s, w2q, w2s, c["topk"], "full-config", tokens=tokens)
+
+
+def test_moe_nan_logits_route_in_bounds():
+    """NaN router logits are outside the layer's contract, but must not send a
+    row outside the expert range: a token whose logits are all NaN, one with
+    fewer than top-k non-NaN logits, one all -inf.  Every routed id is in
+    [0, E); the other tokens' routing equals the oracle's and their outputs
+    are bit-identical to a run where those three rows hold finite logits
+    (each output row depends only on its own token's routing)."""
+    T, H, E, topk, inter = 48, 256, 8, 2, 256
+    x, logits, w13q, w13s, w2q, w2s = make_case(T, H, E, topk, inter, 17)
+    bad_rows = [5, 9, 30]
+    bad = logits.clone()
+    bad[5, :] = float("nan")
+    bad[9, 1:] = float("nan")            # one finite logit, top-2
+    bad[30, :] = float("-inf")
+    print("CASE moe NaN logits", T, H, E, topk, inter, flush=True)
+    y_bad, _, _, _, ids_bad, _ = run_gpu(x, bad, w13q, w13s, w2q, w2s, topk)
+    y_ok, _, _, _, ids_ok, _ = run_gpu(x, logits, w13q, w13s, w2q, w2s, topk)
+    assert ids_bad.min() >= 0 and ids_bad.max() < E, ids_bad
+    assert ids_bad[9, 0] == 0                  # the one finite logit wins
+    keep = np.setdiff1d(np.arange(T), bad_rows)
+    ref_ids, _ = oracle.route_topk_softmax(logits.double().numpy(), topk)
+    assert np.array_equal(ids_bad[keep], ref_ids[keep])
+    assert np.array_equal(ids_ok, ref_ids)
+    assert np.array_equal(y_bad[keep], y_ok[keep])

@@ -40,7 +40,7 @@ def _dense_moe_via_linear(x, logits, w13q, w13s, w2q, w2s, topk):
             e = ids[t, j]
             h = oracle.linear_ref(x[t:t + 1], w13q[e], w13s[e])[0]
             gate, up = h[:inter], h[inter:]
-            a = oracle.bf16_round(gate / (1 + np.exp(-gate)) * up)
+            a = oracle.bf16_round(torch.nn.functional.silu(torch.from_numpy(gate)).numpy() * up)
             y[t] += wts[t, j] * oracle.linear_ref(a[None, :], w2q[e], w2s[e])[0]
     return y
 
@@ -73,7 +73,13 @@ def test_moe_single_expert_one_hot_closed_form():
     y = oracle.moe_ref(x.double().numpy(), np.zeros((1, 1)), q13[None], s13[None], q2[None], s2[None], 1)
     qa, sa = pins.library_quantize(x)
     a = pins.torch_e4m3_values(qa) * np.repeat(2.0 ** (sa.astype(np.int64) - 127), 32, 1)
-    act = oracle.bf16_round(a / (1 + np.exp(-a)) * (0.5 * a))
+    act = oracle.bf16_round(torch.nn.functional.silu(torch.from_numpy(a)).numpy() * (0.5 * a))
     qb, sb = pins.library_quantize(torch.from_numpy(act).to(torch.bfloat16))
     exp = pins.torch_e4m3_values(qb) * np.repeat(2.0 ** (sb.astype(np.int64) - 127), 32, 1)
     assert np.allclose(y, exp, rtol=0, atol=0)
+
+
+def test_silu_pinned():
+    """The oracle's SiLU against torch's float64 SiLU, the odd-part identity
+    and a closed form (tests/pins.py check_silu)."""
+    pins.check_silu(oracle.moe.silu)

@@ -150,3 +150,20 @@ def test_real_oracle_passes_the_same_checks():
     w = synth.scale_stress(synth.randn_bf16((3, 256), 0.02, g), seed=7)
     b = synth.randn_bf16((3,), 0.1, g)
     pins.check_gemm_bruteforce(lin, oracle.quantize_mx, x, w, b)
+
+
+SILU_MUTANTS = {
+    "exponent sign flipped, z / (1 + e^z)": lambda z: z / (1.0 + np.exp(z)),
+    "sigmoid without the factor z": lambda z: 1.0 / (1.0 + np.exp(-z)),
+    "z * sigmoid(-z)": lambda z: z * np.exp(-z) / (1.0 + np.exp(-z)),
+    "sigmoid of z/2": lambda z: z / (1.0 + np.exp(-z / 2)),
+}
+
+
+@pytest.mark.parametrize("name", list(SILU_MUTANTS))
+def test_silu_mutants_caught(name):
+    assert _caught(lambda: pins.check_silu(SILU_MUTANTS[name]))
+
+
+def test_real_silu_passes():
+    pins.check_silu(oracle.moe.silu)
