@@ -46,7 +46,8 @@ typedef enum {
   MXFP8_E_LD = -4,        /* a leading dimension is too small or not a documented multiple */
   MXFP8_E_WORKSPACE = -5, /* workspace NULL or smaller than the *_workspace_bytes query */
   MXFP8_E_DEVICE = -6,    /* the current device is not gfx950, or no device */
-  MXFP8_E_LAUNCH = -7     /* the HIP runtime reported an error at launch */
+  MXFP8_E_LAUNCH = -7,    /* the HIP runtime reported an error at launch */
+  MXFP8_E_SCRATCH = -8    /* mxfp8_linear_noalloc: the shape needs more than its static scratch */
 } mxfp8_status;
 
 /* Static, human readable text for a status code (never NULL). */
@@ -124,6 +125,24 @@ int mxfp8_linear(const void* x_bf16, int64_t M, int64_t K, int64_t ldx,
                  const void* w_packed, const void* s_packed, int64_t N,
                  const void* bias_bf16, void* y_bf16, int64_t ldy,
                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The same layer for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Arguments, results and errors as mxfp8_linear, without the workspace: the
+ * same kernels use a static device array of MXFP8_NOALLOC_SCRATCH_BYTES
+ * (16 MiB) that each GPU the library runs on holds until the process ends.
+ * A shape whose mxfp8_linear_workspace_bytes exceeds it returns
+ * MXFP8_E_SCRATCH with nothing launched (every M <= 128 at K <= 8192 fits;
+ * larger M fits while its packed activations, and split-K partials, do).
+ * The call allocates nothing and never synchronizes.  All calls on one GPU
+ * share that GPU's array: calls that overlap on one GPU (several streams or
+ * host threads at once) race; order them on one stream.
+ */
+#define MXFP8_NOALLOC_SCRATCH_BYTES (16 * 1024 * 1024)
+int mxfp8_linear_noalloc(const void* x_bf16, int64_t M, int64_t K, int64_t ldx,
+                         const void* w_packed, const void* s_packed, int64_t N,
+                         const void* bias_bf16, void* y_bf16, int64_t ldy, void* stream);
 
 /*
  * W4A8: MXFP4 weights (E2M1 elements, one UE8M0 scale per 32 along K) times

@@ -51,7 +51,11 @@ _SIGNATURES = {
     "mxfp8_prepare_weight_fp4": ([_vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
     "mxfp8_linear_w4a8_workspace_bytes": ([_i64, _i64, _i64, ctypes.POINTER(_sz)], ctypes.c_int),
     "mxfp8_linear_w4a8": ([_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _sz, _vp], ctypes.c_int),
+    "mxfp8_linear_noalloc": ([_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp], ctypes.c_int),
 }
+
+# Static scratch of mxfp8_linear_noalloc (bytes; MXFP8_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024
 
 
 class MXFP8Error(RuntimeError):
@@ -132,6 +136,10 @@ def mxfp8_linear_workspace_bytes(M, N, K):
 
 def mxfp8_linear(x, M, K, ldx, wp, sp, N, bias, y, ldy, ws, ws_bytes, stream):
     return lib().mxfp8_linear(x, M, K, ldx, wp, sp, N, bias, y, ldy, ws, ws_bytes, stream)
+
+
+def mxfp8_linear_noalloc(x, M, K, ldx, wp, sp, N, bias, y, ldy, stream):
+    return lib().mxfp8_linear_noalloc(x, M, K, ldx, wp, sp, N, bias, y, ldy, stream)
 
 
 def mxfp8_quantize_fp4(x, M, K, ldx, q, ldq, s, lds, stream):

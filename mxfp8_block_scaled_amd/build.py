@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmxfp8.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "quant.hip", "pack.hip", "gemm_tile.hip", "gemm_skinny.hip", "gemm_mid.hip", "moe.hip"]
+SOURCES = ["api.cpp", "quant.hip", "pack.hip", "gemm_tile.hip", "gemm_skinny.hip", "gemm_mid.hip", "moe.hip", "noalloc.hip"]
 
 # -packed-fp32-ops: hipcc must not form v_pk_{add,mul,fma}_f32 (the host pass
 # warns that it does not know the feature; that is harmless).

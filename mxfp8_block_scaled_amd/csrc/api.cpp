@@ -145,6 +145,40 @@ int mxfp8::device_cu_count() {
   return n;
 }
 
+int mxfp8::check_device_current() { return check_device(); }
+
+int mxfp8::linear_check_args(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, const void* w_packed,
+                             const void* s_packed, int64_t N, const void* bias_bf16, const void* y_bf16,
+                             int64_t ldy) {
+  if (M < 0) return MXFP8_E_SHAPE;
+  if (int st = check_packed(w_packed, s_packed, N, K)) return st;
+  if (M == 0) return MXFP8_OK;
+  if (M > (int64_t)1 << 30) return MXFP8_E_SHAPE;
+  if (!x_bf16) return MXFP8_E_NULLPTR;
+  if (int st = check_output(y_bf16, N, ldy, bias_bf16)) return st;
+  if (ldx < K || ldx % 8 != 0) return MXFP8_E_LD;
+  if (!aligned(x_bf16, 16)) return MXFP8_E_ALIGN;
+  if (linear_path(M, K) == Path::kTile && (n_pad(M) * (K / 8) + 255) / 256 > INT32_MAX) return MXFP8_E_SHAPE;
+  return MXFP8_OK;
+}
+
+int mxfp8::linear_launch(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, const void* w_packed,
+                         const void* s_packed, int64_t N, const void* bias_bf16, void* y_bf16, int64_t ldy,
+                         void* workspace, hipStream_t s) {
+  const Path path = linear_path(M, K);
+  if (path == Path::kSkinny)
+    return mxfp8::launch_gemm_skinny(x_bf16, ldx, M, K, w_packed, s_packed, N, bias_bf16, y_bf16, ldy, s,
+                                     workspace);
+  if (path == Path::kMid)
+    return mxfp8::launch_gemm_mid(x_bf16, ldx, M, K, w_packed, s_packed, N, bias_bf16, y_bf16, ldy, s, workspace);
+  uint8_t* q = (uint8_t*)workspace;
+  uint8_t* sc = q + round_up((size_t)n_pad(M) * (size_t)K, 256);
+  uint8_t* part = q + tile_ws_act_bytes(M, K);
+  if (int st = mxfp8::launch_quantize_act_packed(x_bf16, M, K, ldx, q, sc, s)) return st;
+  return mxfp8::launch_gemm_tile(q, sc, M, K, w_packed, s_packed, N, bias_bf16, y_bf16, ldy, s,
+                                 mxfp8::gemm_tile_splits(M, N, K), part);
+}
+
 bool mxfp8::set_lds_limit_once(const void* fn, int bytes, std::atomic<int>* flags) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return false;
@@ -169,6 +203,9 @@ const char* mxfp8_status_string(int status) {
     case MXFP8_E_WORKSPACE: return "workspace missing or smaller than mxfp8_linear_workspace_bytes";
     case MXFP8_E_DEVICE: return "current HIP device is not a gfx950 (MI355X) or is unavailable";
     case MXFP8_E_LAUNCH: return "kernel launch failed";
+    case MXFP8_E_SCRATCH:
+      return "shape needs more scratch than mxfp8_linear_noalloc's static maximum (MXFP8_NOALLOC_SCRATCH_BYTES); "
+             "call mxfp8_linear with a workspace";
     default: return "unknown status";
   }
 }
@@ -230,33 +267,15 @@ int mxfp8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes)
 int mxfp8_linear(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, const void* w_packed,
                  const void* s_packed, int64_t N, const void* bias_bf16, void* y_bf16, int64_t ldy,
                  void* workspace, size_t workspace_bytes, void* stream) {
-  if (M < 0) return MXFP8_E_SHAPE;
-  if (int st = check_packed(w_packed, s_packed, N, K)) return st;
+  if (int st = mxfp8::linear_check_args(x_bf16, M, K, ldx, w_packed, s_packed, N, bias_bf16, y_bf16, ldy)) return st;
   if (M == 0) return MXFP8_OK;
-  if (M > (int64_t)1 << 30) return MXFP8_E_SHAPE;
-  if (!x_bf16) return MXFP8_E_NULLPTR;
-  if (int st = check_output(y_bf16, N, ldy, bias_bf16)) return st;
-  if (ldx < K || ldx % 8 != 0) return MXFP8_E_LD;
-  if (!aligned(x_bf16, 16)) return MXFP8_E_ALIGN;
-  const Path path = linear_path(M, K);
-  if (path == Path::kTile && (n_pad(M) * (K / 8) + 255) / 256 > INT32_MAX) return MXFP8_E_SHAPE;
   size_t need = 0;
   mxfp8_linear_workspace_bytes(M, N, K, &need);
   if (!workspace || workspace_bytes < need) return MXFP8_E_WORKSPACE;
   if (!aligned(workspace, 256)) return MXFP8_E_ALIGN;
   if (int st = check_device()) return st;
-  hipStream_t s = (hipStream_t)stream;
-  if (path == Path::kSkinny)
-    return mxfp8::launch_gemm_skinny(x_bf16, ldx, M, K, w_packed, s_packed, N, bias_bf16, y_bf16, ldy, s,
-                                     workspace);
-  if (path == Path::kMid)
-    return mxfp8::launch_gemm_mid(x_bf16, ldx, M, K, w_packed, s_packed, N, bias_bf16, y_bf16, ldy, s, workspace);
-  uint8_t* q = (uint8_t*)workspace;
-  uint8_t* sc = q + round_up((size_t)n_pad(M) * (size_t)K, 256);
-  uint8_t* part = q + tile_ws_act_bytes(M, K);
-  if (int st = mxfp8::launch_quantize_act_packed(x_bf16, M, K, ldx, q, sc, s)) return st;
-  return mxfp8::launch_gemm_tile(q, sc, M, K, w_packed, s_packed, N, bias_bf16, y_bf16, ldy, s,
-                                 mxfp8::gemm_tile_splits(M, N, K), part);
+  return mxfp8::linear_launch(x_bf16, M, K, ldx, w_packed, s_packed, N, bias_bf16, y_bf16, ldy, workspace,
+                              (hipStream_t)stream);
 }
 
 // ---------------------------------------------------------------- W4A8

@@ -18,6 +18,17 @@ constexpr int kMaxDevices = 64;
 // Returns false if the device is out of range or the runtime refused.
 bool set_lds_limit_once(const void* fn, int bytes, std::atomic<int>* flags);
 
+// MXFP8_OK if the current device is a gfx950 (cached per device).
+int check_device_current();
+
+// The host-side argument checks of mxfp8_linear (everything but the
+// workspace and the device), and its launches once they passed (M >= 1,
+// workspace of mxfp8_linear_workspace_bytes, device checked).
+int linear_check_args(const void* x, int64_t M, int64_t K, int64_t ldx, const void* wp, const void* sp, int64_t N,
+                      const void* bias, const void* y, int64_t ldy);
+int linear_launch(const void* x, int64_t M, int64_t K, int64_t ldx, const void* wp, const void* sp, int64_t N,
+                  const void* bias, void* y, int64_t ldy, void* workspace, hipStream_t stream);
+
 int launch_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx, void* q, int64_t ldq, void* s,
                         int64_t lds, hipStream_t stream);
 

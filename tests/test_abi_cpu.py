@@ -30,8 +30,8 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings():
-    for s in range(0, -8, -1):
-        assert api.mxfp8_status_string(s)
+    for s in range(0, -9, -1):
+        assert api.mxfp8_status_string(s) != "unknown status"
     assert api.mxfp8_status_string(-99) == "unknown status"
 
 
@@ -258,3 +258,19 @@ def test_quantize_fp4_validation():
     assert f(P, 4, 64, 64, P, 34, P, 2, None) == -4          # ldq % 4
     assert f(P, 4, 64, 64, P + 2, 32, P, 2, None) == -3      # q alignment
     assert f(None, 4, 64, 64, P, 32, P, 2, None) == -1
+
+
+def test_noalloc_validation():
+    """mxfp8_linear_noalloc: mxfp8_linear's checks, then the static scratch
+    limit (MXFP8_E_SCRATCH), all before any device call."""
+    f = api.mxfp8_linear_noalloc
+    ok = (P, 64, 512, 512, P, P, 256, None, P, 256, None)
+    expect_no_device(f, *ok)
+    bad = list(ok); bad[2] = 320; assert f(*bad) == -2          # K % 256
+    bad = list(ok); bad[1] = 0; assert f(*bad) == 0             # M == 0 no-op
+    bad = list(ok); bad[0] = None; assert f(*bad) == -1
+    bad = list(ok); bad[9] = 100; assert f(*bad) == -4          # ldy < N
+    bad = list(ok); bad[4] = P + 64; assert f(*bad) == -3
+    assert api.mxfp8_linear_workspace_bytes(16384, 5120, 2048) > api.NOALLOC_SCRATCH_BYTES
+    assert f(P, 16384, 2048, 2048, P, P, 5120, None, P, 5120, None) == -8
+    assert api.mxfp8_linear_workspace_bytes(128, 4096, 8192) <= api.NOALLOC_SCRATCH_BYTES
