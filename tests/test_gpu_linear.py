@@ -284,3 +284,48 @@ def test_persistent_ragged_sampled(M, N, K):
     xn = x[rows].to(torch.float64).numpy()
     r = oracle.linear_ref(xn, wq, ws, b[cols].to(torch.float64).numpy())
     gpu_util.compare(ys, r, gpu_util.tolerance(xn, wq, ws, len(cols), K), f"persistent {M}x{N}x{K} sampled")
+
+
+def _strided_case(M, N, K, seed):
+    g = torch.Generator().manual_seed(seed)
+    x = synth.scale_stress(synth.randn_bf16((M, K), 1.0, g), seed=seed + 1)
+    w = synth.scale_stress(synth.randn_bf16((N, K), 0.02, g), seed=seed + 2)
+    b = synth.randn_bf16((N,), 0.1, g)
+    return x, w, b
+
+
+@pytest.mark.parametrize("path,M", [(0, 7), (1, 7), (0, 100), (1, 100), (0, 300)])
+def test_strided_io_and_canary(path, M):
+    """ldx > K and ldy > N through the C ABI on every GEMM path (decode and
+    mid-M kernels automatic at M = 7 and 100, the tile GEMM forced there and
+    automatic at M = 300): x is a view into a wider buffer whose extra
+    columns hold huge values, y is written into a wider buffer whose columns
+    >= N hold a canary.  The canary must survive, the extra x columns must
+    not leak into the result, and y[:, :N] matches the oracle."""
+    N, K = 200, 768
+    x, w, b = _strided_case(M, N, K, seed=M + path)
+    d = gpu_util.dev()
+    ldx, ldy = K + 72, N + 24
+    xbuf = torch.full((M, ldx), 3.0e38, dtype=torch.bfloat16)
+    xbuf[:, :K] = x
+    xbuf = xbuf.to(d)
+    ybuf = torch.full((M, ldy), -7.0, dtype=torch.bfloat16, device=d)
+    pw = gpu_util.gpu_prepare(w)
+    bd = b.to(d)
+    prev = api.mxfp8_debug_force_path(path)
+    try:
+        ws = torch.zeros(api.mxfp8_linear_workspace_bytes(M, N, K), dtype=torch.uint8, device=d)
+        st = api.mxfp8_linear(xbuf.data_ptr(), M, K, ldx, pw.w_packed.data_ptr(), pw.s_packed.data_ptr(), N,
+                              bd.data_ptr(), ybuf.data_ptr(), ldy, ws.data_ptr(), ws.numel(),
+                              torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+    finally:
+        api.mxfp8_debug_force_path(prev)
+    assert st == 0
+    yb = ybuf.float().cpu().numpy()
+    assert np.all(yb[:, N:] == -7.0), "columns >= N were written"
+    wq, wsc = gpu_util.oracle_weight(w)
+    xn = x.to(torch.float64).numpy()
+    r = oracle.linear_ref(xn, wq, wsc, b.to(torch.float64).numpy())
+    gpu_util.compare(yb[:, :N], r, gpu_util.tolerance(xn, wq, wsc, N, K), f"strided path{path} M{M}")
+

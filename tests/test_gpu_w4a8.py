@@ -85,7 +85,7 @@ def test_one_hot_weight_exact(M):
     """W[n, perm[n]] = 1 (E2M1 code 6 = 4 under scale 2^-2): y[m, n] =
     bf16(deq(A)[m, perm[n]]) exactly.  Pins the 4-bit operand's nibble order,
     lane mapping and the weight scale lookup (M = 5: decode kernel), and the
-    widening to E4M3 tiles (M = 40: tile GEMM)."""
+    4-bit operand of the mid-M kernel (M = 40)."""
     g = torch.Generator().manual_seed(17)
     K, N = 512, 200
     x = synth.scale_stress(synth.randn_bf16((M, K), 1.0, g), seed=9)
@@ -120,3 +120,25 @@ def test_w4a8_matches_mxfp8_on_widened_weight():
     finally:
         api.mxfp8_debug_force_path(prev)
     assert torch.equal(y8, y4)
+
+
+@pytest.mark.parametrize("path", [1, 3])
+def test_one_hot_weight_exact_forced(path):
+    """The one-hot pin at M = 40 on the widened tile GEMM (path 1) and on the
+    mid-M kernel's 4-bit operand (path 3)."""
+    g = torch.Generator().manual_seed(18)
+    M, K, N = 40, 1024, 200
+    x = synth.scale_stress(synth.randn_bf16((M, K), 1.0, g), seed=10)
+    perm = torch.randint(0, K, (N,), generator=g).numpy()
+    w = np.zeros((N, K))
+    w[np.arange(N), perm] = 1.0
+    codes, ws = oracle.quantize_mxfp4(w)
+    pw = prepare(codes, ws)
+    prev = api.mxfp8_debug_force_path(path)
+    try:
+        y = api.linear(x.to(gpu_util.dev()), pw).float().cpu().numpy()
+    finally:
+        api.mxfp8_debug_force_path(prev)
+    qa, sa = oracle.quantize_mx(x.double().numpy())
+    exp = oracle.bf16_round(oracle.dequantize_mx(qa, sa)[:, perm])
+    assert np.array_equal(y, exp)

@@ -20,7 +20,7 @@ def _call_both(x, pw, bias, N):
     bp = None if bias is None else bias.data_ptr()
     y_ref = torch.full((M, N + 8), 7.0, dtype=torch.bfloat16, device=d)   # ldy > N: columns >= N untouched
     y_new = torch.full((M, N + 8), 7.0, dtype=torch.bfloat16, device=d)
-    ws = torch.empty(api.mxfp8_linear_workspace_bytes(M, N, K), dtype=torch.uint8, device=d)
+    ws = torch.zeros(api.mxfp8_linear_workspace_bytes(M, N, K), dtype=torch.uint8, device=d)
     assert api.mxfp8_linear(x.data_ptr(), M, K, K, pw.w_packed.data_ptr(), pw.s_packed.data_ptr(), N, bp,
                             y_ref.data_ptr(), N + 8, ws.data_ptr(), ws.numel(), s) == 0
     assert api.mxfp8_linear_noalloc(x.data_ptr(), M, K, K, pw.w_packed.data_ptr(), pw.s_packed.data_ptr(), N, bp,
