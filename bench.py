@@ -17,8 +17,14 @@ workload shapes (M=7 single layer, the decode sweep M in {1,7,16,128} at
 N=K=4096 with the weights rotated through 48 copies so they do not sit in the
 256 MB last-level cache, the M=16384 prefill shape, and the standalone
 quantizer, and one forward of the routed MoE layer at its full size);
-``cpu_baseline``, the CPU oracle timed on a bounded sample of the headline
-workload.
+``ceilings``, what this GPU sustains as measured by the calibration kernels
+of libmxfp8_calib.so (scaled-MFMA rate, 1 GiB HBM read rate, one 16 MiB read
+per launch), with the headline GEMM's fraction of the measured MFMA rate
+(``roofline.frac_of_measured``) and each sweep row's fraction of the
+measured read rate; ``cpu_baseline``, the CPU oracle timed on a bounded
+sample of the headline workload.  The untimed warm-up runs at least
+``--warmup`` steps and at least ``--warmup-ms`` (300) of wall time, since
+the clock ramps up over the first ~50 ms of load.
 """
 
 import argparse
@@ -43,7 +49,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=50,
-                   help="untimed steps first (the GPU clock ramps up over the first ~50 ms of load)")
+                   help="untimed steps first; the warm-up also runs for at least --warmup-ms of wall time "
+                        "(the GPU clock ramps up over the first ~50 ms of load)")
+    p.add_argument("--warmup-ms", type=float, default=300.0)
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--calib-copy", action="store_true",
@@ -115,9 +123,16 @@ def main():
         if st != 0:
             raise RuntimeError(f"launch failed: {st}")
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    # Untimed warm-up: at least --warmup steps and at least --warmup-ms of
+    # wall time, whichever is longer.
+    tw0 = time.perf_counter()
+    nwarm = 0
+    while nwarm < args.warmup or (time.perf_counter() - tw0) * 1e3 < args.warmup_ms:
+        for _ in range(10):
+            step()
+        nwarm += 10
+        torch.cuda.synchronize()
+    warmup_ms = (time.perf_counter() - tw0) * 1e3
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -154,6 +169,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": nwarm,
+        "warmup_ms": round(warmup_ms, 1),
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -173,8 +190,22 @@ def main():
     }
     del q, s, y, x
 
+    # Measured ceilings of this GPU (calibration kernels), and the headline
+    # GEMM against the measured MFMA rate.
+    ceil = ceilings(torch, dev, stream)
+    out["ceilings"] = ceil
+    if ceil.get("mfma_tflops"):
+        out["roofline"]["frac_of_measured"] = round(gemm_tflops / ceil["mfma_tflops"], 4)
+
     if not args.no_sweep:
         out["sweep"] = sweep(api, synth, torch, np, dev, stream)
+        floor = ceil.get("read_16mib_us")
+        for row in out["sweep"]:
+            if floor and row.get("workload", "").startswith("decode M="):
+                # the weight read alone (16 MiB + scales) at the measured floor
+                row["pct_of_read_floor"] = round(100 * floor * (4096 * 4096 * (1 + 1 / 32)) / (16 << 20) / row["us"], 1)
+            if ceil.get("hbm_read_gbs") and "GB/s" in row:
+                row["pct_of_measured_hbm"] = round(100 * row["GB/s"] / ceil["hbm_read_gbs"], 1)
 
     if args.calib_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -188,6 +219,63 @@ def main():
         out["cpu_baseline"] = cpu_baseline(synth, np, torch)
 
     print(json.dumps(out))
+
+
+def ceilings(torch, dev, stream):
+    """What this GPU sustains, measured with libmxfp8_calib.so: the scaled
+    16x16x128 MFMA rate over a grid that fills the chip, the HBM read rate
+    of a 1 GiB stream, and the time of one 16 MiB read per launch rotating
+    over 48 copies (the floor of a decode-sized weight read)."""
+    import ctypes
+    path = os.path.join(ROOT, "mxfp8_block_scaled_amd", "libmxfp8_calib.so")
+    if not os.path.exists(path):
+        return {"error": "libmxfp8_calib.so not built"}
+    lib = ctypes.CDLL(path)
+    vp = ctypes.c_void_p
+    lib.mxfp8_calib_read.argtypes = [vp, ctypes.c_uint64, ctypes.c_int, vp, vp]
+    lib.mxfp8_calib_mfma.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp]
+    sptr = stream.cuda_stream
+    out = {}
+    # scaled MFMA: 4096 waves x iters x 8 MFMAs of 2*16*16*128 flops
+    blocks, iters = 1024, 1500
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    for _ in range(3):
+        lib.mxfp8_calib_mfma(blocks, iters, sink.data_ptr(), sptr)
+    torch.cuda.synchronize()
+    ms = min(time_calls(lambda r: lib.mxfp8_calib_mfma(blocks, iters, sink.data_ptr(), sptr), 5, stream, torch)
+             for _ in range(3))
+    flops = blocks * 4 * iters * 8 * 2.0 * 16 * 16 * 128
+    out["mfma_tflops"] = round(flops / (ms * 1e-3) / 1e12, 1)
+    # 1 GiB read stream (best of two grid sizes)
+    big = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    words = torch.empty(8192, dtype=torch.int32, device=dev)
+    best = None
+    for blocks in (4096, 8192):
+        for _ in range(3):
+            lib.mxfp8_calib_read(big.data_ptr(), big.numel(), blocks, words.data_ptr(), sptr)
+        torch.cuda.synchronize()
+        ms = min(time_calls(lambda r: lib.mxfp8_calib_read(big.data_ptr(), big.numel(), blocks, words.data_ptr(),
+                                                           sptr), 10, stream, torch) for _ in range(3))
+        best = ms if best is None else min(best, ms)
+    out["hbm_read_gbs"] = round(big.numel() / (best * 1e-3) / 1e9, 1)
+    del big
+    # one 16 MiB read per launch over 48 rotated copies (> 3x the last-level
+    # cache), best of three grid sizes
+    n16 = 16 << 20
+    pool = torch.empty(48 * n16, dtype=torch.uint8, device=dev)
+    best = None
+    for blocks in (512, 1024, 2048):
+        for r in range(96):
+            lib.mxfp8_calib_read(pool.data_ptr() + (r % 48) * n16, n16, blocks, words.data_ptr(), sptr)
+        torch.cuda.synchronize()
+        ms = min(time_calls(lambda r: lib.mxfp8_calib_read(pool.data_ptr() + (r % 48) * n16, n16, blocks,
+                                                           words.data_ptr(), sptr), 480, stream, torch)
+                 for _ in range(3))
+        best = ms if best is None else min(best, ms)
+    out["read_16mib_us"] = round(best * 1e3, 3)
+    del pool
+    print(f"ceilings: {out}", file=sys.stderr, flush=True)
+    return out
 
 
 def time_calls(fn, reps, stream, torch):
@@ -370,7 +458,8 @@ def cpu_baseline(synth, np, torch):
     4096 activation rows x 16384 weight rows x the full K = 8192, drawn with
     the workload's distributions (quantize both, exact dequantized fp64
     product, bias; about 10-20 s on a 16-core host).  Reported in the
-    metric's unit."""
+    metric's unit.  cores: the threads it used (the BLAS pool; the
+    quantization runs on one); host_cpus: os.cpu_count()."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -389,7 +478,7 @@ def cpu_baseline(synth, np, torch):
     dt = time.perf_counter() - t0
     flops = 2.0 * Ms * Ns * K
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas_threads),
-            "kind": "oracle", "seconds": round(dt, 2),
+            "host_cpus": os.cpu_count(), "kind": "oracle", "seconds": round(dt, 2),
             "sample": f"M={Ms} x N={Ns} x K={K} slice of the M=8192 N=28672 K=8192 "
                       "workload: MX-quantize x and W (numpy, 1 thread), fp64 dequantized product "
                       "(BLAS threads) + bias"}

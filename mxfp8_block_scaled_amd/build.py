@@ -19,6 +19,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmxfp8.so")
+# The benchmark's calibration kernels (read stream, scaled-MFMA loop): a
+# library of their own, outside the layer's C ABI.
+CALIB_LIB = os.path.join(PKG, "libmxfp8_calib.so")
+CALIB_SOURCES = ["calib.hip"]
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "quant.hip", "pack.hip", "gemm_tile.hip", "gemm_skinny.hip", "gemm_mid.hip", "moe.hip", "noalloc.hip"]
@@ -48,18 +52,24 @@ def _compile(src):
     return obj
 
 
-def build(verbose=True):
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC"] + objs + ["-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr[-4000:]}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose=True):
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + CALIB_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[: len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], CALIB_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CALIB_LIB}")
     return LIB
 
 

@@ -274,3 +274,21 @@ def test_noalloc_validation():
     assert api.mxfp8_linear_workspace_bytes(16384, 5120, 2048) > api.NOALLOC_SCRATCH_BYTES
     assert f(P, 16384, 2048, 2048, P, P, 5120, None, P, 5120, None) == -8
     assert api.mxfp8_linear_workspace_bytes(128, 4096, 8192) <= api.NOALLOC_SCRATCH_BYTES
+
+
+def test_calibration_library_exports_and_rejects():
+    """The benchmark's calibration library (read stream, scaled-MFMA loop)
+    loads, exports its two entry points and rejects invalid arguments before
+    any launch."""
+    path = os.path.join(os.path.dirname(api.lib_path()), "libmxfp8_calib.so")
+    if not os.path.exists(path):
+        pytest.skip("libmxfp8_calib.so not built")
+    lib = ctypes.CDLL(path)
+    vp = ctypes.c_void_p
+    lib.mxfp8_calib_read.argtypes = [vp, ctypes.c_uint64, ctypes.c_int, vp, vp]
+    lib.mxfp8_calib_mfma.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp]
+    assert lib.mxfp8_calib_read(None, 1 << 20, 64, P, None) == -2
+    assert lib.mxfp8_calib_read(P, (1 << 20) + 16, 64, P, None) == -2       # not 16 * blocks divisible
+    assert lib.mxfp8_calib_read(P + 8, 1 << 20, 64, P, None) == -2          # alignment
+    assert lib.mxfp8_calib_mfma(0, 10, P, None) == -2
+    assert lib.mxfp8_calib_mfma(4, 10, None, None) == -2
