@@ -217,6 +217,25 @@ int mxfp8_gemm_packed(const void* q_packed, const void* s_packed, int64_t M, int
                       void* y_bf16, int64_t ldy, void* stream);
 
 /*
+ * Test entry: step 3 alone on activations quantized elsewhere, in the
+ * boundary's row-major layout (the GEMM given quantized A: the output of
+ * mxfp8_quantize_act, or of a reference quantizer, drives the block-scaled
+ * GEMM + epilogue directly, so the GEMM can be checked apart from the
+ * quantizer):
+ *   q_e4m3 [M, K] bytes, row stride ldq (ldq >= K, ldq % 16 == 0, 16-byte aligned)
+ *   s_e8m0 [M, >= K/32] bytes, row stride lds (lds >= K/32)
+ *   other arguments as mxfp8_linear; workspace of at least
+ *   mxfp8_gemm_prequant_workspace_bytes(M, N, K), 256-byte aligned, no
+ *   initialization needed (it receives the activations in the packed layout).
+ * Always the large-tile GEMM (for every M), so its output equals
+ * mxfp8_linear's on that path bit for bit.
+ */
+int mxfp8_gemm_prequant_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes);
+int mxfp8_gemm_prequant(const void* q_e4m3, int64_t ldq, const void* s_e8m0, int64_t lds, int64_t M, int64_t K,
+                        const void* w_packed, const void* ws_packed, int64_t N, const void* bias_bf16, void* y_bf16,
+                        int64_t ldy, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * ---------------------------------------------------------------------------
  * Top-k routed MXFP8 mixture-of-experts layer (the grouped variant).
  *

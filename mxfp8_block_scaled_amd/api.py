@@ -52,6 +52,9 @@ _SIGNATURES = {
     "mxfp8_linear_w4a8_workspace_bytes": ([_i64, _i64, _i64, ctypes.POINTER(_sz)], ctypes.c_int),
     "mxfp8_linear_w4a8": ([_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _sz, _vp], ctypes.c_int),
     "mxfp8_linear_noalloc": ([_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp], ctypes.c_int),
+    "mxfp8_gemm_prequant_workspace_bytes": ([_i64, _i64, _i64, ctypes.POINTER(_sz)], ctypes.c_int),
+    "mxfp8_gemm_prequant": ([_vp, _i64, _vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _sz, _vp],
+                            ctypes.c_int),
 }
 
 # Static scratch of mxfp8_linear_noalloc (bytes; MXFP8_NOALLOC_SCRATCH_BYTES).
@@ -194,6 +197,36 @@ def mxfp8_quantize_act_packed(x, M, K, ldx, qp, sp, stream):
 
 def mxfp8_gemm_packed(qp, sp, M, K, wp, wsp, N, bias, y, ldy, stream):
     return lib().mxfp8_gemm_packed(qp, sp, M, K, wp, wsp, N, bias, y, ldy, stream)
+
+
+def mxfp8_gemm_prequant_workspace_bytes(M, N, K):
+    b = _sz()
+    _check(lib().mxfp8_gemm_prequant_workspace_bytes(M, N, K, ctypes.byref(b)), "mxfp8_gemm_prequant_workspace_bytes")
+    return b.value
+
+
+def mxfp8_gemm_prequant(q, ldq, s, lds, M, K, wp, wsp, N, bias, y, ldy, ws, ws_bytes, stream):
+    return lib().mxfp8_gemm_prequant(q, ldq, s, lds, M, K, wp, wsp, N, bias, y, ldy, ws, ws_bytes, stream)
+
+
+def gemm_prequant(q, s, pw, bias=None):
+    """The block-scaled GEMM + epilogue on row-major quantized activations
+    (uint8 E4M3 ``q[M, K]``, UE8M0 ``s[M, >= K/32]``, GPU): bf16 ``[M, N]``."""
+    q = _as_bytes(q)
+    s = _as_bytes(s)
+    _require_cuda(q, "q")
+    if q.stride(-1) != 1 or q.stride(0) % 16 != 0 or q.data_ptr() % 16 != 0:
+        q = q.contiguous()
+    if s.stride(-1) != 1:
+        s = s.contiguous()
+    M, K = q.shape
+    assert K == pw.K
+    y = torch.empty((M, pw.N), dtype=torch.bfloat16, device=q.device)
+    ws = torch.empty(mxfp8_gemm_prequant_workspace_bytes(M, pw.N, K), dtype=torch.uint8, device=q.device)
+    _check(mxfp8_gemm_prequant(_ptr(q), q.stride(0), _ptr(s), s.stride(0), M, K, _ptr(pw.w_packed), _ptr(pw.s_packed),
+                               pw.N, _ptr(bias), _ptr(y), y.stride(0), _ptr(ws), ws.numel(), _stream(q.device)),
+           "mxfp8_gemm_prequant")
+    return y
 
 
 def mxfp8_debug_force_path(path):

@@ -397,6 +397,41 @@ int mxfp8_gemm_packed(const void* q_packed, const void* s_packed, int64_t M, int
                                  (hipStream_t)stream);
 }
 
+int mxfp8_gemm_prequant_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes) {
+  if (!bytes) return MXFP8_E_NULLPTR;
+  if (M < 0 || N < 1 || K < 256 || K % 256 != 0) return MXFP8_E_SHAPE;
+  *bytes = M == 0 ? 256 : tile_ws_bytes(M, N, K);
+  return MXFP8_OK;
+}
+
+int mxfp8_gemm_prequant(const void* q_e4m3, int64_t ldq, const void* s_e8m0, int64_t lds, int64_t M, int64_t K,
+                        const void* w_packed, const void* ws_packed, int64_t N, const void* bias_bf16, void* y_bf16,
+                        int64_t ldy, void* workspace, size_t workspace_bytes, void* stream) {
+  if (M < 0) return MXFP8_E_SHAPE;
+  if (int st = check_packed(w_packed, ws_packed, N, K)) return st;
+  if (M == 0) return MXFP8_OK;
+  if (M > (int64_t)1 << 30) return MXFP8_E_SHAPE;
+  if (!q_e4m3 || !s_e8m0) return MXFP8_E_NULLPTR;
+  if (int st = check_output(y_bf16, N, ldy, bias_bf16)) return st;
+  if (ldq < K || ldq % 16 != 0 || lds < K / 32) return MXFP8_E_LD;
+  if (!aligned(q_e4m3, 16)) return MXFP8_E_ALIGN;
+  if ((n_pad(M) * (K / 8) + 255) / 256 > INT32_MAX) return MXFP8_E_SHAPE;
+  size_t need = 0;
+  mxfp8_gemm_prequant_workspace_bytes(M, N, K, &need);
+  if (!workspace || workspace_bytes < need) return MXFP8_E_WORKSPACE;
+  if (!aligned(workspace, 256)) return MXFP8_E_ALIGN;
+  if (int st = check_device()) return st;
+  hipStream_t s = (hipStream_t)stream;
+  // The row-major quantized activations packed like a weight (pad rows zero;
+  // their scale byte does not reach the output), then the tile GEMM.
+  uint8_t* q = (uint8_t*)workspace;
+  uint8_t* sc = q + round_up((size_t)n_pad(M) * (size_t)K, 256);
+  uint8_t* part = q + tile_ws_act_bytes(M, K);
+  if (int st = mxfp8::launch_pack_weight(q_e4m3, s_e8m0, M, K, ldq, lds, q, sc, s)) return st;
+  return mxfp8::launch_gemm_tile(q, sc, M, K, w_packed, ws_packed, N, bias_bf16, y_bf16, ldy, s,
+                                 mxfp8::gemm_tile_splits(M, N, K), part);
+}
+
 int mxfp8_moe_prepared_bytes(int64_t E, int64_t H, int64_t I, size_t* w13_bytes, size_t* s13_bytes,
                              size_t* w2_bytes, size_t* s2_bytes) {
   if (!w13_bytes || !s13_bytes || !w2_bytes || !s2_bytes) return MXFP8_E_NULLPTR;

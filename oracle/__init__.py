@@ -13,6 +13,7 @@ from .mx import (  # noqa: F401
     e4m3_decode,
     e4m3_encode,
     e8m0_decode,
+    gemm_dequant,
     linear_ref,
     quantize_mx,
     scale_exponent,

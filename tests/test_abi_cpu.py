@@ -292,3 +292,25 @@ def test_calibration_library_exports_and_rejects():
     assert lib.mxfp8_calib_read(P + 8, 1 << 20, 64, P, None) == -2          # alignment
     assert lib.mxfp8_calib_mfma(0, 10, P, None) == -2
     assert lib.mxfp8_calib_mfma(4, 10, None, None) == -2
+
+
+def test_gemm_prequant_validation():
+    """mxfp8_gemm_prequant (the GEMM given row-major quantized activations):
+    sizes and argument checks, all before any device call."""
+    ws = api.mxfp8_gemm_prequant_workspace_bytes(300, 130, 512)
+    assert ws >= 384 * 512 + 384 * 16
+    assert api.mxfp8_gemm_prequant_workspace_bytes(0, 130, 512) == 256
+    with pytest.raises(api.MXFP8Error):
+        api.mxfp8_gemm_prequant_workspace_bytes(300, 130, 500)
+    f = api.mxfp8_gemm_prequant
+    ok = (P, 512, P, 16, 300, 512, P, P, 130, None, P, 130, P, ws, None)
+    expect_no_device(f, *ok)
+    bad = list(ok); bad[4] = 0; assert f(*bad) == 0              # M == 0 no-op
+    bad = list(ok); bad[5] = 320; assert f(*bad) == -2           # K % 256
+    bad = list(ok); bad[0] = None; assert f(*bad) == -1
+    bad = list(ok); bad[1] = 500; assert f(*bad) == -4           # ldq < K
+    bad = list(ok); bad[1] = 520; assert f(*bad) == -4           # ldq % 16
+    bad = list(ok); bad[3] = 15; assert f(*bad) == -4            # lds < K/32
+    bad = list(ok); bad[0] = P + 8; assert f(*bad) == -3         # q alignment
+    bad = list(ok); bad[13] = ws - 1; assert f(*bad) == -5
+    bad = list(ok); bad[11] = 100; assert f(*bad) == -4          # ldy < N

@@ -329,3 +329,58 @@ def test_strided_io_and_canary(path, M):
     r = oracle.linear_ref(xn, wq, wsc, b.to(torch.float64).numpy())
     gpu_util.compare(yb[:, :N], r, gpu_util.tolerance(xn, wq, wsc, N, K), f"strided path{path} M{M}")
 
+
+
+def _prequant_bound(A, W, r, K):
+    acc = (K / 64.0) * 2.0 ** -10 * np.outer(np.abs(A).max(axis=1), np.abs(W).max(axis=1)) \
+        + K * 2.0 ** -23 * (np.abs(A) @ np.abs(W).T)
+    return (1 + 2.0 ** -8) * acc + 2.0 ** -133
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 130, 512), (256, 2048, 4096), (7, 384, 768), (129, 200, 1024)])
+def test_gemm_prequant_oracle_codes(M, N, K):
+    """The GEMM alone, driven by activations the oracle's side chose: random
+    E4M3 codes (every finite code, both signs) and random scale bytes, in
+    the boundary's row-major layout through mxfp8_gemm_prequant.  The result
+    is checked against the oracle's exact dequantized product with the GEMM
+    bound, so a GEMM error cannot hide behind a matching quantizer error.
+    (256, 2048, 4096) has 8 tiles: K split 8 ways."""
+    rng = np.random.default_rng(M * 7 + N + K)
+    codes = rng.integers(0, 254, size=(M, K), dtype=np.int64)
+    qa = np.where(codes >= 0x7F, codes + 1, codes).astype(np.uint8)     # skip the NaN code 0x7F (and 0xFF)
+    sa = rng.integers(110, 140, size=(M, K // 32 + 3), dtype=np.int64).astype(np.uint8)   # wider than K/32
+    g = torch.Generator().manual_seed(M + N)
+    w = synth.scale_stress(synth.randn_bf16((N, K), 0.02, g), seed=N)
+    bias = synth.randn_bf16((N,), 0.1, g)
+    pw = gpu_util.gpu_prepare(w)
+    d = gpu_util.dev()
+    y = api.gemm_prequant(torch.from_numpy(qa).to(d), torch.from_numpy(sa).to(d), pw, bias.to(d))
+    torch.cuda.synchronize()
+    wq, ws = gpu_util.oracle_weight(w)
+    A = oracle.dequantize_mx(qa, sa[:, : K // 32])
+    W = oracle.dequantize_mx(wq, ws)
+    r = oracle.gemm_dequant(qa, sa[:, : K // 32], wq, ws) + bias.to(torch.float64).numpy()[None, :]
+    gpu_util.compare(y.float().cpu().numpy(), r, _prequant_bound(A, W, r, K), f"prequant {M}x{N}x{K}")
+
+
+def test_gemm_prequant_matches_linear_tile_path():
+    """Quantizing on the GPU and feeding the bytes to mxfp8_gemm_prequant
+    gives mxfp8_linear's tile-path output bit for bit (the same GEMM on the
+    same packed bytes; pad rows differ only in a scale byte that multiplies
+    zeros)."""
+    g = torch.Generator().manual_seed(12)
+    d = gpu_util.dev()
+    for M, N, K in [(300, 640, 1024), (64, 256, 512)]:
+        x = synth.scale_stress(synth.randn_bf16((M, K), 1.0, g), seed=M).to(d)
+        w = synth.randn_bf16((N, K), 0.02, g)
+        b = synth.randn_bf16((N,), 0.1, g).to(d)
+        pw = gpu_util.gpu_prepare(w)
+        q, s = api.quantize_act(x)
+        y1 = api.gemm_prequant(q, s, pw, b)
+        prev = api.mxfp8_debug_force_path(1)
+        try:
+            y2 = api.linear(x, pw, b)
+        finally:
+            api.mxfp8_debug_force_path(prev)
+        torch.cuda.synchronize()
+        assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), (M, N, K)
