@@ -130,6 +130,17 @@ Path linear_path(int64_t M, int64_t K) {
 
 }  // namespace
 
+// K splits of the tile GEMM: a shape with fewer than 128 256x256 tiles splits
+// K over up to 8 workgroups per tile (each slice a multiple of four 64-K
+// steps) while tiles x splits stays within 256.
+int mxfp8::gemm_tile_splits(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t KS = K / 64;
+  int s = 1;
+  while (s < kMaxSplitK && tiles * s * 2 <= 256 && KS % (8 * s) == 0) s *= 2;
+  return tiles < 128 ? s : 1;
+}
+
 // Compute units of the current device (the persistent GEMM's grid); the
 // device check caches it on the first call of any entry point.
 int mxfp8::device_cu_count() {

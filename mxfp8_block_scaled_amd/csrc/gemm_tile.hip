@@ -149,14 +149,6 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   if (n + 3 < N) d[3] = (uint16_t)(hi >> 16);
 }
 
-int gemm_tile_splits(int64_t M, int64_t N, int64_t K) {
-  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  const int64_t KS = K / kStepK;
-  int s = 1;
-  while (s < kMaxSplitK && tiles * s * 2 <= 256 && KS % (8 * s) == 0) s *= 2;
-  return tiles < 128 ? s : 1;
-}
-
 int launch_gemm_tile(const void* qp, const void* sp, int64_t M, int64_t K, const void* wp, const void* wsp,
                      int64_t N, const void* bias, void* y, int64_t ldy, hipStream_t stream, int splits,
                      void* part) {
