@@ -109,7 +109,7 @@ size_t moe_layout(int64_t T, int64_t H, int64_t E, int64_t topk, int64_t I, uint
   v.a1s = take(p_max * (H / 32));
   v.a2q = take(p_max * I);
   v.a2s = take(p_max * (I / 32));
-  v.ys = (float*)take(R * H * 4);
+  v.ys = (uint16_t*)take(R * H * 2);
   v.p_max = p_max;
   v.mt_max = mt_max;
   if (w) *w = v;

@@ -12,7 +12,8 @@
 //              over those k;
 //   h        = deq(q(x_t)) . deq(W13[e])^T            for each selected e,
 //   act      = bf16( silu(h[:I]) * h[I:] ),  q(act) = MX quantization along I,
-//   y_t      = bf16( sum_j w_j . deq(q(act_j)) . deq(W2[e_j])^T ), rounded once.
+//   o_j      = bf16( deq(q(act_j)) . deq(W2[e_j])^T )  (the expert's output row),
+//   y_t      = bf16( sum_j w_j . o_j ), the products and the sum in fp32.
 //
 // Pipeline (one stream, every step deterministic):
 //  1. route    one wave per token: k rounds of a wave arg-max, softmax over
@@ -31,11 +32,12 @@
 //              lane holds gate and up of the same intermediate index; the
 //              epilogue applies SiLU-gating, rounds to bf16, MX-quantizes
 //              along I and writes the packed operand of gemm2.
-//  6. gemm2    per (M-tile, 256-row slice of W2[e]): the tile loop, then the
-//              routing weight of each row; each real row written in fp32 to
-//              its slot row t*k + j (pad rows are not stored).
-//  7. combine  y_t = bf16( sum_j ys[t*k + j] ), fp32 sum in slot order, one
-//              rounding; a token's k slot rows are contiguous.
+//  6. gemm2    per (M-tile, 256-row slice of W2[e]): the tile loop; each
+//              real row rounded to bf16 and written to its slot row t*k + j
+//              (pad rows are not stored).
+//  7. combine  (the finalize) y_t = bf16( sum_j w_j * ys[t*k + j] ), the
+//              products and the sum in fp32 in slot order, one rounding; a
+//              token's k slot rows are contiguous.
 #include <cfloat>
 #include <climits>
 
@@ -417,8 +419,7 @@ __global__ __launch_bounds__(tile::kThreads, 1) void moe_gemm2_kernel(
     const uint8_t* __restrict__ a2q, const uint8_t* __restrict__ a2s, const uint8_t* __restrict__ w2p,
     const uint8_t* __restrict__ s2p, const int* __restrict__ meta, const int* __restrict__ tile_e,
     const int* __restrict__ tile_g0, const int* __restrict__ tile_ng, const int* __restrict__ sorted_row,
-    const float* __restrict__ wts, int H, int I, float* __restrict__ ys) {
-  __shared__ float row_w[256];
+    int H, int I, uint16_t* __restrict__ ys) {
   __shared__ int row_dst[256];
   __shared__ __attribute__((aligned(16))) uint8_t st0[tile::kStage];
   __shared__ __attribute__((aligned(16))) uint8_t st1[tile::kStage];
@@ -441,40 +442,39 @@ __global__ __launch_bounds__(tile::kThreads, 1) void moe_gemm2_kernel(
                    se + (2 * nt + 1) * sc_stride, a2s + (size_t)g0 * sc_stride, a2s + (size_t)(g0 + 1) * sc_stride,
                    KS, acc);
 
-  // Routing weight and slot (t * k + j) of each tile row; pad rows and the
-  // rows past the tile's groups are not stored.
+  // Slot (t * k + j) of each tile row; pad rows and the rows past the tile's
+  // groups are not stored.
   for (int m = threadIdx.x; m < 256; m += tile::kThreads) {
-    float wv = 0.0f;
     int src = -1;
-    if (m < ng * kGroupRows) {
-      src = sorted_row[g0 * kGroupRows + m];
-      if (src >= 0) wv = wts[src];
-    }
-    row_w[m] = wv;
+    if (m < ng * kGroupRows) src = sorted_row[g0 * kGroupRows + m];
     row_dst[m] = src;
   }
   __syncthreads();
-  tile::store_bf16<true, float, true>(st0, st1, st2, st3, acc, ys, H, 0, 0, nt * 256, H, nullptr, 1, row_w,
-                                      row_dst);
+  tile::store_bf16<false, uint16_t, true>(st0, st1, st2, st3, acc, ys, H, 0, 0, nt * 256, H, nullptr, 1, nullptr,
+                                          row_dst);
 }
 
 // ---------------------------------------------------------------- 7. combine
-__global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ ys, int T, int H, int topk,
-                                                          uint16_t* __restrict__ y) {
+__global__ __launch_bounds__(256) void moe_combine_kernel(const uint16_t* __restrict__ ys, const float* __restrict__ wts,
+                                                          int T, int H, int topk, uint16_t* __restrict__ y) {
   const int64_t t8 = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int per_row = H / 8;
   if (t8 >= (int64_t)T * per_row) return;
   const int64_t t = t8 / per_row;
   const int c = (int)(t8 - t * per_row);
-  float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = s0;
+  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < topk; ++j) {
-    const float4* p = reinterpret_cast<const float4*>(ys + (t * topk + j) * H + c * 8);
-    const float4 a = p[0], b = p[1];
-    s0.x += a.x; s0.y += a.y; s0.z += a.z; s0.w += a.w;
-    s1.x += b.x; s1.y += b.y; s1.z += b.z; s1.w += b.w;
+    const float w = wts[t * topk + j];
+    const uint4 r = *reinterpret_cast<const uint4*>(ys + (t * topk + j) * H + c * 8);
+    const uint32_t rv[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s[2 * e] += w * bf16_lo(rv[e]);
+      s[2 * e + 1] += w * bf16_hi(rv[e]);
+    }
   }
-  *reinterpret_cast<uint4*>(y + t * H + c * 8) = make_uint4(pack_bf16x2(s0.x, s0.y), pack_bf16x2(s0.z, s0.w),
-                                                            pack_bf16x2(s1.x, s1.y), pack_bf16x2(s1.z, s1.w));
+  *reinterpret_cast<uint4*>(y + t * H + c * 8) = make_uint4(pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]),
+                                                            pack_bf16x2(s[4], s[5]), pack_bf16x2(s[6], s[7]));
 }
 
 // ---------------------------------------------------------------- launcher
@@ -505,10 +505,10 @@ int launch_moe(const MoeArgs& a, hipStream_t stream) {
                      (uint16_t*)a.dbg_act, (uint8_t*)a.dbg_q, (uint8_t*)a.dbg_s);
   hipLaunchKernelGGL(moe_gemm2_kernel, dim3((unsigned)(a.ws.mt_max * nt2)), dim3(tile::kThreads), 0, stream,
                      a.ws.a2q, a.ws.a2s, (const uint8_t*)a.w2p, (const uint8_t*)a.s2p, a.ws.meta, a.ws.tile_e,
-                     a.ws.tile_g0, a.ws.tile_ng, a.ws.sorted_row, a.ws.wts, (int)a.H, (int)a.I, a.ws.ys);
+                     a.ws.tile_g0, a.ws.tile_ng, a.ws.sorted_row, (int)a.H, (int)a.I, a.ws.ys);
   const int64_t cb_total = a.T * (a.H / 8);
   hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((cb_total + 255) / 256)), dim3(256), 0, stream, a.ws.ys,
-                     (int)a.T, (int)a.H, (int)a.topk, (uint16_t*)a.y);
+                     a.ws.wts, (int)a.T, (int)a.H, (int)a.topk, (uint16_t*)a.y);
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 
