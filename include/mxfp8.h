@@ -256,7 +256,10 @@ int mxfp8_gemm_prequant(const void* q_e4m3, int64_t ldq, const void* s_e8m0, int
  * dimension (H for x, I for a).
  *
  * Shapes: H % 256 == 0, I % 256 == 0, 1 <= E <= 256, 1 <= topk <= min(E, 16),
- * T >= 0 (T == 0 is a no-op).  Checkpoint layouts (contiguous, row-major):
+ * T >= 0 (T == 0 is a no-op); limits H, I <= 2^20, T <= 2^24, T*topk <= 2^26
+ * and (T+1)*H < 2^32 (the quantized token rows are addressed with 32-bit
+ * offsets); anything else returns MXFP8_E_SHAPE.  Checkpoint layouts
+ * (contiguous, row-major):
  *   w13 E4M3 [E, 2I, H] with UE8M0 [E, 2I, H/32]  (rows 0..I-1 gate, I..2I-1 up)
  *   w2  E4M3 [E, H, I]  with UE8M0 [E, H, I/32]
  * The whole layer runs in this library's kernels on `stream`; results are

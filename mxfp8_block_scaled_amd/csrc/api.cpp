@@ -77,6 +77,7 @@ int check_moe_shape(int64_t T, int64_t H, int64_t E, int64_t topk, int64_t I) {
   if (T < 0 || H < 256 || H % 256 != 0 || I < 256 || I % 256 != 0) return MXFP8_E_SHAPE;
   if (E < 1 || E > mxfp8::kMoeMaxExperts || topk < 1 || topk > E || topk > mxfp8::kMoeMaxTopk) return MXFP8_E_SHAPE;
   if (H > (1 << 20) || I > (1 << 20) || T > (1 << 24) || T * topk > (1 << 26)) return MXFP8_E_SHAPE;
+  if ((T + 1) * H > (int64_t(1) << 32) - 1) return MXFP8_E_SHAPE;   // token rows addressed with 32-bit offsets
   return MXFP8_OK;
 }
 
@@ -109,7 +110,7 @@ size_t moe_layout(int64_t T, int64_t H, int64_t E, int64_t topk, int64_t I, uint
   v.a1s = take(p_max * (H / 32));
   v.a2q = take(p_max * I);
   v.a2s = take(p_max * (I / 32));
-  v.ys = (uint16_t*)take(R * H * 2);
+  v.ys = (uint16_t*)take((R + 1) * H * 2);     // row R: spare row for pad rows
   v.p_max = p_max;
   v.mt_max = mt_max;
   if (w) *w = v;

@@ -117,7 +117,7 @@ struct MoeWorkspace {
   uint8_t* a1s;      // packed scales of the expert-sorted token rows [p_max, H / 32]
   uint8_t* a2q;      // packed MXFP8 gated activations [p_max, I]
   uint8_t* a2s;
-  uint16_t* ys;      // expert output rows, bf16 [T*k, H], row t*k + j
+  uint16_t* ys;      // expert output rows, bf16 [T*k + 1, H], row t*k + j (row T*k: spare)
   int64_t p_max;     // sorted positions (multiple of 128, one spare group)
   int64_t mt_max;    // upper bound of M-tiles
 };

@@ -38,6 +38,7 @@
 //  7. combine  (the finalize) y_t = bf16( sum_j w_j * ys[t*k + j] ), the
 //              products and the sum in fp32 in slot order, one rounding; a
 //              token's k slot rows are contiguous.
+#include <algorithm>
 #include <cfloat>
 #include <climits>
 
@@ -296,162 +297,254 @@ __global__ __launch_bounds__(256) void moe_gather_scales_kernel(const uint8_t* _
 }
 
 // ---------------------------------------------------------------- 5. gemm1
-// Packed W13 row p of an expert's 256-row slice nt holds, for wave half
-// wn = (p / 128) % 2 and q = p % 128: gate row nt*128 + wn*64 + q (q < 64) or
-// up row I + nt*128 + wn*64 + q - 64 (q >= 64).  So in the tile loop's lane
-// layout acc[a][b][r] (a < 2) is the gate and acc[a + 2][b][r] the up value of
-// intermediate index i = nt*128 + wn*64 + 32a + 8(r/4) + 4lg + r%4.
+// Persistent over the (M-tile, 256-row slice nt of W13[e]) list, on the
+// 16x16x128 tile loop (tile::persistent16_run).  Packed W13 row p of an
+// expert's slice nt holds, for wave half wn = (p / 128) % 2 and q = p % 128:
+// gate row nt*128 + wn*64 + q (q < 64) or up row I + nt*128 + wn*64 + q - 64
+// (q >= 64).  In the loop's lane layout acc[a][b][j] (a < 4) is then the gate
+// and acc[a + 4][b][j] the up value of intermediate index
+// i = nt*128 + wn*64 + 16a + 4g + j, for tile row m = wm*128 + 16b + li
+// (lane = li + 16 g): gate and up of one index meet in one lane.
+// The activation rows are copied from the token rows of xq by row index
+// (GBufSrc).  The row indices of the workgroup's next tile are copied into
+// LDS at the start of the current one, so building its copy source needs no
+// global load while copies are in flight.
+struct Moe1Job {
+  const uint8_t *wga, *wgb, *swa, *swb, *sxa, *sxb;
+  uint32_t rowoff[4];   // byte offsets in xq of tile rows tid / 4 + 64 i
+  int g0, ng, nt;
+};
+
 __global__ __launch_bounds__(tile::kThreads, 1) void moe_gemm1_kernel(
     const uint8_t* __restrict__ xq, int T, int topk, const uint8_t* __restrict__ a1s,
     const uint8_t* __restrict__ w13p, const uint8_t* __restrict__ s13p, const int* __restrict__ meta,
     const int* __restrict__ tile_e, const int* __restrict__ tile_g0, const int* __restrict__ tile_ng,
-    const int* __restrict__ sorted_row, int H, int I, uint8_t* __restrict__ a2q, uint8_t* __restrict__ a2s, uint16_t* __restrict__ dbg_act,
-    uint8_t* __restrict__ dbg_q, uint8_t* __restrict__ dbg_s) {
+    const int* __restrict__ sorted_row, int H, int I, uint8_t* __restrict__ a2q, uint8_t* __restrict__ a2s,
+    uint16_t* __restrict__ dbg_act, uint8_t* __restrict__ dbg_q, uint8_t* __restrict__ dbg_s) {
   __shared__ __attribute__((aligned(16))) uint8_t st0[tile::kStage];
   __shared__ __attribute__((aligned(16))) uint8_t st1[tile::kStage];
   __shared__ __attribute__((aligned(16))) uint8_t st2[tile::kStage];
   __shared__ __attribute__((aligned(16))) uint8_t st3[tile::kStage];
+  __shared__ __attribute__((aligned(16))) int rowbuf[256];   // sorted_row of the next tile's rows
   const int NT = (2 * I) / 256;
   const int total = meta[0] * NT;
-  if ((int)blockIdx.x >= total) return;
-  const int logical = tile::xcd_remap((int)blockIdx.x, total);
-  const int mt = logical / NT, nt = logical % NT;
-  const int e = tile_e[mt], g0 = tile_g0[mt], ng = tile_ng[mt];
-
-  const int KS = H / kStepK;
+  const int KS = H / kStepK, KS2 = I / kStepK;
   const size_t op_stride = (size_t)KS * kTileBytes, sc_stride = (size_t)KS * kTileScaleBytes;
-  const uint8_t* we = w13p + (size_t)e * (size_t)(2 * I) * (size_t)H;
-  const uint8_t* se = s13p + (size_t)e * (size_t)(2 * I) * (size_t)(H / 32);
-  // Activation rows m = tid / 4 + 64 i of the tile, copied from their token's
-  // row of xq (row T, all zero, for pad rows and rows past the tile's groups).
-  tile::GatherX gx;
-  {
-    const int tid = threadIdx.x;
-    const int chunk = (tid & 3) ^ swz(tid >> 2);     // rows tid / 4 + 64 i share one swizzle
+  const uint32_t xq_bytes = (uint32_t)(((int64_t)T + 1) * H);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave >> 1, wm = wave & 1;
+  const int li = lane & 15, lg = lane >> 4;
+
+  auto decode = [&](int bidx, bool later) {
+    const int logical = tile::xcd_remap(bidx, total);
+    const int mt = logical / NT, nt = logical % NT;
+    const int e = tile_e[mt], g0 = tile_g0[mt], ng = tile_ng[mt];
+    const uint8_t* we = w13p + (size_t)e * (size_t)(2 * I) * (size_t)H;
+    const uint8_t* se = s13p + (size_t)e * (size_t)(2 * I) * (size_t)(H / 32);
+    Moe1Job j;
+    j.wga = we + (2 * nt) * op_stride;
+    j.wgb = we + (2 * nt + 1) * op_stride;
+    j.swa = se + (2 * nt) * sc_stride;
+    j.swb = se + (2 * nt + 1) * sc_stride;
+    j.sxa = a1s + (size_t)g0 * sc_stride;
+    j.sxb = a1s + (size_t)(g0 + 1) * sc_stride;
+    j.g0 = g0;
+    j.ng = ng;
+    j.nt = nt;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      // Row T of xq is all zero: pad rows and rows past the tile's groups.
       const int m = (tid >> 2) + 64 * i;
       int tok = T;
       if (m < ng * kGroupRows) {
-        const int src = sorted_row[g0 * kGroupRows + m];
+        const int src = later ? rowbuf[m] : sorted_row[g0 * kGroupRows + m];
         if (src >= 0) tok = src / topk;
       }
-      gx.p[i] = xq + (size_t)tok * H + chunk * 16;
+      j.rowoff[i] = (uint32_t)tok * (uint32_t)H;
     }
-  }
-  v16f acc[4][4];
-  tile::mainloop<true>(st0, st1, st2, st3, we + (2 * nt) * op_stride, we + (2 * nt + 1) * op_stride, xq, xq,
-                       se + (2 * nt) * sc_stride, se + (2 * nt + 1) * sc_stride, a1s + (size_t)g0 * sc_stride,
-                       a1s + (size_t)(g0 + 1) * sc_stride, KS, acc, gx);
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wn = wave >> 1, wm = wave & 1;
-  const int li = lane & 31, lg = lane >> 5;
-  const int KS2 = I / kStepK;
+    return j;
+  };
+  auto make_src = [&](const Moe1Job& j) {
+    return tile::GBufSrc(j.wga, j.wgb, j.swa, j.swb, j.sxa, j.sxb, xq, xq_bytes, j.rowoff, KS);
+  };
+  auto tile_start = [&](int bnext) {
+    if (bnext >= total) return;
+    const int mt = tile::xcd_remap(bnext, total) / NT;
+    const int g0 = tile_g0[mt], ng = tile_ng[mt];
+    // Wave w copies rows 64 w .. 64 w + 63 (past the tile's groups: zeros, unused).
+    const tile::i4v r = tile::buffer_rsrc(sorted_row + (size_t)g0 * kGroupRows, (uint32_t)(ng * kGroupRows * 4));
+    tile::b2l_4((uint32_t)((wave * 64 + lane) * 4), r, 0u, reinterpret_cast<const uint8_t*>(rowbuf) + wave * 256);
+  };
+  auto epilogue = [&](const v4f (&acc)[8][8], const Moe1Job& j, const uint8_t*) {
+    const int ks = 2 * j.nt + wn;                 // the 64-K step of this wave's intermediate indices
+    const int valid = j.ng * kGroupRows;
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int ml = wm * 128 + 32 * b + li;      // row inside the tile
-    const int pos = g0 * kGroupRows + ml;
-    const bool row_ok = ml < ng * kGroupRows;
-    const int g = pos / kGroupRows, rr = pos % kGroupRows;
-    const int src = (dbg_act != nullptr && row_ok) ? sorted_row[pos] : -1;
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      // Gated activation, rounded to bf16 (pairs r, r+1 in one word).
-      uint32_t w[8];
-#pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        float o[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          // silu(g) = g / (1 + e^-g), with e^-g = 2^(-g log2 e) from the
-          // hardware exp2 and the hardware reciprocal (each within about an
-          // ulp of fp32; far below the bf16 rounding that follows).  For
-          // g < -88 the exponential overflows to +inf and silu(g) -> 0.
-          const float gt = acc[a][b][2 * p + h], up = acc[a + 2][b][2 * p + h];
-          const float ex = __builtin_amdgcn_exp2f(-gt * 1.44269504088896341f);
-          o[h] = gt * __builtin_amdgcn_rcpf(1.0f + ex) * up;
-        }
-        w[p] = pack_bf16x2(o[0], o[1]);
-      }
-      // MX block = this lane's 16 values and those of lane ^ 32.
-      u16x2 mp = {0, 0};
-#pragma unroll
-      for (int p = 0; p < 8; ++p) mp = absmax_pk(mp, w[p]);
-      uint32_t m = max((uint32_t)mp[0], (uint32_t)mp[1]);
-      m = max(m, (uint32_t)__shfl_xor((int)m, 32));
-      const uint32_t sb = (uint32_t)max((int)(m >> 7) - 8, 0);
-      const float scale = mx_scale_value(sb);
-      uint32_t q[4];
-      cvt8s(w, scale, q);
-      cvt8s(w + 4, scale, q + 2);
-      const int iblk = nt * 128 + wn * 64 + 32 * a;   // first intermediate index of the block
-      const int ks = iblk / kStepK;
+    for (int bb = 0; bb < 8; ++bb) {
+      const int ml = wm * 128 + 16 * bb + li;     // row inside the tile
+      const bool row_ok = ml < valid;
+      const int pos = j.g0 * kGroupRows + ml;
+      const int g = pos / kGroupRows, rr = pos % kGroupRows;
       uint8_t* gbase = a2q + (size_t)g * KS2 * kTileBytes;
-      if (row_ok) {
+      const int src = (dbg_act != nullptr && row_ok) ? sorted_row[pos] : -1;
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-          const int k = (iblk % kStepK) + 8 * s4 + 4 * lg;  // within the 64-K step
-          *reinterpret_cast<uint32_t*>(gbase + packed_off(rr, ks, k >> 4, KS2) + (k & 15)) = q[s4];
-        }
-        if (lg == 0) a2s[((size_t)g * KS2 + ks) * kTileScaleBytes + scale_off(rr, (iblk >> 5) & 1)] = (uint8_t)sb;
-      }
-      if (src >= 0) {
+      for (int h = 0; h < 2; ++h) {
+        // MX block h of the step: a = 2h, 2h + 1 of this lane and of the
+        // lanes li + 16 g' (32 values).  Gated activation rounded to bf16,
+        // value e = 4t + jj being a = 2h + t, j = jj.
+        uint32_t w[4];
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-          const int i0 = iblk + 8 * s4 + 4 * lg;
-          uint16_t* da = dbg_act + (int64_t)src * I + i0;
-          da[0] = (uint16_t)w[2 * s4];
-          da[1] = (uint16_t)(w[2 * s4] >> 16);
-          da[2] = (uint16_t)w[2 * s4 + 1];
-          da[3] = (uint16_t)(w[2 * s4 + 1] >> 16);
-          *reinterpret_cast<uint32_t*>(dbg_q + (int64_t)src * I + i0) = q[s4];
+        for (int p = 0; p < 4; ++p) {
+          float o[2];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int e = 2 * p + hh, a = 2 * h + (e >> 2), jj = e & 3;
+            // silu(g) = g / (1 + e^-g), with e^-g = 2^(-g log2 e) from the
+            // hardware exp2 and the hardware reciprocal (each within about an
+            // ulp of fp32; far below the bf16 rounding that follows).  For
+            // g < -88 the exponential overflows to +inf and silu(g) -> 0.
+            const float gt = acc[a][bb][jj], up = acc[a + 4][bb][jj];
+            const float ex = __builtin_amdgcn_exp2f(-gt * 1.44269504088896341f);
+            o[hh] = gt * __builtin_amdgcn_rcpf(1.0f + ex) * up;
+          }
+          w[p] = pack_bf16x2(o[0], o[1]);
         }
-        if (lg == 0) dbg_s[(int64_t)src * (I / 32) + iblk / 32] = (uint8_t)sb;
+        u16x2 mp = {0, 0};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) mp = absmax_pk(mp, w[p]);
+        uint32_t m = max((uint32_t)mp[0], (uint32_t)mp[1]);
+        m = max(m, (uint32_t)__shfl_xor((int)m, 16));
+        m = max(m, (uint32_t)__shfl_xor((int)m, 32));
+        const uint32_t sb = (uint32_t)max((int)(m >> 7) - 8, 0);
+        uint32_t q[2];
+        cvt8s(w, mx_scale_value(sb), q);
+        if (row_ok) {
+          // bytes j = 0..3 of a = 2h + t sit at k = 16a + 4g + j of step ks
+          *reinterpret_cast<uint32_t*>(gbase + packed_off(rr, ks, 2 * h, KS2) + 4 * lg) = q[0];
+          *reinterpret_cast<uint32_t*>(gbase + packed_off(rr, ks, 2 * h + 1, KS2) + 4 * lg) = q[1];
+          if (lg == 0) a2s[((size_t)g * KS2 + ks) * kTileScaleBytes + scale_off(rr, h)] = (uint8_t)sb;
+        }
+        if (src >= 0) {
+          const int iblk = j.nt * 128 + wn * 64 + 32 * h;     // first intermediate index of the block
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int i0 = iblk + 16 * t + 4 * lg;
+            uint16_t* da = dbg_act + (int64_t)src * I + i0;
+            da[0] = (uint16_t)w[2 * t];
+            da[1] = (uint16_t)(w[2 * t] >> 16);
+            da[2] = (uint16_t)w[2 * t + 1];
+            da[3] = (uint16_t)(w[2 * t + 1] >> 16);
+            *reinterpret_cast<uint32_t*>(dbg_q + (int64_t)src * I + i0) = q[t];
+          }
+          if (lg == 0) dbg_s[(int64_t)src * (I / 32) + iblk / 32] = (uint8_t)sb;
+        }
       }
     }
-  }
+    return false;   // the number of stores depends on the rows
+  };
+  tile::persistent16_run<0, 0, true>(st0, st1, st2, st3, nullptr, total, KS, decode, make_src,
+                               [](const Moe1Job&) { return tile::buffer_rsrc(nullptr, 0); },
+                               [](tile::i4v, uint8_t*) {}, tile_start, epilogue);
 }
 
 // ---------------------------------------------------------------- 6. gemm2
+// Persistent over the (M-tile, 256-row slice of W2[e]) list on the same
+// loop.  Side data of a tile: the sorted_row entries of its 256 rows (wave w
+// copies rows 64 w ..), so the epilogue finds each row's slot row t*k + j in
+// LDS.  Each row is rounded once to bf16 and stored to its slot row; pad rows
+// and rows past the tile's groups go to the spare row R, so every wave issues
+// exactly 32 stores per tile.
+struct Moe2Job {
+  const uint8_t *wga, *wgb, *xga, *xgb, *swa, *swb, *sxa, *sxb;
+  const int* rows;      // sorted_row of the tile's first row
+  int ng, col0;
+};
+
 __global__ __launch_bounds__(tile::kThreads, 1) void moe_gemm2_kernel(
     const uint8_t* __restrict__ a2q, const uint8_t* __restrict__ a2s, const uint8_t* __restrict__ w2p,
     const uint8_t* __restrict__ s2p, const int* __restrict__ meta, const int* __restrict__ tile_e,
     const int* __restrict__ tile_g0, const int* __restrict__ tile_ng, const int* __restrict__ sorted_row,
-    int H, int I, uint16_t* __restrict__ ys) {
-  __shared__ int row_dst[256];
+    int H, int I, int R, uint16_t* __restrict__ ys) {
   __shared__ __attribute__((aligned(16))) uint8_t st0[tile::kStage];
   __shared__ __attribute__((aligned(16))) uint8_t st1[tile::kStage];
   __shared__ __attribute__((aligned(16))) uint8_t st2[tile::kStage];
   __shared__ __attribute__((aligned(16))) uint8_t st3[tile::kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t epi[tile::kEpiBytes];
+  constexpr int kRowSlot = 256 * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t side[2 * kRowSlot];
+  typedef unsigned int u4v __attribute__((ext_vector_type(4)));
   const int NT = H / 256;
   const int total = meta[0] * NT;
-  if ((int)blockIdx.x >= total) return;
-  const int logical = tile::xcd_remap((int)blockIdx.x, total);
-  const int mt = logical / NT, nt = logical % NT;
-  const int e = tile_e[mt], g0 = tile_g0[mt], ng = tile_ng[mt];
-
   const int KS = I / kStepK;
   const size_t op_stride = (size_t)KS * kTileBytes, sc_stride = (size_t)KS * kTileScaleBytes;
-  const uint8_t* we = w2p + (size_t)e * (size_t)H * (size_t)I;
-  const uint8_t* se = s2p + (size_t)e * (size_t)H * (size_t)(I / 32);
-  v4f acc[8][8];
-  tile::mainloop16(st0, st1, st2, st3, we + (2 * nt) * op_stride, we + (2 * nt + 1) * op_stride,
-                   a2q + (size_t)g0 * op_stride, a2q + (size_t)(g0 + 1) * op_stride, se + (2 * nt) * sc_stride,
-                   se + (2 * nt + 1) * sc_stride, a2s + (size_t)g0 * sc_stride, a2s + (size_t)(g0 + 1) * sc_stride,
-                   KS, acc);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = wave >> 1, wm = wave & 1;
+  const int li = lane & 15, lg = lane >> 4;
 
-  // Slot (t * k + j) of each tile row; pad rows and the rows past the tile's
-  // groups are not stored.
-  for (int m = threadIdx.x; m < 256; m += tile::kThreads) {
-    int src = -1;
-    if (m < ng * kGroupRows) src = sorted_row[g0 * kGroupRows + m];
-    row_dst[m] = src;
-  }
-  __syncthreads();
-  tile::store_bf16<false, uint16_t, true>(st0, st1, st2, st3, acc, ys, H, 0, 0, nt * 256, H, nullptr, 1, nullptr,
-                                          row_dst);
+  auto decode = [&](int bidx, bool) {
+    const int logical = tile::xcd_remap(bidx, total);
+    const int mt = logical / NT, nt = logical % NT;
+    const int e = tile_e[mt], g0 = tile_g0[mt], ng = tile_ng[mt];
+    const uint8_t* we = w2p + (size_t)e * (size_t)H * (size_t)I;
+    const uint8_t* se = s2p + (size_t)e * (size_t)H * (size_t)(I / 32);
+    Moe2Job j;
+    j.wga = we + (2 * nt) * op_stride;
+    j.wgb = we + (2 * nt + 1) * op_stride;
+    j.xga = a2q + (size_t)g0 * op_stride;
+    j.xgb = a2q + (size_t)(g0 + 1) * op_stride;
+    j.swa = se + (2 * nt) * sc_stride;
+    j.swb = se + (2 * nt + 1) * sc_stride;
+    j.sxa = a2s + (size_t)g0 * sc_stride;
+    j.sxb = a2s + (size_t)(g0 + 1) * sc_stride;
+    j.rows = sorted_row + (size_t)g0 * kGroupRows;
+    j.ng = ng;
+    j.col0 = nt * 256;
+    return j;
+  };
+  auto make_src = [&](const Moe2Job& j) {
+    return tile::BufSrc(j.wga, j.wgb, j.xga, j.xgb, j.swa, j.swb, j.sxa, j.sxb, KS, KS);
+  };
+  auto side_of = [&](const Moe2Job& j) { return tile::buffer_rsrc(j.rows, (uint32_t)(j.ng * kGroupRows * 4)); };
+  auto side_copy = [&](tile::i4v r, uint8_t* slot) {
+    tile::b2l_4((uint32_t)((wave * 64 + lane) * 4), r, 0u, slot + wave * 256);
+  };
+  // As tile::epi16: the wave's 128 x 128 block staged as bf16 16 rows at a
+  // time, read back as 8 consecutive columns per lane, one 16-byte store per
+  // (row, 8 columns); H % 256 == 0, so every column is in range.
+  auto epilogue = [&](const v4f (&acc)[8][8], const Moe2Job& j, const uint8_t* slot) {
+    const int* rmap = reinterpret_cast<const int*>(slot);
+    uint8_t* reg = epi + wave * tile::kEpiWaveBytes;
+    const int valid = j.ng * kGroupRows;
+    const int nw = j.col0 + wn * 128;
+    const int rr = lane >> 4, cc = (lane & 15) * 8;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+#pragma unroll
+      for (int a = 0; a < 8; ++a) {
+        const v4f v = acc[a][k];
+        const uint2 w = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        *reinterpret_cast<uint2*>(reg + (li * tile::kEpiPitchH + 16 * a + 4 * lg) * 2) = w;
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      u4v t[4];
+      int dst[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        t[r] = *reinterpret_cast<const u4v*>(reg + ((rr + 4 * r) * tile::kEpiPitchH + cc) * 2);
+        const int ml = wm * 128 + 16 * k + rr + 4 * r;
+        const int s = rmap[ml];
+        dst[r] = (ml < valid && s >= 0) ? s : R;
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        __builtin_nontemporal_store(t[r], reinterpret_cast<u4v*>(ys + (size_t)dst[r] * H + nw + cc));
+    }
+    return true;
+  };
+  tile::persistent16_run<1, kRowSlot, false>(st0, st1, st2, st3, side, total, KS, decode, make_src, side_of, side_copy,
+                                      [](int) {}, epilogue);
 }
 
 // ---------------------------------------------------------------- 7. combine
@@ -498,14 +591,21 @@ int launch_moe(const MoeArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(moe_gather_scales_kernel, dim3((unsigned)(a.ws.p_max / kGroupRows * KS1 / 4)), dim3(256), 0,
                      stream, a.ws.xs, (int)a.H, (int)a.topk, a.ws.sorted_row, a.ws.meta, KS1, a.ws.a1s,
                      a.ws.xq + a.T * a.H);
-  const int nt1 = (int)(2 * a.I / 256), nt2 = (int)(a.H / 256);
-  hipLaunchKernelGGL(moe_gemm1_kernel, dim3((unsigned)(a.ws.mt_max * nt1)), dim3(tile::kThreads), 0, stream,
+  // Both GEMMs are persistent: at most one workgroup per CU (a multiple of 8,
+  // one per XCD each), each running tiles b, b + grid, ... of the device-side
+  // tile list; workgroups past its length return at once.
+  const int64_t nt1 = 2 * a.I / 256, nt2 = a.H / 256;
+  const int cus = device_cu_count();
+  const int64_t pgrid = cus >= 8 ? cus - cus % 8 : cus;
+  const unsigned g1 = (unsigned)std::min<int64_t>(a.ws.mt_max * nt1, pgrid);
+  const unsigned g2 = (unsigned)std::min<int64_t>(a.ws.mt_max * nt2, pgrid);
+  hipLaunchKernelGGL(moe_gemm1_kernel, dim3(g1), dim3(tile::kThreads), 0, stream,
                      a.ws.xq, (int)a.T, (int)a.topk, a.ws.a1s, (const uint8_t*)a.w13p, (const uint8_t*)a.s13p, a.ws.meta, a.ws.tile_e,
                      a.ws.tile_g0, a.ws.tile_ng, a.ws.sorted_row, (int)a.H, (int)a.I, a.ws.a2q, a.ws.a2s,
                      (uint16_t*)a.dbg_act, (uint8_t*)a.dbg_q, (uint8_t*)a.dbg_s);
-  hipLaunchKernelGGL(moe_gemm2_kernel, dim3((unsigned)(a.ws.mt_max * nt2)), dim3(tile::kThreads), 0, stream,
-                     a.ws.a2q, a.ws.a2s, (const uint8_t*)a.w2p, (const uint8_t*)a.s2p, a.ws.meta, a.ws.tile_e,
-                     a.ws.tile_g0, a.ws.tile_ng, a.ws.sorted_row, (int)a.H, (int)a.I, a.ws.ys);
+  hipLaunchKernelGGL(moe_gemm2_kernel, dim3(g2), dim3(tile::kThreads), 0, stream, a.ws.a2q, a.ws.a2s,
+                     (const uint8_t*)a.w2p, (const uint8_t*)a.s2p, a.ws.meta, a.ws.tile_e, a.ws.tile_g0,
+                     a.ws.tile_ng, a.ws.sorted_row, (int)a.H, (int)a.I, R, a.ws.ys);
   const int64_t cb_total = a.T * (a.H / 8);
   hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((cb_total + 255) / 256)), dim3(256), 0, stream, a.ws.ys,
                      a.ws.wts, (int)a.T, (int)a.H, (int)a.topk, (uint16_t*)a.y);

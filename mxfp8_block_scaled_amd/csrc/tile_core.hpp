@@ -217,6 +217,56 @@ struct BufSrc {
   }
 };
 
+// BufSrc with a row-gathered activation operand: the 16 bytes thread tid
+// copies for tile row m = tid / 4 + 64 i (i = 0..3) in 64-K step ks come from
+// byte vx[i] + 64 ks of a row-major E4M3 matrix (resource xr, one row of K
+// bytes per token), vx[i] being the row's offset plus the logical chunk that
+// lands in LDS slot tid % 4 of the packed layout, chunk (tid % 4) ^ swz(m).
+// Weights and all four scale tiles are packed, as in BufSrc.
+struct GBufSrc {
+  i4v w0, w1, xr, sc;
+  uint32_t vlo, vhi, soff_lane;
+  uint32_t vx[4];
+  int wave;
+
+  GBufSrc() = default;
+
+  __device__ __forceinline__ GBufSrc(const uint8_t* wga, const uint8_t* wgb, const uint8_t* swa,
+                                     const uint8_t* swb, const uint8_t* sxa, const uint8_t* sxb,
+                                     const uint8_t* xrows, uint32_t xrows_bytes, const uint32_t (&rowoff)[4],
+                                     int KS) {
+    const int tid = threadIdx.x;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t data = (uint32_t)KS * kTileBytes, scales = (uint32_t)KS * kTileScaleBytes;
+    w0 = buffer_rsrc(wga, data);
+    w1 = buffer_rsrc(wgb, data);
+    xr = buffer_rsrc(xrows, xrows_bytes);
+    sc = buffer_rsrc(wave == 0 ? swa : wave == 1 ? swb : wave == 2 ? sxa : sxb, scales);
+    vlo = (uint32_t)wave * KS * kPieceBytes + (uint32_t)(tid & 63) * 16;
+    vhi = vlo + 4u * KS * kPieceBytes;
+    soff_lane = (uint32_t)(tid & 63) * 4;
+    const uint32_t chunk = (uint32_t)(((tid & 3) ^ swz(tid >> 2)) * 16);   // rows tid / 4 + 64 i share it
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vx[i] = rowoff[i] + chunk;
+  }
+
+  __device__ __forceinline__ void issue(int j, int ks, uint8_t* st) const {
+    uint8_t* base = st + wave * 1024;
+    const uint32_t off = (uint32_t)ks * kPieceBytes, xoff = (uint32_t)ks * kStepK;
+    switch (j) {
+      case 0: b2l_16(vlo, w0, off, base); break;
+      case 1: b2l_16(vhi, w0, off, base + 4096); break;
+      case 2: b2l_16(vlo, w1, off, base + 8192); break;
+      case 3: b2l_16(vhi, w1, off, base + 12288); break;
+      case 4: b2l_16(vx[0], xr, xoff, base + kOpBytes); break;
+      case 5: b2l_16(vx[1], xr, xoff, base + kOpBytes + 4096); break;
+      case 6: b2l_16(vx[2], xr, xoff, base + kOpBytes + 8192); break;
+      case 7: b2l_16(vx[3], xr, xoff, base + kOpBytes + 12288); break;
+      default: b2l_4(soff_lane, sc, (uint32_t)ks * kTileScaleBytes, st + 2 * kOpBytes + wave * 256); break;
+    }
+  }
+};
+
 // acc = the tile's product over all KS 64-K steps.  wga / wgb: the packed
 // weight groups of tile rows 0-127 / 128-255 at step 0; xga / xgb: the packed
 // activation groups (kGatherX: unused, gx gives the rows instead); swa, swb,
@@ -841,11 +891,34 @@ __device__ __forceinline__ bool epi16(uint8_t* epi, const uint8_t* bias_slot, co
   return full;
 }
 
-template <typename Decode>
-__device__ __forceinline__ void persistent16(uint8_t* st0, uint8_t* st1, uint8_t* st2, uint8_t* st3, uint8_t* epi,
-                                             uint8_t* bias_lds, int total, int KS, Decode decode,
-                                             uint16_t* __restrict__ y, int64_t ldy, int M, int N,
-                                             const uint16_t* __restrict__ bias, int vec_store) {
+// The persistent loop over any tile list.
+//  * decode(b, later) gives tile b's job (any struct); later is false only
+//    for the workgroup's first tile (decoded before any copy is in flight).
+//  * make_src(job): its copy source (BufSrc or GBufSrc).
+//  * Side data: kSide LDS-DMA copies per wave, issued by side_copy(side_of(job),
+//    slot) together with the tile's second step into one of two slots of
+//    kSideSlot bytes at side_lds (e.g. the tile's bias).  The epilogue of the
+//    tile finds it there: epilogue(acc, job, slot) stores the tile and returns
+//    true when the wave issued exactly 32 vector memory operations in it (the
+//    next tile's first wait then lets them stay in flight), false for any
+//    other number.
+//  * tile_start(b_next) runs at the start of each tile with the index of the
+//    workgroup's next tile (may be >= total); vector memory operations it
+//    issues are complete by the tile's first barrier after its first wait.
+//  * kCarry: the last step of a tile reads the next tile's first fragments
+//    (held in registers through the epilogue); otherwise they are read from
+//    LDS after the epilogue (their stage pair is not refilled before the
+//    next tile's first barrier), which frees those registers for an
+//    epilogue that needs them.
+// total: tiles of the list; gridDim.x % 8 == 0 keeps every workgroup's tiles
+// on one XCD under xcd_remap.
+template <int kSide, int kSideSlot, bool kCarry, typename Decode, typename MakeSrc, typename SideOf, typename SideCopy,
+          typename TileStart, typename Epilogue>
+__device__ __forceinline__ void persistent16_run(uint8_t* st0, uint8_t* st1, uint8_t* st2, uint8_t* st3,
+                                                 uint8_t* side_lds, int total, int KS, Decode decode,
+                                                 MakeSrc make_src, SideOf side_of, SideCopy side_copy,
+                                                 TileStart tile_start, Epilogue epilogue) {
+  static_assert(kSide >= 0 && kSide <= 4, "side copies per wave");
   int b = blockIdx.x;
   if (b >= total) return;
   const int lane = threadIdx.x & 63;
@@ -871,32 +944,31 @@ __device__ __forceinline__ void persistent16(uint8_t* st0, uint8_t* st1, uint8_t
     const uint8_t* st = (lg >> 1) ? od : ev;
     return *reinterpret_cast<const int*>(st + offS + base + 128 * e);
   };
-  auto issue_w = [&](const BufSrc& sr, int k, int q, uint8_t* ev, uint8_t* od) {
+  using Job = decltype(decode(0, false));
+  using Src = decltype(make_src(decode(0, false)));
+  auto issue_w = [&](const Src& sr, int k, int q, uint8_t* ev, uint8_t* od) {
     const int t = k / 5, c = k % 5;
     sr.issue(c < 4 ? c : 8, 2 * q + t, t ? od : ev);
   };
-  auto issue_x = [&](const BufSrc& sr, int k, int q, uint8_t* ev, uint8_t* od) {
+  auto issue_x = [&](const Src& sr, int k, int q, uint8_t* ev, uint8_t* od) {
     const int t = k >> 2;
     sr.issue(4 + (k & 3), 2 * q + t, t ? od : ev);
   };
-  auto issue_bias = [&](i4v r, int buf) {
-    b2l_4((uint32_t)(wn * 256 + lane * 4), r, 0u, bias_lds + buf * kBiasSlot + wave * 256);
-  };
-  auto make_src = [&](const Job16& j) { return BufSrc(j.wga, j.wgb, j.xga, j.xgb, j.swa, j.swb, j.sxa, j.sxb, KS, KS); };
+  auto issue_side = [&](i4v r, int buf) { side_copy(r, side_lds + buf * kSideSlot); };
 
   v4f acc[8][8];
   State S;
   // One 128-K step on pair (ev, od); (nev, nod) holds the next step (of this
   // tile or the next).  Copies step q of sr into this pair when kIssue, or
   // (kRtIssue) when the runtime flag rt_issue is set: weights and scales
-  // after column 1, activations after column 6, and with with_bias also the
-  // bias of sr's tile into slot bbuf.  The wait before column 6 needs the
+  // after column 1, activations after column 6, and with with_side also the
+  // side data of sr's tile into slot bbuf.  The wait before column 6 needs the
   // next step's copies: besides the ten weight copies issued in this step (if
   // any), vm_extra stores of the previous epilogue may still be in flight
   // after them (32, or 0 when unknown).  The next step's fragments are always
   // read (after the last tile they are stale and unused).
-  auto step = [&](auto kIssue, auto kRtIssue, auto with_bias, auto kVm, bool rt_issue, uint8_t* ev, uint8_t* od,
-                  const uint8_t* nev, const uint8_t* nod, const BufSrc& sr, int q, int vm_extra, i4v brs, int bbuf) {
+  auto step = [&](auto kIssue, auto kRtIssue, auto with_side, auto kVm, auto kNext, bool rt_issue, uint8_t* ev, uint8_t* od,
+                  const uint8_t* nev, const uint8_t* nod, const Src& sr, int q, int vm_extra, i4v brs, int bbuf) {
     constexpr bool kI = decltype(kIssue)::value, kR = decltype(kRtIssue)::value;
     const bool issue = kI || (kR && rt_issue);
     int nsa[2], nsb[2];
@@ -931,34 +1003,44 @@ __device__ __forceinline__ void persistent16(uint8_t* st0, uint8_t* st1, uint8_t
         if (issue) {
           if constexpr (j >= 8 && j < 18) issue_w(sr, j - 8, q, ev, od);
           if constexpr (j >= 48 && j < 56) issue_x(sr, j - 48, q, ev, od);
-          if constexpr (decltype(with_bias)::value && j == 56) issue_bias(brs, bbuf);
+          if constexpr (decltype(with_side)::value && j == 56) issue_side(brs, bbuf);
         }
       }
       if constexpr (a == 0 && bb < 6) S.bf[(bb + 2) & 3] = frag(ev, od, offB + 1024 * (bb + 2));
-      if constexpr (j == 48) {
-        nsa[0] = rd_scale(nev, nod, swA, 0);
-        nsa[1] = rd_scale(nev, nod, swA, 1);
-        S.bf[0] = frag(nev, nod, offB);
+      if constexpr (decltype(kNext)::value) {
+        if constexpr (j == 48) {
+          nsa[0] = rd_scale(nev, nod, swA, 0);
+          nsa[1] = rd_scale(nev, nod, swA, 1);
+          S.bf[0] = frag(nev, nod, offB);
+        }
+        if constexpr (j == 49) { nsb[0] = rd_scale(nev, nod, swB, 0); nsb[1] = rd_scale(nev, nod, swB, 1); }
+        if constexpr (j == 56) S.bf[1] = frag(nev, nod, offB + 1024);
+        if constexpr (j >= 56) S.a[a] = frag(nev, nod, offA + 1024 * a);
       }
-      if constexpr (j == 49) { nsb[0] = rd_scale(nev, nod, swB, 0); nsb[1] = rd_scale(nev, nod, swB, 1); }
-      if constexpr (j == 56) S.bf[1] = frag(nev, nod, offB + 1024);
-      if constexpr (j >= 56) S.a[a] = frag(nev, nod, offA + 1024 * a);
       __builtin_amdgcn_sched_barrier(0);
     });
-    S.sa[0] = nsa[0]; S.sa[1] = nsa[1];
-    S.sb[0] = nsb[0]; S.sb[1] = nsb[1];
+    if constexpr (decltype(kNext)::value) {
+      S.sa[0] = nsa[0]; S.sa[1] = nsa[1];
+      S.sb[0] = nsb[0]; S.sb[1] = nsb[1];
+    }
+  };
+  // The first fragments of the step in (ev, od).
+  auto read_first = [&](const uint8_t* ev, const uint8_t* od) {
+    S.sa[0] = rd_scale(ev, od, swA, 0);
+    S.sa[1] = rd_scale(ev, od, swA, 1);
+    S.sb[0] = rd_scale(ev, od, swB, 0);
+    S.sb[1] = rd_scale(ev, od, swB, 1);
+#pragma unroll
+    for (int a = 0; a < 8; ++a) S.a[a] = frag(ev, od, offA + 1024 * a);
+    S.bf[0] = frag(ev, od, offB);
+    S.bf[1] = frag(ev, od, offB + 1024);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   };
   using T = std::true_type;
   using F = std::false_type;
 
-  BufSrc src;
-  int row0, col0;
-  {
-    const Job16 first = decode(b);
-    src = make_src(first);
-    row0 = first.row0;
-    col0 = first.col0;
-  }
+  Job cur = decode(b, false);
+  Src src = make_src(cur);
   // First tile: its two first steps and its bias, then its first fragments.
 #pragma unroll
   for (int k = 0; k < 10; ++k) issue_w(src, k, 0, st0, st1);
@@ -968,23 +1050,16 @@ __device__ __forceinline__ void persistent16(uint8_t* st0, uint8_t* st1, uint8_t
   for (int k = 0; k < 10; ++k) issue_w(src, k, 1, st2, st3);
 #pragma unroll
   for (int k = 0; k < 8; ++k) issue_x(src, k, 1, st2, st3);
-  issue_bias(bias_rsrc(bias, col0, N), 0);
-  wait_vmcnt<19>();
+  if constexpr (kSide > 0) issue_side(side_of(cur), 0);
+  wait_vmcnt<18 + kSide>();
   __builtin_amdgcn_s_barrier();
-  S.sa[0] = rd_scale(st0, st1, swA, 0);
-  S.sa[1] = rd_scale(st0, st1, swA, 1);
-  S.sb[0] = rd_scale(st0, st1, swB, 0);
-  S.sb[1] = rd_scale(st0, st1, swB, 1);
-#pragma unroll
-  for (int a = 0; a < 8; ++a) S.a[a] = frag(st0, st1, offA + 1024 * a);
-  S.bf[0] = frag(st0, st1, offB);
-  S.bf[1] = frag(st0, st1, offB + 1024);
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  read_first(st0, st1);
 
   const int P = KS / 2;       // 128-K steps per tile: even, at least 2
   const i4v nob = buffer_rsrc(nullptr, 0);
   int vm_extra = 0, buf = 0;
   for (;;) {
+    tile_start(b + (int)gridDim.x);
 #pragma unroll
     for (int a = 0; a < 8; ++a)
 #pragma unroll
@@ -993,33 +1068,62 @@ __device__ __forceinline__ void persistent16(uint8_t* st0, uint8_t* st1, uint8_t
     if (P >= 4) {
       // The first step alone may find the previous epilogue's stores in
       // flight (see step).
-      step(T{}, F{}, F{}, T{}, true, st0, st1, st2, st3, src, 2, vm_extra, nob, 0);
-      step(T{}, F{}, F{}, F{}, true, st2, st3, st0, st1, src, 3, 0, nob, 0);
+      step(T{}, F{}, F{}, T{}, T{}, true, st0, st1, st2, st3, src, 2, vm_extra, nob, 0);
+      step(T{}, F{}, F{}, F{}, T{}, true, st2, st3, st0, st1, src, 3, 0, nob, 0);
       for (p = 2; p + 4 <= P; p += 2) {
-        step(T{}, F{}, F{}, F{}, true, st0, st1, st2, st3, src, p + 2, 0, nob, 0);
-        step(T{}, F{}, F{}, F{}, true, st2, st3, st0, st1, src, p + 3, 0, nob, 0);
+        step(T{}, F{}, F{}, F{}, T{}, true, st0, st1, st2, st3, src, p + 2, 0, nob, 0);
+        step(T{}, F{}, F{}, F{}, T{}, true, st2, st3, st0, st1, src, p + 3, 0, nob, 0);
       }
       vm_extra = 0;
     }
     // The next tile is decoded only now, so its sources do not occupy
-    // registers during the loop above.
+    // registers during the loop above.  With no step above, what tile_start
+    // issued has not been waited for yet: wait for it (and every wave's).
+    if (P < 4) {
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+    }
     const int nb = b + (int)gridDim.x;
     const bool has_next = nb < total;
-    const Job16 nxt = decode(has_next ? nb : b);
-    const BufSrc nsrc = make_src(nxt);
-    step(F{}, T{}, F{}, T{}, has_next, st0, st1, st2, st3, nsrc, 0, vm_extra, nob, 0);
-    step(F{}, T{}, T{}, F{}, has_next, st2, st3, st0, st1, nsrc, 1, 0, bias_rsrc(bias, nxt.col0, N), buf ^ 1);
+    const Job nxt = decode(has_next ? nb : b, true);
+    const Src nsrc = make_src(nxt);
+    step(F{}, T{}, F{}, T{}, T{}, has_next, st0, st1, st2, st3, nsrc, 0, vm_extra, nob, 0);
+    step(F{}, T{}, std::integral_constant<bool, (kSide > 0)>{}, F{}, std::integral_constant<bool, kCarry>{}, has_next,
+         st2, st3, st0, st1, nsrc, 1, 0, side_of(nxt), buf ^ 1);
     // The last MFMAs must retire before the epilogue reads the accumulators.
     asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
-    const bool full = epi16(epi, bias_lds + buf * kBiasSlot + wave * 256, acc, y, ldy, row0, M, col0, N, vec_store);
+    const bool full = epilogue(acc, cur, side_lds + buf * kSideSlot);
     if (!has_next) break;
+    if constexpr (!kCarry) read_first(st0, st1);
     vm_extra = full ? 32 : 0;
     src = nsrc;
-    row0 = nxt.row0;
-    col0 = nxt.col0;
+    cur = nxt;
     b = nb;
     buf ^= 1;
   }
+}
+
+// The dense layer's persistent GEMM: tiles of packed operands, bf16 output
+// with bias (epi16).
+template <typename Decode>
+__device__ __forceinline__ void persistent16(uint8_t* st0, uint8_t* st1, uint8_t* st2, uint8_t* st3, uint8_t* epi,
+                                             uint8_t* bias_lds, int total, int KS, Decode decode,
+                                             uint16_t* __restrict__ y, int64_t ldy, int M, int N,
+                                             const uint16_t* __restrict__ bias, int vec_store) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = wave >> 1;
+  // Side data: the tile's 256 bias values; wave w copies the 128 of its
+  // columns (wn * 128 ..) into its own 256 bytes of the slot.
+  persistent16_run<1, kBiasSlot, true>(
+      st0, st1, st2, st3, bias_lds, total, KS, [&](int bidx, bool) { return decode(bidx); },
+      [&](const Job16& j) { return BufSrc(j.wga, j.wgb, j.xga, j.xgb, j.swa, j.swb, j.sxa, j.sxb, KS, KS); },
+      [&](const Job16& j) { return bias_rsrc(bias, j.col0, N); },
+      [&](i4v r, uint8_t* slot) { b2l_4((uint32_t)(wn * 256 + lane * 4), r, 0u, slot + wave * 256); },
+      [&](int) {},
+      [&](const v4f (&acc)[8][8], const Job16& j, const uint8_t* slot) {
+        return epi16(epi, slot + wave * 256, acc, y, ldy, j.row0, M, j.col0, N, vec_store);
+      });
 }
 
 }  // namespace tile

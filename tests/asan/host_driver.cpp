@@ -136,7 +136,7 @@ int launch_moe(const MoeArgs& a, hipStream_t) {
   touch(w.a1s, w.p_max * (a.H / 32));
   touch(w.a2q, w.p_max * a.I);
   touch(w.a2s, w.p_max * (a.I / 32));
-  touch(w.ys, R * a.H * 2);
+  touch(w.ys, (R + 1) * a.H * 2);
   touch(a.y, a.T * a.H * 2);
   return 0;
 }
