@@ -539,7 +539,7 @@ __global__ __launch_bounds__(tile::kThreads, 1) void moe_gemm2_kernel(
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        __builtin_nontemporal_store(t[r], reinterpret_cast<u4v*>(ys + (size_t)dst[r] * H + nw + cc));
+        *reinterpret_cast<u4v*>(ys + (size_t)dst[r] * H + nw + cc) = t[r];
     }
     return true;
   };
