@@ -12,7 +12,7 @@
 //    remapped so that each XCD works on a contiguous, M-grouped range of tiles
 //    and its private L2 sees the reuse of weight and activation K-slices.
 //  * Epilogue (tile::store16): fp32 staged through LDS, bias added in fp32,
-//    one rounding to bf16, 16-byte stores covering whole
+//    one rounding to bf16, 16-byte non-temporal stores covering whole
 //    256-byte row segments.
 #include "common.hpp"
 #include "launch.hpp"

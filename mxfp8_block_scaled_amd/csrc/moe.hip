@@ -453,7 +453,8 @@ __global__ __launch_bounds__(tile::kThreads, 1) void moe_gemm1_kernel(
 // copies rows 64 w ..), so the epilogue finds each row's slot row t*k + j in
 // LDS.  Each row is rounded once to bf16 and stored to its slot row; pad rows
 // and rows past the tile's groups go to the spare row R, so every wave issues
-// exactly 32 stores per tile.
+// exactly 32 stores per tile (ordinary stores: the combine reads the rows
+// right after).
 struct Moe2Job {
   const uint8_t *wga, *wgb, *xga, *xgb, *swa, *swb, *sxa, *sxb;
   const int* rows;      // sorted_row of the tile's first row

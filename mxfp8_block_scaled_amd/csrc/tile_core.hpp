@@ -719,9 +719,8 @@ __device__ __forceinline__ void store_bf16(uint8_t* st0, uint8_t* st1, uint8_t* 
 // Epilogue of the 16x16x128 loop (the dense layer): y[m][n] = OutT(acc +
 // bias[n]) for tile rows m with row0 + m < row_end and columns col0 + n < N.
 // OutT = uint16_t: bf16 (one rounding after the fp32 bias add), written with
-// ordinary stores (the output stays in cache for the layer that reads it
-// next; measured on MI355X, the quantize + GEMM step runs equally fast with
-// non-temporal ones); OutT = float: the fp32 values (split-K partials; bias
+// non-temporal stores (the output is not read again, so it need not displace
+// operand tiles in L2); OutT = float: the fp32 values (split-K partials; bias
 // must be null).  Each wave stages 64 rows of its 128 x 128 block at a time in
 // its own LDS stage buffer and reads them back so that a lane holds 8
 // consecutive columns of one row: lanes 16G + 8r + q (G = 0..3, r = 0..1,
@@ -789,7 +788,7 @@ __device__ __forceinline__ void store16(uint8_t* st0, uint8_t* st1, uint8_t* st2
           const u4v w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
                          pack_bf16x2(v[6], v[7])};
           if (vec_store == 2 && full8) {
-            *reinterpret_cast<u4v*>(d) = w;
+            __builtin_nontemporal_store(w, reinterpret_cast<u4v*>(d));
           } else if (vec_store == 1 && full8) {
             *reinterpret_cast<uint2*>(d) = make_uint2(w[0], w[1]);
             *reinterpret_cast<uint2*>(d + 4) = make_uint2(w[2], w[3]);
@@ -841,8 +840,7 @@ __device__ inline i4v bias_rsrc(const uint16_t* bias, int col0, int N) {
 // rows at a time as bf16 in its own kEpiWaveBytes region (lane (i, g) writes
 // columns 16a + 4g .. +3 of row i for a = 0..7), reads each pass back as 8
 // consecutive columns per lane (4 rows per read) and writes 16-byte
-// stores covering whole 256-byte row segments (ordinary
-// stores, as in store16).  bias_slot: the
+// non-temporal stores covering whole 256-byte row segments.  bias_slot: the
 // wave's 256-byte bias slice (columns wn * 128 ..).  Returns true when the
 // wave issued exactly 32 stores (block fully in range, vec_store == 2).
 __device__ __forceinline__ bool epi16(uint8_t* epi, const uint8_t* bias_slot, const v4f (&acc)[8][8],
@@ -879,7 +877,7 @@ __device__ __forceinline__ bool epi16(uint8_t* epi, const uint8_t* bias_slot, co
       const int m = mw + 16 * k + rr + 4 * r, n = nw + cc;
       uint16_t* d = y + (size_t)m * ldy + n;
       if (full) {
-        *reinterpret_cast<u4v*>(d) = t[r];
+        __builtin_nontemporal_store(t[r], reinterpret_cast<u4v*>(d));
       } else if (m < row_end && n < N) {
         if (vec_store == 2 && n + 7 < N) {
           *reinterpret_cast<u4v*>(d) = t[r];
