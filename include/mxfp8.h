@@ -309,13 +309,28 @@ int mxfp8_moe_grouped(const void* x_bf16, const float* logits_f32, int64_t T, in
 int mxfp8_moe_debug_capture(void* act_bf16, void* act_e4m3, void* act_e8m0, void* ids_i32, void* wts_f32);
 
 /*
- * Test hook: force the GEMM path of mxfp8_linear and mxfp8_linear_w4a8
- * (0 or 2 = automatic by shape: decode kernel for M <= 16, mid-M kernel for
- * M <= 128, both for K <= 8192, large-tile GEMM otherwise; 1 = large-tile
- * path; 3 = mid-M kernel for every M <= 128).  Process-wide; returns the
- * previous value, or MXFP8_E_SHAPE for an unknown path.
+ * Test hook: force the GEMM path of mxfp8_linear and mxfp8_linear_w4a8.
+ * 0 or 2 = automatic: the path and the tile GEMM's K splits come from the
+ * shape table measured on MI355X (shape_table.inc, written by
+ * mxfp8_block_scaled_amd/tune_shapes.py), within each kernel's limits (decode
+ * kernel M <= 16 and K <= 8192, mid-M kernel M <= 128 and K <= 8192, K splits
+ * s need (K/64) % (4s) == 0); 1 = large-tile path with the table's splits;
+ * 3 = mid-M kernel where it applies; 4 = decode kernel where it applies;
+ * 16 + s (s = 1, 2, 4, 8) = large-tile path with s K splits where they apply
+ * (else one).  A forced path that a shape cannot take falls back to the
+ * large-tile path; mxfp8_linear_workspace_bytes follows the forced choice.
+ * Process-wide; returns the previous value, or MXFP8_E_SHAPE for an unknown
+ * value.
  */
 int mxfp8_debug_force_path(int path);
+
+/*
+ * Test hook (host only): the plan mxfp8_linear takes for an M x N x K call
+ * under the current forcing: *path = 0 large-tile GEMM, 1 decode kernel,
+ * 2 mid-M kernel; *splits = the tile GEMM's K splits (1 for the other paths).
+ * MXFP8_E_SHAPE for M < 1, N < 1 or K not a positive multiple of 256.
+ */
+int mxfp8_debug_plan(int64_t M, int64_t N, int64_t K, int* path, int* splits);
 
 #ifdef __cplusplus
 }

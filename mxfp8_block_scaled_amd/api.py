@@ -39,6 +39,7 @@ _SIGNATURES = {
     "mxfp8_quantize_act_packed": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
     "mxfp8_gemm_packed": ([_vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp], ctypes.c_int),
     "mxfp8_debug_force_path": ([ctypes.c_int], ctypes.c_int),
+    "mxfp8_debug_plan": ([_i64, _i64, _i64, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)], ctypes.c_int),
     "mxfp8_moe_prepared_bytes": ([_i64, _i64, _i64, ctypes.POINTER(_sz), ctypes.POINTER(_sz),
                                   ctypes.POINTER(_sz), ctypes.POINTER(_sz)], ctypes.c_int),
     "mxfp8_moe_prepare_weights": ([_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
@@ -231,6 +232,14 @@ def gemm_prequant(q, s, pw, bias=None):
 
 def mxfp8_debug_force_path(path):
     return lib().mxfp8_debug_force_path(path)
+
+
+def mxfp8_debug_plan(M, N, K):
+    """(path, splits) mxfp8_linear takes for M x N x K: path 0 = large-tile
+    GEMM, 1 = decode kernel, 2 = mid-M kernel."""
+    p, sp = ctypes.c_int(0), ctypes.c_int(0)
+    _check(lib().mxfp8_debug_plan(M, N, K, ctypes.byref(p), ctypes.byref(sp)), "mxfp8_debug_plan")
+    return p.value, sp.value
 
 
 # ---------------------------------------------------------------------------

@@ -9,6 +9,7 @@
 #include <mutex>
 
 #include "launch.hpp"
+#include "shape_table.inc"
 #include "mxfp8.h"
 
 namespace {
@@ -117,30 +118,52 @@ size_t moe_layout(int64_t T, int64_t H, int64_t E, int64_t topk, int64_t I, uint
   return off;
 }
 
-// GEMM path of a linear call: the decode kernel (M <= 16), the mid-M kernel
-// (M <= 128) or the large-tile GEMM; mxfp8_debug_force_path can pin it.
-enum class Path { kTile, kSkinny, kMid };
-Path linear_path(int64_t M, int64_t K) {
-  const int force = g_force_path.load(std::memory_order_relaxed);
-  const bool small_k = K <= mxfp8::kSkinnyMaxK;
-  if (force == 1 || !small_k) return Path::kTile;
-  if (force == 3) return M <= mxfp8::kMidMaxM ? Path::kMid : Path::kTile;
-  if (M <= mxfp8::kSkinnyMaxM) return Path::kSkinny;
-  return M <= mxfp8::kMidMaxM ? Path::kMid : Path::kTile;
+// GEMM path of a linear call and the K splits of the tile GEMM, from the
+// measured shape table (shape_table.inc): the decode kernel (M <= 16,
+// K <= 8192), the mid-M kernel (M <= 128, K <= 8192) or the large-tile GEMM
+// with 1 (persistent), 2, 4 or 8 K splits (a split count s needs (K / 64) %
+// (4 s) == 0: each slice a whole number of 128-K step pairs).  A table entry a
+// shape cannot take falls back to the tile GEMM / one split.
+// mxfp8_debug_force_path can pin the path and the splits.
+enum class Path { kTile = 0, kSkinny = 1, kMid = 2 };
+struct Plan {
+  Path path;
+  int splits;   // K splits of the tile GEMM (also when the path is not the tile)
+};
+
+int bucket(const int64_t* bounds, int n, int64_t v) {
+  for (int i = 0; i < n; ++i)
+    if (v <= bounds[i]) return i;
+  return n - 1;
 }
+bool splits_ok(int64_t K, int s) { return s == 1 || ((s == 2 || s == 4 || s == 8) && (K / 64) % (4 * s) == 0); }
+
+Plan linear_plan(int64_t M, int64_t N, int64_t K) {
+  const int im = bucket(mxfp8::kShapeTabM, mxfp8::kShapeTabNM, M);
+  const int in = bucket(mxfp8::kShapeTabN, mxfp8::kShapeTabNN, N);
+  const int ik = bucket(mxfp8::kShapeTabK, mxfp8::kShapeTabNK, K);
+  const int code = mxfp8::kShapeTabPlan[im][in][ik];
+  int s = mxfp8::kShapeTabTileSplits[im][in][ik];
+  if (!splits_ok(K, s)) s = 1;
+  Path path = (Path)(code >> 4);
+  const int force = g_force_path.load(std::memory_order_relaxed);
+  if (force == 1) path = Path::kTile;
+  if (force == 3) path = Path::kMid;
+  if (force == 4) path = Path::kSkinny;
+  if (force >= 16) {
+    path = Path::kTile;
+    if (splits_ok(K, force - 16)) s = force - 16;
+  }
+  const bool small_k = K <= mxfp8::kSkinnyMaxK;
+  if (path == Path::kSkinny && !(small_k && M <= mxfp8::kSkinnyMaxM)) path = Path::kTile;
+  if (path == Path::kMid && !(small_k && M <= mxfp8::kMidMaxM)) path = Path::kTile;
+  return {path, s};
+}
+Path linear_path(int64_t M, int64_t N, int64_t K) { return linear_plan(M, N, K).path; }
 
 }  // namespace
 
-// K splits of the tile GEMM: a shape with fewer than 128 256x256 tiles splits
-// K over up to 8 workgroups per tile (each slice a multiple of four 64-K
-// steps) while tiles x splits stays within 256.
-int mxfp8::gemm_tile_splits(int64_t M, int64_t N, int64_t K) {
-  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  const int64_t KS = K / 64;
-  int s = 1;
-  while (s < kMaxSplitK && tiles * s * 2 <= 256 && KS % (8 * s) == 0) s *= 2;
-  return tiles < 128 ? s : 1;
-}
+int mxfp8::gemm_tile_splits(int64_t M, int64_t N, int64_t K) { return linear_plan(M, N, K).splits; }
 
 // Compute units of the current device (the persistent GEMM's grid); the
 // device check caches it on the first call of any entry point.
@@ -170,14 +193,14 @@ int mxfp8::linear_check_args(const void* x_bf16, int64_t M, int64_t K, int64_t l
   if (int st = check_output(y_bf16, N, ldy, bias_bf16)) return st;
   if (ldx < K || ldx % 8 != 0) return MXFP8_E_LD;
   if (!aligned(x_bf16, 16)) return MXFP8_E_ALIGN;
-  if (linear_path(M, K) == Path::kTile && (n_pad(M) * (K / 8) + 255) / 256 > INT32_MAX) return MXFP8_E_SHAPE;
+  if (linear_path(M, N, K) == Path::kTile && (n_pad(M) * (K / 8) + 255) / 256 > INT32_MAX) return MXFP8_E_SHAPE;
   return MXFP8_OK;
 }
 
 int mxfp8::linear_launch(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, const void* w_packed,
                          const void* s_packed, int64_t N, const void* bias_bf16, void* y_bf16, int64_t ldy,
                          void* workspace, hipStream_t s) {
-  const Path path = linear_path(M, K);
+  const Path path = linear_path(M, N, K);
   if (path == Path::kSkinny)
     return mxfp8::launch_gemm_skinny(x_bf16, ldx, M, K, w_packed, s_packed, N, bias_bf16, y_bf16, ldy, s,
                                      workspace);
@@ -268,7 +291,7 @@ int mxfp8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes)
     *bytes = 256;
     return MXFP8_OK;
   }
-  switch (linear_path(M, K)) {
+  switch (linear_path(M, N, K)) {
     case Path::kSkinny: *bytes = mxfp8::skinny_ws_bytes(M, K); break;
     case Path::kMid: *bytes = mxfp8::mid_ws_bytes(M, K); break;
     default: *bytes = tile_ws_bytes(M, N, K);
@@ -328,7 +351,7 @@ int mxfp8_linear_w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* b
     *bytes = 256;
     return MXFP8_OK;
   }
-  switch (linear_path(M, K)) {
+  switch (linear_path(M, N, K)) {
     case Path::kSkinny: *bytes = mxfp8::skinny_ws_bytes(M, K); break;
     case Path::kMid: *bytes = mxfp8::mid_ws_bytes(M, K); break;
     default: *bytes = tile_ws_bytes(M, N, K) + (size_t)n_pad(N) * (size_t)K;
@@ -347,7 +370,7 @@ int mxfp8_linear_w4a8(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, con
   if (int st = check_output(y_bf16, N, ldy, bias_bf16)) return st;
   if (ldx < K || ldx % 8 != 0) return MXFP8_E_LD;
   if (!aligned(x_bf16, 16)) return MXFP8_E_ALIGN;
-  const Path path = linear_path(M, K);
+  const Path path = linear_path(M, N, K);
   if (path == Path::kTile && (n_pad(M) * (K / 8) + 255) / 256 > INT32_MAX) return MXFP8_E_SHAPE;
   size_t need = 0;
   mxfp8_linear_w4a8_workspace_bytes(M, N, K, &need);
@@ -530,8 +553,18 @@ int mxfp8_moe_debug_capture(void* act_bf16, void* act_e4m3, void* act_e8m0, void
 }
 
 int mxfp8_debug_force_path(int path) {
-  if (path < 0 || path > 3) return MXFP8_E_SHAPE;
+  const bool tile_splits = path == 17 || path == 18 || path == 20 || path == 24;
+  if (!(path >= 0 && path <= 4) && !tile_splits) return MXFP8_E_SHAPE;
   return g_force_path.exchange(path);
+}
+
+int mxfp8_debug_plan(int64_t M, int64_t N, int64_t K, int* path, int* splits) {
+  if (!path || !splits) return MXFP8_E_NULLPTR;
+  if (M < 1 || N < 1 || K < 256 || K % 256 != 0) return MXFP8_E_SHAPE;
+  const Plan pl = linear_plan(M, N, K);
+  *path = (int)pl.path;
+  *splits = pl.path == Path::kTile ? pl.splits : 1;
+  return MXFP8_OK;
 }
 
 }  // extern "C"

@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from mxfp8_block_scaled_amd import api
@@ -113,25 +114,60 @@ def test_linear_validation():
     bad = list(ok); bad[0] = P + 2; assert f(*bad) == -3
 
 
+def _round_up(v, a):
+    return (v + a - 1) // a * a
+
+
+def _expected_ws(M, N, K):
+    """Workspace of the plan the library reports: nothing stored on the decode
+    path; one 128-row group of packed activations (E4M3 tiles, then scale
+    tiles) on the mid-M path; the tile path's padded packed activations, then
+    the fp32 partials of its K splits."""
+    path, s = api.mxfp8_debug_plan(M, N, K)
+    if path == 1:
+        return 256
+    if path == 2:
+        return 128 * K + 128 * (K // 32)
+    mp = (M + 127) // 128 * 128
+    act = _round_up(mp * K, 256) + _round_up(mp * (K // 32), 256)
+    part = s * M * ((N + 3) // 4 * 4) * 4 if s > 1 else 0
+    return act + _round_up(part, 256)
+
+
 def test_linear_paths_workspace():
-    """Workspace per path: nothing stored for M <= 16; one 128-row group of
-    packed activations (E4M3 tiles, then scale tiles) for 16 < M <= 128; the
-    tile path's padded packed activations above; K > 8192 always takes the
-    tile path.  The forced paths move the M = 64 shape between them."""
+    """Workspace per planned path; K > 8192 always takes the tile path; the
+    forced paths move shapes between paths and split counts."""
     ws = api.mxfp8_linear_workspace_bytes
-    assert ws(16, 4096, 4096) == 256
-    assert ws(17, 4096, 4096) == ws(128, 4096, 4096) == 128 * 4096 + 128 * 128
-    assert ws(129, 4096, 4096) >= 256 * 4096 + 256 * 128
-    assert ws(8, 4096, 8448) >= 128 * 8448 + 128 * 264          # K > 8192: tile path
+    for M, N, K in [(1, 4096, 4096), (16, 4096, 4096), (17, 4096, 4096), (128, 4096, 4096), (129, 4096, 4096),
+                    (8, 4096, 8448), (300, 700, 2048), (4096, 4096, 1024), (64, 256, 512)]:
+        assert ws(M, N, K) == _expected_ws(M, N, K), (M, N, K)
+    assert api.mxfp8_debug_plan(8, 4096, 8448)[0] == 0              # K > 8192: tile path
     prev = api.mxfp8_debug_force_path(1)
     try:
-        assert ws(64, 4096, 4096) >= 128 * 4096 + 128 * 128      # tile path (split-K partials on top)
-        assert ws(8, 4096, 4096) >= 128 * 4096 + 128 * 128
+        assert api.mxfp8_debug_plan(64, 4096, 4096)[0] == 0
+        assert ws(64, 4096, 4096) == _expected_ws(64, 4096, 4096) >= 128 * 4096 + 128 * 128
         api.mxfp8_debug_force_path(3)
-        assert ws(8, 4096, 4096) == 128 * 4096 + 128 * 128       # mid path forced at M = 8
-        assert ws(200, 4096, 4096) >= 256 * 4096 + 256 * 128     # above 128: still the tile path
+        assert api.mxfp8_debug_plan(8, 4096, 4096) == (2, 1)
+        assert ws(8, 4096, 4096) == 128 * 4096 + 128 * 128           # mid path forced at M = 8
+        assert api.mxfp8_debug_plan(200, 4096, 4096)[0] == 0        # above 128: the tile path
+        api.mxfp8_debug_force_path(4)
+        assert api.mxfp8_debug_plan(16, 4096, 4096) == (1, 1)
+        assert ws(16, 4096, 4096) == 256
+        assert api.mxfp8_debug_plan(17, 4096, 4096)[0] != 1         # decode kernel only to M = 16
+        for sp in (1, 2, 4, 8):
+            api.mxfp8_debug_force_path(16 + sp)
+            assert api.mxfp8_debug_plan(300, 700, 2048) == (0, sp)   # K / 64 = 32 takes every split count
+            assert ws(300, 700, 2048) == _expected_ws(300, 700, 2048)
+        api.mxfp8_debug_force_path(24)
+        assert api.mxfp8_debug_plan(300, 700, 1280) == (0, 1)       # 20 steps: 8 slices do not divide
+        for bad in (-1, 5, 16, 19, 25, 40):
+            assert api.mxfp8_debug_force_path(bad) == -2
     finally:
         api.mxfp8_debug_force_path(prev)
+    with pytest.raises(api.MXFP8Error):
+        api.mxfp8_debug_plan(0, 256, 512)
+    with pytest.raises(api.MXFP8Error):
+        api.mxfp8_debug_plan(4, 256, 500)
     f = api.mxfp8_linear
     need = ws(64, 256, 512)
     ok = (P, 64, 512, 512, P, P, 256, None, P, 256, P, need, None)
@@ -139,8 +175,62 @@ def test_linear_paths_workspace():
     bad = list(ok); bad[11] = need - 1; assert f(*bad) == -5
     bad = list(ok); bad[10] = P + 128; assert f(*bad) == -3       # workspace 256-byte alignment
     g = api.mxfp8_linear_w4a8
-    assert api.mxfp8_linear_w4a8_workspace_bytes(64, 256, 512) == need   # no widened weight on this path
+    if api.mxfp8_debug_plan(64, 256, 512)[0] != 0:
+        assert api.mxfp8_linear_w4a8_workspace_bytes(64, 256, 512) == need   # no widened weight on this path
     expect_no_device(g, *ok)
+
+
+def _shape_table():
+    """The compiled-in shape table, parsed from its source."""
+    import re
+    text = open(os.path.join(ROOT, "mxfp8_block_scaled_amd", "csrc", "shape_table.inc")).read()
+    bounds = {}
+    for ax in "MNK":
+        m = re.search(r"kShapeTab%s\[kShapeTabN%s\] = \{([^}]*)\}" % (ax, ax), text)
+        bounds[ax] = [int(v) for v in m.group(1).split(",")]
+    def arr(name):
+        m = re.search(name + r"\[kShapeTabNM\]\[kShapeTabNN\]\[kShapeTabNK\] = (\{.*?\n\});", text, re.S)
+        vals = [int(v) for v in re.findall(r"\d+", m.group(1))]
+        nm, nn, nk = (len(bounds[a]) for a in "MNK")
+        assert len(vals) == nm * nn * nk
+        return [[[vals[(i * nn + j) * nk + k] for k in range(nk)] for j in range(nn)] for i in range(nm)]
+    return bounds, arr("kShapeTabPlan"), arr("kShapeTabTileSplits")
+
+
+def test_shape_table_well_formed_and_dispatched():
+    """Every table entry names a path and a split count; the library's plan
+    is the table's entry for the shape's bucket, limited by what each kernel
+    takes (decode M <= 16 and mid-M M <= 128, both K <= 8192; s splits need
+    (K/64) % (4s) == 0), checked over random shapes."""
+    bounds, plan, tsplit = _shape_table()
+    for ax in "MNK":
+        assert bounds[ax] == sorted(bounds[ax]) and len(set(bounds[ax])) == len(bounds[ax])
+    for i, row in enumerate(plan):
+        for j, col in enumerate(row):
+            for k, code in enumerate(col):
+                assert code >> 4 in (0, 1, 2) and (code & 15) in (1, 2, 4, 8)
+                assert tsplit[i][j][k] in (1, 2, 4, 8)
+
+    def bucket(ax, v):
+        for i, b in enumerate(bounds[ax]):
+            if v <= b:
+                return i
+        return len(bounds[ax]) - 1
+
+    rng = np.random.default_rng(7)
+    for _ in range(3000):
+        M = int(rng.choice([rng.integers(1, 300), rng.integers(1, 20000)]))
+        N = int(rng.integers(1, 40000))
+        K = int(rng.integers(1, 80)) * 256
+        i, j, k = bucket("M", M), bucket("N", N), bucket("K", K)
+        path, s = plan[i][j][k] >> 4, tsplit[i][j][k]
+        if path == 1 and not (M <= 16 and K <= 8192):
+            path = 0
+        if path == 2 and not (M <= 128 and K <= 8192):
+            path = 0
+        if s != 1 and (K // 64) % (4 * s) != 0:
+            s = 1
+        assert api.mxfp8_debug_plan(M, N, K) == (path, s if path == 0 else 1), (M, N, K)
 
 
 def test_packed_entries_validation():

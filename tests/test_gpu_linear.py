@@ -384,3 +384,21 @@ def test_gemm_prequant_matches_linear_tile_path():
             api.mxfp8_debug_force_path(prev)
         torch.cuda.synchronize()
         assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), (M, N, K)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 4, 8])
+def test_forced_tile_splits(splits):
+    """Every K split count the shape table may choose, on a ragged shape
+    (M = 300, N = 650: 2 x 3 tiles with a ragged last row and column tile)
+    whose K = 2048 (32 64-K steps) takes all of them: each within the derived
+    bound of the oracle's exact product."""
+    g = torch.Generator().manual_seed(500 + splits)
+    x = synth.randn_bf16((300, 2048), 1.0, g)
+    w = synth.randn_bf16((650, 2048), 0.02, g)
+    b = synth.randn_bf16((650,), 0.1, g)
+    prev = api.mxfp8_debug_force_path(16 + splits)
+    try:
+        assert api.mxfp8_debug_plan(300, 650, 2048) == (0, splits)
+    finally:
+        api.mxfp8_debug_force_path(prev)
+    gpu_util.run_linear_and_check(x, w, b, f"tile splits {splits}", force_path=16 + splits)
