@@ -17,15 +17,17 @@
 //
 // Pipeline (one stream, every step deterministic):
 //  1. route    one wave per token: k rounds of a wave arg-max, softmax over
-//              the k; per-block (16-token) expert histograms.
+//              the k; per-block (16-token) expert histograms; the token's
+//              row of x MX-quantized once, row-major, into xq / xs; the
+//              sorted-row list filled with -1.
 //  2. plan     one workgroup: per-expert counts, expert segments of the
 //              sorted row space padded to 128-row groups, per-block offsets,
 //              the M-tile list (256 rows = two groups of one expert).
 //  3. scatter  row (t, j) -> its position in its expert's segment, in
 //              increasing t*k + j order (wave ballots + per-wave counts).
-//  4. quant    x rows MX-quantized once, row-major, plus an all-zero row;
-//              the expert-sorted scale tiles of the GEMM operand gathered
-//              from them (pad rows: scale 0).
+//  4. gather   the expert-sorted scale tiles of the GEMM operand gathered
+//              from the token rows' scales (pad rows: scale 0); row T of xq
+//              (all zero) for pad rows.
 //  5. gemm1    per (M-tile, 256-row slice of W13[e]) the shared tile loop,
 //              its activation rows copied from the quantized x by row index;
 //              W13 is packed with gate and up rows interleaved so that each
@@ -57,15 +59,40 @@ __device__ inline bool route_better(float v, int e, float bv, int be) { return v
 }  // namespace
 
 // ---------------------------------------------------------------- 1. route
+// One wave per token also MX-quantizes the token's row of x into xq / xs
+// (row-major), by quant_act_kernel's rule and lane layout: four lanes per
+// 32-element block, 8 elements each, the block maximum over the four lanes
+// by two lane exchanges.  Its loads go out before the routing, so they are in
+// flight while the wave selects the experts.  Every block also fills its
+// share of the sorted-row list with -1 (the scatter writes the real rows
+// after the plan).
 __global__ __launch_bounds__(1024) void moe_route_kernel(const float* __restrict__ logits, int T, int E, int topk,
                                                          int* __restrict__ ids, float* __restrict__ wts,
-                                                         int* __restrict__ blk_cnt, int nblk) {
+                                                         int* __restrict__ blk_cnt, int nblk,
+                                                         const uint16_t* __restrict__ x, int H,
+                                                         uint8_t* __restrict__ xq, uint8_t* __restrict__ xs,
+                                                         int* __restrict__ sorted_row, int p_max) {
   __shared__ int hist[kMoeMaxExperts];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int e = tid; e < E; e += 1024) hist[e] = 0;
+  {
+    // p_max is a multiple of 128: 16-byte stores, a contiguous share per block.
+    const int n4 = p_max / 4, per = (n4 + nblk - 1) / nblk;
+    const int b0 = blockIdx.x * per, b1 = min(b0 + per, n4);
+    for (int i = b0 + tid; i < b1; i += 1024) reinterpret_cast<int4*>(sorted_row)[i] = make_int4(-1, -1, -1, -1);
+  }
   __syncthreads();
   const int t = blockIdx.x * kRouteTokens + wave;
   if (t < T) {
+    // The first (up to) four 8-element chunks of this lane in the row.
+    const int nc8 = H / 8;
+    const uint16_t* xr = x + (int64_t)t * H;
+    uint4 xv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c8 = u * 64 + lane;
+      xv[u] = c8 < nc8 ? *reinterpret_cast<const uint4*>(xr + c8 * 8) : make_uint4(0u, 0u, 0u, 0u);
+    }
     float v[4];
     bool ok[4];
 #pragma unroll
@@ -117,6 +144,37 @@ __global__ __launch_bounds__(1024) void moe_route_kernel(const float* __restrict
       wts[(int64_t)t * topk + lane] = z / s;
       atomicAdd(&hist[seli], 1);
     }
+    // MX quantization of the row (H % 256 == 0, so a block's four lanes are
+    // always all in range or all out).
+    uint8_t* qr = xq + (int64_t)t * H;
+    uint8_t* sr = xs + (int64_t)t * (H / 32);
+    for (int base = 0; base < nc8; base += 256) {
+      if (base > 0) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int c8 = base + u * 64 + lane;
+          xv[u] = c8 < nc8 ? *reinterpret_cast<const uint4*>(xr + c8 * 8) : make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c8 = base + u * 64 + lane;
+        const uint32_t w[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
+        u16x2 mp = {0, 0};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mp = absmax_pk(mp, w[i]);
+        uint32_t m = max((uint32_t)mp[0], (uint32_t)mp[1]);
+        m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+        m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+        const uint32_t sb = (uint32_t)max((int)(m >> 7) - 8, 0);
+        uint32_t qd[2];
+        cvt8s(w, mx_scale_value(sb), qd);
+        if (c8 < nc8) {
+          *reinterpret_cast<uint2*>(qr + c8 * 8) = make_uint2(qd[0], qd[1]);
+          if ((c8 & 3) == 0) sr[c8 >> 2] = (uint8_t)sb;
+        }
+      }
+    }
   }
   __syncthreads();
   for (int e = tid; e < E; e += 1024) blk_cnt[(int64_t)blockIdx.x * E + e] = hist[e];
@@ -126,14 +184,14 @@ __global__ __launch_bounds__(1024) void moe_route_kernel(const float* __restrict
 // meta[0] = number of M-tiles, meta[1] = number of 128-row groups in use.
 // One workgroup; every phase is parallel over experts and blocks.  Stores
 // count in the same vmcnt as loads, so each phase issues its loads, waits
-// once, and only then stores; the large -1 fill of sorted_row comes last.
+// once, and only then stores.  (The route kernel fills the sorted-row list
+// with -1.)
 constexpr int kPlanChunk = 32;
 
 __global__ __launch_bounds__(1024) void moe_plan_kernel(const int* __restrict__ blk_cnt, int nblk, int E,
                                                         int* __restrict__ blk_off, int* __restrict__ seg_off,
                                                         int* __restrict__ tile_e, int* __restrict__ tile_g0,
-                                                        int* __restrict__ tile_ng, int* __restrict__ meta,
-                                                        int* __restrict__ sorted_row, int p_max) {
+                                                        int* __restrict__ tile_ng, int* __restrict__ meta) {
   __shared__ int part[1024];
   __shared__ int cnt[kMoeMaxExperts], gstart[kMoeMaxExperts], tstart[kMoeMaxExperts];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -152,12 +210,19 @@ __global__ __launch_bounds__(1024) void moe_plan_kernel(const int* __restrict__ 
     for (int u = 0; u < kPlanChunk; ++u) v[u] = blk_cnt[(int64_t)min(b + u, b1 - 1) * E + e];
   };
   int sum = 0;
+  // With at most one chunk per thread (T <= 32 * 16 * 1024 / E tokens) the
+  // counts stay in registers for the offsets below.
+  const bool one_chunk = b1 - b0 <= kPlanChunk;
+  int v0[kPlanChunk];
   if (mine)
     for (int b = b0; b < b1; b += kPlanChunk) {
       int v[kPlanChunk];
       load_chunk(b, v);
 #pragma unroll
-      for (int u = 0; u < kPlanChunk; ++u) sum += (b + u < b1) ? v[u] : 0;
+      for (int u = 0; u < kPlanChunk; ++u) {
+        sum += (b + u < b1) ? v[u] : 0;
+        v0[u] = v[u];
+      }
     }
   part[tid] = sum;
   __syncthreads();
@@ -208,8 +273,13 @@ __global__ __launch_bounds__(1024) void moe_plan_kernel(const int* __restrict__ 
     for (int k = 0; k < c; ++k) run += part[k * E + e];
     for (int b = b0; b < b1; b += kPlanChunk) {
       int v[kPlanChunk];
-      load_chunk(b, v);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (one_chunk) {
+#pragma unroll
+        for (int u = 0; u < kPlanChunk; ++u) v[u] = v0[u];
+      } else {
+        load_chunk(b, v);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
 #pragma unroll
       for (int u = 0; u < kPlanChunk; ++u) {
         if (b + u < b1) blk_off[(int64_t)(b + u) * E + e] = run;
@@ -226,8 +296,6 @@ __global__ __launch_bounds__(1024) void moe_plan_kernel(const int* __restrict__ 
       tile_ng[tstart[tid] + u] = min(2, groups - 2 * u);
     }
   }
-  // p_max is a multiple of 128: fill with 16-byte stores.
-  for (int p = tid; p < p_max / 4; p += 1024) reinterpret_cast<int4*>(sorted_row)[p] = make_int4(-1, -1, -1, -1);
 }
 
 // ---------------------------------------------------------------- 3. scatter
@@ -576,19 +644,17 @@ int launch_moe(const MoeArgs& a, hipStream_t stream) {
   const int nblk = (int)((a.T + kRouteTokens - 1) / kRouteTokens);
   const int R = (int)(a.T * a.topk);
   hipLaunchKernelGGL(moe_route_kernel, dim3(nblk), dim3(1024), 0, stream, a.logits, (int)a.T, (int)a.E,
-                     (int)a.topk, a.ws.ids, a.ws.wts, a.ws.blk_cnt, nblk);
+                     (int)a.topk, a.ws.ids, a.ws.wts, a.ws.blk_cnt, nblk, (const uint16_t*)a.x, (int)a.H, a.ws.xq,
+                     a.ws.xs, a.ws.sorted_row, (int)a.ws.p_max);
   if (a.dbg_ids != nullptr) {
     hipMemcpyAsync(a.dbg_ids, a.ws.ids, (size_t)R * 4, hipMemcpyDeviceToDevice, stream);
     hipMemcpyAsync(a.dbg_wts, a.ws.wts, (size_t)R * 4, hipMemcpyDeviceToDevice, stream);
   }
   hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(1024), 0, stream, a.ws.blk_cnt, nblk, (int)a.E, a.ws.blk_off,
-                     a.ws.seg_off, a.ws.tile_e, a.ws.tile_g0, a.ws.tile_ng, a.ws.meta, a.ws.sorted_row,
-                     (int)a.ws.p_max);
+                     a.ws.seg_off, a.ws.tile_e, a.ws.tile_g0, a.ws.tile_ng, a.ws.meta);
   hipLaunchKernelGGL(moe_scatter_kernel, dim3(nblk), dim3(256), 0, stream, a.ws.ids, R, (int)a.topk, (int)a.E,
                      a.ws.blk_off, a.ws.seg_off, a.ws.sorted_row);
   const int KS1 = (int)(a.H / kStepK);
-  const int qs = launch_quantize_act(a.x, a.T, a.H, a.H, a.ws.xq, a.H, a.ws.xs, a.H / 32, stream);
-  if (qs != 0) return qs;
   hipLaunchKernelGGL(moe_gather_scales_kernel, dim3((unsigned)(a.ws.p_max / kGroupRows * KS1 / 4)), dim3(256), 0,
                      stream, a.ws.xs, (int)a.H, (int)a.topk, a.ws.sorted_row, a.ws.meta, KS1, a.ws.a1s,
                      a.ws.xq + a.T * a.H);
