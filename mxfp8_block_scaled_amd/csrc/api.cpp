@@ -354,7 +354,10 @@ int mxfp8_linear_w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* b
   switch (linear_path(M, N, K)) {
     case Path::kSkinny: *bytes = mxfp8::skinny_ws_bytes(M, K); break;
     case Path::kMid: *bytes = mxfp8::mid_ws_bytes(M, K); break;
-    default: *bytes = tile_ws_bytes(M, N, K) + (size_t)n_pad(N) * (size_t)K;
+    default:
+      // K splits: the weight widened to MXFP8 tiles after the split-K
+      // workspace; one split: the 4-bit tile GEMM, no widened copy.
+      *bytes = tile_ws_bytes(M, N, K) + (mxfp8::gemm_tile_splits(M, N, K) > 1 ? (size_t)n_pad(N) * (size_t)K : 0);
   }
   return MXFP8_OK;
 }
@@ -384,16 +387,19 @@ int mxfp8_linear_w4a8(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, con
   if (path == Path::kMid)
     return mxfp8::launch_gemm_mid_fp4(x_bf16, ldx, M, K, w_packed, s_packed, N, bias_bf16, y_bf16, ldy, s,
                                       workspace);
-  // Larger M is MFMA-bound: widen the weight to the MXFP8 tiles (exact) and
-  // run the MXFP8 tile GEMM.
+  // Larger M is MFMA-bound: the 4-bit tile GEMM on the packed activations;
+  // where the shape table splits K, the weight widened to the MXFP8 tiles
+  // (exact) and the split-K MXFP8 tile GEMM.
   uint8_t* q = (uint8_t*)workspace;
   uint8_t* sc = q + round_up((size_t)n_pad(M) * (size_t)K, 256);
   uint8_t* part = q + tile_ws_act_bytes(M, K);
+  const int splits = mxfp8::gemm_tile_splits(M, N, K);
+  if (int st = mxfp8::launch_quantize_act_packed(x_bf16, M, K, ldx, q, sc, s)) return st;
+  if (splits == 1)
+    return mxfp8::launch_gemm_tile_w4(q, sc, M, K, w_packed, s_packed, N, bias_bf16, y_bf16, ldy, s);
   uint8_t* w8 = q + tile_ws_bytes(M, N, K);
   if (int st = mxfp8::launch_widen_fp4(w_packed, N, K, w8, s)) return st;
-  if (int st = mxfp8::launch_quantize_act_packed(x_bf16, M, K, ldx, q, sc, s)) return st;
-  return mxfp8::launch_gemm_tile(q, sc, M, K, w8, s_packed, N, bias_bf16, y_bf16, ldy, s,
-                                 mxfp8::gemm_tile_splits(M, N, K), part);
+  return mxfp8::launch_gemm_tile(q, sc, M, K, w8, s_packed, N, bias_bf16, y_bf16, ldy, s, splits, part);
 }
 
 int mxfp8_packed_act_bytes(int64_t M, int64_t K, size_t* q_bytes, size_t* s_bytes) {

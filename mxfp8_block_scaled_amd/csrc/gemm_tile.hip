@@ -124,6 +124,64 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_persistent_kernel(
   tile::persistent16(st0, st1, st2, st3, epi, blds, total, KS, decode, y, ldy, M, N, bias, vec_store);
 }
 
+// W4A8: the persistent GEMM with the weight operand as packed MXFP4 (the
+// 4-bit loop of persistent16_run: two 50 KiB step buffers, each one 128-K
+// step of 4-bit weights, E4M3 activations and both scale tiles).  The weight
+// group of 128 rows holds KS/2 pieces per band; the scales are laid out as
+// for MXFP8.
+__global__ __launch_bounds__(kThreads, 1) void gemm_persistent_w4_kernel(
+    const uint8_t* __restrict__ qp, const uint8_t* __restrict__ qsp, int M, int K,
+    const uint8_t* __restrict__ wp, const uint8_t* __restrict__ wsp, int N, int GN, int GM,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int64_t ldy, int tiles_m, int tiles_n,
+    int vec_store) {
+  __shared__ __attribute__((aligned(16))) uint8_t buf0[tile::kW4Buf];
+  __shared__ __attribute__((aligned(16))) uint8_t buf1[tile::kW4Buf];
+  __shared__ __attribute__((aligned(16))) uint8_t epi[tile::kEpiBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t blds[tile::kBiasBytes];
+
+  const int total = tiles_m * tiles_n;
+  const int KS = K / kStepK;
+  const size_t op_stride = (size_t)KS * kTileBytes;          // activations: bytes per 128-row group
+  const size_t w_stride = (size_t)(KS / 2) * kTileBytes;     // 4-bit weights: half of that
+  const size_t sc_stride = (size_t)KS * kTileScaleBytes;
+  auto decode = [&](int bidx, bool) {
+    const int logical = tile::xcd_remap(bidx, total);
+    const int per_group = kGroupM * tiles_n;
+    const int group = logical / per_group;
+    const int first_m = group * kGroupM;
+    const int gm = min(tiles_m - first_m, kGroupM);
+    const int in_group = logical - group * per_group;
+    const int tm = first_m + in_group % gm;
+    const int tn = in_group / gm;
+    const int wa = min(2 * tn, GN - 1), wb = min(2 * tn + 1, GN - 1);
+    const int xa = min(2 * tm, GM - 1), xb = min(2 * tm + 1, GM - 1);
+    tile::Job16 j;
+    j.wga = wp + wa * w_stride;
+    j.wgb = wp + wb * w_stride;
+    j.xga = qp + xa * op_stride;
+    j.xgb = qp + xb * op_stride;
+    j.swa = wsp + wa * sc_stride;
+    j.swb = wsp + wb * sc_stride;
+    j.sxa = qsp + xa * sc_stride;
+    j.sxb = qsp + xb * sc_stride;
+    j.row0 = tm * 256;
+    j.col0 = tn * 256;
+    return j;
+  };
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = wave >> 1;
+  tile::persistent16_run<1, tile::kBiasSlot, true, true>(
+      buf0, buf0 + tile::kOpBytes, buf1, buf1 + tile::kOpBytes, blds, total, KS, decode,
+      [&](const tile::Job16& j) { return tile::W4Src(j.wga, j.wgb, j.xga, j.xgb, j.swa, j.swb, j.sxa, j.sxb, KS); },
+      [&](const tile::Job16& j) { return tile::bias_rsrc(bias, j.col0, N); },
+      [&](tile::i4v r, uint8_t* slot) { tile::b2l_4((uint32_t)(wn * 256 + lane * 4), r, 0u, slot + wave * 256); },
+      [&](int) {},
+      [&](const v4f (&acc)[8][8], const tile::Job16& j, const uint8_t* slot) {
+        return tile::epi16(epi, slot + wave * 256, acc, y, ldy, j.row0, M, j.col0, N, vec_store);
+      });
+}
+
 // y[m][n] = bf16( sum_s part[s][m][n] + bias[n] ), slices added in order.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int splits, int M, int N,
                                                             int64_t ldp, const uint16_t* __restrict__ bias,
@@ -176,6 +234,22 @@ int launch_gemm_tile(const void* qp, const void* sp, int64_t M, int64_t K, const
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
                        (const float*)part, splits, (int)M, (int)N, ldp, (const uint16_t*)bias, (uint16_t*)y, ldy);
   }
+  return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+int launch_gemm_tile_w4(const void* qp, const void* sp, int64_t M, int64_t K, const void* w4p, const void* wsp,
+                        int64_t N, const void* bias, void* y, int64_t ldy, hipStream_t stream) {
+  const int64_t GN = (N + kGroupRows - 1) / kGroupRows;
+  const int64_t GM = (M + kGroupRows - 1) / kGroupRows;
+  const int tiles_n = (int)((GN + 1) / 2);
+  const int tiles_m = (int)((GM + 1) / 2);
+  const int vec = (ldy % 8 == 0 && ((uintptr_t)y & 15) == 0) ? 2 : (ldy % 4 == 0 && ((uintptr_t)y & 7) == 0) ? 1 : 0;
+  const int total = tiles_m * tiles_n;
+  const int cus = device_cu_count();
+  const int grid = total <= cus ? total : (cus >= 8 ? cus - cus % 8 : cus);
+  hipLaunchKernelGGL(gemm_persistent_w4_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, (const uint8_t*)qp,
+                     (const uint8_t*)sp, (int)M, (int)K, (const uint8_t*)w4p, (const uint8_t*)wsp, (int)N, (int)GN,
+                     (int)GM, (const uint16_t*)bias, (uint16_t*)y, ldy, tiles_m, tiles_n, vec);
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 

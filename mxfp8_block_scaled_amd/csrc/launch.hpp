@@ -59,6 +59,10 @@ int gemm_tile_splits(int64_t M, int64_t N, int64_t K);
 int launch_gemm_tile(const void* qp, const void* sp, int64_t M, int64_t K, const void* wp, const void* wsp,
                      int64_t N, const void* bias, void* y, int64_t ldy, hipStream_t stream, int splits = 1,
                      void* part = nullptr);
+// The same persistent tile GEMM with the weight as packed MXFP4 (W4A8, no
+// K split; pack_weight_fp4's layout, scales as for MXFP8).
+int launch_gemm_tile_w4(const void* qp, const void* sp, int64_t M, int64_t K, const void* w4p, const void* wsp,
+                        int64_t N, const void* bias, void* y, int64_t ldy, hipStream_t stream);
 
 // Skinny GEMM (M <= kSkinnyMaxM, K <= kSkinnyMaxK) with the activation
 // quantization fused in; it needs no workspace (skinny_ws_bytes is the

@@ -510,7 +510,7 @@ __global__ __launch_bounds__(tile::kThreads, 1) void moe_gemm1_kernel(
     }
     return false;   // the number of stores depends on the rows
   };
-  tile::persistent16_run<0, 0, true>(st0, st1, st2, st3, nullptr, total, KS, decode, make_src,
+  tile::persistent16_run<0, 0, true, false>(st0, st1, st2, st3, nullptr, total, KS, decode, make_src,
                                [](const Moe1Job&) { return tile::buffer_rsrc(nullptr, 0); },
                                [](tile::i4v, uint8_t*) {}, tile_start, epilogue);
 }
@@ -612,7 +612,7 @@ __global__ __launch_bounds__(tile::kThreads, 1) void moe_gemm2_kernel(
     }
     return true;
   };
-  tile::persistent16_run<1, kRowSlot, false>(st0, st1, st2, st3, side, total, KS, decode, make_src, side_of, side_copy,
+  tile::persistent16_run<1, kRowSlot, false, false>(st0, st1, st2, st3, side, total, KS, decode, make_src, side_of, side_copy,
                                       [](int) {}, epilogue);
 }
 

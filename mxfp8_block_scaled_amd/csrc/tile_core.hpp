@@ -410,6 +410,71 @@ __device__ __forceinline__ void mfma16(v4f& c, const v8i& a, const v8i& b, int s
                : "v"(a), "v"(b), "v"(sa), "v"(sb), "n"(kSelA & 1), "n"(kSelB & 1), "n"(kSelA >> 1), "n"(kSelB >> 1));
 }
 
+// c += A x B with A (the weight) in E2M1: one 16-byte register quad per lane
+// holds K [32g, 32g + 32) of the lane's row (cbsz:4 selects the format); the
+// scales and everything else as in mfma16.
+template <int kSelA, int kSelB>
+__device__ __forceinline__ void mfma16w4(v4f& c, const i4v& a, const v8i& b, int sa, int sb) {
+  asm volatile(
+      "s_nop 1\n\tv_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[%5,%6,0] op_sel_hi:[%7,%8,0] cbsz:4"
+      : "+a"(c)
+      : "v"(a), "v"(b), "v"(sa), "v"(sb), "n"(kSelA & 1), "n"(kSelB & 1), "n"(kSelA >> 1), "n"(kSelB >> 1));
+}
+
+// Copy source of the 4-bit weight tile (persistent16_run<..., kW4 = true>).
+// A step buffer of 50 KiB holds one 128-K step: the weights as packed MXFP4
+// (a 128-K step of a 16-row band is one 1 KiB piece, bands KS/2 pieces
+// apart: 16 KiB for the 256 rows at offset 0), the activations' even and odd
+// 64-K stages at kOpBytes and 2 kOpBytes (as in a stage pair), and the scale
+// tiles of the two 64-K steps (weights and activations, 1 KiB each) at
+// 3 kOpBytes and 3 kOpBytes + 1024.  issue(j, s, st): j = 0..3 weight pieces
+// of 128-K step s (bands w, w + 4 of the two groups), 4..7 activation pieces
+// of 64-K step s as BufSrc, 8 and 9 the wave's 256-byte scale run of 64-K
+// step s into the even or odd scale slot.
+struct W4Src {
+  i4v w0, w1, x0, x1, sc;
+  uint32_t wlo, whi, xlo, xhi, soff_lane;
+  int wave;
+
+  W4Src() = default;
+
+  __device__ __forceinline__ W4Src(const uint8_t* wga, const uint8_t* wgb, const uint8_t* xga, const uint8_t* xgb,
+                                   const uint8_t* swa, const uint8_t* swb, const uint8_t* sxa, const uint8_t* sxb,
+                                   int KS) {
+    const int tid = threadIdx.x;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int KS4 = KS / 2;
+    w0 = buffer_rsrc(wga, (uint32_t)KS4 * kTileBytes);
+    w1 = buffer_rsrc(wgb, (uint32_t)KS4 * kTileBytes);
+    x0 = buffer_rsrc(xga, (uint32_t)KS * kTileBytes);
+    x1 = buffer_rsrc(xgb, (uint32_t)KS * kTileBytes);
+    sc = buffer_rsrc(wave == 0 ? swa : wave == 1 ? swb : wave == 2 ? sxa : sxb, (uint32_t)KS * kTileScaleBytes);
+    wlo = (uint32_t)wave * KS4 * kPieceBytes + (uint32_t)(tid & 63) * 16;
+    whi = wlo + 4u * KS4 * kPieceBytes;
+    xlo = (uint32_t)wave * KS * kPieceBytes + (uint32_t)(tid & 63) * 16;
+    xhi = xlo + 4u * KS * kPieceBytes;
+    soff_lane = (uint32_t)(tid & 63) * 4;
+  }
+
+  __device__ __forceinline__ void issue(int j, int s, uint8_t* st) const {
+    uint8_t* base = st + wave * 1024;
+    const uint32_t off = (uint32_t)s * kPieceBytes;
+    switch (j) {
+      case 0: b2l_16(wlo, w0, off, base); break;
+      case 1: b2l_16(whi, w0, off, base + 4096); break;
+      case 2: b2l_16(wlo, w1, off, base + 8192); break;
+      case 3: b2l_16(whi, w1, off, base + 12288); break;
+      case 4: b2l_16(xlo, x0, off, base + kOpBytes); break;
+      case 5: b2l_16(xhi, x0, off, base + kOpBytes + 4096); break;
+      case 6: b2l_16(xlo, x1, off, base + kOpBytes + 8192); break;
+      case 7: b2l_16(xhi, x1, off, base + kOpBytes + 12288); break;
+      case 8: b2l_4(soff_lane, sc, (uint32_t)s * kTileScaleBytes, st + 3 * kOpBytes + wave * 256); break;
+      default: b2l_4(soff_lane, sc, (uint32_t)s * kTileScaleBytes, st + 3 * kOpBytes + 1024 + wave * 256); break;
+    }
+  }
+};
+constexpr int kW4Buf = 3 * kOpBytes + 2048;          // 51200: one 128-K step of the 4-bit tile
+
 // The same 256 x 256 tile on v_mfma_scale_f32_16x16x128_f8f6f4.  A 16x16x128
 // MFMA does the work of half a 32x32x64 one with the same operand bytes per
 // flop and a quarter of the accumulator traffic, and on gfx950 the chip
@@ -910,10 +975,15 @@ __device__ __forceinline__ bool epi16(uint8_t* epi, const uint8_t* bias_slot, co
 //    LDS after the epilogue (their stage pair is not refilled before the
 //    next tile's first barrier), which frees those registers for an
 //    epilogue that needs them.
+//  * kW4: the weight operand is packed MXFP4 (W4Src, mfma16w4): a 128-K step
+//    is one step buffer of kW4Buf bytes, passed as (st0, st1) = (buffer 0,
+//    buffer 0 + kOpBytes) and (st2, st3) likewise for buffer 1, so that the
+//    activation stages sit where a stage pair puts them; six weight and scale
+//    copies per step instead of ten.
 // total: tiles of the list; gridDim.x % 8 == 0 keeps every workgroup's tiles
 // on one XCD under xcd_remap.
-template <int kSide, int kSideSlot, bool kCarry, typename Decode, typename MakeSrc, typename SideOf, typename SideCopy,
-          typename TileStart, typename Epilogue>
+template <int kSide, int kSideSlot, bool kCarry, bool kW4, typename Decode, typename MakeSrc, typename SideOf,
+          typename SideCopy, typename TileStart, typename Epilogue>
 __device__ __forceinline__ void persistent16_run(uint8_t* st0, uint8_t* st1, uint8_t* st2, uint8_t* st3,
                                                  uint8_t* side_lds, int total, int KS, Decode decode,
                                                  MakeSrc make_src, SideOf side_of, SideCopy side_copy,
@@ -926,8 +996,10 @@ __device__ __forceinline__ void persistent16_run(uint8_t* st0, uint8_t* st1, uin
   const int wn = wave >> 1, wm = wave & 1;
   const int li = lane & 15, lg = lane >> 4;
 
+  using AFrag = typename std::conditional<kW4, i4v, v8i>::type;
+  constexpr int kWCopies = kW4 ? 6 : 10;         // weight + scale copies per 128-K step
   struct State {
-    v8i a[8];
+    AFrag a[8];
     v8i bf[4];
     int sa[2], sb[2];
   };
@@ -940,15 +1012,35 @@ __device__ __forceinline__ void persistent16_run(uint8_t* st0, uint8_t* st1, uin
     const uint4 lo = rd16(ev + off), hi = rd16(od + off);
     return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   };
+  // The weight fragment of tile row block a: 32 bytes from the stage pair, or
+  // (kW4) 16 bytes of the step buffer's 4-bit weights.
+  auto frag_a = [&](const uint8_t* ev, const uint8_t* od, int a) -> AFrag {
+    if constexpr (kW4) {
+      const uint4 v = rd16(ev + offA + 1024 * a);
+      return i4v{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+    } else {
+      return frag(ev, od, offA + 1024 * a);
+    }
+  };
   auto rd_scale = [&](const uint8_t* ev, const uint8_t* od, int base, int e) {
-    const uint8_t* st = (lg >> 1) ? od : ev;
-    return *reinterpret_cast<const int*>(st + offS + base + 128 * e);
+    if constexpr (kW4) {
+      return *reinterpret_cast<const int*>(ev + 3 * kOpBytes + (lg >> 1) * 1024 + scale_off(li, lg & 1) + base +
+                                           128 * e);
+    } else {
+      const uint8_t* st = (lg >> 1) ? od : ev;
+      return *reinterpret_cast<const int*>(st + offS + base + 128 * e);
+    }
   };
   using Job = decltype(decode(0, false));
   using Src = decltype(make_src(decode(0, false)));
   auto issue_w = [&](const Src& sr, int k, int q, uint8_t* ev, uint8_t* od) {
-    const int t = k / 5, c = k % 5;
-    sr.issue(c < 4 ? c : 8, 2 * q + t, t ? od : ev);
+    if constexpr (kW4) {
+      if (k < 4) sr.issue(k, q, ev);
+      else sr.issue(4 + k, 2 * q + (k - 4), ev);      // scale slots 8, 9
+    } else {
+      const int t = k / 5, c = k % 5;
+      sr.issue(c < 4 ? c : 8, 2 * q + t, t ? od : ev);
+    }
   };
   auto issue_x = [&](const Src& sr, int k, int q, uint8_t* ev, uint8_t* od) {
     const int t = k >> 2;
@@ -984,12 +1076,12 @@ __device__ __forceinline__ void persistent16_run(uint8_t* st0, uint8_t* st1, uin
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         const bool extra = decltype(kVm)::value && vm_extra == 32;
         if constexpr (kI) {
-          if (extra) wait_vmcnt<42>();
-          else wait_vmcnt<10>();
+          if (extra) wait_vmcnt<kWCopies + 32>();
+          else wait_vmcnt<kWCopies>();
         } else {
           if (issue) {
-            if (extra) wait_vmcnt<42>();
-            else wait_vmcnt<10>();
+            if (extra) wait_vmcnt<kWCopies + 32>();
+            else wait_vmcnt<kWCopies>();
           } else {
             if (extra) wait_vmcnt<32>();
             else wait_vmcnt<0>();
@@ -998,10 +1090,11 @@ __device__ __forceinline__ void persistent16_run(uint8_t* st0, uint8_t* st1, uin
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
       }
-      mfma16<(a >> 1), (bb >> 1)>(acc[a][bb], S.a[a], S.bf[bb & 3], S.sa[a & 1], S.sb[bb & 1]);
+      if constexpr (kW4) mfma16w4<(a >> 1), (bb >> 1)>(acc[a][bb], S.a[a], S.bf[bb & 3], S.sa[a & 1], S.sb[bb & 1]);
+      else mfma16<(a >> 1), (bb >> 1)>(acc[a][bb], S.a[a], S.bf[bb & 3], S.sa[a & 1], S.sb[bb & 1]);
       if constexpr (kI || kR) {
         if (issue) {
-          if constexpr (j >= 8 && j < 18) issue_w(sr, j - 8, q, ev, od);
+          if constexpr (j >= 8 && j < 8 + kWCopies) issue_w(sr, j - 8, q, ev, od);
           if constexpr (j >= 48 && j < 56) issue_x(sr, j - 48, q, ev, od);
           if constexpr (decltype(with_side)::value && j == 56) issue_side(brs, bbuf);
         }
@@ -1015,7 +1108,7 @@ __device__ __forceinline__ void persistent16_run(uint8_t* st0, uint8_t* st1, uin
         }
         if constexpr (j == 49) { nsb[0] = rd_scale(nev, nod, swB, 0); nsb[1] = rd_scale(nev, nod, swB, 1); }
         if constexpr (j == 56) S.bf[1] = frag(nev, nod, offB + 1024);
-        if constexpr (j >= 56) S.a[a] = frag(nev, nod, offA + 1024 * a);
+        if constexpr (j >= 56) S.a[a] = frag_a(nev, nod, a);
       }
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -1031,7 +1124,7 @@ __device__ __forceinline__ void persistent16_run(uint8_t* st0, uint8_t* st1, uin
     S.sb[0] = rd_scale(ev, od, swB, 0);
     S.sb[1] = rd_scale(ev, od, swB, 1);
 #pragma unroll
-    for (int a = 0; a < 8; ++a) S.a[a] = frag(ev, od, offA + 1024 * a);
+    for (int a = 0; a < 8; ++a) S.a[a] = frag_a(ev, od, a);
     S.bf[0] = frag(ev, od, offB);
     S.bf[1] = frag(ev, od, offB + 1024);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -1043,15 +1136,15 @@ __device__ __forceinline__ void persistent16_run(uint8_t* st0, uint8_t* st1, uin
   Src src = make_src(cur);
   // First tile: its two first steps and its bias, then its first fragments.
 #pragma unroll
-  for (int k = 0; k < 10; ++k) issue_w(src, k, 0, st0, st1);
+  for (int k = 0; k < kWCopies; ++k) issue_w(src, k, 0, st0, st1);
 #pragma unroll
   for (int k = 0; k < 8; ++k) issue_x(src, k, 0, st0, st1);
 #pragma unroll
-  for (int k = 0; k < 10; ++k) issue_w(src, k, 1, st2, st3);
+  for (int k = 0; k < kWCopies; ++k) issue_w(src, k, 1, st2, st3);
 #pragma unroll
   for (int k = 0; k < 8; ++k) issue_x(src, k, 1, st2, st3);
   if constexpr (kSide > 0) issue_side(side_of(cur), 0);
-  wait_vmcnt<18 + kSide>();
+  wait_vmcnt<kWCopies + 8 + kSide>();
   __builtin_amdgcn_s_barrier();
   read_first(st0, st1);
 
@@ -1115,7 +1208,7 @@ __device__ __forceinline__ void persistent16(uint8_t* st0, uint8_t* st1, uint8_t
   const int wn = wave >> 1;
   // Side data: the tile's 256 bias values; wave w copies the 128 of its
   // columns (wn * 128 ..) into its own 256 bytes of the slot.
-  persistent16_run<1, kBiasSlot, true>(
+  persistent16_run<1, kBiasSlot, true, false>(
       st0, st1, st2, st3, bias_lds, total, KS, [&](int bidx, bool) { return decode(bidx); },
       [&](const Job16& j) { return BufSrc(j.wga, j.wgb, j.xga, j.xgb, j.swa, j.swb, j.sxa, j.sxb, KS, KS); },
       [&](const Job16& j) { return bias_rsrc(bias, j.col0, N); },

@@ -81,6 +81,11 @@ int launch_gemm_tile(const void*, const void*, int64_t M, int64_t, const void*, 
   touch(nullptr, 0);
   return 0;
 }
+int launch_gemm_tile_w4(const void*, const void*, int64_t M, int64_t, const void*, const void*, int64_t N,
+                        const void*, void* y, int64_t ldy, hipStream_t) {
+  touch_rows(y, M, N, ldy, 2);
+  return 0;
+}
 int launch_gemm_skinny(const void*, int64_t, int64_t M, int64_t, const void*, const void*, int64_t N, const void*,
                        void* y, int64_t ldy, hipStream_t, void*) {
   touch_rows(y, M, N, ldy, 2);

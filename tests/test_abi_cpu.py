@@ -315,13 +315,24 @@ def test_w4a8_sizes_and_validation():
     assert api.mxfp8_prepared_weight_fp4_bytes(4096, 4096) == (4096 * 2048, 4096 * 128)
     with pytest.raises(api.MXFP8Error):
         api.mxfp8_prepared_weight_fp4_bytes(130, 384)
-    # workspace: decode shapes as the MXFP8 layer; larger M adds the widened weight
+    # workspace: decode and mid-M shapes as the MXFP8 layer; on the tile path
+    # the 4-bit GEMM (one K split) needs nothing more, the split-K route adds
+    # the weight widened to MXFP8 tiles (N padded to 128 rows x K bytes)
     assert api.mxfp8_linear_w4a8_workspace_bytes(7, 4096, 4096) == api.mxfp8_linear_workspace_bytes(7, 4096, 4096)
     assert api.mxfp8_linear_w4a8_workspace_bytes(16, 4096, 4096) == api.mxfp8_linear_workspace_bytes(16, 4096, 4096)
-    # M <= 16 (K <= 8192) stores nothing in the workspace: the 256-byte minimum
-    assert api.mxfp8_linear_workspace_bytes(16, 4096, 8192) == 256
-    assert (api.mxfp8_linear_w4a8_workspace_bytes(512, 130, 256)
-            == api.mxfp8_linear_workspace_bytes(512, 130, 256) + 256 * 256)
+    assert api.mxfp8_linear_workspace_bytes(16, 4096, 8192) == _expected_ws(16, 4096, 8192)
+    for M, N, K in [(512, 130, 256), (300, 700, 2048), (4096, 4096, 4096), (256, 4096, 4096)]:
+        path, sp = api.mxfp8_debug_plan(M, N, K)
+        extra = (N + 127) // 128 * 128 * K if path == 0 and sp > 1 else 0
+        assert api.mxfp8_linear_w4a8_workspace_bytes(M, N, K) == api.mxfp8_linear_workspace_bytes(M, N, K) + extra
+    prev = api.mxfp8_debug_force_path(18)          # tile GEMM, 2 K splits: the widened route
+    try:
+        assert (api.mxfp8_linear_w4a8_workspace_bytes(300, 700, 2048)
+                == api.mxfp8_linear_workspace_bytes(300, 700, 2048) + 768 * 2048)
+        api.mxfp8_debug_force_path(17)             # one split: the 4-bit tile GEMM
+        assert api.mxfp8_linear_w4a8_workspace_bytes(300, 700, 2048) == api.mxfp8_linear_workspace_bytes(300, 700, 2048)
+    finally:
+        api.mxfp8_debug_force_path(prev)
     p = api.mxfp8_prepare_weight_fp4
     expect_no_device(p, P, P, 130, 256, 128, 8, P, P, None)       # valid (ldw = K/2), no device
     assert p(P, P, 130, 224, 112, 7, P, P, None) == -2       # K % 256

@@ -1,8 +1,8 @@
 """The W4A8 layer (MXFP4 weights x MXFP8 activations) on the GPU vs the
 oracle (oracle/mxfp4.py), with the GEMM tolerance of tests/gpu_util.py
 applied to the dequantized MXFP4 weight, plus exact one-hot pins on both
-paths (the 4-bit decode kernel for M <= 16, the widened-weight tile GEMM
-above)."""
+paths (the 4-bit decode kernel for M <= 16, the 4-bit tile GEMM above; the
+widened-weight split-K GEMM where the shape table splits K)."""
 
 import numpy as np
 import pytest
@@ -63,9 +63,72 @@ def test_decode_parity(M, N, K):
 
 @pytest.mark.parametrize("M,N,K", [(300, 640, 512), (129, 200, 1024), (128, 4096, 4096), (17, 130, 256)])
 def test_tile_path_parity(M, N, K):
-    """The weight widened to MXFP8 tiles (exact) for the tile GEMM: automatic
-    above M = 128, forced below (M = 128, N = 4096 also exercises split-K)."""
+    """The tile path (automatic above M = 128, forced below): the 4-bit tile
+    GEMM where the shape table takes one K split, else the weight widened to
+    MXFP8 tiles (exact) for the split-K GEMM."""
     run_and_check(M, N, K, seed=M + N, force_path=1 if M <= 128 else 0)
+
+
+@pytest.mark.parametrize("M,N,K,force", [
+    (300, 650, 2048, 17),     # 4-bit tile GEMM: 2 x 3 tiles, ragged last row and column tile
+    (300, 650, 2048, 18),     # the widened split-K route on the same shape
+    (520, 130, 256, 17),      # K = 256: one 128-K step pair per tile
+    (257, 300, 8448, 17),     # K > 8192, 66 steps
+])
+def test_w4_tile_forced_parity(M, N, K, force):
+    run_and_check(M, N, K, seed=M + 5 * N + K, force_path=force)
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 650, 2048), (520, 130, 256), (257, 300, 8448), (2048, 1536, 4096)])
+def test_w4_tile_vs_mxfp8_tile(M, N, K):
+    """The 4-bit tile GEMM (E2M1 weight operand) and the MXFP8 tile GEMM fed
+    the same weight values as E4M3 bytes, both with one K split.  The scaled
+    MFMA does not return the same bits for the two operand formats, so each
+    element may differ by the two kernels' error bounds together (each is
+    within its bound of the exact product, tests/gpu_util.py)."""
+    g = torch.Generator().manual_seed(M + N + K)
+    xc = synth.randn_bf16((M, K), 1.0, g)
+    x = xc.to(gpu_util.dev())
+    w = synth.randn_bf16((N, K), 0.02, g).to(torch.float64).numpy()
+    codes, ws = oracle.quantize_mxfp4(w)
+    w8 = torch.from_numpy(oracle.e2m1_decode(codes).astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8)
+    pw8 = api.prepare_weight(w8.to(gpu_util.dev()), torch.from_numpy(ws).to(gpu_util.dev()))
+    pw4 = prepare(codes, ws)
+    prev = api.mxfp8_debug_force_path(17)
+    try:
+        assert api.mxfp8_debug_plan(M, N, K) == (0, 1)
+        y8 = api.linear(x, pw8).double().cpu().numpy()
+        y4 = api.linear(x, pw4).double().cpu().numpy()
+    finally:
+        api.mxfp8_debug_force_path(prev)
+    bound = 2 * (2.0 ** -8 * np.maximum(np.abs(y8), np.abs(y4)) + tolerance4(xc.double().numpy(), codes, ws, K))
+    diff = np.abs(y8 - y4)
+    print("W4 vs MXFP8 tile", (M, N, K), {"identical": float(np.mean(diff == 0)),
+                                         "max_diff_over_bound": float((diff / bound).max())}, flush=True)
+    assert np.all(diff <= bound)
+
+
+def test_one_hot_weight_exact_w4_tile():
+    """W[n, perm[n]] = 1 on the 4-bit tile GEMM (M = 300: two M-tiles, the
+    second ragged): y[m, n] = bf16(deq(A)[m, perm[n]]) exactly; pins the
+    E2M1 weight fragment (nibble order, chunk of each lane group) and the
+    weight scale slots of the 4-bit step buffer."""
+    g = torch.Generator().manual_seed(71)
+    M, K, N = 300, 1024, 300
+    x = synth.scale_stress(synth.randn_bf16((M, K), 1.0, g), seed=12)
+    perm = torch.randint(0, K, (N,), generator=g).numpy()
+    w = np.zeros((N, K))
+    w[np.arange(N), perm] = 1.0
+    codes, ws = oracle.quantize_mxfp4(w)
+    pw = prepare(codes, ws)
+    prev = api.mxfp8_debug_force_path(17)
+    try:
+        y = api.linear(x.to(gpu_util.dev()), pw).float().cpu().numpy()
+    finally:
+        api.mxfp8_debug_force_path(prev)
+    qa, sa = oracle.quantize_mx(x.double().numpy())
+    exp = oracle.bf16_round(oracle.dequantize_mx(qa, sa)[:, perm])
+    assert np.array_equal(y, exp)
 
 
 @pytest.mark.parametrize("M,N,K", [(17, 130, 256), (40, 384, 768), (128, 4096, 4096), (100, 200, 8192), (5, 256, 512)])
@@ -102,8 +165,9 @@ def test_one_hot_weight_exact(M):
 
 def test_w4a8_matches_mxfp8_on_widened_weight():
     """The GPU W4A8 layer and the GPU MXFP8 layer fed the same weight (E2M1
-    values written as E4M3 bytes by torch's cast, same scales) agree
-    bit for bit on the tile path (the same GEMM after the exact widening)."""
+    values written as E4M3 bytes by torch's cast, same scales) agree bit for
+    bit on the split-K tile route (the same MXFP8 GEMM after the exact
+    widening of the 4-bit weight)."""
     g = torch.Generator().manual_seed(23)
     M, N, K = 64, 256, 1024
     x = synth.randn_bf16((M, K), 1.0, g).to(gpu_util.dev())
@@ -112,8 +176,9 @@ def test_w4a8_matches_mxfp8_on_widened_weight():
     w8 = torch.from_numpy(oracle.e2m1_decode(codes).astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8)
     pw8 = api.prepare_weight(w8.to(gpu_util.dev()), torch.from_numpy(ws).to(gpu_util.dev()))
     pw4 = prepare(codes, ws)
-    prev = api.mxfp8_debug_force_path(1)
+    prev = api.mxfp8_debug_force_path(18)
     try:
+        assert api.mxfp8_debug_plan(M, N, K) == (0, 2)
         y8 = api.linear(x, pw8)
         y4 = api.linear(x, pw4)
         torch.cuda.synchronize()
