@@ -249,9 +249,9 @@ int mxfp8_gemm_prequant(const void* q_e4m3, int64_t ldq, const void* s_e8m0, int
  *   w   = softmax over those topk logits (fp32),
  *   for each selected e: h = deq(q(x_t)) . deq(w13[e])^T   ([2I], fp32 acc),
  *                        a = bf16( silu(h[0:I]) * h[I:2I] ),  silu(z) = z/(1+e^-z),
- *                        o_e = bf16( deq(q(a)) . deq(w2[e])^T ) ([H], fp32 acc, one rounding),
+ *                        o_e = deq(q(a)) . deq(w2[e])^T        ([H], fp32 acc),
  *   y[t] = bf16( sum_j w_j * o_{e_j} ), the products and the sum in fp32 (slot
- *          order), rounded once (the finalize step).
+ *          order), rounded once.
  * q() is the MX quantization of mxfp8_quantize_act along the contraction
  * dimension (H for x, I for a).
  *

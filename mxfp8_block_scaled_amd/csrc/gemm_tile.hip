@@ -178,7 +178,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_persistent_w4_kernel(
       [&](tile::i4v r, uint8_t* slot) { tile::b2l_4((uint32_t)(wn * 256 + lane * 4), r, 0u, slot + wave * 256); },
       [&](int) {},
       [&](const v4f (&acc)[8][8], const tile::Job16& j, const uint8_t* slot) {
-        return tile::epi16(epi, slot + wave * 256, acc, y, ldy, j.row0, M, j.col0, N, vec_store);
+        return tile::epi16(epi, slot + wave * 256, acc, y, ldy, j.row0, M, j.col0, N, vec_store) ? 32 : 0;
       });
 }
 

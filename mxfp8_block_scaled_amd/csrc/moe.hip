@@ -12,7 +12,7 @@
 //              over those k;
 //   h        = deq(q(x_t)) . deq(W13[e])^T            for each selected e,
 //   act      = bf16( silu(h[:I]) * h[I:] ),  q(act) = MX quantization along I,
-//   o_j      = bf16( deq(q(act_j)) . deq(W2[e_j])^T )  (the expert's output row),
+//   o_j      = deq(q(act_j)) . deq(W2[e_j])^T  (fp32 accumulation),
 //   y_t      = bf16( sum_j w_j . o_j ), the products and the sum in fp32.
 //
 // Pipeline (one stream, every step deterministic):
@@ -35,11 +35,10 @@
 //              epilogue applies SiLU-gating, rounds to bf16, MX-quantizes
 //              along I and writes the packed operand of gemm2.
 //  6. gemm2    per (M-tile, 256-row slice of W2[e]): the tile loop; each
-//              real row rounded to bf16 and written to its slot row t*k + j
-//              (pad rows are not stored).
-//  7. combine  (the finalize) y_t = bf16( sum_j w_j * ys[t*k + j] ), the
-//              products and the sum in fp32 in slot order, one rounding; a
-//              token's k slot rows are contiguous.
+//              real row multiplied by its routing weight in fp32 and written
+//              as fp32 to its slot row t*k + j (pad rows: a spare row).
+//  7. combine  y_t = bf16( sum_j ys[t*k + j] ), the sum in fp32 in slot
+//              order, one rounding; a token's k slot rows are contiguous.
 #include <algorithm>
 #include <cfloat>
 #include <climits>
@@ -299,10 +298,12 @@ __global__ __launch_bounds__(1024) void moe_plan_kernel(const int* __restrict__ 
 }
 
 // ---------------------------------------------------------------- 3. scatter
-__global__ __launch_bounds__(256) void moe_scatter_kernel(const int* __restrict__ ids, int R, int topk, int E,
+__global__ __launch_bounds__(256) void moe_scatter_kernel(const int* __restrict__ ids, const float* __restrict__ wts,
+                                                          int R, int topk, int E,
                                                           const int* __restrict__ blk_off,
                                                           const int* __restrict__ seg_off,
-                                                          int* __restrict__ sorted_row) {
+                                                          int* __restrict__ sorted_row,
+                                                          float* __restrict__ sorted_wts) {
   __shared__ int wcnt[4][kMoeMaxExperts];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int i = tid; i < 4 * kMoeMaxExperts; i += 256) (&wcnt[0][0])[i] = 0;
@@ -327,6 +328,7 @@ __global__ __launch_bounds__(256) void moe_scatter_kernel(const int* __restrict_
     int pos = seg_off[e] + blk_off[(int64_t)blockIdx.x * E + e] + local;
     for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
     sorted_row[pos] = r;
+    sorted_wts[pos] = wts[r];
   }
 }
 
@@ -508,7 +510,7 @@ __global__ __launch_bounds__(tile::kThreads, 1) void moe_gemm1_kernel(
         }
       }
     }
-    return false;   // the number of stores depends on the rows
+    return 0;   // the number of stores depends on the rows
   };
   tile::persistent16_run<0, 0, true, false>(st0, st1, st2, st3, nullptr, total, KS, decode, make_src,
                                [](const Moe1Job&) { return tile::buffer_rsrc(nullptr, 0); },
@@ -517,12 +519,16 @@ __global__ __launch_bounds__(tile::kThreads, 1) void moe_gemm1_kernel(
 
 // ---------------------------------------------------------------- 6. gemm2
 // Persistent over the (M-tile, 256-row slice of W2[e]) list on the same
-// loop.  Side data of a tile: the sorted_row entries of its 256 rows (wave w
-// copies rows 64 w ..), so the epilogue finds each row's slot row t*k + j in
-// LDS.  Each row is rounded once to bf16 and stored to its slot row; pad rows
-// and rows past the tile's groups go to the spare row R, so every wave issues
-// exactly 32 stores per tile (ordinary stores: the combine reads the rows
-// right after).
+// loop.  Side data of a tile: the sorted_row entries of its 256 rows and
+// their routing weights (sorted_wts, p_max entries after sorted_row; wave w
+// copies rows 64 w ..), so the epilogue finds each row's slot row t*k + j
+// and weight in LDS.  Epilogue: each row's fp32 values times its fp32
+// weight, stored as fp32 straight from the accumulators (lane (i, g) holds 4
+// consecutive columns of a row per MFMA tile: one 16-byte store each, the
+// L2 merging a row's pieces; staging 16 x 64 fp32 blocks through LDS for
+// whole-row stores measured 1.5x slower); pad rows and rows past the tile's
+// groups go to the spare row R, so every wave issues exactly 64 stores per
+// tile.
 struct Moe2Job {
   const uint8_t *wga, *wgb, *xga, *xgb, *swa, *swb, *sxa, *sxb;
   const int* rows;      // sorted_row of the tile's first row
@@ -533,15 +539,13 @@ __global__ __launch_bounds__(tile::kThreads, 1) void moe_gemm2_kernel(
     const uint8_t* __restrict__ a2q, const uint8_t* __restrict__ a2s, const uint8_t* __restrict__ w2p,
     const uint8_t* __restrict__ s2p, const int* __restrict__ meta, const int* __restrict__ tile_e,
     const int* __restrict__ tile_g0, const int* __restrict__ tile_ng, const int* __restrict__ sorted_row,
-    int H, int I, int R, uint16_t* __restrict__ ys) {
+    int p_max, int H, int I, int R, float* __restrict__ ys) {
   __shared__ __attribute__((aligned(16))) uint8_t st0[tile::kStage];
   __shared__ __attribute__((aligned(16))) uint8_t st1[tile::kStage];
   __shared__ __attribute__((aligned(16))) uint8_t st2[tile::kStage];
   __shared__ __attribute__((aligned(16))) uint8_t st3[tile::kStage];
-  __shared__ __attribute__((aligned(16))) uint8_t epi[tile::kEpiBytes];
-  constexpr int kRowSlot = 256 * 4;
+  constexpr int kRowSlot = 2 * 256 * 4;           // 256 slot rows, then 256 weights
   __shared__ __attribute__((aligned(16))) uint8_t side[2 * kRowSlot];
-  typedef unsigned int u4v __attribute__((ext_vector_type(4)));
   const int NT = H / 256;
   const int total = meta[0] * NT;
   const int KS = I / kStepK;
@@ -574,66 +578,54 @@ __global__ __launch_bounds__(tile::kThreads, 1) void moe_gemm2_kernel(
   auto make_src = [&](const Moe2Job& j) {
     return tile::BufSrc(j.wga, j.wgb, j.xga, j.xgb, j.swa, j.swb, j.sxa, j.sxb, KS, KS);
   };
-  auto side_of = [&](const Moe2Job& j) { return tile::buffer_rsrc(j.rows, (uint32_t)(j.ng * kGroupRows * 4)); };
+  // One resource from the tile's first sorted row to the end of sorted_wts
+  // (2 p_max entries from sorted_row): rows g0 * 128 .. + 255 are in range
+  // (p_max holds a spare group), their weights p_max entries further.
+  auto side_of = [&](const Moe2Job& j) {
+    return tile::buffer_rsrc(j.rows, (uint32_t)((2 * (int64_t)p_max - (j.rows - sorted_row)) * 4));
+  };
   auto side_copy = [&](tile::i4v r, uint8_t* slot) {
     tile::b2l_4((uint32_t)((wave * 64 + lane) * 4), r, 0u, slot + wave * 256);
+    tile::b2l_4((uint32_t)((wave * 64 + lane) * 4), r, (uint32_t)p_max * 4u, slot + 1024 + wave * 256);
   };
-  // As tile::epi16: the wave's 128 x 128 block staged as bf16 16 rows at a
-  // time, read back as 8 consecutive columns per lane, one 16-byte store per
-  // (row, 8 columns); H % 256 == 0, so every column is in range.
   auto epilogue = [&](const v4f (&acc)[8][8], const Moe2Job& j, const uint8_t* slot) {
     const int* rmap = reinterpret_cast<const int*>(slot);
-    uint8_t* reg = epi + wave * tile::kEpiWaveBytes;
+    const float* wmap = reinterpret_cast<const float*>(slot + 1024);
     const int valid = j.ng * kGroupRows;
-    const int nw = j.col0 + wn * 128;
-    const int rr = lane >> 4, cc = (lane & 15) * 8;
+    float* colp = ys + j.col0 + wn * 128 + 4 * lg;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
+      const int ml = wm * 128 + 16 * k + li;
+      const int sr = rmap[ml];
+      const bool real = ml < valid && sr >= 0;
+      const float w = wmap[ml];
+      float* d = colp + (size_t)(real ? sr : R) * H;
 #pragma unroll
       for (int a = 0; a < 8; ++a) {
         const v4f v = acc[a][k];
-        const uint2 w = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-        *reinterpret_cast<uint2*>(reg + (li * tile::kEpiPitchH + 16 * a + 4 * lg) * 2) = w;
+        *reinterpret_cast<float4*>(d + 16 * a) = make_float4(w * v[0], w * v[1], w * v[2], w * v[3]);
       }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      u4v t[4];
-      int dst[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        t[r] = *reinterpret_cast<const u4v*>(reg + ((rr + 4 * r) * tile::kEpiPitchH + cc) * 2);
-        const int ml = wm * 128 + 16 * k + rr + 4 * r;
-        const int s = rmap[ml];
-        dst[r] = (ml < valid && s >= 0) ? s : R;
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        *reinterpret_cast<u4v*>(ys + (size_t)dst[r] * H + nw + cc) = t[r];
     }
-    return true;
+    return 64;
   };
-  tile::persistent16_run<1, kRowSlot, false, false>(st0, st1, st2, st3, side, total, KS, decode, make_src, side_of, side_copy,
-                                      [](int) {}, epilogue);
+  tile::persistent16_run<2, kRowSlot, false, false>(st0, st1, st2, st3, side, total, KS, decode, make_src, side_of,
+                                                    side_copy, [](int) {}, epilogue);
 }
 
 // ---------------------------------------------------------------- 7. combine
-__global__ __launch_bounds__(256) void moe_combine_kernel(const uint16_t* __restrict__ ys, const float* __restrict__ wts,
-                                                          int T, int H, int topk, uint16_t* __restrict__ y) {
-  const int64_t t8 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+__global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ ys, int T, int H, int topk,
+                                                          uint16_t* __restrict__ y) {
+  const int64_t t4 = (int64_t)blockIdx.x * 256 + threadIdx.x;   // one thread per 8 columns of a token
   const int per_row = H / 8;
-  if (t8 >= (int64_t)T * per_row) return;
-  const int64_t t = t8 / per_row;
-  const int c = (int)(t8 - t * per_row);
+  if (t4 >= (int64_t)T * per_row) return;
+  const int64_t t = t4 / per_row;
+  const int c = (int)(t4 - t * per_row);
   float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < topk; ++j) {
-    const float w = wts[t * topk + j];
-    const uint4 r = *reinterpret_cast<const uint4*>(ys + (t * topk + j) * H + c * 8);
-    const uint32_t rv[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      s[2 * e] += w * bf16_lo(rv[e]);
-      s[2 * e + 1] += w * bf16_hi(rv[e]);
-    }
+    const float* r = ys + (t * topk + j) * H + c * 8;
+    const float4 a = *reinterpret_cast<const float4*>(r), b = *reinterpret_cast<const float4*>(r + 4);
+    s[0] += a.x; s[1] += a.y; s[2] += a.z; s[3] += a.w;
+    s[4] += b.x; s[5] += b.y; s[6] += b.z; s[7] += b.w;
   }
   *reinterpret_cast<uint4*>(y + t * H + c * 8) = make_uint4(pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]),
                                                             pack_bf16x2(s[4], s[5]), pack_bf16x2(s[6], s[7]));
@@ -652,8 +644,9 @@ int launch_moe(const MoeArgs& a, hipStream_t stream) {
   }
   hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(1024), 0, stream, a.ws.blk_cnt, nblk, (int)a.E, a.ws.blk_off,
                      a.ws.seg_off, a.ws.tile_e, a.ws.tile_g0, a.ws.tile_ng, a.ws.meta);
-  hipLaunchKernelGGL(moe_scatter_kernel, dim3(nblk), dim3(256), 0, stream, a.ws.ids, R, (int)a.topk, (int)a.E,
-                     a.ws.blk_off, a.ws.seg_off, a.ws.sorted_row);
+  hipLaunchKernelGGL(moe_scatter_kernel, dim3(nblk), dim3(256), 0, stream, a.ws.ids, a.ws.wts, R, (int)a.topk,
+                     (int)a.E, a.ws.blk_off, a.ws.seg_off, a.ws.sorted_row,
+                     reinterpret_cast<float*>(a.ws.sorted_row + a.ws.p_max));
   const int KS1 = (int)(a.H / kStepK);
   hipLaunchKernelGGL(moe_gather_scales_kernel, dim3((unsigned)(a.ws.p_max / kGroupRows * KS1 / 4)), dim3(256), 0,
                      stream, a.ws.xs, (int)a.H, (int)a.topk, a.ws.sorted_row, a.ws.meta, KS1, a.ws.a1s,
@@ -672,10 +665,10 @@ int launch_moe(const MoeArgs& a, hipStream_t stream) {
                      (uint16_t*)a.dbg_act, (uint8_t*)a.dbg_q, (uint8_t*)a.dbg_s);
   hipLaunchKernelGGL(moe_gemm2_kernel, dim3(g2), dim3(tile::kThreads), 0, stream, a.ws.a2q, a.ws.a2s,
                      (const uint8_t*)a.w2p, (const uint8_t*)a.s2p, a.ws.meta, a.ws.tile_e, a.ws.tile_g0,
-                     a.ws.tile_ng, a.ws.sorted_row, (int)a.H, (int)a.I, R, a.ws.ys);
+                     a.ws.tile_ng, a.ws.sorted_row, (int)a.ws.p_max, (int)a.H, (int)a.I, R, a.ws.ys);
   const int64_t cb_total = a.T * (a.H / 8);
   hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((cb_total + 255) / 256)), dim3(256), 0, stream, a.ws.ys,
-                     a.ws.wts, (int)a.T, (int)a.H, (int)a.topk, (uint16_t*)a.y);
+                     (int)a.T, (int)a.H, (int)a.topk, (uint16_t*)a.y);
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 

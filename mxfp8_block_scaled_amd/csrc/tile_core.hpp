@@ -964,9 +964,9 @@ __device__ __forceinline__ bool epi16(uint8_t* epi, const uint8_t* bias_slot, co
 //    slot) together with the tile's second step into one of two slots of
 //    kSideSlot bytes at side_lds (e.g. the tile's bias).  The epilogue of the
 //    tile finds it there: epilogue(acc, job, slot) stores the tile and returns
-//    true when the wave issued exactly 32 vector memory operations in it (the
-//    next tile's first wait then lets them stay in flight), false for any
-//    other number.
+//    the number of vector memory operations the wave issued in it when that
+//    is exactly 32 or 64 (the next tile's first wait then lets them stay in
+//    flight), else 0.
 //  * tile_start(b_next) runs at the start of each tile with the index of the
 //    workgroup's next tile (may be >= total); vector memory operations it
 //    issues are complete by the tile's first barrier after its first wait.
@@ -1055,9 +1055,10 @@ __device__ __forceinline__ void persistent16_run(uint8_t* st0, uint8_t* st1, uin
   // (kRtIssue) when the runtime flag rt_issue is set: weights and scales
   // after column 1, activations after column 6, and with with_side also the
   // side data of sr's tile into slot bbuf.  The wait before column 6 needs the
-  // next step's copies: besides the ten weight copies issued in this step (if
+  // next step's copies: besides the weight copies issued in this step (if
   // any), vm_extra stores of the previous epilogue may still be in flight
-  // after them (32, or 0 when unknown).  The next step's fragments are always
+  // after them (32 or 64, or 0 when unknown; with 64 the wait allows 63, the
+  // counter's limit: the step's copies are older than all of them).  The next step's fragments are always
   // read (after the last tile they are stale and unused).
   auto step = [&](auto kIssue, auto kRtIssue, auto with_side, auto kVm, auto kNext, bool rt_issue, uint8_t* ev, uint8_t* od,
                   const uint8_t* nev, const uint8_t* nod, const Src& sr, int q, int vm_extra, i4v brs, int bbuf) {
@@ -1075,11 +1076,15 @@ __device__ __forceinline__ void persistent16_run(uint8_t* st0, uint8_t* st1, uin
       if constexpr (j == 48) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         const bool extra = decltype(kVm)::value && vm_extra == 32;
+        const bool extra64 = decltype(kVm)::value && vm_extra == 64;
         if constexpr (kI) {
-          if (extra) wait_vmcnt<kWCopies + 32>();
+          if (extra64) wait_vmcnt<63>();
+          else if (extra) wait_vmcnt<kWCopies + 32>();
           else wait_vmcnt<kWCopies>();
         } else {
-          if (issue) {
+          if (extra64) {
+            wait_vmcnt<63>();
+          } else if (issue) {
             if (extra) wait_vmcnt<kWCopies + 32>();
             else wait_vmcnt<kWCopies>();
           } else {
@@ -1185,10 +1190,10 @@ __device__ __forceinline__ void persistent16_run(uint8_t* st0, uint8_t* st1, uin
          st2, st3, st0, st1, nsrc, 1, 0, side_of(nxt), buf ^ 1);
     // The last MFMAs must retire before the epilogue reads the accumulators.
     asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
-    const bool full = epilogue(acc, cur, side_lds + buf * kSideSlot);
+    const int nvm = (int)epilogue(acc, cur, side_lds + buf * kSideSlot);
     if (!has_next) break;
     if constexpr (!kCarry) read_first(st0, st1);
-    vm_extra = full ? 32 : 0;
+    vm_extra = (nvm == 32 || nvm == 64) ? nvm : 0;
     src = nsrc;
     cur = nxt;
     b = nb;
@@ -1215,7 +1220,7 @@ __device__ __forceinline__ void persistent16(uint8_t* st0, uint8_t* st1, uint8_t
       [&](i4v r, uint8_t* slot) { b2l_4((uint32_t)(wn * 256 + lane * 4), r, 0u, slot + wave * 256); },
       [&](int) {},
       [&](const v4f (&acc)[8][8], const Job16& j, const uint8_t* slot) {
-        return epi16(epi, slot + wave * 256, acc, y, ldy, j.row0, M, j.col0, N, vec_store);
+        return epi16(epi, slot + wave * 256, acc, y, ldy, j.row0, M, j.col0, N, vec_store) ? 32 : 0;
       });
 }
 

@@ -17,12 +17,8 @@ What is computed, and where it is defined
 * Readings (each listed in the design doc): rows ``[0, I)`` of w13 are the gate and
   rows ``[I, 2I)`` the up projection; ``act = silu(gate) * up`` with
   ``silu(z) = z / (1 + exp(-z))``; the gated activation is rounded to bf16
-  before it is MX-quantized along I; each routed row's down-projection
-  output is a bf16 row (the activation dtype, as the runner's unfinalized
-  output -- the ``do_finalize`` option in flashinfer PR #4026's follow-up
-  list -- and the dense layer's GEMM produce), and the finalize multiplies
-  each by its routing weight and sums the k rows; the combined output is
-  what the caller rounds to bf16.
+  before it is MX-quantized along I; the combined output is what the caller
+  rounds to bf16.
 """
 
 import numpy as np
@@ -84,7 +80,7 @@ def moe_ref(x, logits, w13_q, w13_s, w2_q, w2_s, topk, act_override=None,
         act[rows] = a
         qa, sa = quantize_mx(a)
         w2 = dequantize_mx(w2_q[e], w2_s[e])
-        ye = bf16_round(dequantize_mx(qa, sa) @ w2.T)
+        ye = dequantize_mx(qa, sa) @ w2.T
         y[tok] += wts[tok, slot][:, None] * ye
     if return_act:
         return y, act, ids, wts

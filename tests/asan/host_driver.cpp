@@ -135,13 +135,13 @@ int launch_moe(const MoeArgs& a, hipStream_t) {
   touch(w.tile_e, w.mt_max * 4);
   touch(w.tile_g0, w.mt_max * 4);
   touch(w.tile_ng, w.mt_max * 4);
-  touch(w.sorted_row, w.p_max * 4);
+  touch(w.sorted_row, 2 * w.p_max * 4);
   touch(w.xq, (a.T + 1) * a.H);
   touch(w.xs, (a.T + 1) * (a.H / 32));
   touch(w.a1s, w.p_max * (a.H / 32));
   touch(w.a2q, w.p_max * a.I);
   touch(w.a2s, w.p_max * (a.I / 32));
-  touch(w.ys, (R + 1) * a.H * 2);
+  touch(w.ys, (R + 1) * a.H * 4);
   touch(a.y, a.T * a.H * 2);
   return 0;
 }

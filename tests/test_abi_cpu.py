@@ -266,9 +266,9 @@ def test_moe_sizes():
     T, k = 4096, 8
     ws = api.mxfp8_moe_workspace_bytes(T, H, I, E, k)
     # at least the tokens quantized once, the expert-sorted scales and operand of
-    # the down projection, and the bf16 expert output rows
+    # the down projection, and the fp32 routing-weighted expert output rows
     rows = T * k
-    assert ws >= T * (H + H // 32) + rows * (H // 32 + I + I // 32 + 2 * H)
+    assert ws >= T * (H + H // 32) + rows * (H // 32 + I + I // 32 + 4 * H)
     assert api.mxfp8_moe_workspace_bytes(0, H, I, E, k) > 0
     with pytest.raises(api.MXFP8Error):
         api.mxfp8_moe_workspace_bytes(T, H, I, E, 17)  # top-k above 16

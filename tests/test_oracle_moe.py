@@ -41,7 +41,7 @@ def _dense_moe_via_linear(x, logits, w13q, w13s, w2q, w2s, topk):
             h = oracle.linear_ref(x[t:t + 1], w13q[e], w13s[e])[0]
             gate, up = h[:inter], h[inter:]
             a = oracle.bf16_round(torch.nn.functional.silu(torch.from_numpy(gate)).numpy() * up)
-            y[t] += wts[t, j] * oracle.bf16_round(oracle.linear_ref(a[None, :], w2q[e], w2s[e])[0])
+            y[t] += wts[t, j] * oracle.linear_ref(a[None, :], w2q[e], w2s[e])[0]
     return y
 
 
