@@ -171,14 +171,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_persistent_w4_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wave >> 1;
-  tile::persistent16_run<1, tile::kBiasSlot, true, true>(
+  tile::persistent16_run<1, tile::kBiasSlot, true, true, true>(
       buf0, buf0 + tile::kOpBytes, buf1, buf1 + tile::kOpBytes, blds, total, KS, decode,
       [&](const tile::Job16& j) { return tile::W4Src(j.wga, j.wgb, j.xga, j.xgb, j.swa, j.swb, j.sxa, j.sxb, KS); },
       [&](const tile::Job16& j) { return tile::bias_rsrc(bias, j.col0, N); },
       [&](tile::i4v r, uint8_t* slot) { tile::b2l_4((uint32_t)(wn * 256 + lane * 4), r, 0u, slot + wave * 256); },
-      [&](int) {},
-      [&](const v4f (&acc)[8][8], const tile::Job16& j, const uint8_t* slot) {
-        return tile::epi16(epi, slot + wave * 256, acc, y, ldy, j.row0, M, j.col0, N, vec_store) ? 32 : 0;
+      [&](int) {}, [&](v4f (&acc)[8][8], const uint8_t* slot) { tile::bias_init16(acc, slot + wave * 256); },
+      [&](const v4f (&acc)[8][8], const tile::Job16& j, const uint8_t*) {
+        return tile::epi16(epi, acc, y, ldy, j.row0, M, j.col0, N, vec_store) ? 32 : 0;
       });
 }
 

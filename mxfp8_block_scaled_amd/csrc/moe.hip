@@ -512,9 +512,10 @@ __global__ __launch_bounds__(tile::kThreads, 1) void moe_gemm1_kernel(
     }
     return 0;   // the number of stores depends on the rows
   };
-  tile::persistent16_run<0, 0, true, false>(st0, st1, st2, st3, nullptr, total, KS, decode, make_src,
-                               [](const Moe1Job&) { return tile::buffer_rsrc(nullptr, 0); },
-                               [](tile::i4v, uint8_t*) {}, tile_start, epilogue);
+  tile::persistent16_run<0, 0, true, false, false>(st0, st1, st2, st3, nullptr, total, KS, decode, make_src,
+                                                   [](const Moe1Job&) { return tile::buffer_rsrc(nullptr, 0); },
+                                                   [](tile::i4v, uint8_t*) {}, tile_start,
+                                                   [](v4f (&)[8][8], const uint8_t*) {}, epilogue);
 }
 
 // ---------------------------------------------------------------- 6. gemm2
@@ -608,8 +609,9 @@ __global__ __launch_bounds__(tile::kThreads, 1) void moe_gemm2_kernel(
     }
     return 64;
   };
-  tile::persistent16_run<2, kRowSlot, false, false>(st0, st1, st2, st3, side, total, KS, decode, make_src, side_of,
-                                                    side_copy, [](int) {}, epilogue);
+  tile::persistent16_run<2, kRowSlot, false, false, false>(st0, st1, st2, st3, side, total, KS, decode, make_src,
+                                                           side_of, side_copy, [](int) {},
+                                                           [](v4f (&)[8][8], const uint8_t*) {}, epilogue);
 }
 
 // ---------------------------------------------------------------- 7. combine

@@ -900,26 +900,38 @@ __device__ inline i4v bias_rsrc(const uint16_t* bias, int col0, int N) {
   return buffer_rsrc(reinterpret_cast<const uint8_t*>(bias) + 2 * (size_t)col0, (uint32_t)valid * 2);
 }
 
-// Epilogue of one tile of the persistent loop: y = bf16(acc + bias) for rows
-// < row_end and columns < N.  Wave (wn, wm) stages its 128 x 128 block 16
-// rows at a time as bf16 in its own kEpiWaveBytes region (lane (i, g) writes
-// columns 16a + 4g .. +3 of row i for a = 0..7), reads each pass back as 8
+// The accumulators of a tile start at its bias (fp32, exact from bf16), so
+// that the MFMAs add the products to it and the epilogue only rounds: this
+// wave's 128 bias values are at bias_slot (zeros past N or without a bias);
+// acc[a][k][e] is column 16 a + 4 lg + e of the wave's 128.
+__device__ __forceinline__ void bias_init16(v4f (&acc)[8][8], const uint8_t* bias_slot) {
+  const int lg = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int a = 0; a < 8; ++a) {
+    const uint2 w = *reinterpret_cast<const uint2*>(bias_slot + (16 * a + 4 * lg) * 2);
+    const v4f v = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[a][k] = v;
+  }
+}
+
+// Epilogue of one tile of the persistent loop: y = bf16(acc) for rows
+// < row_end and columns < N, the accumulators having started at the bias
+// (bias_init16).  Wave (wn, wm) stages its 128 x 128 block 16 rows at a time
+// as bf16 in its own kEpiWaveBytes region (lane (i, g) writes columns
+// 16a + 4g .. +3 of row i for a = 0..7), reads each pass back as 8
 // consecutive columns per lane (4 rows per read) and writes 16-byte
-// non-temporal stores covering whole 256-byte row segments.  bias_slot: the
-// wave's 256-byte bias slice (columns wn * 128 ..).  Returns true when the
-// wave issued exactly 32 stores (block fully in range, vec_store == 2).
-__device__ __forceinline__ bool epi16(uint8_t* epi, const uint8_t* bias_slot, const v4f (&acc)[8][8],
-                                      uint16_t* __restrict__ y, int64_t ldy, int row0, int row_end, int col0,
-                                      int N, int vec_store) {
+// non-temporal stores covering whole 256-byte row segments.  Returns true
+// when the wave issued exactly 32 stores (block fully in range,
+// vec_store == 2).
+__device__ __forceinline__ bool epi16(uint8_t* epi, const v4f (&acc)[8][8], uint16_t* __restrict__ y, int64_t ldy,
+                                      int row0, int row_end, int col0, int N, int vec_store) {
   typedef unsigned int u4v __attribute__((ext_vector_type(4)));
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wave >> 1, wm = wave & 1;
   const int li = lane & 15, lg = lane >> 4;
   uint8_t* reg = epi + wave * kEpiWaveBytes;
-  uint2 bw[8];
-#pragma unroll
-  for (int a = 0; a < 8; ++a) bw[a] = *reinterpret_cast<const uint2*>(bias_slot + (16 * a + 4 * lg) * 2);
   const int nw = col0 + wn * 128, mw = row0 + wm * 128;
   const bool full = vec_store == 2 && mw + 128 <= row_end && nw + 128 <= N;
   const int rr = lane >> 4, cc = (lane & 15) * 8;
@@ -928,8 +940,7 @@ __device__ __forceinline__ bool epi16(uint8_t* epi, const uint8_t* bias_slot, co
 #pragma unroll
     for (int a = 0; a < 8; ++a) {
       const v4f v = acc[a][k];
-      const uint2 w = make_uint2(pack_bf16x2(v[0] + bf16_lo(bw[a].x), v[1] + bf16_hi(bw[a].x)),
-                                 pack_bf16x2(v[2] + bf16_lo(bw[a].y), v[3] + bf16_hi(bw[a].y)));
+      const uint2 w = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
       *reinterpret_cast<uint2*>(reg + (li * kEpiPitchH + 16 * a + 4 * lg) * 2) = w;
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -970,6 +981,9 @@ __device__ __forceinline__ bool epi16(uint8_t* epi, const uint8_t* bias_slot, co
 //  * tile_start(b_next) runs at the start of each tile with the index of the
 //    workgroup's next tile (may be >= total); vector memory operations it
 //    issues are complete by the tile's first barrier after its first wait.
+//  * kAccInit: acc_init(acc, slot) sets the tile's accumulators from its side
+//    data (this wave's own copies, complete when it runs); otherwise they
+//    start at zero.
 //  * kCarry: the last step of a tile reads the next tile's first fragments
 //    (held in registers through the epilogue); otherwise they are read from
 //    LDS after the epilogue (their stage pair is not refilled before the
@@ -982,12 +996,12 @@ __device__ __forceinline__ bool epi16(uint8_t* epi, const uint8_t* bias_slot, co
 //    copies per step instead of ten.
 // total: tiles of the list; gridDim.x % 8 == 0 keeps every workgroup's tiles
 // on one XCD under xcd_remap.
-template <int kSide, int kSideSlot, bool kCarry, bool kW4, typename Decode, typename MakeSrc, typename SideOf,
-          typename SideCopy, typename TileStart, typename Epilogue>
+template <int kSide, int kSideSlot, bool kCarry, bool kW4, bool kAccInit, typename Decode, typename MakeSrc,
+          typename SideOf, typename SideCopy, typename TileStart, typename AccInit, typename Epilogue>
 __device__ __forceinline__ void persistent16_run(uint8_t* st0, uint8_t* st1, uint8_t* st2, uint8_t* st3,
                                                  uint8_t* side_lds, int total, int KS, Decode decode,
                                                  MakeSrc make_src, SideOf side_of, SideCopy side_copy,
-                                                 TileStart tile_start, Epilogue epilogue) {
+                                                 TileStart tile_start, AccInit acc_init, Epilogue epilogue) {
   static_assert(kSide >= 0 && kSide <= 4, "side copies per wave");
   int b = blockIdx.x;
   if (b >= total) return;
@@ -1158,10 +1172,19 @@ __device__ __forceinline__ void persistent16_run(uint8_t* st0, uint8_t* st1, uin
   int vm_extra = 0, buf = 0;
   for (;;) {
     tile_start(b + (int)gridDim.x);
+    if constexpr (kAccInit) {
+      // The tile's side data is older than the previous epilogue's stores
+      // (none before the first tile).
+      if (vm_extra == 64) wait_vmcnt<63>();
+      else if (vm_extra == 32) wait_vmcnt<32>();
+      else wait_vmcnt<0>();
+      acc_init(acc, side_lds + buf * kSideSlot);
+    } else {
 #pragma unroll
-    for (int a = 0; a < 8; ++a)
+      for (int a = 0; a < 8; ++a)
 #pragma unroll
-      for (int c = 0; c < 8; ++c) acc[a][c] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int c = 0; c < 8; ++c) acc[a][c] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    }
     int p = 0;
     if (P >= 4) {
       // The first step alone may find the previous epilogue's stores in
@@ -1213,14 +1236,14 @@ __device__ __forceinline__ void persistent16(uint8_t* st0, uint8_t* st1, uint8_t
   const int wn = wave >> 1;
   // Side data: the tile's 256 bias values; wave w copies the 128 of its
   // columns (wn * 128 ..) into its own 256 bytes of the slot.
-  persistent16_run<1, kBiasSlot, true, false>(
+  persistent16_run<1, kBiasSlot, true, false, true>(
       st0, st1, st2, st3, bias_lds, total, KS, [&](int bidx, bool) { return decode(bidx); },
       [&](const Job16& j) { return BufSrc(j.wga, j.wgb, j.xga, j.xgb, j.swa, j.swb, j.sxa, j.sxb, KS, KS); },
       [&](const Job16& j) { return bias_rsrc(bias, j.col0, N); },
       [&](i4v r, uint8_t* slot) { b2l_4((uint32_t)(wn * 256 + lane * 4), r, 0u, slot + wave * 256); },
-      [&](int) {},
-      [&](const v4f (&acc)[8][8], const Job16& j, const uint8_t* slot) {
-        return epi16(epi, slot + wave * 256, acc, y, ldy, j.row0, M, j.col0, N, vec_store) ? 32 : 0;
+      [&](int) {}, [&](v4f (&acc)[8][8], const uint8_t* slot) { bias_init16(acc, slot + wave * 256); },
+      [&](const v4f (&acc)[8][8], const Job16& j, const uint8_t*) {
+        return epi16(epi, acc, y, ldy, j.row0, M, j.col0, N, vec_store) ? 32 : 0;
       });
 }
 
