@@ -483,8 +483,16 @@ __global__ __launch_bounds__(tile::kThreads, 1) void moe_gemm1_kernel(
 #pragma unroll
         for (int p = 0; p < 4; ++p) mp = absmax_pk(mp, w[p]);
         uint32_t m = max((uint32_t)mp[0], (uint32_t)mp[1]);
-        m = max(m, (uint32_t)__shfl_xor((int)m, 16));
-        m = max(m, (uint32_t)__shfl_xor((int)m, 32));
+        // Maximum over the four lanes li + 16 g' (rows of 16 lanes): the
+        // gfx950 row swaps with both operands m give the exchanges with the
+        // lanes 16 and 32 apart as VALU operations (no LDS permute, whose
+        // queue the next tile's copies fill at this point).
+        {
+          const auto s16 = __builtin_amdgcn_permlane16_swap(m, m, false, false);
+          m = max((uint32_t)s16[0], (uint32_t)s16[1]);
+          const auto s32 = __builtin_amdgcn_permlane32_swap(m, m, false, false);
+          m = max((uint32_t)s32[0], (uint32_t)s32[1]);
+        }
         const uint32_t sb = (uint32_t)max((int)(m >> 7) - 8, 0);
         uint32_t q[2];
         cvt8s(w, mx_scale_value(sb), q);
