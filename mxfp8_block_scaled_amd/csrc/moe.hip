@@ -42,6 +42,7 @@
 #include <algorithm>
 #include <cfloat>
 #include <climits>
+#include <type_traits>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -115,14 +116,37 @@ __global__ __launch_bounds__(1024) void moe_route_kernel(const float* __restrict
           bv = v[c];
           bi = lane + 64 * c;
         }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int oi = __shfl_xor(bi, off);
+      // The best (value, index) of the wave: quads (DPP lane exchanges),
+      // then 8- and 16-lane rows (mirrors), then rows and halves (gfx950 row
+      // swaps); all VALU.  The order is a strict total order, so the result
+      // is the same for any reduction tree.
+      auto take = [&](float ov, int oi) {
         if (route_better(ov, oi, bv, bi)) {
           bv = ov;
           bi = oi;
         }
+      };
+      auto dpp = [&](auto ctrl) {
+        constexpr int c = decltype(ctrl)::value;
+        const int ovb = __builtin_amdgcn_update_dpp(0, __float_as_int(bv), c, 0xF, 0xF, true);
+        const int oi = __builtin_amdgcn_update_dpp(0, bi, c, 0xF, 0xF, true);
+        take(__int_as_float(ovb), oi);
+      };
+      dpp(std::integral_constant<int, 0xB1>{});    // quad_perm [1, 0, 3, 2]
+      dpp(std::integral_constant<int, 0x4E>{});    // quad_perm [2, 3, 0, 1]
+      dpp(std::integral_constant<int, 0x141>{});   // row_half_mirror
+      dpp(std::integral_constant<int, 0x140>{});   // row_mirror
+      {
+        const auto sv = __builtin_amdgcn_permlane16_swap(__float_as_uint(bv), __float_as_uint(bv), false, false);
+        const auto si = __builtin_amdgcn_permlane16_swap((uint32_t)bi, (uint32_t)bi, false, false);
+        take(__uint_as_float(sv[0]), (int)si[0]);
+        take(__uint_as_float(sv[1]), (int)si[1]);
+      }
+      {
+        const auto sv = __builtin_amdgcn_permlane32_swap(__float_as_uint(bv), __float_as_uint(bv), false, false);
+        const auto si = __builtin_amdgcn_permlane32_swap((uint32_t)bi, (uint32_t)bi, false, false);
+        take(__uint_as_float(sv[0]), (int)si[0]);
+        take(__uint_as_float(sv[1]), (int)si[1]);
       }
 #pragma unroll
       for (int c = 0; c < 4; ++c)
