@@ -203,6 +203,13 @@ __device__ inline void cvt8s(const uint32_t* w, float scale, uint32_t* q) {
 
 // Running maximum of bf16 magnitudes, two lanes of 16 bits (v_pk_max_u16 on
 // the sign-cleared words; integer order = magnitude order for finite bf16).
+// Maximum of m over the four lanes of a quad (lanes 4q .. 4q + 3): two DPP
+// quad_perm exchanges ([1, 0, 3, 2], then [2, 3, 0, 1]), VALU only.
+__device__ inline uint32_t quad_max(uint32_t m) {
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, true));
+  return max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, true));
+}
+
 __device__ inline u16x2 absmax_pk(u16x2 acc, uint32_t w) {
   return __builtin_elementwise_max(acc, __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu));
 }

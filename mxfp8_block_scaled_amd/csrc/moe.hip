@@ -187,8 +187,7 @@ __global__ __launch_bounds__(1024) void moe_route_kernel(const float* __restrict
 #pragma unroll
         for (int i = 0; i < 4; ++i) mp = absmax_pk(mp, w[i]);
         uint32_t m = max((uint32_t)mp[0], (uint32_t)mp[1]);
-        m = max(m, (uint32_t)__shfl_xor((int)m, 1));
-        m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+        m = quad_max(m);
         const uint32_t sb = (uint32_t)max((int)(m >> 7) - 8, 0);
         uint32_t qd[2];
         cvt8s(w, mx_scale_value(sb), qd);

@@ -48,8 +48,7 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
 #pragma unroll
     for (int i = 0; i < 4; ++i) mp = absmax_pk(mp, w[i]);
     uint32_t m = max((uint32_t)mp[0], (uint32_t)mp[1]);
-    m = max(m, (uint32_t)__shfl_xor((int)m, 1));
-    m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+    m = quad_max(m);
     const uint32_t sb = (uint32_t)max((int)(m >> 7) - 8, 0);
     uint32_t qd[2];
     cvt8s(w, mx_scale_value(sb), qd);
@@ -97,8 +96,7 @@ __global__ __launch_bounds__(256) void quant_act_packed_kernel(const uint16_t* _
 #pragma unroll
     for (int i = 0; i < 4; ++i) mp = absmax_pk(mp, v4[i]);
     uint32_t m = max((uint32_t)mp[0], (uint32_t)mp[1]);
-    m = max(m, (uint32_t)__shfl_xor((int)m, 1));
-    m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+    m = quad_max(m);
     const uint32_t sb = (uint32_t)max((int)(m >> 7) - 8, 0);
     uint32_t qd[2];
     cvt8s(v4, mx_scale_value(sb), qd);
@@ -134,8 +132,7 @@ __global__ __launch_bounds__(256) void quant_fp4_kernel(const uint16_t* __restri
 #pragma unroll
   for (int i = 0; i < 4; ++i) mp = absmax_pk(mp, w[i]);
   uint32_t m = max((uint32_t)mp[0], (uint32_t)mp[1]);
-  m = max(m, (uint32_t)__shfl_xor((int)m, 1));
-  m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+  m = quad_max(m);
   const uint32_t sb = (uint32_t)max((int)(m >> 7) - 2, 0);    // E2M1 emax = 2
   const float scale = mx_scale_value(sb);
   uint32_t d = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, __builtin_bit_cast(bf16x2, w[0]), scale, 0);
