@@ -105,7 +105,7 @@ size_t moe_layout(int64_t T, int64_t H, int64_t E, int64_t topk, int64_t I, uint
   v.tile_e = (int*)take(mt_max * 4);
   v.tile_g0 = (int*)take(mt_max * 4);
   v.tile_ng = (int*)take(mt_max * 4);
-  v.sorted_row = (int*)take(2 * p_max * 4);        // slot rows, then their routing weights
+  v.sorted_row = (int*)take(p_max * 4);
   v.xq = take((T + 1) * H);
   v.xs = take((T + 1) * (H / 32));
   v.a1s = take(p_max * (H / 32));

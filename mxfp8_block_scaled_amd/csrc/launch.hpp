@@ -115,13 +115,13 @@ struct MoeWorkspace {
   int* tile_e;       // [mt_max] expert of each M-tile
   int* tile_g0;      // [mt_max] its first 128-row group
   int* tile_ng;      // [mt_max] its groups (1 or 2)
-  int* sorted_row;   // [p_max] row t*k + j at each sorted position, -1 = pad; then [p_max] its routing weight (fp32)
+  int* sorted_row;   // [p_max] row t*k + j at each sorted position, -1 = pad
   uint8_t* xq;       // MXFP8 token rows, row-major [T + 1, H] (row T all zero)
   uint8_t* xs;       // their scales [T + 1, H / 32]
   uint8_t* a1s;      // packed scales of the expert-sorted token rows [p_max, H / 32]
   uint8_t* a2q;      // packed MXFP8 gated activations [p_max, I]
   uint8_t* a2s;
-  float* ys;         // routing-weighted expert output rows, fp32 [T*k + 1, H], row t*k + j (row T*k: spare)
+  float* ys;         // expert output rows, fp32 [T*k + 1, H], row t*k + j (row T*k: spare)
   int64_t p_max;     // sorted positions (multiple of 128, one spare group)
   int64_t mt_max;    // upper bound of M-tiles
 };

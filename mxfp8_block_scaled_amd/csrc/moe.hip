@@ -35,10 +35,11 @@
 //              epilogue applies SiLU-gating, rounds to bf16, MX-quantizes
 //              along I and writes the packed operand of gemm2.
 //  6. gemm2    per (M-tile, 256-row slice of W2[e]): the tile loop; each
-//              real row multiplied by its routing weight in fp32 and written
-//              as fp32 to its slot row t*k + j (pad rows: a spare row).
-//  7. combine  y_t = bf16( sum_j ys[t*k + j] ), the sum in fp32 in slot
-//              order, one rounding; a token's k slot rows are contiguous.
+//              real row's fp32 accumulators written to its slot row t*k + j
+//              (pad rows: a spare row).
+//  7. combine  y_t = bf16( sum_j w_j * ys[t*k + j] ), each product rounded to
+//              fp32, the sum in fp32 in slot order, one rounding; a token's
+//              k slot rows are contiguous.
 #include <algorithm>
 #include <cfloat>
 #include <climits>
@@ -321,12 +322,10 @@ __global__ __launch_bounds__(1024) void moe_plan_kernel(const int* __restrict__ 
 }
 
 // ---------------------------------------------------------------- 3. scatter
-__global__ __launch_bounds__(256) void moe_scatter_kernel(const int* __restrict__ ids, const float* __restrict__ wts,
-                                                          int R, int topk, int E,
+__global__ __launch_bounds__(256) void moe_scatter_kernel(const int* __restrict__ ids, int R, int topk, int E,
                                                           const int* __restrict__ blk_off,
                                                           const int* __restrict__ seg_off,
-                                                          int* __restrict__ sorted_row,
-                                                          float* __restrict__ sorted_wts) {
+                                                          int* __restrict__ sorted_row) {
   __shared__ int wcnt[4][kMoeMaxExperts];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int i = tid; i < 4 * kMoeMaxExperts; i += 256) (&wcnt[0][0])[i] = 0;
@@ -351,7 +350,6 @@ __global__ __launch_bounds__(256) void moe_scatter_kernel(const int* __restrict_
     int pos = seg_off[e] + blk_off[(int64_t)blockIdx.x * E + e] + local;
     for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
     sorted_row[pos] = r;
-    sorted_wts[pos] = wts[r];
   }
 }
 
@@ -551,14 +549,15 @@ __global__ __launch_bounds__(tile::kThreads, 1) void moe_gemm1_kernel(
 
 // ---------------------------------------------------------------- 6. gemm2
 // Persistent over the (M-tile, 256-row slice of W2[e]) list on the same
-// loop.  Side data of a tile: the sorted_row entries of its 256 rows and
-// their routing weights (sorted_wts, p_max entries after sorted_row; wave w
-// copies rows 64 w ..), so the epilogue finds each row's slot row t*k + j
-// and weight in LDS.  Epilogue: each row's fp32 values times its fp32
-// weight, stored as fp32 straight from the accumulators (lane (i, g) holds 4
-// consecutive columns of a row per MFMA tile: one 16-byte store each, the
-// L2 merging a row's pieces; staging 16 x 64 fp32 blocks through LDS for
-// whole-row stores measured 1.5x slower); pad rows and rows past the tile's
+// loop.  Side data of a tile: the sorted_row entries of its 256 rows (wave
+// w copies rows 64 w ..), so the epilogue finds each row's slot row t*k + j
+// in LDS.  Epilogue: each row's fp32 accumulators stored as they are, straight
+// from the accumulator registers (lane (i, g) holds 4 consecutive columns of
+// a row per MFMA tile: one 16-byte store each, the L2 merging a row's
+// pieces; staging 16 x 64 fp32 blocks through LDS for whole-row stores
+// measured 1.5x slower).  The routing weight is applied by the combine:
+// multiplying here took every accumulator through VGPRs, and the kernel
+// then spilled inside its MFMA loop.  Pad rows and rows past the tile's
 // groups go to the spare row R, so every wave issues exactly 64 stores per
 // tile.
 struct Moe2Job {
@@ -576,7 +575,7 @@ __global__ __launch_bounds__(tile::kThreads, 1) void moe_gemm2_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t st1[tile::kStage];
   __shared__ __attribute__((aligned(16))) uint8_t st2[tile::kStage];
   __shared__ __attribute__((aligned(16))) uint8_t st3[tile::kStage];
-  constexpr int kRowSlot = 2 * 256 * 4;           // 256 slot rows, then 256 weights
+  constexpr int kRowSlot = 256 * 4;               // the tile's 256 slot rows
   __shared__ __attribute__((aligned(16))) uint8_t side[2 * kRowSlot];
   const int NT = H / 256;
   const int total = meta[0] * NT;
@@ -610,19 +609,17 @@ __global__ __launch_bounds__(tile::kThreads, 1) void moe_gemm2_kernel(
   auto make_src = [&](const Moe2Job& j) {
     return tile::BufSrc(j.wga, j.wgb, j.xga, j.xgb, j.swa, j.swb, j.sxa, j.sxb, KS, KS);
   };
-  // One resource from the tile's first sorted row to the end of sorted_wts
-  // (2 p_max entries from sorted_row): rows g0 * 128 .. + 255 are in range
-  // (p_max holds a spare group), their weights p_max entries further.
+  // One resource from the tile's first sorted row to the end of sorted_row
+  // (p_max entries): rows g0 * 128 .. + 255 are in range (p_max holds a
+  // spare group).
   auto side_of = [&](const Moe2Job& j) {
-    return tile::buffer_rsrc(j.rows, (uint32_t)((2 * (int64_t)p_max - (j.rows - sorted_row)) * 4));
+    return tile::buffer_rsrc(j.rows, (uint32_t)(((int64_t)p_max - (j.rows - sorted_row)) * 4));
   };
   auto side_copy = [&](tile::i4v r, uint8_t* slot) {
     tile::b2l_4((uint32_t)((wave * 64 + lane) * 4), r, 0u, slot + wave * 256);
-    tile::b2l_4((uint32_t)((wave * 64 + lane) * 4), r, (uint32_t)p_max * 4u, slot + 1024 + wave * 256);
   };
   auto epilogue = [&](const v4f (&acc)[8][8], const Moe2Job& j, const uint8_t* slot) {
     const int* rmap = reinterpret_cast<const int*>(slot);
-    const float* wmap = reinterpret_cast<const float*>(slot + 1024);
     const int valid = j.ng * kGroupRows;
     float* colp = ys + j.col0 + wn * 128 + 4 * lg;
 #pragma unroll
@@ -630,23 +627,22 @@ __global__ __launch_bounds__(tile::kThreads, 1) void moe_gemm2_kernel(
       const int ml = wm * 128 + 16 * k + li;
       const int sr = rmap[ml];
       const bool real = ml < valid && sr >= 0;
-      const float w = wmap[ml];
       float* d = colp + (size_t)(real ? sr : R) * H;
 #pragma unroll
-      for (int a = 0; a < 8; ++a) {
-        const v4f v = acc[a][k];
-        *reinterpret_cast<float4*>(d + 16 * a) = make_float4(w * v[0], w * v[1], w * v[2], w * v[3]);
-      }
+      for (int a = 0; a < 8; ++a) *reinterpret_cast<v4f*>(d + 16 * a) = acc[a][k];
     }
     return 64;
   };
-  tile::persistent16_run<2, kRowSlot, false, false, false>(st0, st1, st2, st3, side, total, KS, decode, make_src,
+  tile::persistent16_run<1, kRowSlot, false, false, false>(st0, st1, st2, st3, side, total, KS, decode, make_src,
                                                            side_of, side_copy, [](int) {},
                                                            [](v4f (&)[8][8], const uint8_t*) {}, epilogue);
 }
 
 // ---------------------------------------------------------------- 7. combine
-__global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ ys, int T, int H, int topk,
+// Each product is rounded to fp32 before it is added (contraction into
+// fused multiply-adds is off in the loop), as the sum's definition has it.
+__global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ ys,
+                                                          const float* __restrict__ wts, int T, int H, int topk,
                                                           uint16_t* __restrict__ y) {
   const int64_t t4 = (int64_t)blockIdx.x * 256 + threadIdx.x;   // one thread per 8 columns of a token
   const int per_row = H / 8;
@@ -655,10 +651,13 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
   const int c = (int)(t4 - t * per_row);
   float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < topk; ++j) {
+#pragma clang fp contract(off)
     const float* r = ys + (t * topk + j) * H + c * 8;
+    const float w = wts[t * topk + j];
     const float4 a = *reinterpret_cast<const float4*>(r), b = *reinterpret_cast<const float4*>(r + 4);
-    s[0] += a.x; s[1] += a.y; s[2] += a.z; s[3] += a.w;
-    s[4] += b.x; s[5] += b.y; s[6] += b.z; s[7] += b.w;
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s[i] += w * v[i];
   }
   *reinterpret_cast<uint4*>(y + t * H + c * 8) = make_uint4(pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]),
                                                             pack_bf16x2(s[4], s[5]), pack_bf16x2(s[6], s[7]));
@@ -677,9 +676,8 @@ int launch_moe(const MoeArgs& a, hipStream_t stream) {
   }
   hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(1024), 0, stream, a.ws.blk_cnt, nblk, (int)a.E, a.ws.blk_off,
                      a.ws.seg_off, a.ws.tile_e, a.ws.tile_g0, a.ws.tile_ng, a.ws.meta);
-  hipLaunchKernelGGL(moe_scatter_kernel, dim3(nblk), dim3(256), 0, stream, a.ws.ids, a.ws.wts, R, (int)a.topk,
-                     (int)a.E, a.ws.blk_off, a.ws.seg_off, a.ws.sorted_row,
-                     reinterpret_cast<float*>(a.ws.sorted_row + a.ws.p_max));
+  hipLaunchKernelGGL(moe_scatter_kernel, dim3(nblk), dim3(256), 0, stream, a.ws.ids, R, (int)a.topk, (int)a.E,
+                     a.ws.blk_off, a.ws.seg_off, a.ws.sorted_row);
   const int KS1 = (int)(a.H / kStepK);
   hipLaunchKernelGGL(moe_gather_scales_kernel, dim3((unsigned)(a.ws.p_max / kGroupRows * KS1 / 4)), dim3(256), 0,
                      stream, a.ws.xs, (int)a.H, (int)a.topk, a.ws.sorted_row, a.ws.meta, KS1, a.ws.a1s,
@@ -701,7 +699,7 @@ int launch_moe(const MoeArgs& a, hipStream_t stream) {
                      a.ws.tile_ng, a.ws.sorted_row, (int)a.ws.p_max, (int)a.H, (int)a.I, R, a.ws.ys);
   const int64_t cb_total = a.T * (a.H / 8);
   hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((cb_total + 255) / 256)), dim3(256), 0, stream, a.ws.ys,
-                     (int)a.T, (int)a.H, (int)a.topk, (uint16_t*)a.y);
+                     a.ws.wts, (int)a.T, (int)a.H, (int)a.topk, (uint16_t*)a.y);
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 

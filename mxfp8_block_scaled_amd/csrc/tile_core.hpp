@@ -1186,6 +1186,12 @@ __device__ __forceinline__ void persistent16_run(uint8_t* st0, uint8_t* st1, uin
       for (int a = 0; a < 8; ++a)
 #pragma unroll
         for (int c = 0; c < 8; ++c) acc[a][c] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      // (an AGPR-only definition of the zeros: the MoE GEMMs' register
+      // allocation otherwise gives some accumulators VGPR homes and spills)
+#pragma unroll
+      for (int a = 0; a < 8; ++a)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) asm volatile("" : "+a"(acc[a][c]));
     }
     int p = 0;
     if (P >= 4) {

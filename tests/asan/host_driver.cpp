@@ -135,7 +135,7 @@ int launch_moe(const MoeArgs& a, hipStream_t) {
   touch(w.tile_e, w.mt_max * 4);
   touch(w.tile_g0, w.mt_max * 4);
   touch(w.tile_ng, w.mt_max * 4);
-  touch(w.sorted_row, 2 * w.p_max * 4);
+  touch(w.sorted_row, w.p_max * 4);
   touch(w.xq, (a.T + 1) * a.H);
   touch(w.xs, (a.T + 1) * (a.H / 32));
   touch(w.a1s, w.p_max * (a.H / 32));
