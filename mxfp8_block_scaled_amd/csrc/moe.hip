@@ -467,16 +467,21 @@ __global__ __launch_bounds__(tile::kThreads, 1) void moe_gemm1_kernel(
     const tile::i4v r = tile::buffer_rsrc(sorted_row + (size_t)g0 * kGroupRows, (uint32_t)(ng * kGroupRows * 4));
     tile::b2l_4((uint32_t)((wave * 64 + lane) * 4), r, 0u, reinterpret_cast<const uint8_t*>(rowbuf) + wave * 256);
   };
+  // The tile's two groups of the gated operand and of its scales, as buffers
+  // (rows outside the tile's groups are given an offset past the end, so
+  // every wave issues the same 48 stores per tile).
+  const int64_t qgroup = (int64_t)KS2 * kTileBytes, sgroup = (int64_t)KS2 * kTileScaleBytes;
   auto epilogue = [&](const v4f (&acc)[8][8], const Moe1Job& j, const uint8_t*) {
     const int ks = 2 * j.nt + wn;                 // the 64-K step of this wave's intermediate indices
     const int valid = j.ng * kGroupRows;
+    const __amdgpu_buffer_rsrc_t qb = raw_rsrc(a2q + (size_t)j.g0 * qgroup, (uint32_t)(2 * qgroup));
+    const __amdgpu_buffer_rsrc_t sbuf = raw_rsrc(a2s + (size_t)j.g0 * sgroup, (uint32_t)(2 * sgroup));
 #pragma unroll
     for (int bb = 0; bb < 8; ++bb) {
       const int ml = wm * 128 + 16 * bb + li;     // row inside the tile
       const bool row_ok = ml < valid;
       const int pos = j.g0 * kGroupRows + ml;
       const int g = pos / kGroupRows, rr = pos % kGroupRows;
-      uint8_t* gbase = a2q + (size_t)g * KS2 * kTileBytes;
       const int src = (dbg_act != nullptr && row_ok) ? sorted_row[pos] : -1;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -517,11 +522,16 @@ __global__ __launch_bounds__(tile::kThreads, 1) void moe_gemm1_kernel(
         const uint32_t sb = (uint32_t)max((int)(m >> 7) - 8, 0);
         uint32_t q[2];
         cvt8s(w, mx_scale_value(sb), q);
-        if (row_ok) {
+        {
           // bytes j = 0..3 of a = 2h + t sit at k = 16a + 4g + j of step ks
-          *reinterpret_cast<uint32_t*>(gbase + packed_off(rr, ks, 2 * h, KS2) + 4 * lg) = q[0];
-          *reinterpret_cast<uint32_t*>(gbase + packed_off(rr, ks, 2 * h + 1, KS2) + 4 * lg) = q[1];
-          if (lg == 0) a2s[((size_t)g * KS2 + ks) * kTileScaleBytes + scale_off(rr, h)] = (uint8_t)sb;
+          const uint32_t gq = (uint32_t)((g - j.g0) * qgroup), gs = (uint32_t)((g - j.g0) * sgroup);
+          const uint32_t o0 = gq + (uint32_t)packed_off(rr, ks, 2 * h, KS2) + 4 * lg;
+          const uint32_t o1 = gq + (uint32_t)packed_off(rr, ks, 2 * h + 1, KS2) + 4 * lg;
+          const uint32_t os = gs + (uint32_t)(ks * kTileScaleBytes + scale_off(rr, h));
+          const uint32_t off_end = 0x80000000u;
+          __builtin_amdgcn_raw_buffer_store_b32(q[0], qb, (int)(row_ok ? o0 : off_end), 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(q[1], qb, (int)(row_ok ? o1 : off_end), 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sb, sbuf, (int)(row_ok && lg == 0 ? os : off_end), 0, 0);
         }
         if (src >= 0) {
           const int iblk = j.nt * 128 + wn * 64 + 32 * h;     // first intermediate index of the block
@@ -539,7 +549,7 @@ __global__ __launch_bounds__(tile::kThreads, 1) void moe_gemm1_kernel(
         }
       }
     }
-    return 0;   // the number of stores depends on the rows
+    return dbg_act != nullptr ? 0 : 48;   // (the debug copies' stores depend on the rows)
   };
   tile::persistent16_run<0, 0, true, false, false>(st0, st1, st2, st3, nullptr, total, KS, decode, make_src,
                                                    [](const Moe1Job&) { return tile::buffer_rsrc(nullptr, 0); },

@@ -978,8 +978,8 @@ __device__ __forceinline__ bool epi16(uint8_t* epi, const v4f (&acc)[8][8], uint
 //    kSideSlot bytes at side_lds (e.g. the tile's bias).  The epilogue of the
 //    tile finds it there: epilogue(acc, job, slot) stores the tile and returns
 //    the number of vector memory operations the wave issued in it when that
-//    is exactly 32 or 64 (the next tile's first wait then lets them stay in
-//    flight), else 0.
+//    is exactly 32, 48 or 64 (the next tile's first wait then lets them stay
+//    in flight), else 0.
 //  * tile_start(b_next) runs at the start of each tile with the index of the
 //    workgroup's next tile (may be >= total); vector memory operations it
 //    issues are complete by the tile's first barrier after its first wait.
@@ -1073,7 +1073,7 @@ __device__ __forceinline__ void persistent16_run(uint8_t* st0, uint8_t* st1, uin
   // side data of sr's tile into slot bbuf.  The wait before column 6 needs the
   // next step's copies: besides the weight copies issued in this step (if
   // any), vm_extra stores of the previous epilogue may still be in flight
-  // after them (32 or 64, or 0 when unknown; with 64 the wait allows 63, the
+  // after them (32, 48 or 64, or 0 when unknown; with 64 the wait allows 63, the
   // counter's limit: the step's copies are older than all of them).  The next step's fragments are always
   // read (after the last tile they are stale and unused).
   auto step = [&](auto kIssue, auto kRtIssue, auto with_side, auto kVm, auto kNext, bool rt_issue, uint8_t* ev, uint8_t* od,
@@ -1092,19 +1092,23 @@ __device__ __forceinline__ void persistent16_run(uint8_t* st0, uint8_t* st1, uin
       if constexpr (j == 48) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         const bool extra = decltype(kVm)::value && vm_extra == 32;
+        const bool extra48 = decltype(kVm)::value && vm_extra == 48;
         const bool extra64 = decltype(kVm)::value && vm_extra == 64;
         if constexpr (kI) {
           if (extra64) wait_vmcnt<63>();
+          else if (extra48) wait_vmcnt<kWCopies + 48>();
           else if (extra) wait_vmcnt<kWCopies + 32>();
           else wait_vmcnt<kWCopies>();
         } else {
           if (extra64) {
             wait_vmcnt<63>();
           } else if (issue) {
-            if (extra) wait_vmcnt<kWCopies + 32>();
+            if (extra48) wait_vmcnt<kWCopies + 48>();
+            else if (extra) wait_vmcnt<kWCopies + 32>();
             else wait_vmcnt<kWCopies>();
           } else {
-            if (extra) wait_vmcnt<32>();
+            if (extra48) wait_vmcnt<48>();
+            else if (extra) wait_vmcnt<32>();
             else wait_vmcnt<0>();
           }
         }
@@ -1224,7 +1228,7 @@ __device__ __forceinline__ void persistent16_run(uint8_t* st0, uint8_t* st1, uin
     const int nvm = (int)epilogue(acc, cur, side_lds + buf * kSideSlot);
     if (!has_next) break;
     if constexpr (!kCarry) read_first(st0, st1);
-    vm_extra = (nvm == 32 || nvm == 64) ? nvm : 0;
+    vm_extra = (nvm == 32 || nvm == 48 || nvm == 64) ? nvm : 0;
     src = nsrc;
     cur = nxt;
     b = nb;
