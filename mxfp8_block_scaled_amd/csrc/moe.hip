@@ -561,15 +561,15 @@ __global__ __launch_bounds__(tile::kThreads, 1) void moe_gemm1_kernel(
 // Persistent over the (M-tile, 256-row slice of W2[e]) list on the same
 // loop.  Side data of a tile: the sorted_row entries of its 256 rows (wave
 // w copies rows 64 w ..), so the epilogue finds each row's slot row t*k + j
-// in LDS.  Epilogue: each row's fp32 accumulators stored as they are, straight
-// from the accumulator registers (lane (i, g) holds 4 consecutive columns of
-// a row per MFMA tile: one 16-byte store each, the L2 merging a row's
-// pieces; staging 16 x 64 fp32 blocks through LDS for whole-row stores
-// measured 1.5x slower).  The routing weight is applied by the combine:
-// multiplying here took every accumulator through VGPRs, and the kernel
-// then spilled inside its MFMA loop.  Pad rows and rows past the tile's
-// groups go to the spare row R, so every wave issues exactly 64 stores per
-// tile.
+// in LDS.  Epilogue: each row's fp32 accumulators, as they are, staged 16
+// rows x 64 columns at a time through the wave's LDS region and stored as
+// whole 256-byte row segments, four rows per store (storing each lane's 4
+// columns straight from the accumulators, 64-byte pieces of 16 rows per
+// store, was 4 % slower on the layer).  The routing weight is applied by the
+// combine: multiplying here took every accumulator through VGPRs, and the
+// kernel then spilled inside its MFMA loop.  Pad rows and rows past the
+// tile's groups go to the spare row R, so every wave issues exactly 64
+// stores per tile.
 struct Moe2Job {
   const uint8_t *wga, *wgb, *xga, *xgb, *swa, *swb, *sxa, *sxb;
   const int* rows;      // sorted_row of the tile's first row
@@ -587,6 +587,8 @@ __global__ __launch_bounds__(tile::kThreads, 1) void moe_gemm2_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t st3[tile::kStage];
   constexpr int kRowSlot = 256 * 4;               // the tile's 256 slot rows
   __shared__ __attribute__((aligned(16))) uint8_t side[2 * kRowSlot];
+  constexpr int kPitchF = 68;                     // fp32 per staged row (64 + 4 pad)
+  __shared__ __attribute__((aligned(16))) float stage_epi[4][16 * kPitchF];
   const int NT = H / 256;
   const int total = meta[0] * NT;
   const int KS = I / kStepK;
@@ -631,15 +633,27 @@ __global__ __launch_bounds__(tile::kThreads, 1) void moe_gemm2_kernel(
   auto epilogue = [&](const v4f (&acc)[8][8], const Moe2Job& j, const uint8_t* slot) {
     const int* rmap = reinterpret_cast<const int*>(slot);
     const int valid = j.ng * kGroupRows;
-    float* colp = ys + j.col0 + wn * 128 + 4 * lg;
+    float* reg = stage_epi[wave];
+    const int rr = lane >> 4, cc = (lane & 15) * 4;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const int ml = wm * 128 + 16 * k + li;
-      const int sr = rmap[ml];
-      const bool real = ml < valid && sr >= 0;
-      float* d = colp + (size_t)(real ? sr : R) * H;
 #pragma unroll
-      for (int a = 0; a < 8; ++a) *reinterpret_cast<v4f*>(d + 16 * a) = acc[a][k];
+      for (int hf = 0; hf < 2; ++hf) {
+        // Rows 16 k .. + 15 of the wave's block, columns 64 hf .. + 63: staged
+        // (a wave's LDS operations run in order: no waits), read back as 16
+        // lanes per row, stored as 4 whole 256-byte row segments.
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+          *reinterpret_cast<v4f*>(reg + li * kPitchF + 16 * a + 4 * lg) = acc[4 * hf + a][k];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const v4f v = *reinterpret_cast<const v4f*>(reg + (rr + 4 * q) * kPitchF + cc);
+          const int ml = wm * 128 + 16 * k + rr + 4 * q;
+          const int sr = rmap[ml];
+          const bool real = ml < valid && sr >= 0;
+          *reinterpret_cast<v4f*>(ys + (size_t)(real ? sr : R) * H + j.col0 + wn * 128 + 64 * hf + cc) = v;
+        }
+      }
     }
     return 64;
   };
