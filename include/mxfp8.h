@@ -161,6 +161,10 @@ int mxfp8_linear_noalloc(const void* x_bf16, int64_t M, int64_t K, int64_t ldx,
  *   w_s_e8m0 [N, >= K/32] row stride ldws (only [:N, :K/32] is read)
  *   w_packed, s_packed  outputs of the sizes above, 256-byte aligned.  Pad
  *            rows hold zero elements and scale byte 127.
+ * mxfp8_unpack_weight_fp4: inverse of mxfp8_prepare_weight_fp4, for tests
+ *   and tooling: writes the full padded operand w_e2m1 [N_pad, K/2] bytes
+ *   (contiguous, 16-byte aligned; pad rows zero) and w_s_e8m0 [N_pad, K/32]
+ *   (contiguous; pad rows byte 127).  Same size rules as the pack.
  * mxfp8_linear_w4a8_workspace_bytes: host-only.  M <= 128 (K <= 8192): as
  *   mxfp8_linear; larger M: mxfp8_linear's workspace plus N_pad * K bytes,
  *   where the weight is widened (exactly: every E2M1 value is an E4M3
@@ -185,6 +189,8 @@ int mxfp8_quantize_fp4(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, vo
 int mxfp8_prepared_weight_fp4_bytes(int64_t N, int64_t K, size_t* w_bytes, size_t* s_bytes);
 int mxfp8_prepare_weight_fp4(const void* w_e2m1, const void* w_s_e8m0, int64_t N, int64_t K, int64_t ldw,
                              int64_t ldws, void* w_packed, void* s_packed, void* stream);
+int mxfp8_unpack_weight_fp4(const void* w_packed, const void* s_packed, int64_t N, int64_t K, void* w_e2m1,
+                            void* w_s_e8m0, void* stream);
 int mxfp8_linear_w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes);
 int mxfp8_linear_w4a8(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, const void* w_packed,
                       const void* s_packed, int64_t N, const void* bias_bf16, void* y_bf16, int64_t ldy,

@@ -50,6 +50,7 @@ _SIGNATURES = {
     "mxfp8_quantize_fp4": ([_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp], ctypes.c_int),
     "mxfp8_prepared_weight_fp4_bytes": ([_i64, _i64, ctypes.POINTER(_sz), ctypes.POINTER(_sz)], ctypes.c_int),
     "mxfp8_prepare_weight_fp4": ([_vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
+    "mxfp8_unpack_weight_fp4": ([_vp, _vp, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
     "mxfp8_linear_w4a8_workspace_bytes": ([_i64, _i64, _i64, ctypes.POINTER(_sz)], ctypes.c_int),
     "mxfp8_linear_w4a8": ([_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _sz, _vp], ctypes.c_int),
     "mxfp8_linear_noalloc": ([_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp], ctypes.c_int),
@@ -174,6 +175,10 @@ def mxfp8_prepared_weight_fp4_bytes(N, K):
 
 def mxfp8_prepare_weight_fp4(w, ws, N, K, ldw, ldws, wp, sp, stream):
     return lib().mxfp8_prepare_weight_fp4(w, ws, N, K, ldw, ldws, wp, sp, stream)
+
+
+def mxfp8_unpack_weight_fp4(wp, sp, N, K, w, ws, stream):
+    return lib().mxfp8_unpack_weight_fp4(wp, sp, N, K, w, ws, stream)
 
 
 def mxfp8_linear_w4a8_workspace_bytes(M, N, K):
@@ -354,7 +359,14 @@ class PreparedWeightFP4(PreparedWeight):
     N_pad * K / 2 bytes, and its UE8M0 scales)."""
 
     def unpack(self):
-        raise NotImplementedError("no unpack for the MXFP4 layout")
+        """(E2M1 ``[N_pad, K/2]``, two codes per byte, UE8M0 ``[N_pad, K/32]``)
+        as uint8 tensors."""
+        n_pad = (self.N + 127) // 128 * 128
+        w = torch.empty((n_pad, self.K // 2), dtype=torch.uint8, device=self.device)
+        s = torch.empty((n_pad, self.K // 32), dtype=torch.uint8, device=self.device)
+        _check(mxfp8_unpack_weight_fp4(_ptr(self.w_packed), _ptr(self.s_packed), self.N, self.K, _ptr(w), _ptr(s),
+                                       _stream(self.device)), "mxfp8_unpack_weight_fp4")
+        return w, s
 
 
 def prepare_weight_fp4(w_e2m1, w_s):

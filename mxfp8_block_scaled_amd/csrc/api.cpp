@@ -344,6 +344,15 @@ int mxfp8_prepare_weight_fp4(const void* w_e2m1, const void* w_s_e8m0, int64_t N
   return mxfp8::launch_pack_weight_fp4(w_e2m1, w_s_e8m0, N, K, ldw, ldws, w_packed, s_packed, (hipStream_t)stream);
 }
 
+int mxfp8_unpack_weight_fp4(const void* w_packed, const void* s_packed, int64_t N, int64_t K, void* w_e2m1,
+                            void* w_s_e8m0, void* stream) {
+  if (int st = check_packed(w_packed, s_packed, N, K)) return st;
+  if (!w_e2m1 || !w_s_e8m0) return MXFP8_E_NULLPTR;
+  if (!aligned(w_e2m1, 16)) return MXFP8_E_ALIGN;
+  if (int st = check_device()) return st;
+  return mxfp8::launch_unpack_weight_fp4(w_packed, s_packed, N, K, w_e2m1, w_s_e8m0, (hipStream_t)stream);
+}
+
 int mxfp8_linear_w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes) {
   if (!bytes) return MXFP8_E_NULLPTR;
   if (M < 0 || N < 1 || K < 256 || K % 256 != 0) return MXFP8_E_SHAPE;

@@ -92,6 +92,9 @@ int launch_gemm_skinny_fp4(const void* x, int64_t ldx, int64_t M, int64_t K, con
 // nibble; row stride ldw bytes), ws [N, K/32] UE8M0 -> packed tiles (pack.hip).
 int launch_pack_weight_fp4(const void* w, const void* ws, int64_t N, int64_t K, int64_t ldw, int64_t ldws,
                            void* wp, void* sp, hipStream_t stream);
+// Inverse: packed tiles -> w [N_pad, K/2] and ws [N_pad, K/32], contiguous.
+int launch_unpack_weight_fp4(const void* wp, const void* sp, int64_t N, int64_t K, void* w, void* ws,
+                             hipStream_t stream);
 // Packed MXFP4 weight tiles -> packed MXFP8 tiles of the same values (the
 // scales stay as they are), N_pad * K bytes.
 int launch_widen_fp4(const void* w4, int64_t N, int64_t K, void* w8, hipStream_t stream);

@@ -206,4 +206,20 @@ int launch_unpack_weight(const void* wp, const void* sp, int64_t N, int64_t K, v
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 
+// Inverse of launch_pack_weight_fp4: the byte packing is that of an E4M3
+// operand of K / 2 bytes per row (K / 128 pieces of 64 bytes), the scales
+// those of a K-element row.
+int launch_unpack_weight_fp4(const void* wp, const void* sp, int64_t N, int64_t K, void* w, void* ws,
+                             hipStream_t stream) {
+  const int64_t KS4 = K / 128, KS = K / kStepK;
+  const int64_t G = (N + kGroupRows - 1) / kGroupRows;
+  const int64_t tw = G * KS4 * kChunksPerTile;
+  const int64_t ts = G * KS * kGroupRows;
+  hipLaunchKernelGGL(unpack_w_kernel, dim3((unsigned)((tw + 255) / 256)), dim3(256), 0, stream,
+                     (const uint8_t*)wp, K / 2, KS4, tw, (uint8_t*)w);
+  hipLaunchKernelGGL(unpack_s_kernel, dim3((unsigned)((ts + 255) / 256)), dim3(256), 0, stream,
+                     (const uint8_t*)sp, K, KS, ts, (uint8_t*)ws);
+  return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
 }  // namespace mxfp8

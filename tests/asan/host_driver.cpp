@@ -112,6 +112,11 @@ int launch_pack_weight_fp4(const void*, const void*, int64_t N, int64_t K, int64
   touch(sp, mpad(N) * (K / 32));
   return 0;
 }
+int launch_unpack_weight_fp4(const void*, const void*, int64_t N, int64_t K, void* w, void* ws, hipStream_t) {
+  touch(w, mpad(N) * (K / 2));
+  touch(ws, mpad(N) * (K / 32));
+  return 0;
+}
 int launch_widen_fp4(const void*, int64_t N, int64_t K, void* w8, hipStream_t) {
   touch(w8, mpad(N) * K);
   return 0;
@@ -260,7 +265,10 @@ int main() {
     uint8_t* w4p = alloc_exact(w4b);
     uint8_t* s4p = alloc_exact(s4b);
     CHECK(mxfp8_prepare_weight_fp4(w4, wsc, N, K, K / 2, K / 32, w4p, s4p, nullptr) == 0);
-    for (uint8_t* p : {x, q, s, q4, qp, sp, w, wsc, wp, wps, uw, us, y, pws, w4, w4p, s4p}) std::free(p);
+    uint8_t* uw4 = alloc_exact(w4b);
+    uint8_t* us4 = alloc_exact(s4b);
+    CHECK(mxfp8_unpack_weight_fp4(w4p, s4p, N, K, uw4, us4, nullptr) == 0);
+    for (uint8_t* p : {x, q, s, q4, qp, sp, w, wsc, wp, wps, uw, us, y, pws, w4, w4p, s4p, uw4, us4}) std::free(p);
   }
   // The routed MoE layer: ragged token counts, the largest E and top-k.
   moe_case(200, 256, 8, 2, 256);

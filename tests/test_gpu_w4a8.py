@@ -20,6 +20,25 @@ def prepare(codes, ws):
     return api.prepare_weight_fp4(torch.from_numpy(oracle.pack_fp4(codes)).to(d), torch.from_numpy(ws).to(d))
 
 
+def test_prepare_unpack_roundtrip_fp4():
+    """prepare_weight_fp4 then unpack gives back the E2M1 bytes and the
+    [:N, :K/32] scales exactly, with zero pad rows and scale byte 127."""
+    g = torch.Generator().manual_seed(3)
+    d = gpu_util.dev()
+    for N, K in [(130, 256), (256, 512), (1, 768), (300, 1024), (128, 4096)]:
+        print("CASE roundtrip fp4", N, K, flush=True)
+        w4 = torch.randint(0, 256, (N, K // 2), generator=g, dtype=torch.uint8)
+        ws = torch.randint(0, 256, (N + 3, K // 32 + 5), generator=g, dtype=torch.uint8)  # larger, strided
+        pw = api.prepare_weight_fp4(w4.to(d), ws.to(d))
+        w2, s2 = pw.unpack()
+        torch.cuda.synchronize()
+        n_pad = (N + 127) // 128 * 128
+        assert w2.shape == (n_pad, K // 2) and s2.shape == (n_pad, K // 32)
+        assert torch.equal(w2[:N].cpu(), w4)
+        assert torch.equal(s2[:N].cpu(), ws[:N, : K // 32])
+        assert bool((w2[N:] == 0).all()) and bool((s2[N:] == 127).all())
+
+
 def tolerance4(x_np, codes, ws, K):
     qa, sa = oracle.quantize_mx(x_np)
     A = oracle.dequantize_mx(qa, sa)
