@@ -331,6 +331,51 @@ def test_strided_io_and_canary(path, M):
 
 
 
+@pytest.mark.parametrize("M,N,K", [(2000, 9000, 768), (4352, 4352, 1024), (2304, 8192, 2048)])
+def test_persistent_store_paths_bit_exact(M, N, K):
+    """The persistent GEMM's two epilogue store paths on multi-tile
+    workgroups: with ldy % 8 == 0 full wave blocks leave as 16-byte
+    non-temporal stores (and their count lets the next tile's first copies
+    wait past them), with ldy odd every element is stored on its own.  More
+    tiles than workgroups, so each workgroup runs several tiles; ragged M and
+    N put partial tiles between full ones.  Both layouts must hold the same
+    bits in every element, and neither may write the canary columns >= N."""
+    g = torch.Generator().manual_seed(M + 7 * N + K)
+    x = synth.randn_bf16((M, K), 1.0, g)
+    w = synth.randn_bf16((N, K), 0.02, g)
+    b = synth.randn_bf16((N,), 0.1, g)
+    d = gpu_util.dev()
+    xd, bd = x.to(d), b.to(d)
+    pw = gpu_util.gpu_prepare(w)
+    print("CASE store paths", M, N, K, flush=True)
+    outs = []
+    prev = api.mxfp8_debug_force_path(17)        # tile GEMM, one K split: the persistent kernel
+    try:
+        assert api.mxfp8_debug_plan(M, N, K) == (0, 1)
+        for ldy in (N + 8, N + 3):
+            ybuf = torch.full((M, ldy), -7.0, dtype=torch.bfloat16, device=d)
+            ws = torch.zeros(api.mxfp8_linear_workspace_bytes(M, N, K), dtype=torch.uint8, device=d)
+            st = api.mxfp8_linear(xd.data_ptr(), M, K, K, pw.w_packed.data_ptr(), pw.s_packed.data_ptr(), N,
+                                  bd.data_ptr(), ybuf.data_ptr(), ldy, ws.data_ptr(), ws.numel(),
+                                  torch.cuda.current_stream().cuda_stream)
+            torch.cuda.synchronize()
+            assert st == 0
+            assert bool((ybuf[:, N:] == -7.0).all()), f"ldy {ldy}: columns >= N were written"
+            outs.append(ybuf[:, :N].contiguous())
+    finally:
+        api.mxfp8_debug_force_path(prev)
+    same = outs[0].view(torch.int16) == outs[1].view(torch.int16)
+    assert bool(same.all()), f"{int((~same).sum())} elements differ, first at {(~same).nonzero()[0].tolist()}"
+    # And sampled rows x columns against the oracle.
+    rows = torch.cat([torch.randperm(M, generator=g)[:64], torch.tensor([0, M - 1])])
+    cols = torch.cat([torch.randperm(N, generator=g)[:64], torch.tensor([0, N - 1])])
+    ys = outs[0][rows.to(d)][:, cols.to(d)].float().cpu().numpy()
+    wq, wsc = gpu_util.oracle_weight(w[cols])
+    xn = x[rows].to(torch.float64).numpy()
+    r = oracle.linear_ref(xn, wq, wsc, b[cols].to(torch.float64).numpy())
+    gpu_util.compare(ys, r, gpu_util.tolerance(xn, wq, wsc, len(cols), K), f"store paths {M}x{N}x{K} sampled")
+
+
 def _prequant_bound(A, W, r, K):
     acc = (K / 64.0) * 2.0 ** -10 * np.outer(np.abs(A).max(axis=1), np.abs(W).max(axis=1)) \
         + K * 2.0 ** -23 * (np.abs(A) @ np.abs(W).T)
