@@ -99,11 +99,14 @@ int mxfp8_unpack_weight(const void* w_packed, const void* s_packed, int64_t N, i
                         void* w_e4m3, void* w_s_e8m0, void* stream);
 
 /*
- * Workspace bytes mxfp8_linear needs for this shape (host-only).  For
- * M <= 16 (K <= 8192) nothing is stored there (a 256-byte minimum is still
- * required); otherwise it holds the activations quantized into the packed
- * layout (M padded to 128 rows, plus their scales; for M > 128 also the
- * fp32 split-K partials when the shape has few tiles).  Its
+ * Workspace bytes mxfp8_linear needs for this shape (host-only).  On the
+ * decode kernel (M <= 16, K <= 8192) nothing is stored there (a 256-byte
+ * minimum is still required); on the split-K slab kernel (M <= 128) it holds
+ * fp32 partial outputs, one [M, N_pad] per K slice; otherwise the activations
+ * quantized into the packed layout (M padded to 128 rows, plus their scales;
+ * for M > 128 also the fp32 split-K partials when the shape has few tiles).
+ * Which kernel a shape takes comes from the measured shape table (see
+ * mxfp8_debug_force_path).  Its
  * contents need no initialization.  Calls that share one workspace must be ordered on one
  * stream (concurrent calls on one workspace race).
  */
@@ -165,10 +168,12 @@ int mxfp8_linear_noalloc(const void* x_bf16, int64_t M, int64_t K, int64_t ldx,
  *   and tooling: writes the full padded operand w_e2m1 [N_pad, K/2] bytes
  *   (contiguous, 16-byte aligned; pad rows zero) and w_s_e8m0 [N_pad, K/32]
  *   (contiguous; pad rows byte 127).  Same size rules as the pack.
- * mxfp8_linear_w4a8_workspace_bytes: host-only.  M <= 128 (K <= 8192): as
- *   mxfp8_linear; larger M: mxfp8_linear's workspace plus N_pad * K bytes,
- *   where the weight is widened (exactly: every E2M1 value is an E4M3
- *   value) to the MXFP8 tiles for the MFMA-bound tile GEMM.
+ * mxfp8_linear_w4a8_workspace_bytes: host-only.  M <= 128 (K <= 8192): at
+ *   most one packed 128-row group of activations (the decode or mid-M
+ *   kernel: W4A8 has no slab kernel); otherwise the tile path's workspace
+ *   (as mxfp8_linear's), plus N_pad * K bytes where the table splits K: the
+ *   weight is then widened (exactly: every E2M1 value is an E4M3 value) to
+ *   the MXFP8 tiles for the split-K tile GEMM.
  * mxfp8_linear_w4a8: y[m, n] = bf16( sum_k deq(q(x))[m, k] * deq4(W)[n, k]
  *   + bias[n] ), fp32 accumulate, one rounding; arguments as mxfp8_linear
  *   with the packed MXFP4 weight.  M <= 128 streams the 4-bit weight once
@@ -319,10 +324,12 @@ int mxfp8_moe_debug_capture(void* act_bf16, void* act_e4m3, void* act_e8m0, void
  * 0 or 2 = automatic: the path and the tile GEMM's K splits come from the
  * shape table measured on MI355X (shape_table.inc, written by
  * mxfp8_block_scaled_amd/tune_shapes.py), within each kernel's limits (decode
- * kernel M <= 16 and K <= 8192, mid-M kernel M <= 128 and K <= 8192, K splits
- * s need (K/64) % (4s) == 0); 1 = large-tile path with the table's splits;
- * 3 = mid-M kernel where it applies; 4 = decode kernel where it applies;
- * 16 + s (s = 1, 2, 4, 8) = large-tile path with s K splits where they apply
+ * kernel M <= 16 and K <= 8192, mid-M kernel M <= 128 and K <= 8192, split-K
+ * slab kernel M <= 128 and MXFP8 weights only -- mxfp8_linear_w4a8 runs the
+ * mid-M kernel, or above K = 8192 the tile GEMM, where the table names it --,
+ * K splits s need (K/64) % (4s) == 0); 1 = large-tile path with the table's
+ * splits; 3 = mid-M kernel where it applies; 4 = decode kernel where it
+ * applies; 5 = split-K slab kernel where it applies; 16 + s (s = 1, 2, 4, 8) = large-tile path with s K splits where they apply
  * (else one).  A forced path that a shape cannot take falls back to the
  * large-tile path; mxfp8_linear_workspace_bytes follows the forced choice.
  * Process-wide; returns the previous value, or MXFP8_E_SHAPE for an unknown
@@ -333,7 +340,7 @@ int mxfp8_debug_force_path(int path);
 /*
  * Test hook (host only): the plan mxfp8_linear takes for an M x N x K call
  * under the current forcing: *path = 0 large-tile GEMM, 1 decode kernel,
- * 2 mid-M kernel; *splits = the tile GEMM's K splits (1 for the other paths).
+ * 2 mid-M kernel, 3 split-K slab kernel; *splits = the tile GEMM's K splits (1 for the other paths).
  * MXFP8_E_SHAPE for M < 1, N < 1 or K not a positive multiple of 256.
  */
 int mxfp8_debug_plan(int64_t M, int64_t N, int64_t K, int* path, int* splits);

@@ -120,12 +120,13 @@ size_t moe_layout(int64_t T, int64_t H, int64_t E, int64_t topk, int64_t I, uint
 
 // GEMM path of a linear call and the K splits of the tile GEMM, from the
 // measured shape table (shape_table.inc): the decode kernel (M <= 16,
-// K <= 8192), the mid-M kernel (M <= 128, K <= 8192) or the large-tile GEMM
+// K <= 8192), the mid-M kernel (M <= 128, K <= 8192), the split-K slab
+// kernel (M <= 128, any K; MXFP8 weights only) or the large-tile GEMM
 // with 1 (persistent), 2, 4 or 8 K splits (a split count s needs (K / 64) %
 // (4 s) == 0: each slice a whole number of 128-K step pairs).  A table entry a
 // shape cannot take falls back to the tile GEMM / one split.
 // mxfp8_debug_force_path can pin the path and the splits.
-enum class Path { kTile = 0, kSkinny = 1, kMid = 2 };
+enum class Path { kTile = 0, kSkinny = 1, kMid = 2, kSlab = 3 };
 struct Plan {
   Path path;
   int splits;   // K splits of the tile GEMM (also when the path is not the tile)
@@ -150,6 +151,7 @@ Plan linear_plan(int64_t M, int64_t N, int64_t K) {
   if (force == 1) path = Path::kTile;
   if (force == 3) path = Path::kMid;
   if (force == 4) path = Path::kSkinny;
+  if (force == 5) path = Path::kSlab;
   if (force >= 16) {
     path = Path::kTile;
     if (splits_ok(K, force - 16)) s = force - 16;
@@ -157,9 +159,25 @@ Plan linear_plan(int64_t M, int64_t N, int64_t K) {
   const bool small_k = K <= mxfp8::kSkinnyMaxK;
   if (path == Path::kSkinny && !(small_k && M <= mxfp8::kSkinnyMaxM)) path = Path::kTile;
   if (path == Path::kMid && !(small_k && M <= mxfp8::kMidMaxM)) path = Path::kTile;
+  if (path == Path::kSlab && M > mxfp8::kMidMaxM) path = Path::kTile;
   return {path, s};
 }
-Path linear_path(int64_t M, int64_t N, int64_t K) { return linear_plan(M, N, K).path; }
+// The path of a call whose workspace may hold at most `cap` bytes: where the
+// slab kernel's fp32 partials would not fit, the decode or mid-M kernel
+// (which need at most one packed 128-row group) or the tile GEMM.
+Path linear_path(int64_t M, int64_t N, int64_t K, size_t cap = SIZE_MAX) {
+  const Path p = linear_plan(M, N, K).path;
+  if (p != Path::kSlab || mxfp8::slab_ws_bytes(M, N, K) <= cap) return p;
+  if (K <= mxfp8::kSkinnyMaxK) return M <= mxfp8::kSkinnyMaxM ? Path::kSkinny : Path::kMid;
+  return Path::kTile;
+}
+// W4A8 has no slab kernel: the mid-M kernel takes its shapes (the tile GEMM
+// above the mid-M kernel's K limit).
+Path linear_path_w4a8(int64_t M, int64_t N, int64_t K) {
+  const Path p = linear_path(M, N, K);
+  if (p != Path::kSlab) return p;
+  return K <= mxfp8::kSkinnyMaxK ? Path::kMid : Path::kTile;
+}
 
 }  // namespace
 
@@ -182,6 +200,20 @@ int mxfp8::device_cu_count() {
 
 int mxfp8::check_device_current() { return check_device(); }
 
+int mxfp8::slab_steps_per_wave(int64_t N, int64_t K) {
+  const int64_t G = (N + 127) / 128, KS = K / 128;
+  // The largest of 4, 2 steps per wave that divides K into whole slices and
+  // still gives at least 256 workgroups (one per compute unit), else 1.
+  for (int spw = 4; spw >= 2; spw /= 2)
+    if (KS % (2 * spw) == 0 && G * (KS / (2 * spw)) >= 256) return spw;
+  return 1;
+}
+
+size_t mxfp8::slab_ws_bytes(int64_t M, int64_t N, int64_t K) {
+  const int64_t slices = (K / 128) / (2 * slab_steps_per_wave(N, K));
+  return round_up((size_t)slices * (size_t)M * (size_t)n_pad(N) * 4, 256);
+}
+
 int mxfp8::linear_check_args(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, const void* w_packed,
                              const void* s_packed, int64_t N, const void* bias_bf16, const void* y_bf16,
                              int64_t ldy) {
@@ -197,15 +229,27 @@ int mxfp8::linear_check_args(const void* x_bf16, int64_t M, int64_t K, int64_t l
   return MXFP8_OK;
 }
 
+size_t mxfp8::linear_workspace_within(int64_t M, int64_t N, int64_t K, size_t cap) {
+  if (M == 0) return 256;
+  switch (linear_path(M, N, K, cap)) {
+    case Path::kSkinny: return mxfp8::skinny_ws_bytes(M, K);
+    case Path::kMid: return mxfp8::mid_ws_bytes(M, K);
+    case Path::kSlab: return mxfp8::slab_ws_bytes(M, N, K);
+    default: return tile_ws_bytes(M, N, K);
+  }
+}
+
 int mxfp8::linear_launch(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, const void* w_packed,
                          const void* s_packed, int64_t N, const void* bias_bf16, void* y_bf16, int64_t ldy,
-                         void* workspace, hipStream_t s) {
-  const Path path = linear_path(M, N, K);
+                         void* workspace, hipStream_t s, size_t cap) {
+  const Path path = linear_path(M, N, K, cap);
   if (path == Path::kSkinny)
     return mxfp8::launch_gemm_skinny(x_bf16, ldx, M, K, w_packed, s_packed, N, bias_bf16, y_bf16, ldy, s,
                                      workspace);
   if (path == Path::kMid)
     return mxfp8::launch_gemm_mid(x_bf16, ldx, M, K, w_packed, s_packed, N, bias_bf16, y_bf16, ldy, s, workspace);
+  if (path == Path::kSlab)
+    return mxfp8::launch_gemm_slab(x_bf16, ldx, M, K, w_packed, s_packed, N, bias_bf16, y_bf16, ldy, s, workspace);
   uint8_t* q = (uint8_t*)workspace;
   uint8_t* sc = q + round_up((size_t)n_pad(M) * (size_t)K, 256);
   uint8_t* part = q + tile_ws_act_bytes(M, K);
@@ -287,15 +331,7 @@ int mxfp8_unpack_weight(const void* w_packed, const void* s_packed, int64_t N, i
 int mxfp8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes) {
   if (!bytes) return MXFP8_E_NULLPTR;
   if (M < 0 || N < 1 || K < 256 || K % 256 != 0) return MXFP8_E_SHAPE;
-  if (M == 0) {
-    *bytes = 256;
-    return MXFP8_OK;
-  }
-  switch (linear_path(M, N, K)) {
-    case Path::kSkinny: *bytes = mxfp8::skinny_ws_bytes(M, K); break;
-    case Path::kMid: *bytes = mxfp8::mid_ws_bytes(M, K); break;
-    default: *bytes = tile_ws_bytes(M, N, K);
-  }
+  *bytes = mxfp8::linear_workspace_within(M, N, K, SIZE_MAX);
   return MXFP8_OK;
 }
 
@@ -310,7 +346,7 @@ int mxfp8_linear(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, const vo
   if (!aligned(workspace, 256)) return MXFP8_E_ALIGN;
   if (int st = check_device()) return st;
   return mxfp8::linear_launch(x_bf16, M, K, ldx, w_packed, s_packed, N, bias_bf16, y_bf16, ldy, workspace,
-                              (hipStream_t)stream);
+                              (hipStream_t)stream, SIZE_MAX);
 }
 
 // ---------------------------------------------------------------- W4A8
@@ -360,7 +396,7 @@ int mxfp8_linear_w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* b
     *bytes = 256;
     return MXFP8_OK;
   }
-  switch (linear_path(M, N, K)) {
+  switch (linear_path_w4a8(M, N, K)) {
     case Path::kSkinny: *bytes = mxfp8::skinny_ws_bytes(M, K); break;
     case Path::kMid: *bytes = mxfp8::mid_ws_bytes(M, K); break;
     default:
@@ -382,7 +418,7 @@ int mxfp8_linear_w4a8(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, con
   if (int st = check_output(y_bf16, N, ldy, bias_bf16)) return st;
   if (ldx < K || ldx % 8 != 0) return MXFP8_E_LD;
   if (!aligned(x_bf16, 16)) return MXFP8_E_ALIGN;
-  const Path path = linear_path(M, N, K);
+  const Path path = linear_path_w4a8(M, N, K);
   if (path == Path::kTile && (n_pad(M) * (K / 8) + 255) / 256 > INT32_MAX) return MXFP8_E_SHAPE;
   size_t need = 0;
   mxfp8_linear_w4a8_workspace_bytes(M, N, K, &need);
@@ -569,7 +605,7 @@ int mxfp8_moe_debug_capture(void* act_bf16, void* act_e4m3, void* act_e8m0, void
 
 int mxfp8_debug_force_path(int path) {
   const bool tile_splits = path == 17 || path == 18 || path == 20 || path == 24;
-  if (!(path >= 0 && path <= 4) && !tile_splits) return MXFP8_E_SHAPE;
+  if (!(path >= 0 && path <= 5) && !tile_splits) return MXFP8_E_SHAPE;
   return g_force_path.exchange(path);
 }
 

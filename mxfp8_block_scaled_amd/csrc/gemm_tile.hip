@@ -183,9 +183,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_persistent_w4_kernel(
 }
 
 // y[m][n] = bf16( sum_s part[s][m][n] + bias[n] ), slices added in order.
+// vec: y rows 8-byte aligned (ldy % 4 == 0), so four columns go out as one
+// 8-byte store.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int splits, int M, int N,
                                                             int64_t ldp, const uint16_t* __restrict__ bias,
-                                                            uint16_t* __restrict__ y, int64_t ldy) {
+                                                            uint16_t* __restrict__ y, int64_t ldy, int vec) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;   // one thread per 4 columns
   const int64_t per_row = (N + 3) / 4;
   if (t >= (int64_t)M * per_row) return;
@@ -201,10 +203,23 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     for (int e = 0; e < 4; ++e) b[e] = (n + e < N) ? __uint_as_float((uint32_t)bias[n + e] << 16) : 0.f;
   const uint32_t lo = pack_bf16x2(a.x + b[0], a.y + b[1]), hi = pack_bf16x2(a.z + b[2], a.w + b[3]);
   uint16_t* d = y + m * ldy + n;
+  if (vec && n + 3 < N) {
+    *reinterpret_cast<uint2*>(d) = make_uint2(lo, hi);
+    return;
+  }
   d[0] = (uint16_t)lo;
   if (n + 1 < N) d[1] = (uint16_t)(lo >> 16);
   if (n + 2 < N) d[2] = (uint16_t)hi;
   if (n + 3 < N) d[3] = (uint16_t)(hi >> 16);
+}
+
+int launch_splitk_reduce(const float* part, int splits, int64_t M, int64_t N, int64_t ldp, const void* bias,
+                         void* y, int64_t ldy, hipStream_t stream) {
+  const int64_t threads = M * ((N + 3) / 4);
+  const int vec = (ldy % 4 == 0) && (((uintptr_t)y & 7) == 0);
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, part,
+                     splits, (int)M, (int)N, ldp, (const uint16_t*)bias, (uint16_t*)y, ldy, vec);
+  return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 
 int launch_gemm_tile(const void* qp, const void* sp, int64_t M, int64_t K, const void* wp, const void* wsp,
@@ -229,12 +244,9 @@ int launch_gemm_tile(const void* qp, const void* sp, int64_t M, int64_t K, const
                      (const uint8_t*)qp, (const uint8_t*)sp, (int)M, (int)K, (const uint8_t*)wp,
                      (const uint8_t*)wsp, (int)N, (int)GN, (int)GM, (const uint16_t*)bias, (uint16_t*)y, ldy,
                      tiles_m, tiles_n, vec, splits, (float*)part, ldp);
-  if (splits > 1) {
-    const int64_t threads = M * ((N + 3) / 4);
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
-                       (const float*)part, splits, (int)M, (int)N, ldp, (const uint16_t*)bias, (uint16_t*)y, ldy);
-  }
-  return hipGetLastError() == hipSuccess ? 0 : -7;
+  if (hipGetLastError() != hipSuccess) return -7;
+  if (splits > 1) return launch_splitk_reduce((const float*)part, splits, M, N, ldp, bias, y, ldy, stream);
+  return 0;
 }
 
 int launch_gemm_tile_w4(const void* qp, const void* sp, int64_t M, int64_t K, const void* w4p, const void* wsp,

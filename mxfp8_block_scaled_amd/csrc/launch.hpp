@@ -26,8 +26,13 @@ int check_device_current();
 // workspace of mxfp8_linear_workspace_bytes, device checked).
 int linear_check_args(const void* x, int64_t M, int64_t K, int64_t ldx, const void* wp, const void* sp, int64_t N,
                       const void* bias, const void* y, int64_t ldy);
+// cap: the workspace bytes the caller can give (SIZE_MAX: whatever the
+// planned path needs); a planned slab path whose partials exceed it runs the
+// decode or mid-M kernel, or the tile GEMM, instead.  linear_workspace_within
+// is the workspace of the path so chosen.
+size_t linear_workspace_within(int64_t M, int64_t N, int64_t K, size_t cap);
 int linear_launch(const void* x, int64_t M, int64_t K, int64_t ldx, const void* wp, const void* sp, int64_t N,
-                  const void* bias, void* y, int64_t ldy, void* workspace, hipStream_t stream);
+                  const void* bias, void* y, int64_t ldy, void* workspace, hipStream_t stream, size_t cap);
 
 int launch_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx, void* q, int64_t ldq, void* s,
                         int64_t lds, hipStream_t stream);
@@ -63,6 +68,21 @@ int launch_gemm_tile(const void* qp, const void* sp, int64_t M, int64_t K, const
 // K split; pack_weight_fp4's layout, scales as for MXFP8).
 int launch_gemm_tile_w4(const void* qp, const void* sp, int64_t M, int64_t K, const void* w4p, const void* wsp,
                         int64_t N, const void* bias, void* y, int64_t ldy, hipStream_t stream);
+
+// y [M, N] (bf16, row stride ldy) = the sum of `splits` fp32 partials
+// part[s][M][ldp] in split order, plus the bias, rounded once.
+int launch_splitk_reduce(const float* part, int splits, int64_t M, int64_t N, int64_t ldp, const void* bias,
+                         void* y, int64_t ldy, hipStream_t stream);
+
+// Split-K slab GEMM (M <= kMidMaxM, any K) with the activation
+// quantization fused in (gemm_slab.hip): each workgroup multiplies one
+// 128-row weight group by one K slice of 2 * slab_steps_per_wave 128-K steps
+// and writes an fp32 partial into ws (slab_ws_bytes); launch_splitk_reduce
+// then adds the slices.
+int slab_steps_per_wave(int64_t N, int64_t K);
+size_t slab_ws_bytes(int64_t M, int64_t N, int64_t K);
+int launch_gemm_slab(const void* x, int64_t ldx, int64_t M, int64_t K, const void* wp, const void* sp, int64_t N,
+                     const void* bias, void* y, int64_t ldy, hipStream_t stream, void* ws);
 
 // Skinny GEMM (M <= kSkinnyMaxM, K <= kSkinnyMaxK) with the activation
 // quantization fused in; it needs no workspace (skinny_ws_bytes is the

@@ -52,12 +52,13 @@ extern "C" int mxfp8_linear_noalloc(const void* x_bf16, int64_t M, int64_t K, in
                                     int64_t ldy, void* stream) {
   if (int st = mxfp8::linear_check_args(x_bf16, M, K, ldx, w_packed, s_packed, N, bias_bf16, y_bf16, ldy)) return st;
   if (M == 0) return MXFP8_OK;
-  size_t need = 0;
-  if (int st = mxfp8_linear_workspace_bytes(M, N, K, &need)) return st;
+  // Where the planned path's workspace (the slab kernel's fp32 partials)
+  // exceeds the array, a path that fits runs instead.
+  const size_t need = mxfp8::linear_workspace_within(M, N, K, MXFP8_NOALLOC_SCRATCH_BYTES);
   if (need > (size_t)MXFP8_NOALLOC_SCRATCH_BYTES) return MXFP8_E_SCRATCH;
   if (int st = mxfp8::check_device_current()) return st;
   void* ws = scratch_ptr();
   if (ws == nullptr) return MXFP8_E_DEVICE;
   return mxfp8::linear_launch(x_bf16, M, K, ldx, w_packed, s_packed, N, bias_bf16, y_bf16, ldy, ws,
-                              (hipStream_t)stream);
+                              (hipStream_t)stream, MXFP8_NOALLOC_SCRATCH_BYTES);
 }

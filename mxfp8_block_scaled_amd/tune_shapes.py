@@ -12,6 +12,7 @@ under every GEMM path that applies to it:
 
 * the decode kernel (M <= 16, K <= 8192),
 * the mid-M kernel (M <= 128, K <= 8192),
+* the split-K slab kernel (M <= 128, any K),
 * the large-tile GEMM with s = 1 (persistent), 2, 4 or 8 K splits
   ((K / 64) % (4 s) == 0; split counts whose grid exceeds four workgroups
   per CU are not tried).
@@ -35,7 +36,7 @@ BOUNDS = {
     "N": [1024, 2048, 4096, 8192, 16384, 32768],
     "K": [1024, 2048, 4096, 8192, 16384],
 }
-PATH_CODE = {"tile": 0, "decode": 1, "mid": 2}
+PATH_CODE = {"tile": 0, "decode": 1, "mid": 2, "slab": 3}
 SKINNY_MAX_M, MID_MAX_M, SMALL_K = 16, 128, 8192
 INC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", "shape_table.inc")
 
@@ -52,6 +53,8 @@ def candidates(M, N, K, cus=256):
         out.append(("decode", 4))
     if M <= MID_MAX_M and K <= SMALL_K:
         out.append(("mid", 3))
+    if M <= MID_MAX_M:
+        out.append(("slab", 5))
     tiles = ((M + 255) // 256) * ((N + 255) // 256)
     for s in (1, 2, 4, 8):
         if splits_ok(K, s) and (s == 1 or tiles * s <= 4 * cus):
@@ -88,7 +91,7 @@ def write_inc(plan, tile_splits, source, path=INC):
 // >= its size on each axis (the last bucket takes everything larger).
 // kShapeTabPlan: path << 4 | K splits of the fastest candidate measured at the
 // bucket's upper corner (path 0 large-tile GEMM, 1 decode kernel, 2 mid-M
-// kernel); kShapeTabTileSplits: K splits of the fastest large-tile candidate.
+// kernel, 3 split-K slab kernel); kShapeTabTileSplits: K splits of the fastest large-tile candidate.
 #pragma once
 #include <cstdint>
 
@@ -214,7 +217,7 @@ def measure(out_csv):
     device = f"{torch.cuda.get_device_name(dev)}, {getattr(props, 'gcnArchName', '?').split(':')[0]}"
     date = datetime.date.today().isoformat()
     if out_csv:
-        names = ["decode", "mid", "tile1", "tile2", "tile4", "tile8"]
+        names = ["decode", "mid", "slab", "tile1", "tile2", "tile4", "tile8"]
         os.makedirs(os.path.dirname(os.path.abspath(out_csv)), exist_ok=True)
         with open(out_csv, "w") as f:
             f.write(f"# mxfp8_linear per GEMM path, microseconds per call ({device}, {cus} CUs, {date})\n")

@@ -128,6 +128,13 @@ def _expected_ws(M, N, K):
         return 256
     if path == 2:
         return 128 * K + 128 * (K // 32)
+    if path == 3:
+        # the slab kernel's fp32 partials: one [M, N_pad] per K slice; a slice
+        # is 2 spw 128-K steps, spw the largest of 4, 2 that still leaves
+        # >= 256 workgroups (N_pad / 128 per slice), else 1
+        G, KS = (N + 127) // 128, K // 128
+        spw = next((v for v in (4, 2) if KS % (2 * v) == 0 and G * (KS // (2 * v)) >= 256), 1)
+        return _round_up((KS // (2 * spw)) * M * G * 128 * 4, 256)
     mp = (M + 127) // 128 * 128
     act = _round_up(mp * K, 256) + _round_up(mp * (K // 32), 256)
     part = s * M * ((N + 3) // 4 * 4) * 4 if s > 1 else 0
@@ -141,7 +148,7 @@ def test_linear_paths_workspace():
     for M, N, K in [(1, 4096, 4096), (16, 4096, 4096), (17, 4096, 4096), (128, 4096, 4096), (129, 4096, 4096),
                     (8, 4096, 8448), (300, 700, 2048), (4096, 4096, 1024), (64, 256, 512)]:
         assert ws(M, N, K) == _expected_ws(M, N, K), (M, N, K)
-    assert api.mxfp8_debug_plan(8, 4096, 8448)[0] == 0              # K > 8192: tile path
+    assert api.mxfp8_debug_plan(8, 4096, 8448)[0] in (0, 3)         # K > 8192: tile or slab
     prev = api.mxfp8_debug_force_path(1)
     try:
         assert api.mxfp8_debug_plan(64, 4096, 4096)[0] == 0
@@ -154,13 +161,22 @@ def test_linear_paths_workspace():
         assert api.mxfp8_debug_plan(16, 4096, 4096) == (1, 1)
         assert ws(16, 4096, 4096) == 256
         assert api.mxfp8_debug_plan(17, 4096, 4096)[0] != 1         # decode kernel only to M = 16
+        api.mxfp8_debug_force_path(5)
+        for M, N, K in [(1, 256, 256), (128, 4096, 4096), (33, 4096, 8192), (100, 384, 8192), (113, 200, 6144)]:
+            assert api.mxfp8_debug_plan(M, N, K) == (3, 1), (M, N, K)
+            assert ws(M, N, K) == _expected_ws(M, N, K), (M, N, K)
+        assert ws(128, 4096, 4096) == 8 * 128 * 4096 * 4              # 8 slices of 512 K
+        assert ws(33, 4096, 8192) == 8 * 33 * 4096 * 4                # 8 slices of 1024 K
+        assert api.mxfp8_debug_plan(129, 4096, 4096)[0] == 0        # above 128: the tile path
+        assert api.mxfp8_debug_plan(64, 4096, 8448) == (3, 1)        # any K
+        assert ws(64, 4096, 8448) == _expected_ws(64, 4096, 8448)
         for sp in (1, 2, 4, 8):
             api.mxfp8_debug_force_path(16 + sp)
             assert api.mxfp8_debug_plan(300, 700, 2048) == (0, sp)   # K / 64 = 32 takes every split count
             assert ws(300, 700, 2048) == _expected_ws(300, 700, 2048)
         api.mxfp8_debug_force_path(24)
         assert api.mxfp8_debug_plan(300, 700, 1280) == (0, 1)       # 20 steps: 8 slices do not divide
-        for bad in (-1, 5, 16, 19, 25, 40):
+        for bad in (-1, 6, 16, 19, 25, 40):
             assert api.mxfp8_debug_force_path(bad) == -2
     finally:
         api.mxfp8_debug_force_path(prev)
@@ -175,9 +191,14 @@ def test_linear_paths_workspace():
     bad = list(ok); bad[11] = need - 1; assert f(*bad) == -5
     bad = list(ok); bad[10] = P + 128; assert f(*bad) == -3       # workspace 256-byte alignment
     g = api.mxfp8_linear_w4a8
-    if api.mxfp8_debug_plan(64, 256, 512)[0] != 0:
+    path = api.mxfp8_debug_plan(64, 256, 512)[0]
+    if path in (1, 2):
         assert api.mxfp8_linear_w4a8_workspace_bytes(64, 256, 512) == need   # no widened weight on this path
+    if path == 3:   # no 4-bit slab kernel: W4A8 takes the mid-M kernel (one packed 128-row group)
+        assert api.mxfp8_linear_w4a8_workspace_bytes(64, 256, 512) == 128 * 512 + 128 * 16
     expect_no_device(g, *ok)
+    ok4 = list(ok); ok4[11] = api.mxfp8_linear_w4a8_workspace_bytes(64, 256, 512)
+    expect_no_device(g, *ok4)
 
 
 def _shape_table():
@@ -200,15 +221,16 @@ def _shape_table():
 def test_shape_table_well_formed_and_dispatched():
     """Every table entry names a path and a split count; the library's plan
     is the table's entry for the shape's bucket, limited by what each kernel
-    takes (decode M <= 16 and mid-M M <= 128, both K <= 8192; s splits need
-    (K/64) % (4s) == 0), checked over random shapes."""
+    takes (decode M <= 16 and mid-M M <= 128, both K <= 8192; the slab
+    kernel M <= 128; s splits need (K/64) % (4s) == 0), checked over random
+    shapes."""
     bounds, plan, tsplit = _shape_table()
     for ax in "MNK":
         assert bounds[ax] == sorted(bounds[ax]) and len(set(bounds[ax])) == len(bounds[ax])
     for i, row in enumerate(plan):
         for j, col in enumerate(row):
             for k, code in enumerate(col):
-                assert code >> 4 in (0, 1, 2) and (code & 15) in (1, 2, 4, 8)
+                assert code >> 4 in (0, 1, 2, 3) and (code & 15) in (1, 2, 4, 8)
                 assert tsplit[i][j][k] in (1, 2, 4, 8)
 
     def bucket(ax, v):
@@ -227,6 +249,8 @@ def test_shape_table_well_formed_and_dispatched():
         if path == 1 and not (M <= 16 and K <= 8192):
             path = 0
         if path == 2 and not (M <= 128 and K <= 8192):
+            path = 0
+        if path == 3 and M > 128:
             path = 0
         if s != 1 and (K // 64) % (4 * s) != 0:
             s = 1

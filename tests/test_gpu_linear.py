@@ -114,6 +114,24 @@ def test_mid_path(M, N, K):
     assert st["over_bound"] == 0
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 256, 256), (5, 130, 512), (17, 1, 256), (48, 255, 768), (64, 130, 1024),
+                                   (80, 384, 2048), (90, 255, 512), (100, 384, 8192), (128, 4096, 4096),
+                                   (113, 200, 6144), (33, 4096, 8192), (127, 1000, 2048), (9, 1024, 16384),
+                                   (128, 512, 10240)])
+def test_slab_path(M, N, K):
+    """The split-K slab kernel (path 5 forces it): 1, 2 and 4 K steps per
+    wave (4 at N = 4096, K = 8192; 2 at N = K = 4096 and at N = 1024,
+    K = 16384; 1 where fewer than 256 workgroups would result), 1..8 row
+    groups with a ragged last one, one K slice (K = 256) up to 40, K above
+    the other small-M kernels' limit, ragged N, bias on and off."""
+    g = torch.Generator().manual_seed(M * 37 + N + K)
+    x = synth.scale_stress(synth.randn_bf16((M, K), 1.0, g), seed=M + 7)
+    w = synth.scale_stress(synth.randn_bf16((N, K), 0.02, g), seed=N + 8)
+    b = synth.randn_bf16((N,), 0.1, g) if M % 2 == 0 else None
+    st = gpu_util.run_linear_and_check(x, w, b, f"slab {M}x{N}x{K}", force_path=5)
+    assert st["over_bound"] == 0
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 130, 8192), (7, 384, 6144), (16, 255, 8192), (4, 256, 8448)])
 def test_decode_large_k(M, N, K):
     """The decode kernel with four K steps per wave (K = 6144: one of them
