@@ -168,10 +168,9 @@ int mxfp8_linear_noalloc(const void* x_bf16, int64_t M, int64_t K, int64_t ldx,
  *   and tooling: writes the full padded operand w_e2m1 [N_pad, K/2] bytes
  *   (contiguous, 16-byte aligned; pad rows zero) and w_s_e8m0 [N_pad, K/32]
  *   (contiguous; pad rows byte 127).  Same size rules as the pack.
- * mxfp8_linear_w4a8_workspace_bytes: host-only.  M <= 128 (K <= 8192): at
- *   most one packed 128-row group of activations (the decode or mid-M
- *   kernel: W4A8 has no slab kernel); otherwise the tile path's workspace
- *   (as mxfp8_linear's), plus N_pad * K bytes where the table splits K: the
+ * mxfp8_linear_w4a8_workspace_bytes: host-only.  As mxfp8_linear's on the
+ *   decode, mid-M and slab kernels (each has a 4-bit form); on the tile
+ *   path, mxfp8_linear's plus N_pad * K bytes where the table splits K: the
  *   weight is then widened (exactly: every E2M1 value is an E4M3 value) to
  *   the MXFP8 tiles for the split-K tile GEMM.
  * mxfp8_linear_w4a8: y[m, n] = bf16( sum_k deq(q(x))[m, k] * deq4(W)[n, k]
@@ -323,17 +322,16 @@ int mxfp8_moe_debug_capture(void* act_bf16, void* act_e4m3, void* act_e8m0, void
  * Test hook: force the GEMM path of mxfp8_linear and mxfp8_linear_w4a8.
  * 0 or 2 = automatic: the path and the tile GEMM's K splits come from the
  * shape table measured on MI355X (shape_table.inc, written by
- * mxfp8_block_scaled_amd/tune_shapes.py), within each kernel's limits (decode
- * kernel M <= 16 and K <= 8192, mid-M kernel M <= 128 and K <= 8192, split-K
- * slab kernel M <= 128 and MXFP8 weights only -- mxfp8_linear_w4a8 runs the
- * mid-M kernel, or above K = 8192 the tile GEMM, where the table names it --,
- * K splits s need (K/64) % (4s) == 0); 1 = large-tile path with the table's
- * splits; 3 = mid-M kernel where it applies; 4 = decode kernel where it
- * applies; 5 = split-K slab kernel where it applies; 16 + s (s = 1, 2, 4, 8) = large-tile path with s K splits where they apply
- * (else one).  A forced path that a shape cannot take falls back to the
- * large-tile path; mxfp8_linear_workspace_bytes follows the forced choice.
- * Process-wide; returns the previous value, or MXFP8_E_SHAPE for an unknown
- * value.
+ * mxfp8_block_scaled_amd/tune_shapes.py), within each kernel's limits
+ * (decode kernel M <= 16 and K <= 8192, mid-M kernel M <= 128 and
+ * K <= 8192, split-K slab kernel M <= 128; K splits s need
+ * (K/64) % (4s) == 0); 1 = large-tile path with the table's splits; 3 =
+ * mid-M kernel where it applies; 4 = decode kernel where it applies; 5 =
+ * split-K slab kernel where it applies; 16 + s (s = 1, 2, 4, 8) = large-tile
+ * path with s K splits where they apply (else one).  A forced path that a
+ * shape cannot take falls back to the large-tile path;
+ * mxfp8_linear_workspace_bytes follows the forced choice.  Process-wide;
+ * returns the previous value, or MXFP8_E_SHAPE for an unknown value.
  */
 int mxfp8_debug_force_path(int path);
 

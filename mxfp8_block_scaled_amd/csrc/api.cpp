@@ -121,7 +121,7 @@ size_t moe_layout(int64_t T, int64_t H, int64_t E, int64_t topk, int64_t I, uint
 // GEMM path of a linear call and the K splits of the tile GEMM, from the
 // measured shape table (shape_table.inc): the decode kernel (M <= 16,
 // K <= 8192), the mid-M kernel (M <= 128, K <= 8192), the split-K slab
-// kernel (M <= 128, any K; MXFP8 weights only) or the large-tile GEMM
+// kernel (M <= 128, any K) or the large-tile GEMM
 // with 1 (persistent), 2, 4 or 8 K splits (a split count s needs (K / 64) %
 // (4 s) == 0: each slice a whole number of 128-K step pairs).  A table entry a
 // shape cannot take falls back to the tile GEMM / one split.
@@ -159,7 +159,11 @@ Plan linear_plan(int64_t M, int64_t N, int64_t K) {
   const bool small_k = K <= mxfp8::kSkinnyMaxK;
   if (path == Path::kSkinny && !(small_k && M <= mxfp8::kSkinnyMaxM)) path = Path::kTile;
   if (path == Path::kMid && !(small_k && M <= mxfp8::kMidMaxM)) path = Path::kTile;
-  if (path == Path::kSlab && M > mxfp8::kMidMaxM) path = Path::kTile;
+  // The slab kernel: M <= 128, and its grid (128-row groups x K slices) and
+  // its reduce (one thread per 4 outputs) in 32-bit range.
+  if (path == Path::kSlab &&
+      (M > mxfp8::kMidMaxM || n_pad(N) / 128 * (K / 256) > INT32_MAX || M * (n_pad(N) / 4) > INT32_MAX))
+    path = Path::kTile;
   return {path, s};
 }
 // The path of a call whose workspace may hold at most `cap` bytes: where the
@@ -171,13 +175,8 @@ Path linear_path(int64_t M, int64_t N, int64_t K, size_t cap = SIZE_MAX) {
   if (K <= mxfp8::kSkinnyMaxK) return M <= mxfp8::kSkinnyMaxM ? Path::kSkinny : Path::kMid;
   return Path::kTile;
 }
-// W4A8 has no slab kernel: the mid-M kernel takes its shapes (the tile GEMM
-// above the mid-M kernel's K limit).
-Path linear_path_w4a8(int64_t M, int64_t N, int64_t K) {
-  const Path p = linear_path(M, N, K);
-  if (p != Path::kSlab) return p;
-  return K <= mxfp8::kSkinnyMaxK ? Path::kMid : Path::kTile;
-}
+// W4A8 takes the MXFP8 table's paths (each kernel has a 4-bit form).
+Path linear_path_w4a8(int64_t M, int64_t N, int64_t K) { return linear_path(M, N, K); }
 
 }  // namespace
 
@@ -399,6 +398,7 @@ int mxfp8_linear_w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* b
   switch (linear_path_w4a8(M, N, K)) {
     case Path::kSkinny: *bytes = mxfp8::skinny_ws_bytes(M, K); break;
     case Path::kMid: *bytes = mxfp8::mid_ws_bytes(M, K); break;
+    case Path::kSlab: *bytes = mxfp8::slab_ws_bytes(M, N, K); break;
     default:
       // K splits: the weight widened to MXFP8 tiles after the split-K
       // workspace; one split: the 4-bit tile GEMM, no widened copy.
@@ -432,6 +432,9 @@ int mxfp8_linear_w4a8(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, con
   if (path == Path::kMid)
     return mxfp8::launch_gemm_mid_fp4(x_bf16, ldx, M, K, w_packed, s_packed, N, bias_bf16, y_bf16, ldy, s,
                                       workspace);
+  if (path == Path::kSlab)
+    return mxfp8::launch_gemm_slab_fp4(x_bf16, ldx, M, K, w_packed, s_packed, N, bias_bf16, y_bf16, ldy, s,
+                                       workspace);
   // Larger M is MFMA-bound: the 4-bit tile GEMM on the packed activations;
   // where the shape table splits K, the weight widened to the MXFP8 tiles
   // (exact) and the split-K MXFP8 tile GEMM.

@@ -1,5 +1,6 @@
 // Split-K "slab" MXFP8 linear layer for M <= 128 at any K, with the
-// activation quantization fused in.
+// activation quantization fused in (and its W4A8 form: MXFP4 weights as the
+// MFMA's E2M1 A operand, the same activations).
 //
 // Up to M = 128 the weight is still the dominant HBM stream, but every
 // workgroup of a kernel that owns a few weight rows over the whole K has to
@@ -51,8 +52,9 @@ struct SlabLds {
 };
 
 // x: bf16 [M, K] (row stride ldx elements); wp, sp: the packed weight (G
-// groups of 128 rows); part: fp32 [K / (128 kSK)][M][ldp], ldp = 128 G.
-template <int kSpw, int kMG>
+// groups of 128 rows; kFp4: packed MXFP4, one 1 KiB piece per band and
+// 128-K step); part: fp32 [K / (128 kSK)][M][ldp], ldp = 128 G.
+template <bool kFp4, int kSpw, int kMG>
 __global__ __launch_bounds__(kThreads) void gemm_slab_kernel(const uint16_t* __restrict__ x, int64_t ldx, int M,
                                                              int K, const uint8_t* __restrict__ wp,
                                                              const uint8_t* __restrict__ sp, int G,
@@ -72,7 +74,8 @@ __global__ __launch_bounds__(kThreads) void gemm_slab_kernel(const uint16_t* __r
   const int item = xcd_remap((int)blockIdx.x, (int)gridDim.x);
   const int slice = item / G, grp = item - slice * G;
   const int s0 = slice * L::kSK;               // first 128-K step of the slice
-  const int KT = K / kStepK;                   // packed tiles along K
+  const int KTs = K / kStepK;                          // packed scale tiles along K
+  const int KTw = kFp4 ? K / 128 : K / kStepK;         // packed weight tiles along K
 
   // 1. The slab: rows [0, M), K [128 s0, 128 (s0 + kSK)), chunk c = tid +
   // 1024 j is 16 bytes of row c / kChunksRow.  Rows are a multiple of four
@@ -93,20 +96,26 @@ __global__ __launch_bounds__(kThreads) void gemm_slab_kernel(const uint16_t* __r
 
   // 2. Weight loads: wave (band b, half h) takes steps s0 + h kSpw + u of
   // rows 16 b .. 16 b + 15 of the group: E4M3 pieces 2 ks and 2 ks + 1 of the
-  // band, chunk g of row r (the band is one contiguous run along K); block
-  // 4 ks + g of this lane is block g & 1 of scale tile 2 ks + g / 2.
+  // band, chunk g of row r (the band is one contiguous run along K); E2M1
+  // (kFp4) piece ks, chunk g = K [32g, 32g + 32) of the step.  Block 4 ks + g
+  // of this lane is block g & 1 of scale tile 2 ks + g / 2.
   const int b = wave & 7, h = wave >> 3;
   const int r = 16 * b + i;
-  const uint8_t* wrow = wp + (size_t)grp * KT * kTileBytes + packed_off(r, 0, g, KT);
-  const uint8_t* srow = sp + (size_t)grp * KT * kTileScaleBytes + scale_off(r, g & 1);
+  const uint8_t* wrow = wp + (size_t)grp * KTw * kTileBytes + packed_off(r, 0, g, KTw);
+  const uint8_t* srow = sp + (size_t)grp * KTs * kTileScaleBytes + scale_off(r, g & 1);
   uint4 w0[kSpw], w1[kSpw];
   uint32_t wsd[kSpw];
 #pragma unroll
   for (int u = 0; u < kSpw; ++u) {
     const int ks = s0 + h * kSpw + u;
-    const uint8_t* wt = wrow + (size_t)(2 * ks) * kPieceBytes;
-    w0[u] = *reinterpret_cast<const uint4*>(wt);
-    w1[u] = *reinterpret_cast<const uint4*>(wt + kPieceBytes);
+    if constexpr (kFp4) {
+      w0[u] = *reinterpret_cast<const uint4*>(wrow + (size_t)ks * kPieceBytes);
+      w1[u] = make_uint4(0u, 0u, 0u, 0u);   // an E2M1 operand uses four registers
+    } else {
+      const uint8_t* wt = wrow + (size_t)(2 * ks) * kPieceBytes;
+      w0[u] = *reinterpret_cast<const uint4*>(wt);
+      w1[u] = *reinterpret_cast<const uint4*>(wt + kPieceBytes);
+    }
     wsd[u] = srow[(size_t)(2 * ks + (g >> 1)) * kTileScaleBytes];
   }
   // Every load above this point: the scheduler would otherwise start the
@@ -156,7 +165,9 @@ __global__ __launch_bounds__(kThreads) void gemm_slab_kernel(const uint16_t* __r
       const uint4 b1 = *reinterpret_cast<const uint4*>(p + 64);
       const int xsc = xs[row * L::kScaleRow + sl * 4 + g];
       const v8i xb{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-      acc[mg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wa, xb, acc[mg], 0, 0, 0, (int)wsd[u], 0, xsc);
+      // A format: 0 = E4M3, 4 = E2M1; B (the activations) E4M3.
+      acc[mg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wa, xb, acc[mg], kFp4 ? 4 : 0, 0, 0, (int)wsd[u],
+                                                                 0, xsc);
     }
   }
 
@@ -181,48 +192,61 @@ __global__ __launch_bounds__(kThreads) void gemm_slab_kernel(const uint16_t* __r
 
 namespace {
 
-template <int kSpw, int kMG>
+template <bool kFp4, int kSpw, int kMG>
 int launch_slab_k(const void* x, int64_t ldx, int64_t M, int64_t K, const void* wp, const void* sp, int G,
                   int slices, float* part, int64_t ldp, hipStream_t stream) {
   constexpr int lds = SlabLds<kSpw, kMG>::kBytes;
   static std::atomic<int> lds_set[kMaxDevices];
-  if (!set_lds_limit_once((const void*)gemm_slab_kernel<kSpw, kMG>, lds, lds_set)) return -7;
-  hipLaunchKernelGGL((gemm_slab_kernel<kSpw, kMG>), dim3((unsigned)(G * slices)), dim3(kThreads), lds, stream,
+  if (!set_lds_limit_once((const void*)gemm_slab_kernel<kFp4, kSpw, kMG>, lds, lds_set)) return -7;
+  hipLaunchKernelGGL((gemm_slab_kernel<kFp4, kSpw, kMG>), dim3((unsigned)(G * slices)), dim3(kThreads), lds, stream,
                      (const uint16_t*)x, ldx, (int)M, (int)K, (const uint8_t*)wp, (const uint8_t*)sp, G, part, ldp);
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 
-template <int kSpw>
+template <bool kFp4, int kSpw>
 int launch_slab_s(const void* x, int64_t ldx, int64_t M, int64_t K, const void* wp, const void* sp, int G,
                   int slices, float* part, int64_t ldp, hipStream_t stream) {
   switch ((M + 15) / 16) {
-    case 1: return launch_slab_k<kSpw, 1>(x, ldx, M, K, wp, sp, G, slices, part, ldp, stream);
-    case 2: return launch_slab_k<kSpw, 2>(x, ldx, M, K, wp, sp, G, slices, part, ldp, stream);
-    case 3: return launch_slab_k<kSpw, 3>(x, ldx, M, K, wp, sp, G, slices, part, ldp, stream);
-    case 4: return launch_slab_k<kSpw, 4>(x, ldx, M, K, wp, sp, G, slices, part, ldp, stream);
-    case 5: return launch_slab_k<kSpw, 5>(x, ldx, M, K, wp, sp, G, slices, part, ldp, stream);
-    case 6: return launch_slab_k<kSpw, 6>(x, ldx, M, K, wp, sp, G, slices, part, ldp, stream);
-    case 7: return launch_slab_k<kSpw, 7>(x, ldx, M, K, wp, sp, G, slices, part, ldp, stream);
-    case 8: return launch_slab_k<kSpw, 8>(x, ldx, M, K, wp, sp, G, slices, part, ldp, stream);
+    case 1: return launch_slab_k<kFp4, kSpw, 1>(x, ldx, M, K, wp, sp, G, slices, part, ldp, stream);
+    case 2: return launch_slab_k<kFp4, kSpw, 2>(x, ldx, M, K, wp, sp, G, slices, part, ldp, stream);
+    case 3: return launch_slab_k<kFp4, kSpw, 3>(x, ldx, M, K, wp, sp, G, slices, part, ldp, stream);
+    case 4: return launch_slab_k<kFp4, kSpw, 4>(x, ldx, M, K, wp, sp, G, slices, part, ldp, stream);
+    case 5: return launch_slab_k<kFp4, kSpw, 5>(x, ldx, M, K, wp, sp, G, slices, part, ldp, stream);
+    case 6: return launch_slab_k<kFp4, kSpw, 6>(x, ldx, M, K, wp, sp, G, slices, part, ldp, stream);
+    case 7: return launch_slab_k<kFp4, kSpw, 7>(x, ldx, M, K, wp, sp, G, slices, part, ldp, stream);
+    case 8: return launch_slab_k<kFp4, kSpw, 8>(x, ldx, M, K, wp, sp, G, slices, part, ldp, stream);
     default: return -2;
   }
 }
 
 }  // namespace
 
-int launch_gemm_slab(const void* x, int64_t ldx, int64_t M, int64_t K, const void* wp, const void* sp, int64_t N,
-                     const void* bias, void* y, int64_t ldy, hipStream_t stream, void* ws) {
+namespace {
+template <bool kFp4>
+int launch_slab(const void* x, int64_t ldx, int64_t M, int64_t K, const void* wp, const void* sp, int64_t N,
+                const void* bias, void* y, int64_t ldy, hipStream_t stream, void* ws) {
   const int spw = slab_steps_per_wave(N, K);
   const int G = (int)((N + 127) / 128);
   const int slices = (int)((K / 128) / (2 * spw));
   const int64_t ldp = (int64_t)G * 128;
   float* part = (float*)ws;
   int st = -2;
-  if (spw == 4) st = launch_slab_s<4>(x, ldx, M, K, wp, sp, G, slices, part, ldp, stream);
-  if (spw == 2) st = launch_slab_s<2>(x, ldx, M, K, wp, sp, G, slices, part, ldp, stream);
-  if (spw == 1) st = launch_slab_s<1>(x, ldx, M, K, wp, sp, G, slices, part, ldp, stream);
+  if (spw == 4) st = launch_slab_s<kFp4, 4>(x, ldx, M, K, wp, sp, G, slices, part, ldp, stream);
+  if (spw == 2) st = launch_slab_s<kFp4, 2>(x, ldx, M, K, wp, sp, G, slices, part, ldp, stream);
+  if (spw == 1) st = launch_slab_s<kFp4, 1>(x, ldx, M, K, wp, sp, G, slices, part, ldp, stream);
   if (st) return st;
   return launch_splitk_reduce(part, slices, M, N, ldp, bias, y, ldy, stream);
+}
+}  // namespace
+
+int launch_gemm_slab(const void* x, int64_t ldx, int64_t M, int64_t K, const void* wp, const void* sp, int64_t N,
+                     const void* bias, void* y, int64_t ldy, hipStream_t stream, void* ws) {
+  return launch_slab<false>(x, ldx, M, K, wp, sp, N, bias, y, ldy, stream, ws);
+}
+
+int launch_gemm_slab_fp4(const void* x, int64_t ldx, int64_t M, int64_t K, const void* wp, const void* sp,
+                         int64_t N, const void* bias, void* y, int64_t ldy, hipStream_t stream, void* ws) {
+  return launch_slab<true>(x, ldx, M, K, wp, sp, N, bias, y, ldy, stream, ws);
 }
 
 }  // namespace mxfp8

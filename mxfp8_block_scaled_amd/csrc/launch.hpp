@@ -83,6 +83,9 @@ int slab_steps_per_wave(int64_t N, int64_t K);
 size_t slab_ws_bytes(int64_t M, int64_t N, int64_t K);
 int launch_gemm_slab(const void* x, int64_t ldx, int64_t M, int64_t K, const void* wp, const void* sp, int64_t N,
                      const void* bias, void* y, int64_t ldy, hipStream_t stream, void* ws);
+// The same with a packed MXFP4 weight (launch_pack_weight_fp4).
+int launch_gemm_slab_fp4(const void* x, int64_t ldx, int64_t M, int64_t K, const void* wp, const void* sp,
+                         int64_t N, const void* bias, void* y, int64_t ldy, hipStream_t stream, void* ws);
 
 // Skinny GEMM (M <= kSkinnyMaxM, K <= kSkinnyMaxK) with the activation
 // quantization fused in; it needs no workspace (skinny_ws_bytes is the

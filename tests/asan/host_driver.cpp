@@ -110,6 +110,10 @@ int launch_gemm_slab(const void*, int64_t, int64_t M, int64_t K, const void*, co
   touch_rows(y, M, N, ldy, 2);
   return 0;
 }
+int launch_gemm_slab_fp4(const void* x, int64_t ldx, int64_t M, int64_t K, const void* wp, const void* sp,
+                         int64_t N, const void* b, void* y, int64_t ldy, hipStream_t s, void* ws) {
+  return launch_gemm_slab(x, ldx, M, K, wp, sp, N, b, y, ldy, s, ws);
+}
 int launch_gemm_mid_fp4(const void* x, int64_t ldx, int64_t M, int64_t K, const void* wp, const void* sp, int64_t N,
                         const void* b, void* y, int64_t ldy, hipStream_t s, void* ws) {
   return launch_gemm_mid(x, ldx, M, K, wp, sp, N, b, y, ldy, s, ws);

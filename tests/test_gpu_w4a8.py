@@ -157,7 +157,16 @@ def test_mid_path_parity(M, N, K):
     run_and_check(M, N, K, seed=M + 3 * N, force_path=3)
 
 
-@pytest.mark.parametrize("path", [0, 1])
+@pytest.mark.parametrize("M,N,K", [(5, 256, 512), (40, 384, 768), (128, 4096, 4096), (9, 1024, 16384),
+                                   (100, 200, 10240), (33, 4096, 8192)])
+def test_slab_path_parity(M, N, K):
+    """The split-K slab kernel with the 4-bit weight (path 5 forces it): 1, 2
+    and 4 K steps per wave, 1..8 row groups, K above the decode and mid-M
+    kernels' limit."""
+    run_and_check(M, N, K, seed=M + 7 * N + K, force_path=5)
+
+
+@pytest.mark.parametrize("path", [0, 1, 5])
 def test_scale_stress_both_paths(path):
     run_and_check(13, 256, 512, seed=31, force_path=path, stress=True)
 
@@ -206,10 +215,10 @@ def test_w4a8_matches_mxfp8_on_widened_weight():
     assert torch.equal(y8, y4)
 
 
-@pytest.mark.parametrize("path", [1, 3])
+@pytest.mark.parametrize("path", [1, 3, 5])
 def test_one_hot_weight_exact_forced(path):
-    """The one-hot pin at M = 40 on the widened tile GEMM (path 1) and on the
-    mid-M kernel's 4-bit operand (path 3)."""
+    """The one-hot pin at M = 40 on the widened tile GEMM (path 1), on the
+    mid-M kernel's 4-bit operand (path 3) and on the slab kernel's (path 5)."""
     g = torch.Generator().manual_seed(18)
     M, K, N = 40, 1024, 200
     x = synth.scale_stress(synth.randn_bf16((M, K), 1.0, g), seed=10)
