@@ -19,7 +19,7 @@ N=K=4096 with the weights rotated through 48 copies so they do not sit in the
 quantizer, and one forward of the routed MoE layer at its full size);
 ``ceilings``, what this GPU sustains as measured by the calibration kernels
 of libmxfp8_calib.so (scaled-MFMA rate, 1 GiB HBM read rate, one 16 MiB read
-per launch), with the headline GEMM's fraction of the measured MFMA rate
+per launch, the time per launch of an empty kernel), with the headline GEMM's fraction of the measured MFMA rate
 (``roofline.frac_of_measured``) and each sweep row's fraction of the
 measured read rate; ``cpu_baseline``, the CPU oracle timed on a bounded
 sample of the headline workload.  The untimed warm-up runs at least
@@ -206,6 +206,10 @@ def main():
                 row["pct_of_read_floor"] = round(100 * floor * (4096 * 4096 * (1 + 1 / 32)) / (16 << 20) / row["us"], 1)
             if ceil.get("hbm_read_gbs") and "GB/s" in row:
                 row["pct_of_measured_hbm"] = round(100 * row["GB/s"] / ceil["hbm_read_gbs"], 1)
+            if row.get("workload", "").startswith("single ") and ceil.get("launch_floor_us"):
+                # a one-kernel call against an empty kernel of the same grid
+                row["launch_floor_us"] = ceil["launch_floor_us"]
+                row["x_launch_floor"] = round(row["us"] / ceil["launch_floor_us"], 2)
 
     if args.calib_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -234,8 +238,19 @@ def ceilings(torch, dev, stream):
     vp = ctypes.c_void_p
     lib.mxfp8_calib_read.argtypes = [vp, ctypes.c_uint64, ctypes.c_int, vp, vp]
     lib.mxfp8_calib_mfma.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp]
+    lib.mxfp8_calib_empty.argtypes = [ctypes.c_int, ctypes.c_int, vp]
     sptr = stream.cuda_stream
     out = {}
+    # one launch of an empty kernel, back to back on the stream: the floor
+    # under a one-kernel call (9 x 1024 threads: the M=7, N=130 layer's grid;
+    # 256 x 1024: the decode kernel's at N = 4096)
+    for blocks, key in ((9, "launch_floor_us"), (256, "launch_floor_256wg_us")):
+        for _ in range(50):
+            lib.mxfp8_calib_empty(blocks, 1024, sptr)
+        torch.cuda.synchronize()
+        ms = min(time_calls(lambda r: lib.mxfp8_calib_empty(blocks, 1024, sptr), 500, stream, torch)
+                 for _ in range(3))
+        out[key] = round(ms * 1e3, 3)
     # scaled MFMA: 4096 waves x iters x 8 MFMAs of 2*16*16*128 flops
     blocks, iters = 1024, 1500
     sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)

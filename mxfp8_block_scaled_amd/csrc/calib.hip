@@ -15,6 +15,9 @@
 //    then stores the sum of its accumulators.  Each MFMA is 2 * 16 * 16 * 128
 //    flops; the rate over a grid that fills the chip is the MFMA throughput
 //    the chip sustains at its clock under that load.
+//  * empty kernel: launched back to back on one stream, the time per launch
+//    is the floor under any call that is one kernel launch (dispatch, the
+//    caches' acquire and release around a kernel, the drain).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -64,6 +67,8 @@ __global__ __launch_bounds__(256) void calib_mfma_kernel(int iters, uint32_t see
   out[t] = s;
 }
 
+__global__ void calib_empty_kernel() {}
+
 }  // namespace
 
 extern "C" {
@@ -85,6 +90,13 @@ int mxfp8_calib_mfma(int blocks, int iters, void* out, void* stream) {
   if (!out || blocks < 1 || iters < 1) return -2;
   hipLaunchKernelGGL(calib_mfma_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, iters, 12345u,
                      (float*)out);
+  return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+// One launch of an empty kernel of blocks x threads (threads <= 1024).
+int mxfp8_calib_empty(int blocks, int threads, void* stream) {
+  if (blocks < 1 || threads < 1 || threads > 1024) return -2;
+  hipLaunchKernelGGL(calib_empty_kernel, dim3((unsigned)blocks), dim3((unsigned)threads), 0, (hipStream_t)stream);
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 

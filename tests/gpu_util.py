@@ -77,6 +77,8 @@ def compare(y, r, acc_bound, label=""):
     if err.size:
         rms = np.sqrt(np.mean(r * r))
         stats["max_rel_2e-2_metric"] = float((err / np.maximum(np.abs(r), 2.0 ** -4 * rms + 1e-300)).max())
+        # the same with the floor max(|r|, 1e-3 max|r|) of the survey's reading
+        stats["max_rel_survey_floor"] = float((err / np.maximum(np.abs(r), 1e-3 * np.abs(r).max() + 1e-300)).max())
         stats["max_err_over_bound"] = float((err / bound).max())
     print("PARITY", stats, flush=True)
     assert stats["over_bound"] == 0, (label, stats, np.argwhere(over)[:5])
