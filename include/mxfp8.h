@@ -102,7 +102,8 @@ int mxfp8_unpack_weight(const void* w_packed, const void* s_packed, int64_t N, i
  * Workspace bytes mxfp8_linear needs for this shape (host-only).  On the
  * decode kernel (M <= 16, K <= 8192) nothing is stored there (a 256-byte
  * minimum is still required); on the split-K slab kernel (M <= 128) it holds
- * fp32 partial outputs, one [M, N_pad] per K slice; otherwise the activations
+ * fp32 partial outputs, one [M, N_pad] per K slice; otherwise (the
+ * mid-M, medium-tile and large-tile GEMMs) the activations
  * quantized into the packed layout (M padded to 128 rows, plus their scales;
  * for M > 128 also the fp32 split-K partials when the shape has few tiles).
  * Which kernel a shape takes comes from the measured shape table (see
@@ -327,8 +328,10 @@ int mxfp8_moe_debug_capture(void* act_bf16, void* act_e4m3, void* act_e8m0, void
  * K <= 8192, split-K slab kernel M <= 128; K splits s need
  * (K/64) % (4s) == 0); 1 = large-tile path with the table's splits; 3 =
  * mid-M kernel where it applies; 4 = decode kernel where it applies; 5 =
- * split-K slab kernel where it applies; 16 + s (s = 1, 2, 4, 8) = large-tile
- * path with s K splits where they apply (else one).  A forced path that a
+ * split-K slab kernel where it applies; 6 / 7 = medium-tile GEMM with
+ * 128 x 128 / 128 x 64 tiles (MXFP8 only: mxfp8_linear_w4a8 takes the
+ * large-tile path there); 16 + s (s = 1, 2, 4, 8) = large-tile path with s K
+ * splits where they apply (else one).  A forced path that a
  * shape cannot take falls back to the large-tile path;
  * mxfp8_linear_workspace_bytes follows the forced choice.  Process-wide;
  * returns the previous value, or MXFP8_E_SHAPE for an unknown value.
@@ -338,7 +341,8 @@ int mxfp8_debug_force_path(int path);
 /*
  * Test hook (host only): the plan mxfp8_linear takes for an M x N x K call
  * under the current forcing: *path = 0 large-tile GEMM, 1 decode kernel,
- * 2 mid-M kernel, 3 split-K slab kernel; *splits = the tile GEMM's K splits (1 for the other paths).
+ * 2 mid-M kernel, 3 split-K slab kernel, 4 / 5 medium-tile GEMM with
+ * 128 / 64 activation rows per tile; *splits = the tile GEMM's K splits (1 for the other paths).
  * MXFP8_E_SHAPE for M < 1, N < 1 or K not a positive multiple of 256.
  */
 int mxfp8_debug_plan(int64_t M, int64_t N, int64_t K, int* path, int* splits);

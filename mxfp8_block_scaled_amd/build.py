@@ -25,7 +25,7 @@ CALIB_LIB = os.path.join(PKG, "libmxfp8_calib.so")
 CALIB_SOURCES = ["calib.hip"]
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "quant.hip", "pack.hip", "gemm_tile.hip", "gemm_skinny.hip", "gemm_mid.hip", "gemm_slab.hip", "moe.hip", "noalloc.hip"]
+SOURCES = ["api.cpp", "quant.hip", "pack.hip", "gemm_tile.hip", "gemm_skinny.hip", "gemm_mid.hip", "gemm_slab.hip", "gemm_med.hip", "moe.hip", "noalloc.hip"]
 
 # -packed-fp32-ops: hipcc must not form v_pk_{add,mul,fma}_f32 (the host pass
 # warns that it does not know the feature; that is harmless).

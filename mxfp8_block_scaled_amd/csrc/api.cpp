@@ -121,12 +121,13 @@ size_t moe_layout(int64_t T, int64_t H, int64_t E, int64_t topk, int64_t I, uint
 // GEMM path of a linear call and the K splits of the tile GEMM, from the
 // measured shape table (shape_table.inc): the decode kernel (M <= 16,
 // K <= 8192), the mid-M kernel (M <= 128, K <= 8192), the split-K slab
-// kernel (M <= 128, any K) or the large-tile GEMM
+// kernel (M <= 128, any K), the medium-tile GEMM (128 x 128 or 128 x 64
+// tiles over the whole K) or the large-tile GEMM
 // with 1 (persistent), 2, 4 or 8 K splits (a split count s needs (K / 64) %
 // (4 s) == 0: each slice a whole number of 128-K step pairs).  A table entry a
 // shape cannot take falls back to the tile GEMM / one split.
 // mxfp8_debug_force_path can pin the path and the splits.
-enum class Path { kTile = 0, kSkinny = 1, kMid = 2, kSlab = 3 };
+enum class Path { kTile = 0, kSkinny = 1, kMid = 2, kSlab = 3, kMed = 4, kMed64 = 5 };
 struct Plan {
   Path path;
   int splits;   // K splits of the tile GEMM (also when the path is not the tile)
@@ -152,6 +153,8 @@ Plan linear_plan(int64_t M, int64_t N, int64_t K) {
   if (force == 3) path = Path::kMid;
   if (force == 4) path = Path::kSkinny;
   if (force == 5) path = Path::kSlab;
+  if (force == 6) path = Path::kMed;
+  if (force == 7) path = Path::kMed64;
   if (force >= 16) {
     path = Path::kTile;
     if (splits_ok(K, force - 16)) s = force - 16;
@@ -161,6 +164,9 @@ Plan linear_plan(int64_t M, int64_t N, int64_t K) {
   if (path == Path::kMid && !(small_k && M <= mxfp8::kMidMaxM)) path = Path::kTile;
   // The slab kernel: M <= 128, and its grid (128-row groups x K slices) and
   // its reduce (one thread per 4 outputs) in 32-bit range.
+  // The medium-tile GEMM: one workgroup per (128-row weight group, tile).
+  if ((path == Path::kMed || path == Path::kMed64) && n_pad(N) / 128 * ((M + 63) / 64) > INT32_MAX)
+    path = Path::kTile;
   if (path == Path::kSlab &&
       (M > mxfp8::kMidMaxM || n_pad(N) / 128 * (K / 256) > INT32_MAX || M * (n_pad(N) / 4) > INT32_MAX))
     path = Path::kTile;
@@ -175,8 +181,14 @@ Path linear_path(int64_t M, int64_t N, int64_t K, size_t cap = SIZE_MAX) {
   if (K <= mxfp8::kSkinnyMaxK) return M <= mxfp8::kSkinnyMaxM ? Path::kSkinny : Path::kMid;
   return Path::kTile;
 }
-// W4A8 takes the MXFP8 table's paths (each kernel has a 4-bit form).
-Path linear_path_w4a8(int64_t M, int64_t N, int64_t K) { return linear_path(M, N, K); }
+// W4A8 takes the MXFP8 table's paths; the medium-tile GEMM has no 4-bit
+// form, so its shapes take the tile path.
+Path linear_path_w4a8(int64_t M, int64_t N, int64_t K) {
+  const Path p = linear_path(M, N, K);
+  return (p == Path::kMed || p == Path::kMed64) ? Path::kTile : p;
+}
+// The paths whose workspace and launch are the packed quantizer's.
+bool packed_path(Path p) { return p == Path::kTile || p == Path::kMed || p == Path::kMed64; }
 
 }  // namespace
 
@@ -224,7 +236,7 @@ int mxfp8::linear_check_args(const void* x_bf16, int64_t M, int64_t K, int64_t l
   if (int st = check_output(y_bf16, N, ldy, bias_bf16)) return st;
   if (ldx < K || ldx % 8 != 0) return MXFP8_E_LD;
   if (!aligned(x_bf16, 16)) return MXFP8_E_ALIGN;
-  if (linear_path(M, N, K) == Path::kTile && (n_pad(M) * (K / 8) + 255) / 256 > INT32_MAX) return MXFP8_E_SHAPE;
+  if (packed_path(linear_path(M, N, K)) && (n_pad(M) * (K / 8) + 255) / 256 > INT32_MAX) return MXFP8_E_SHAPE;
   return MXFP8_OK;
 }
 
@@ -234,6 +246,8 @@ size_t mxfp8::linear_workspace_within(int64_t M, int64_t N, int64_t K, size_t ca
     case Path::kSkinny: return mxfp8::skinny_ws_bytes(M, K);
     case Path::kMid: return mxfp8::mid_ws_bytes(M, K);
     case Path::kSlab: return mxfp8::slab_ws_bytes(M, N, K);
+    case Path::kMed:
+    case Path::kMed64: return tile_ws_act_bytes(M, K);
     default: return tile_ws_bytes(M, N, K);
   }
 }
@@ -253,6 +267,9 @@ int mxfp8::linear_launch(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, 
   uint8_t* sc = q + round_up((size_t)n_pad(M) * (size_t)K, 256);
   uint8_t* part = q + tile_ws_act_bytes(M, K);
   if (int st = mxfp8::launch_quantize_act_packed(x_bf16, M, K, ldx, q, sc, s)) return st;
+  if (path == Path::kMed || path == Path::kMed64)
+    return mxfp8::launch_gemm_med(q, sc, M, K, w_packed, s_packed, N, bias_bf16, y_bf16, ldy, s,
+                                  path == Path::kMed ? 128 : 64);
   return mxfp8::launch_gemm_tile(q, sc, M, K, w_packed, s_packed, N, bias_bf16, y_bf16, ldy, s,
                                  mxfp8::gemm_tile_splits(M, N, K), part);
 }
@@ -608,7 +625,7 @@ int mxfp8_moe_debug_capture(void* act_bf16, void* act_e4m3, void* act_e8m0, void
 
 int mxfp8_debug_force_path(int path) {
   const bool tile_splits = path == 17 || path == 18 || path == 20 || path == 24;
-  if (!(path >= 0 && path <= 5) && !tile_splits) return MXFP8_E_SHAPE;
+  if (!(path >= 0 && path <= 7) && !tile_splits) return MXFP8_E_SHAPE;
   return g_force_path.exchange(path);
 }
 

@@ -74,6 +74,11 @@ int launch_gemm_tile_w4(const void* qp, const void* sp, int64_t M, int64_t K, co
 int launch_splitk_reduce(const float* part, int splits, int64_t M, int64_t N, int64_t ldp, const void* bias,
                          void* y, int64_t ldy, hipStream_t stream);
 
+// Medium-tile GEMM on packed activations: one 128-row weight group x mt
+// (128 or 64) activation rows per workgroup over the whole K (gemm_med.hip).
+int launch_gemm_med(const void* qp, const void* sp, int64_t M, int64_t K, const void* wp, const void* wsp, int64_t N,
+                    const void* bias, void* y, int64_t ldy, hipStream_t stream, int mt);
+
 // Split-K slab GEMM (M <= kMidMaxM, any K) with the activation
 // quantization fused in (gemm_slab.hip): each workgroup multiplies one
 // 128-row weight group by one K slice of 2 * slab_steps_per_wave 128-K steps

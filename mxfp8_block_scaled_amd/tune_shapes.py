@@ -13,6 +13,8 @@ under every GEMM path that applies to it:
 * the decode kernel (M <= 16, K <= 8192),
 * the mid-M kernel (M <= 128, K <= 8192),
 * the split-K slab kernel (M <= 128, any K),
+* the medium-tile GEMM, 128 x 128 and 128 x 64 tiles over the whole K
+  (shapes with at most 4096 such tiles),
 * the large-tile GEMM with s = 1 (persistent), 2, 4 or 8 K splits
   ((K / 64) % (4 s) == 0; split counts whose grid exceeds four workgroups
   per CU are not tried).
@@ -36,7 +38,7 @@ BOUNDS = {
     "N": [1024, 2048, 4096, 8192, 16384, 32768],
     "K": [1024, 2048, 4096, 8192, 16384],
 }
-PATH_CODE = {"tile": 0, "decode": 1, "mid": 2, "slab": 3}
+PATH_CODE = {"tile": 0, "decode": 1, "mid": 2, "slab": 3, "med128": 4, "med64": 5}
 SKINNY_MAX_M, MID_MAX_M, SMALL_K = 16, 128, 8192
 INC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", "shape_table.inc")
 
@@ -55,6 +57,11 @@ def candidates(M, N, K, cus=256):
         out.append(("mid", 3))
     if M <= MID_MAX_M:
         out.append(("slab", 5))
+    groups = (N + 127) // 128
+    if groups * ((M + 127) // 128) <= 4096:
+        out.append(("med128", 6))
+    if groups * ((M + 63) // 64) <= 4096:
+        out.append(("med64", 7))
     tiles = ((M + 255) // 256) * ((N + 255) // 256)
     for s in (1, 2, 4, 8):
         if splits_ok(K, s) and (s == 1 or tiles * s <= 4 * cus):
@@ -91,7 +98,8 @@ def write_inc(plan, tile_splits, source, path=INC):
 // >= its size on each axis (the last bucket takes everything larger).
 // kShapeTabPlan: path << 4 | K splits of the fastest candidate measured at the
 // bucket's upper corner (path 0 large-tile GEMM, 1 decode kernel, 2 mid-M
-// kernel, 3 split-K slab kernel); kShapeTabTileSplits: K splits of the fastest large-tile candidate.
+// kernel, 3 split-K slab kernel, 4 / 5 medium-tile GEMM with 128 / 64
+// activation rows per tile); kShapeTabTileSplits: K splits of the fastest large-tile candidate.
 #pragma once
 #include <cstdint>
 
@@ -217,7 +225,7 @@ def measure(out_csv):
     device = f"{torch.cuda.get_device_name(dev)}, {getattr(props, 'gcnArchName', '?').split(':')[0]}"
     date = datetime.date.today().isoformat()
     if out_csv:
-        names = ["decode", "mid", "slab", "tile1", "tile2", "tile4", "tile8"]
+        names = ["decode", "mid", "slab", "med128", "med64", "tile1", "tile2", "tile4", "tile8"]
         os.makedirs(os.path.dirname(os.path.abspath(out_csv)), exist_ok=True)
         with open(out_csv, "w") as f:
             f.write(f"# mxfp8_linear per GEMM path, microseconds per call ({device}, {cus} CUs, {date})\n")

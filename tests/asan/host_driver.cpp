@@ -102,6 +102,11 @@ int launch_gemm_mid(const void*, int64_t, int64_t M, int64_t K, const void*, con
   touch_rows(y, M, N, ldy, 2);
   return 0;
 }
+int launch_gemm_med(const void*, const void*, int64_t M, int64_t, const void*, const void*, int64_t N, const void*,
+                    void* y, int64_t ldy, hipStream_t, int) {
+  touch_rows(y, M, N, ldy, 2);
+  return 0;
+}
 int launch_gemm_slab(const void*, int64_t, int64_t M, int64_t K, const void*, const void*, int64_t N, const void*,
                      void* y, int64_t ldy, hipStream_t, void* ws) {
   // one fp32 partial [M, N_pad] per K slice, then the reduce's bf16 rows
@@ -234,7 +239,7 @@ int main() {
   for (const auto& s : shapes)
     for (int fp4 = 0; fp4 < 2; ++fp4)
       for (int64_t extra : {0, 24}) linear_case(s[0], s[1], s[2], extra, fp4 != 0);
-  for (int path : {1, 3, 5})   // forced paths
+  for (int path : {1, 3, 5, 6, 7})   // forced paths
   {
     const int prev = mxfp8_debug_force_path(path);
     linear_case(9, 384, 1024, 8, false);

@@ -137,6 +137,8 @@ def _expected_ws(M, N, K):
         return _round_up((KS // (2 * spw)) * M * G * 128 * 4, 256)
     mp = (M + 127) // 128 * 128
     act = _round_up(mp * K, 256) + _round_up(mp * (K // 32), 256)
+    if path in (4, 5):   # the medium-tile GEMM: the packed activations only
+        return act
     part = s * M * ((N + 3) // 4 * 4) * 4 if s > 1 else 0
     return act + _round_up(part, 256)
 
@@ -176,7 +178,13 @@ def test_linear_paths_workspace():
             assert ws(300, 700, 2048) == _expected_ws(300, 700, 2048)
         api.mxfp8_debug_force_path(24)
         assert api.mxfp8_debug_plan(300, 700, 1280) == (0, 1)       # 20 steps: 8 slices do not divide
-        for bad in (-1, 6, 16, 19, 25, 40):
+        api.mxfp8_debug_force_path(6)
+        assert api.mxfp8_debug_plan(1024, 4096, 4096) == (4, 1)
+        assert ws(1024, 4096, 4096) == _expected_ws(1024, 4096, 4096) == 1024 * 4096 + 1024 * 128
+        api.mxfp8_debug_force_path(7)
+        assert api.mxfp8_debug_plan(300, 700, 2048) == (5, 1)
+        assert ws(300, 700, 2048) == _expected_ws(300, 700, 2048)
+        for bad in (-1, 8, 16, 19, 25, 40):
             assert api.mxfp8_debug_force_path(bad) == -2
     finally:
         api.mxfp8_debug_force_path(prev)
@@ -226,7 +234,7 @@ def test_shape_table_well_formed_and_dispatched():
     for i, row in enumerate(plan):
         for j, col in enumerate(row):
             for k, code in enumerate(col):
-                assert code >> 4 in (0, 1, 2, 3) and (code & 15) in (1, 2, 4, 8)
+                assert code >> 4 in (0, 1, 2, 3, 4, 5) and (code & 15) in (1, 2, 4, 8)
                 assert tsplit[i][j][k] in (1, 2, 4, 8)
 
     def bucket(ax, v):
@@ -273,7 +281,8 @@ def test_packed_entries_validation():
 def test_force_path_hook():
     prev = api.mxfp8_debug_force_path(1)
     assert api.mxfp8_debug_force_path(prev) == 1
-    assert api.mxfp8_debug_force_path(7) == -2
+    assert api.mxfp8_debug_force_path(9) == -2                        # unknown: refused, nothing changed
+    assert api.mxfp8_debug_force_path(prev) == prev
 
 
 def test_moe_sizes():

@@ -29,11 +29,12 @@ def test_prepare_unpack_roundtrip():
         assert bool((w2[N:] == 0).all()) and bool((s2[N:] == 127).all())
 
 
-@pytest.mark.parametrize("path", [1, 2])
+@pytest.mark.parametrize("path", [1, 2, 6, 7])
 def test_one_hot_weight_exact(path):
     """W[n, perm[n]] = 1: y[m, n] = bf16(deq(A)[m, perm[n]]) exactly (a single
     nonzero term per output).  Pins the MFMA operand/scale lane mapping, the K
-    and N indexing, padding and zero-scale blocks, on both GEMM paths."""
+    and N indexing, padding and zero-scale blocks, on the tile GEMM, the
+    automatic path at M = 9 and the medium-tile GEMM's two tile heights."""
     M = 9 if path == 2 else 300
     g = torch.Generator().manual_seed(4)
     K, N = 512, 200
@@ -53,7 +54,7 @@ def test_one_hot_weight_exact(path):
     assert np.array_equal(y, exp)
 
 
-@pytest.mark.parametrize("path", [1, 2])
+@pytest.mark.parametrize("path", [1, 2, 6, 7])
 def test_one_hot_activation_exact(path):
     """x[m, perm[m]] = 1 (scale-stressed weight): y[m, n] = bf16(deq(W)[n, perm[m]] + bias[n])."""
     M = 11 if path == 2 else 260
@@ -129,6 +130,21 @@ def test_slab_path(M, N, K):
     w = synth.scale_stress(synth.randn_bf16((N, K), 0.02, g), seed=N + 8)
     b = synth.randn_bf16((N,), 0.1, g) if M % 2 == 0 else None
     st = gpu_util.run_linear_and_check(x, w, b, f"slab {M}x{N}x{K}", force_path=5)
+    assert st["over_bound"] == 0
+
+
+@pytest.mark.parametrize("force", [6, 7])
+@pytest.mark.parametrize("M,N,K", [(1, 130, 256), (17, 1, 512), (64, 384, 768), (100, 255, 1024), (129, 130, 2048),
+                                   (200, 1000, 256), (300, 640, 4096), (513, 384, 1024), (1024, 520, 8448)])
+def test_med_path(M, N, K, force):
+    """The medium-tile GEMM (path 6: 128 x 128 tiles, 7: 128 x 64): one and
+    many tiles along M and N, ragged last tiles in both, K from one 128-K
+    step pair to 66 steps, bias on and off."""
+    g = torch.Generator().manual_seed(M * 13 + N + K + force)
+    x = synth.scale_stress(synth.randn_bf16((M, K), 1.0, g), seed=M + 3)
+    w = synth.scale_stress(synth.randn_bf16((N, K), 0.02, g), seed=N + 4)
+    b = synth.randn_bf16((N,), 0.1, g) if (M + N) % 2 else None
+    st = gpu_util.run_linear_and_check(x, w, b, f"med{force} {M}x{N}x{K}", force_path=force)
     assert st["over_bound"] == 0
 
 
