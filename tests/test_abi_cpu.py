@@ -350,8 +350,23 @@ def test_w4a8_sizes_and_validation():
     assert api.mxfp8_linear_w4a8_workspace_bytes(7, 4096, 4096) == api.mxfp8_linear_workspace_bytes(7, 4096, 4096)
     assert api.mxfp8_linear_w4a8_workspace_bytes(16, 4096, 4096) == api.mxfp8_linear_workspace_bytes(16, 4096, 4096)
     assert api.mxfp8_linear_workspace_bytes(16, 4096, 8192) == _expected_ws(16, 4096, 8192)
+    bounds, _, tsplit = _shape_table()
+
+    def bucket(ax, v):
+        return next((i for i, b in enumerate(bounds[ax]) if v <= b), len(bounds[ax]) - 1)
+
     for M, N, K in [(512, 130, 256), (300, 700, 2048), (4096, 4096, 4096), (256, 4096, 4096)]:
         path, sp = api.mxfp8_debug_plan(M, N, K)
+        if path in (4, 5):
+            # no 4-bit medium-tile GEMM: the tile path with the table's K splits
+            sp = tsplit[bucket("M", M)][bucket("N", N)][bucket("K", K)]
+            sp = sp if (K // 64) % (4 * sp) == 0 else 1
+            mp = (M + 127) // 128 * 128
+            act = _round_up(mp * K, 256) + _round_up(mp * (K // 32), 256)
+            tile = act + (_round_up(sp * M * ((N + 3) // 4 * 4) * 4, 256) if sp > 1 else 0)
+            extra = (N + 127) // 128 * 128 * K if sp > 1 else 0
+            assert api.mxfp8_linear_w4a8_workspace_bytes(M, N, K) == tile + extra, (M, N, K)
+            continue
         extra = (N + 127) // 128 * 128 * K if path == 0 and sp > 1 else 0
         assert api.mxfp8_linear_w4a8_workspace_bytes(M, N, K) == api.mxfp8_linear_workspace_bytes(M, N, K) + extra
     prev = api.mxfp8_debug_force_path(18)          # tile GEMM, 2 K splits: the widened route
