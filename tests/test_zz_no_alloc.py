@@ -42,6 +42,8 @@ def _call_both(x, pw, bias, N, force_ref=0, force_new=0):
     ("decode", (16, 3), 4096, 4096, 0),
     ("mid-M", (128, 40), 4096, 4096, 0),
     ("slab", (64, 17), 4096, 8192, 5),
+    ("medium tile", (1024, 300), 640, 1024, 6),
+    ("medium tile, 64 rows", (513, 200), 384, 2048, 7),
     ("tile", (300, 200), 640, 1024, 0),
     ("tile split-K", (256, 129), 512, 2048, 0),
 ])
