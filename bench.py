@@ -196,6 +196,15 @@ def main():
     out["ceilings"] = ceil
     if ceil.get("mfma_tflops"):
         out["roofline"]["frac_of_measured"] = round(gemm_tflops / ceil["mfma_tflops"], 4)
+    if ceil.get("l2_to_lds_gbs_per_cu"):
+        # The GEMM's operand copies: every 256 x 256 tile copies its 512 rows
+        # of K bytes (plus 1/32 in scales) from L2 into LDS; per CU per second
+        # against what one CU pulls from L2 in the calibration kernel.
+        tiles = ((M + 255) // 256) * ((N + 255) // 256)
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        copy_gbs = tiles * 512 * K * (1 + 1 / 32) / cus / (gemm_ms * 1e-3) / 1e9
+        out["roofline"]["copy_gbs_per_cu"] = round(copy_gbs, 1)
+        out["roofline"]["frac_of_copy_ceiling"] = round(copy_gbs / ceil["l2_to_lds_gbs_per_cu"], 4)
 
     if not args.no_sweep:
         out["sweep"] = sweep(api, synth, torch, np, dev, stream)
@@ -239,6 +248,7 @@ def ceilings(torch, dev, stream):
     lib.mxfp8_calib_read.argtypes = [vp, ctypes.c_uint64, ctypes.c_int, vp, vp]
     lib.mxfp8_calib_mfma.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp]
     lib.mxfp8_calib_empty.argtypes = [ctypes.c_int, ctypes.c_int, vp]
+    lib.mxfp8_calib_l2.argtypes = [vp, ctypes.c_uint32, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp]
     sptr = stream.cuda_stream
     out = {}
     # one launch of an empty kernel, back to back on the stream: the floor
@@ -289,6 +299,21 @@ def ceilings(torch, dev, stream):
         best = ms if best is None else min(best, ms)
     out["read_16mib_us"] = round(best * 1e3, 3)
     del pool
+    # L2 -> CU: one workgroup per CU re-reading one 1 MiB buffer (served by
+    # each die's L2 after the first pass), into registers and by direct
+    # L2 -> LDS copies; GB/s per CU
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    l2buf = torch.zeros(1 << 20, dtype=torch.uint8, device=dev)
+    reps = 100
+    for lds, key in ((0, "l2_to_vgpr_gbs_per_cu"), (1, "l2_to_lds_gbs_per_cu")):
+        for _ in range(2):
+            lib.mxfp8_calib_l2(l2buf.data_ptr(), l2buf.numel(), cus, reps, lds, words.data_ptr(), sptr)
+        torch.cuda.synchronize()
+        ms = min(time_calls(lambda r: lib.mxfp8_calib_l2(l2buf.data_ptr(), l2buf.numel(), cus, reps, lds,
+                                                         words.data_ptr(), sptr), 3, stream, torch)
+                 for _ in range(3))
+        out[key] = round(l2buf.numel() * reps / (ms * 1e-3) / 1e9, 1)
+    del l2buf
     print(f"ceilings: {out}", file=sys.stderr, flush=True)
     return out
 

@@ -4,10 +4,9 @@
 // few thousand at moderate N) and whose split-K partials cost more than they
 // save.
 //
-// On this chip a workgroup pulls its operands from L2 into LDS at about
-// 47 GB/s per CU, whatever the tile (the persistent 256 x 256 GEMM and the
-// mid-M kernel measure the same rate), so a tile's time is its operand bytes,
-// (rows_n + rows_m) * K, over that rate.  At M = 1024, N = K = 4096 the
+// The tile GEMMs here copy their operands from L2 into LDS at 40-50 GB/s per
+// CU (the persistent 256 x 256 GEMM: 47 GB/s), so a tile's time follows its
+// operand bytes, (rows_n + rows_m) * K.  At M = 1024, N = K = 4096 the
 // 256 x 256 tiling has 64 tiles of 2 MiB each (64 CUs busy for 45 us); the
 // 128 x 128 tiling has 256 tiles of 1 MiB.  The fp32 accumulators of a
 // 128 x 128 tile are 64 registers per lane and its four 64-K stages 68 KiB,
