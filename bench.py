@@ -19,7 +19,8 @@ N=K=4096 with the weights rotated through 48 copies so they do not sit in the
 quantizer, and one forward of the routed MoE layer at its full size);
 ``ceilings``, what this GPU sustains as measured by the calibration kernels
 of libmxfp8_calib.so (scaled-MFMA rate, 1 GiB HBM read rate, one 16 MiB read
-per launch, the time per launch of an empty kernel), with the headline GEMM's fraction of the measured MFMA rate
+per launch and one read of the W4A8 decode weight's 8.5 MiB per launch, the
+time per launch of an empty kernel), with the headline GEMM's fraction of the measured MFMA rate
 (``roofline.frac_of_measured``) and each sweep row's fraction of the
 measured read rate; ``cpu_baseline``, the CPU oracle timed on a bounded
 sample of the headline workload.  The untimed warm-up runs at least
@@ -213,6 +214,9 @@ def main():
             if floor and row.get("workload", "").startswith("decode M="):
                 # the weight read alone (16 MiB + scales) at the measured floor
                 row["pct_of_read_floor"] = round(100 * floor * (4096 * 4096 * (1 + 1 / 32)) / (16 << 20) / row["us"], 1)
+            if ceil.get("read_w4_4096x4096_us") and row.get("workload", "").startswith("decode W4A8 M="):
+                # the MXFP4 weight read alone, measured at its own size
+                row["pct_of_read_floor"] = round(100 * ceil["read_w4_4096x4096_us"] / row["us"], 1)
             if ceil.get("hbm_read_gbs") and "GB/s" in row:
                 row["pct_of_measured_hbm"] = round(100 * row["GB/s"] / ceil["hbm_read_gbs"], 1)
             if row.get("workload", "").startswith("single ") and ceil.get("launch_floor_us"):
@@ -284,21 +288,25 @@ def ceilings(torch, dev, stream):
         best = ms if best is None else min(best, ms)
     out["hbm_read_gbs"] = round(big.numel() / (best * 1e-3) / 1e9, 1)
     del big
-    # one 16 MiB read per launch over 48 rotated copies (> 3x the last-level
-    # cache), best of three grid sizes
-    n16 = 16 << 20
-    pool = torch.empty(48 * n16, dtype=torch.uint8, device=dev)
-    best = None
-    for blocks in (512, 1024, 2048):
-        for r in range(96):
-            lib.mxfp8_calib_read(pool.data_ptr() + (r % 48) * n16, n16, blocks, words.data_ptr(), sptr)
-        torch.cuda.synchronize()
-        ms = min(time_calls(lambda r: lib.mxfp8_calib_read(pool.data_ptr() + (r % 48) * n16, n16, blocks,
-                                                           words.data_ptr(), sptr), 480, stream, torch)
-                 for _ in range(3))
-        best = ms if best is None else min(best, ms)
-    out["read_16mib_us"] = round(best * 1e3, 3)
-    del pool
+    # one read of n16 bytes per launch over 48 rotated copies (> 3x the
+    # last-level cache at 16 MiB), best of three grid sizes
+    def read_floor_us(n16):
+        pool = torch.empty(48 * n16, dtype=torch.uint8, device=dev)
+        best = None
+        for blocks in (512, 1024, 2048):
+            for r in range(96):
+                lib.mxfp8_calib_read(pool.data_ptr() + (r % 48) * n16, n16, blocks, words.data_ptr(), sptr)
+            torch.cuda.synchronize()
+            ms = min(time_calls(lambda r: lib.mxfp8_calib_read(pool.data_ptr() + (r % 48) * n16, n16, blocks,
+                                                               words.data_ptr(), sptr), 480, stream, torch)
+                     for _ in range(3))
+            best = ms if best is None else min(best, ms)
+        del pool
+        return round(best * 1e3, 3)
+
+    out["read_16mib_us"] = read_floor_us(16 << 20)
+    # the MXFP4 weight of the W4A8 decode rows: 4096 x 4096 E2M1 + scales
+    out["read_w4_4096x4096_us"] = read_floor_us(4096 * 4096 // 2 + 4096 * 4096 // 32)
     # L2 -> CU: one workgroup per CU re-reading one 1 MiB buffer (served by
     # each die's L2 after the first pass), into registers and by direct
     # L2 -> LDS copies; GB/s per CU
